@@ -1,0 +1,182 @@
+"""Invariants and closed forms that hold for the oracle's outputs at any size:
+exactness family, dequantization error bound, layout equivalences, masked-row
+sentinels, and per-token == group quantization with G = K and eps = 0."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+F8 = torch.float8_e4m3fn
+
+
+def decode_e4m3(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(F8).to(torch.float64).numpy()
+
+
+def decode_codes(codes, out_dtype):
+    if out_dtype == "e4m3":
+        return decode_e4m3(codes)
+    return codes.view(np.int8).astype(np.float64)
+
+
+def scales_rowmajor(s, M, ng, fmt, layout):
+    """Scale tensor -> float64 [M, ng] (independent of the oracle's own writer)."""
+    if layout == "row":
+        if fmt == "f32":
+            return s.view(np.float32).reshape(M, ng).astype(np.float64)
+        return np.ldexp(1.0, s.reshape(M, ng).astype(np.int64) - 127)
+    Mp = (M + 3) // 4 * 4
+    if fmt == "f32":
+        return s.view(np.float32).reshape(ng, Mp)[:, :M].T.astype(np.float64)
+    W_ = (ng + 3) // 4
+    b = s.reshape(W_, Mp, 4)                  # word (c, m), byte j -> group 4c+j
+    out = np.empty((M, ng), dtype=np.float64)
+    for g in range(ng):
+        out[:, g] = np.ldexp(1.0, b[g // 4, :M, g % 4].astype(np.int64) - 127)
+    return out
+
+
+def ulp_e4m3(a):
+    a = np.abs(a)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.where(a >= 2.0 ** -6, 2.0 ** (e - 3), 2.0 ** -9)
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+@pytest.mark.parametrize("out_dtype", ["int8", "e4m3"])
+def test_exactness_family(G, out_dtype):
+    """Integers in [-8, 8] with power-of-two scales dequantize exactly
+    (the technique of the sglang #35593 page's unit test)."""
+    d = W.cfg5c(M=48, K=3584)
+    x, M, K = d["x"], d["M"], d["K"]
+    q, s = oracle.ptgq(x, "fp16", M, K, G, False, out_dtype, "ue8m0", "row")
+    deq = decode_codes(q, out_dtype).reshape(M, K // G, G) * \
+        scales_rowmajor(s, M, K // G, "ue8m0", "row")[:, :, None]
+    xf = x.view(np.float16).astype(np.float64).reshape(M, K // G, G)
+    assert np.array_equal(deq, xf)
+
+
+CASES = [(fmt, lay, od) for fmt in ("f32", "ue8m0") for lay in ("row", "col")
+         for od in ("e4m3", "int8")]
+
+
+@pytest.mark.parametrize("fmt,layout,out_dtype", CASES)
+@pytest.mark.parametrize("fuse", [False, True])
+def test_dequant_error_bound(fmt, layout, out_dtype, fuse):
+    """|decode(code) * scale - y| <= half an output ulp times the scale, plus,
+    for fp32 scales, the drift of the two fp32 roundings in y * fl(1/scale)."""
+    M, K, G = 37, 512, 128
+    x = W.normal_bf16(77, (M, 2 * K if fuse else K), factor_cols=[3, 200], factor=40.0)
+    q, s = oracle.ptgq(x, "bf16", M, K, G, fuse, out_dtype, fmt, layout)
+    xf = W.bf16_bits_to_f32(x).reshape(M, -1)
+    y = oracle.silu_mul(xf[:, :K], xf[:, K:]) if fuse else xf
+    y = y.astype(np.float64).reshape(M, K // G, G)
+    sc = scales_rowmajor(s, M, K // G, fmt, layout)[:, :, None]
+    deq = decode_codes(q, out_dtype).reshape(M, K // G, G) * sc
+    # v = fl(y * fl(1/s)) is within |y/s| * 2^-22 of y/s (two roundings), and the
+    # code within half an output ulp of v; UE8M0 multipliers are exact.
+    t = np.abs(y / sc)
+    drift = t * 2.0 ** -22 if fmt == "f32" else 0.0 * t
+    ulp = ulp_e4m3(t + drift) if out_dtype == "e4m3" else np.ones_like(t)
+    bound = (0.5 * ulp + drift) * sc
+    assert np.all(np.abs(deq - y) <= bound)
+    # and the scale is the group absmax over the format maximum (rounded)
+    qmax = 448.0 if out_dtype == "e4m3" else 127.0
+    amax = np.maximum(np.abs(y).max(axis=2), 1e-10)
+    r = (amax / qmax)[:, :, None]
+    if fmt == "f32":
+        assert np.all(np.abs(sc - r) <= r * 2.0 ** -23)
+    else:
+        assert np.all((sc >= r * (1 - 2.0 ** -23)) & (sc < 2 * r * (1 + 2.0 ** -23)))
+
+
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_layouts_hold_the_same_scales_and_pads_are_zero(fmt):
+    for M in (1, 3, 4, 5, 18):
+        for K, G in ((2048, 128), (384, 128), (640, 128), (96, 32)):
+            x = W.normal_bf16(M * 1000 + K, (M, K))
+            q1, s1 = oracle.ptgq(x, "bf16", M, K, G, False, "e4m3", fmt, "row")
+            q2, s2 = oracle.ptgq(x, "bf16", M, K, G, False, "e4m3", fmt, "col")
+            ng = K // G
+            assert np.array_equal(q1, q2)
+            assert np.array_equal(scales_rowmajor(s1, M, ng, fmt, "row"),
+                                  scales_rowmajor(s2, M, ng, fmt, "col"))
+            Mp = (M + 3) // 4 * 4
+            if fmt == "f32":
+                c = s2.view(np.float32).reshape(ng, Mp)
+                assert np.all(c[:, M:] == 0)
+            else:
+                b = s2.reshape((ng + 3) // 4, Mp, 4)
+                assert np.all(b[:, M:, :] == 0)
+                for g in range(ng, (ng + 3) // 4 * 4):
+                    assert np.all(b[g // 4, :, g % 4] == 0)
+
+
+@pytest.mark.parametrize("fmt,layout", [("ue8m0", "col"), ("f32", "row"), ("f32", "col"),
+                                        ("ue8m0", "row")])
+def test_masked_matches_flat_on_live_rows_and_keeps_sentinels(fmt, layout):
+    d = W.cfg4(seed=4100, E=6, T=21, K=256)
+    x, E, T, K, mm = d["x"], d["E"], d["T"], d["K"], d["masked_m"].copy()
+    mm[2] = -5          # negative counts as 0
+    mm[3] = T + 40      # above T counts as T
+    sb = oracle.scale_bytes(T, K, 128, fmt, layout)
+    q0 = np.full((E, T, K), 0x7F, np.uint8)
+    s0 = np.full(E * sb, 0xFF, np.uint8)
+    q, s = oracle.ptgq_masked(x, "bf16", E, T, K, 128, True, mm, "e4m3", fmt, layout,
+                              q_init=q0, s_init=s0)
+    ng = K // 128
+    for e in range(E):
+        live = int(min(max(mm[e], 0), T))
+        assert np.all(q[e, live:] == 0x7F)
+        se = s[e * sb:(e + 1) * sb]
+        if live:
+            qf, sf = oracle.ptgq(np.ascontiguousarray(x[e, :live]), "bf16", live, K, 128, True,
+                                 "e4m3", fmt, "row")
+            assert np.array_equal(q[e, :live], qf)
+            got = scales_rowmajor(se, T, ng, fmt, layout)[:live] if layout == "col" else \
+                scales_rowmajor(se[: live * ng * (4 if fmt == "f32" else 1)], live, ng, fmt, "row")
+            assert np.array_equal(got, scales_rowmajor(sf, live, ng, fmt, "row"))
+        # every scale slot of a dead row is untouched
+        per = 4 if fmt == "f32" else 1
+        if layout == "row":
+            assert np.all(se[live * ng * per:] == 0xFF)
+        elif fmt == "f32":
+            c = se.reshape(ng, -1, 4)
+            assert np.all(c[:, live:, :] == 0xFF)
+        else:
+            c = se.reshape((ng + 3) // 4, -1, 4)
+            assert np.all(c[:, live:, :] == 0xFF)
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp16"])
+def test_per_token_equals_group_quant_with_G_equal_K_and_no_floor(in_dtype):
+    M = 64
+    x = W.normal_bf16(9, (M, 128)) if in_dtype == "bf16" else W.normal_fp16(9, (M, 128))
+    x[5] = 0                                  # a zero row: scale 0, codes 0
+    qt, st = oracle.ptq_fp8(x, in_dtype, M, 128)
+    qg, sg = oracle.ptgq(x, in_dtype, M, 128, 128, False, "e4m3", "f32", "row", eps=0.0)
+    assert np.array_equal(qt, qg)
+    assert np.array_equal(st.view(np.uint32), sg.view(np.uint32))
+    assert st[5] == 0 and np.all(qt[5] == 0)
+
+
+def test_per_token_fp32_input_and_dequant_bound():
+    M, K = 9, 1076
+    x = W.normal_f32(5, (M, K)) * np.float32(3.0)
+    q, s = oracle.ptq_fp8(x, "fp32", M, K)
+    assert np.array_equal(s, (np.abs(x).max(axis=1) / np.float32(448.0)).astype(np.float32))
+    deq = decode_e4m3(q) * s[:, None].astype(np.float64)
+    t = np.abs(x.astype(np.float64) / s[:, None])
+    bound = (0.5 * ulp_e4m3(t * (1 + 2.0 ** -22)) + t * 2.0 ** -22) * s[:, None]
+    assert np.all(np.abs(deq - x) <= bound)
+
+
+def test_rejects_bad_arguments():
+    x = np.zeros((2, 100), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.ptgq(x, "bf16", 2, 100, 128, False, "e4m3", "f32", "row")   # K % G != 0
+    x = np.zeros((2, 96), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.ptgq(x, "bf16", 2, 96, 48, False, "e4m3", "f32", "row")    # G not a power of 2
