@@ -1,0 +1,196 @@
+"""Python binding of libptgq (per-token-group 8-bit activation quantization on
+MI355X / gfx950).
+
+Argument marshalling only: every function below passes device pointers, sizes
+and the current HIP stream straight to the C ABI declared in include/ptgq.h,
+under the same names.  PyTorch supplies device memory and streams.  There is
+no fallback: if the library was not built, importing this package's functions
+raises.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libptgq.so")
+
+PTGQ_OK, PTGQ_EINVAL, PTGQ_EALIGN, PTGQ_EUNSUPPORTED, PTGQ_ELAUNCH, PTGQ_EDEVICE = 0, -1, -2, -3, -4, -5
+PTGQ_BF16, PTGQ_FP16, PTGQ_FP32 = 0, 1, 2
+PTGQ_E4M3, PTGQ_INT8 = 0, 1
+PTGQ_SCALE_F32, PTGQ_SCALE_UE8M0 = 0, 1
+PTGQ_ROW_MAJOR, PTGQ_COL_MAJOR = 0, 1
+
+IN_DTYPES = {"bf16": PTGQ_BF16, "fp16": PTGQ_FP16, "fp32": PTGQ_FP32}
+OUT_DTYPES = {"e4m3": PTGQ_E4M3, "int8": PTGQ_INT8}
+SCALE_FMTS = {"f32": PTGQ_SCALE_F32, "ue8m0": PTGQ_SCALE_UE8M0}
+SCALE_LAYOUTS = {"row": PTGQ_ROW_MAJOR, "col": PTGQ_COL_MAJOR}
+
+EXPORTS = ("ptgq_quant", "ptgq_quant_masked", "ptq_quant_fp8", "ptgq_scale_bytes",
+           "ptgq_status_string", "ptgq_init", "ptgq_probe_e4m3", "ptgq_probe_silu_mul",
+           "ptgq_set_tuning")
+
+
+class PtgqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libptgq.so (raises if it is missing: there is no other path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libptgq.so not built at {path}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    i32, i64, f32, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    lib.ptgq_quant.argtypes = [vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+    lib.ptgq_quant.restype = i32
+    lib.ptgq_quant_masked.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, i64, i32, i32, i32,
+                                      f32, vp, vp, vp]
+    lib.ptgq_quant_masked.restype = i32
+    lib.ptq_quant_fp8.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    lib.ptq_quant_fp8.restype = i32
+    lib.ptgq_scale_bytes.argtypes = [i64, i64, i32, i32, i32]
+    lib.ptgq_scale_bytes.restype = ctypes.c_size_t
+    lib.ptgq_status_string.argtypes = [i32]
+    lib.ptgq_status_string.restype = ctypes.c_char_p
+    lib.ptgq_init.argtypes = [i32]
+    lib.ptgq_init.restype = i32
+    lib.ptgq_probe_e4m3.argtypes = [vp, vp, i64, vp]
+    lib.ptgq_probe_e4m3.restype = i32
+    lib.ptgq_probe_silu_mul.argtypes = [vp, vp, i32, vp, i64, vp]
+    lib.ptgq_probe_silu_mul.restype = i32
+    lib.ptgq_set_tuning.argtypes = [i32, i64]
+    lib.ptgq_set_tuning.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or a raw integer address."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _enum(v, table):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+_IN_SIZE = {PTGQ_BF16: 2, PTGQ_FP16: 2, PTGQ_FP32: 4}
+
+
+def _need(t, nbytes, fn, name):
+    """Host-side guard: a tensor argument must hold every byte the call touches
+    (raw integer addresses are passed through unchecked)."""
+    if t is None or isinstance(t, int):
+        return
+    if t.device.type != "cuda":
+        raise ValueError(f"{fn}: {name} must be a device tensor, got one on {t.device}")
+    have = t.numel() * t.element_size()
+    if not t.is_contiguous() or have < nbytes:
+        raise ValueError(f"{fn}: {name} needs {nbytes} contiguous bytes, has {have}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _check(fn, rc):
+    if rc != PTGQ_OK:
+        raise PtgqError(fn, rc)
+    return rc
+
+
+def status_string(status: int) -> str:
+    return load_library().ptgq_status_string(int(status)).decode()
+
+
+def ptgq_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def ptgq_scale_bytes(rows, K, group_size, scale_fmt, scale_layout) -> int:
+    return int(load_library().ptgq_scale_bytes(rows, K, group_size, _enum(scale_fmt, SCALE_FMTS),
+                                               _enum(scale_layout, SCALE_LAYOUTS)))
+
+
+def ptgq_init(device: int = 0) -> int:
+    return _check("ptgq_init", load_library().ptgq_init(int(device)))
+
+
+def ptgq_set_tuning(knob: int, value: int) -> int:
+    return _check("ptgq_set_tuning", load_library().ptgq_set_tuning(int(knob), int(value)))
+
+
+def ptgq_quant(x, in_dtype, M, K, group_size, fuse_silu_mul, out_dtype, scale_fmt, scale_layout,
+               eps, q, s, stream=None, check=True):
+    ind, fmt, lay = _enum(in_dtype, IN_DTYPES), _enum(scale_fmt, SCALE_FMTS), _enum(scale_layout, SCALE_LAYOUTS)
+    if M > 0 and K > 0 and ind in _IN_SIZE:
+        _need(x, M * K * (2 if fuse_silu_mul else 1) * _IN_SIZE[ind], "ptgq_quant", "x")
+        _need(q, M * K, "ptgq_quant", "q")
+        _need(s, ptgq_scale_bytes(M, K, group_size, fmt, lay), "ptgq_quant", "s")
+    rc = load_library().ptgq_quant(_ptr(x), _enum(in_dtype, IN_DTYPES), M, K, group_size,
+                                   int(bool(fuse_silu_mul)), _enum(out_dtype, OUT_DTYPES),
+                                   _enum(scale_fmt, SCALE_FMTS), _enum(scale_layout, SCALE_LAYOUTS),
+                                   float(eps), _ptr(q), _ptr(s), _stream(stream))
+    return _check("ptgq_quant", rc) if check else rc
+
+
+def ptgq_quant_masked(x, in_dtype, E, tokens_pad, K, group_size, fuse_silu_mul, masked_m,
+                      expected_m, out_dtype, scale_fmt, scale_layout, eps, q, s, stream=None,
+                      check=True):
+    ind, fmt, lay = _enum(in_dtype, IN_DTYPES), _enum(scale_fmt, SCALE_FMTS), _enum(scale_layout, SCALE_LAYOUTS)
+    if E > 0 and tokens_pad > 0 and K > 0 and ind in _IN_SIZE:
+        fn = "ptgq_quant_masked"
+        _need(x, E * tokens_pad * K * (2 if fuse_silu_mul else 1) * _IN_SIZE[ind], fn, "x")
+        _need(q, E * tokens_pad * K, fn, "q")
+        _need(s, E * ptgq_scale_bytes(tokens_pad, K, group_size, fmt, lay), fn, "s")
+        _need(masked_m, 4 * E, fn, "masked_m")
+    rc = load_library().ptgq_quant_masked(
+        _ptr(x), _enum(in_dtype, IN_DTYPES), E, tokens_pad, K, group_size,
+        int(bool(fuse_silu_mul)), _ptr(masked_m), int(expected_m), _enum(out_dtype, OUT_DTYPES),
+        _enum(scale_fmt, SCALE_FMTS), _enum(scale_layout, SCALE_LAYOUTS), float(eps), _ptr(q),
+        _ptr(s), _stream(stream))
+    return _check("ptgq_quant_masked", rc) if check else rc
+
+
+def ptq_quant_fp8(x, in_dtype, M, K, q, s, stream=None, check=True):
+    ind = _enum(in_dtype, IN_DTYPES)
+    if M > 0 and K > 0 and ind in _IN_SIZE:
+        _need(x, M * K * _IN_SIZE[ind], "ptq_quant_fp8", "x")
+        _need(q, M * K, "ptq_quant_fp8", "q")
+        _need(s, 4 * M, "ptq_quant_fp8", "s")
+    rc = load_library().ptq_quant_fp8(_ptr(x), _enum(in_dtype, IN_DTYPES), M, K, _ptr(q), _ptr(s),
+                                      _stream(stream))
+    return _check("ptq_quant_fp8", rc) if check else rc
+
+
+def ptgq_probe_e4m3(v, out, n, stream=None, check=True):
+    if n > 0:
+        _need(v, 4 * n, "ptgq_probe_e4m3", "v")
+        _need(out, n, "ptgq_probe_e4m3", "out")
+    rc = load_library().ptgq_probe_e4m3(_ptr(v), _ptr(out), n, _stream(stream))
+    return _check("ptgq_probe_e4m3", rc) if check else rc
+
+
+def ptgq_probe_silu_mul(g, u, in_dtype, out, n, stream=None, check=True):
+    if n > 0:
+        _need(g, 2 * n, "ptgq_probe_silu_mul", "g")
+        _need(u, 2 * n, "ptgq_probe_silu_mul", "u")
+        _need(out, 4 * n, "ptgq_probe_silu_mul", "out")
+    rc = load_library().ptgq_probe_silu_mul(_ptr(g), _ptr(u), _enum(in_dtype, IN_DTYPES), _ptr(out),
+                                            n, _stream(stream))
+    return _check("ptgq_probe_silu_mul", rc) if check else rc

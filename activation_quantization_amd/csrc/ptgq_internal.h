@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI layer (ptgq_api.cpp) and the kernels
+// (ptgq_kernels.hip).  Not installed; not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace ptgq {
+
+enum : int { IN_BF16 = 0, IN_FP16 = 1, IN_FP32 = 2 };
+enum : int { OUT_E4M3 = 0, OUT_INT8 = 1 };
+enum : int { SCALE_F32 = 0, SCALE_UE8M0 = 1 };
+enum : int { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
+
+// Elements of one "slab": one 16-byte load per lane across a 64-lane wave
+// (8 sixteen-bit elements per lane).  Every group-quant task is 1..4 slabs of
+// one row.
+constexpr int kSlab = 512;
+constexpr int kMaxSlabsPerTask = 4;
+
+// Arguments of the group-quantization kernels (flat and masked).  All shape
+// scalars are computed on the host; the device only indexes.
+struct GroupArgs {
+    const void *x;            // input base (16-bit patterns)
+    uint8_t *q;               // codes base
+    void *s;                  // scale tensor base
+    const int32_t *masked_m;  // masked: live rows per expert; flat: nullptr
+    int64_t rows;             // flat: M; masked: tokens_pad
+    int64_t K;                // output row width
+    int64_t in_stride;        // input row stride in elements (K, or 2K when fused)
+    int64_t ng;               // groups per row, K / G
+    int64_t rows_pad;         // ceil(rows / 4) * 4 (column-major scales)
+    int64_t x_expert_stride;  // masked: elements per expert of x
+    int64_t q_expert_stride;  // masked: bytes per expert of q
+    int64_t s_expert_stride;  // masked: bytes per expert of s
+    float eps;                // amax floor
+    int32_t spr;              // slabs per row, ceil(K / kSlab)
+    int32_t U;                // slabs per task, 1..kMaxSlabsPerTask
+    int32_t tpr;              // tasks per row, ceil(spr / U)
+    int32_t n_tasks;          // flat: rows * tpr
+    int32_t scale_fmt;        // SCALE_F32 / SCALE_UE8M0
+    int32_t scale_layout;     // LAYOUT_ROW / LAYOUT_COL
+    int32_t blocks_per_expert;// masked: blocks given to each expert
+    int32_t pad_cols;         // flat column-major: 4-byte columns whose pad rows
+                              // are zeroed (ceil(ng/4) or ng); 0 = none
+};
+
+// Arguments of the whole-row per-token kernels.
+struct TokenArgs {
+    const void *x;
+    uint8_t *q;
+    float *s;
+    int64_t M;
+    int64_t K;
+    int32_t nv;               // vectors per row (row bytes / vector bytes)
+};
+
+enum TokenMode : int { TOKEN_WAVE = 0, TOKEN_BLOCK = 1, TOKEN_BLOCK_LOOP = 2 };
+
+// Launchers (defined in ptgq_kernels.hip).  They return the hipError_t of the
+// launch.  `grid`/`block` are chosen by the caller.
+hipError_t launch_group(const GroupArgs &a, int in_dtype, int G, bool fuse, int out_dtype,
+                        bool masked, unsigned grid, unsigned block, hipStream_t stream);
+hipError_t launch_token(const TokenArgs &a, int in_dtype, int vec_bytes, TokenMode mode,
+                        int nv_per_lane, unsigned grid, unsigned block, hipStream_t stream);
+hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_t stream);
+hipError_t launch_probe_silu(const void *g, const void *u, int in_dtype, float *out, int64_t n,
+                             hipStream_t stream);
+
+}  // namespace ptgq

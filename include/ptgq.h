@@ -1,0 +1,207 @@
+/*
+ * ptgq.h - per-token-group 8-bit activation quantization on MI355X (gfx950).
+ *
+ * C ABI of libptgq.so.  Plain pointers and sizes only.
+ *
+ * What the library computes (the method of the pages this library follows):
+ *   for every row and every contiguous group of G elements of that row,
+ *     amax  = max |y|                          (y = x, or silu(gate) * up)
+ *     r     = max(amax, eps) / qmax            (qmax 448 for e4m3, 127 for int8;
+ *                                               IEEE fp32 division)
+ *     scale = r            (fp32 format)       multiplier inv = 1 / r (IEEE)
+ *           | 2^ceil(log2 r) (UE8M0 format)    stored as the biased exponent byte
+ *                                               e; multiplier 2^(127-e), exact
+ *     code  = narrow(y * inv)                  round-to-nearest-even, saturated
+ *                                               (e4m3: +-448; int8: [-128,127]);
+ *                                               a negative value rounding to 0
+ *                                               gives e4m3 code 0x80
+ *   Sources: sglang #30924 review page, implementation breakdown (the trait
+ *   set: in/out dtype, group size, fp32 or UE8M0 scale, row- or column-major
+ *   scale, fused silu_and_mul, flat or masked schedule) and key source
+ *   snippets (ref_fp8_ue8m0); sglang #27449 PR body, summary (group sizes,
+ *   scale formats, fused silu+mul, masked scheduler); sglang #34257 review
+ *   page, key source snippets (per-token kernel, reciprocal multiply,
+ *   saturating narrowing); vllm #41326 review page, key source snippets
+ *   (packed column-major UE8M0 words).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or keeps a tensor; outputs are written in
+ *     place.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous on that stream and never synchronize the host, so they may
+ *     be captured into a HIP graph.  The first call on a device (or ptgq_init)
+ *     queries the device's compute-unit count; no other host work happens.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     negative return value means nothing was launched and nothing written.
+ *   - Sizes are int64.  A call with zero rows (M == 0, E == 0, or K == 0)
+ *     returns PTGQ_OK and launches nothing.
+ *   - Inputs must not alias outputs.  Concurrent calls writing the same
+ *     outputs race, as any two kernels would.
+ *   - NaN or infinite inputs give unspecified (but in-bounds) outputs.
+ *
+ * Scale tensor layouts (ng = K / G groups per row, rows_pad = ceil(rows/4)*4):
+ *   PTGQ_ROW_MAJOR + PTGQ_SCALE_F32    float   [rows][ng]
+ *   PTGQ_ROW_MAJOR + PTGQ_SCALE_UE8M0  uint8   [rows][ng]
+ *   PTGQ_COL_MAJOR + PTGQ_SCALE_F32    float   [ng][rows_pad]
+ *   PTGQ_COL_MAJOR + PTGQ_SCALE_UE8M0  uint32  [ceil(ng/4)][rows_pad]; group g
+ *                  of row m is byte g%4 (little-endian) of word
+ *                  (g/4)*rows_pad + m  (vllm #41326 review page, key source
+ *                  snippets, all-zero test; sglang #35593 review page,
+ *                  implementation breakdown: column-major [E, M, hidden/128])
+ *   In flat calls the column-major pad slots (rows rows..rows_pad-1) and the
+ *   unused bytes of a partial packed word are written as zero.
+ */
+#ifndef PTGQ_H
+#define PTGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported symbols of libptgq.so (everything else in it is hidden). */
+#if defined(__GNUC__)
+#define PTGQ_API __attribute__((visibility("default")))
+#else
+#define PTGQ_API
+#endif
+
+/* Return codes. */
+enum ptgq_status {
+    PTGQ_OK = 0,
+    PTGQ_EINVAL = -1,       /* a size, enum or pointer argument is invalid      */
+    PTGQ_EALIGN = -2,       /* a pointer is not aligned as required            */
+    PTGQ_EUNSUPPORTED = -3, /* valid arguments, combination not implemented    */
+    PTGQ_ELAUNCH = -4,      /* the HIP launch failed (hipGetLastError)          */
+    PTGQ_EDEVICE = -5       /* no usable HIP device / device query failed       */
+};
+
+enum ptgq_in_dtype { PTGQ_BF16 = 0, PTGQ_FP16 = 1, PTGQ_FP32 = 2 };
+enum ptgq_out_dtype { PTGQ_E4M3 = 0, PTGQ_INT8 = 1 };
+enum ptgq_scale_fmt { PTGQ_SCALE_F32 = 0, PTGQ_SCALE_UE8M0 = 1 };
+enum ptgq_scale_layout { PTGQ_ROW_MAJOR = 0, PTGQ_COL_MAJOR = 1 };
+
+/*
+ * ptgq_quant - flat per-token-group quantization of x [M, K] (or of
+ * silu(gate) * up for x = [M, 2K] = gate | up when fuse_silu_mul != 0).
+ *
+ *   x          device, in_dtype (PTGQ_BF16 or PTGQ_FP16), row-major contiguous
+ *              [M, K] or [M, 2K]; 16-byte aligned.
+ *   group_size G in {16, 32, 64, 128}; K % G == 0.
+ *   out_dtype  PTGQ_E4M3 (OCP e4m3fn codes) or PTGQ_INT8 (two's complement).
+ *   scale_fmt, scale_layout  see the layouts above.
+ *   eps        floor of the group absmax (finite, >= 0; e.g. 1e-10).
+ *   q          device uint8 [M, K] codes; 16-byte aligned.
+ *   s          device scale tensor of ptgq_scale_bytes(M, K, G, fmt, layout)
+ *              bytes; 4-byte aligned.
+ * Sources: sglang #30924 review page, implementation breakdown (flat
+ * schedule); sglang #27449 PR body, summary (naive scheduler over [M, K]).
+ * Errors: PTGQ_EINVAL (M < 0, K < 0, G not allowed, K % G, bad enum, NULL
+ * pointer with M*K > 0, eps not finite or negative), PTGQ_EALIGN,
+ * PTGQ_ELAUNCH, PTGQ_EDEVICE.
+ */
+PTGQ_API int ptgq_quant(const void *x, int in_dtype, int64_t M, int64_t K, int group_size,
+               int fuse_silu_mul, int out_dtype, int scale_fmt, int scale_layout, float eps,
+               void *q, void *s, void *stream);
+
+/*
+ * ptgq_quant_masked - the masked expert-parallel MoE layout.
+ *
+ *   x          device [E, tokens_pad, K] (or [E, tokens_pad, 2K] fused),
+ *              in_dtype as above; 16-byte aligned.
+ *   masked_m   device int32 [E]: expert e quantizes its rows
+ *              t < min(max(masked_m[e], 0), tokens_pad).  Read on the device;
+ *              the host never waits for it.
+ *   expected_m host hint of the typical masked_m (<= 0: unknown).  It only
+ *              sizes the launch; results never depend on it.
+ *   q          device uint8 [E, tokens_pad, K]; 16-byte aligned.
+ *   s          device, E consecutive per-expert scale tensors, each of
+ *              ptgq_scale_bytes(tokens_pad, K, G, fmt, layout) bytes (so the
+ *              column-major form is [E][ng or ceil(ng/4)][pad4(tokens_pad)]).
+ *   Rows at or past masked_m are neither read nor written, in q or in s
+ *   (column-major pad slots included): the caller's contents stay.
+ * Sources: sglang #30924 review page, implementation breakdown (masked_m and
+ * expected_m); sglang #27449 PR body, summary and validation (masked layout
+ * scheduler, [num_experts, tokens_pad, hidden*2] with silu+mul); sglang
+ * #35593 review page, key source snippets (rows past masked_m untouched).
+ * Errors: as ptgq_quant, plus PTGQ_EINVAL for E < 0, tokens_pad < 0 or a NULL
+ * masked_m with E > 0.
+ */
+PTGQ_API int ptgq_quant_masked(const void *x, int in_dtype, int64_t E, int64_t tokens_pad, int64_t K,
+                      int group_size, int fuse_silu_mul, const int32_t *masked_m,
+                      int64_t expected_m, int out_dtype, int scale_fmt, int scale_layout,
+                      float eps, void *q, void *s, void *stream);
+
+/*
+ * ptq_quant_fp8 - whole-row per-token e4m3: scale[m] = max_k |x[m,k]| / 448
+ * (no floor), multiplier 0 when the scale is 0, codes narrowed with
+ * saturation.
+ *
+ *   x   device [M, K] in_dtype in {PTGQ_BF16, PTGQ_FP16, PTGQ_FP32},
+ *       row-major contiguous; 16-byte aligned.  K % 4 == 0.
+ *   q   device uint8 [M, K] e4m3 codes; 16-byte aligned.
+ *   s   device float [M]; 4-byte aligned.
+ * Sources: sglang #34257 review page, key source snippets (warp kernel and
+ * its dispatch by token count), implementation breakdown (hidden % 4 == 0).
+ * Errors: PTGQ_EINVAL (M < 0, K < 0, K % 4, bad dtype, NULL pointer),
+ * PTGQ_EALIGN, PTGQ_ELAUNCH, PTGQ_EDEVICE.
+ */
+PTGQ_API int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, float *s,
+                  void *stream);
+
+/*
+ * ptgq_scale_bytes - size in bytes of the scale tensor for `rows` rows of K
+ * elements in groups of group_size, in the given format and layout (see the
+ * layout table above).  Returns 0 for invalid arguments.  Host only; no
+ * device access.
+ */
+PTGQ_API size_t ptgq_scale_bytes(int64_t rows, int64_t K, int group_size, int scale_fmt,
+                        int scale_layout);
+
+/* ptgq_status_string - static English text of a return code.  Host only. */
+PTGQ_API const char *ptgq_status_string(int status);
+
+/*
+ * ptgq_init - optional: make `device` (a HIP ordinal) ready, querying its
+ * compute-unit count now rather than at the first call on it.  Calls that
+ * are captured into a HIP graph should follow one ptgq_init (or one ordinary
+ * call) on their device.  Returns PTGQ_OK or PTGQ_EDEVICE.
+ */
+PTGQ_API int ptgq_init(int device);
+
+/*
+ * Single-step device probes, for checking the device arithmetic against
+ * a reference over whole input spaces.  They run exactly the device code the
+ * quantization kernels use for that step.
+ *
+ * ptgq_probe_e4m3: out[i] = e4m3 code of v[i] (round-to-nearest-even,
+ *   saturated to +-448, signed zero kept).  v device float [n], out device
+ *   uint8 [n]; both 4-byte aligned.
+ * ptgq_probe_silu_mul: out[i] = silu(g[i]) * u[i] in fp32, where g, u are
+ *   device arrays of in_dtype (PTGQ_BF16 or PTGQ_FP16) bit patterns [n]
+ *   and out is device float [n].
+ * Errors: PTGQ_EINVAL (n < 0, NULL pointer, bad dtype), PTGQ_ELAUNCH.
+ */
+PTGQ_API int ptgq_probe_e4m3(const float *v, uint8_t *out, int64_t n, void *stream);
+PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, float *out, int64_t n,
+                        void *stream);
+
+/*
+ * ptgq_set_tuning - diagnostics only: override one decision of the launch
+ * geometry chooser for the whole process (value -1 restores the automatic
+ * choice).  Knobs: 0 slabs per task (1..4; one slab = 512 elements of a row),
+ * 1 waves per block (1..4), 2 resident blocks per compute unit (grid cap),
+ * 3 per-token mode (0 one wave per row, 1 one block per row, 2 two-pass
+ * block).  Results never depend on these; only speed does.  Not synchronized
+ * with calls running on other host threads.  Returns PTGQ_OK or PTGQ_EINVAL.
+ */
+PTGQ_API int ptgq_set_tuning(int knob, int64_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTGQ_H */

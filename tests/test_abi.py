@@ -1,0 +1,179 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/ptgq.h declares, and rejects invalid arguments on the host (no device
+is touched, nothing is launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import activation_quantization_amd as aq
+import oracle
+from activation_quantization_amd import build as libbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if libbuild.is_stale():
+        libbuild.build()
+    return aq.load_library()
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "ptgq.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"PTGQ_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(aq.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # nothing but the C ABI is visible
+    out = os.popen(f"nm -D --defined-only {aq.LIB_PATH}").read()
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == declared_functions()
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert aq.status_string(st)
+    assert aq.status_string(7) == "unknown status"
+
+
+@pytest.mark.parametrize("rows,K,G,fmt,lay", [
+    (64, 2048, 128, "f32", "row"), (5, 7168, 128, "ue8m0", "col"), (1, 128, 128, "ue8m0", "col"),
+    (7, 3584, 16, "f32", "col"), (9, 640, 64, "ue8m0", "row"), (0, 2048, 128, "f32", "col"),
+    (384, 2048, 128, "ue8m0", "col"), (3, 96, 32, "ue8m0", "col")])
+def test_scale_bytes_matches_the_oracle(lib, rows, K, G, fmt, lay):
+    assert aq.ptgq_scale_bytes(rows, K, G, fmt, lay) == oracle.scale_bytes(rows, K, G, fmt, lay)
+
+
+def test_scale_bytes_rejects_invalid(lib):
+    assert aq.ptgq_scale_bytes(4, 100, 128, "f32", "row") == 0
+    assert aq.ptgq_scale_bytes(4, 96, 48, "f32", "row") == 0
+    assert aq.ptgq_scale_bytes(-1, 128, 128, "f32", "row") == 0
+    assert aq.ptgq_scale_bytes(4, 128, 128, 7, 0) == 0
+
+
+A16 = 0x10000          # a 16-byte aligned fake address (never dereferenced)
+
+
+def quant(**kw):
+    args = dict(x=A16, in_dtype="bf16", M=4, K=256, group_size=128, fuse_silu_mul=False,
+                out_dtype="e4m3", scale_fmt="ue8m0", scale_layout="col", eps=1e-10, q=A16 * 2,
+                s=A16 * 3, stream=0, check=False)
+    args.update(kw)
+    return aq.ptgq_quant(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(group_size=48), aq.PTGQ_EINVAL),
+    (dict(group_size=256), aq.PTGQ_EINVAL),
+    (dict(K=200), aq.PTGQ_EINVAL),
+    (dict(M=-1), aq.PTGQ_EINVAL),
+    (dict(K=-128), aq.PTGQ_EINVAL),
+    (dict(in_dtype=2), aq.PTGQ_EINVAL),       # fp32 input only for per-token
+    (dict(in_dtype=9), aq.PTGQ_EINVAL),
+    (dict(out_dtype=3), aq.PTGQ_EINVAL),
+    (dict(scale_fmt=2), aq.PTGQ_EINVAL),
+    (dict(scale_layout=5), aq.PTGQ_EINVAL),
+    (dict(eps=float("nan")), aq.PTGQ_EINVAL),
+    (dict(eps=-1.0), aq.PTGQ_EINVAL),
+    (dict(eps=float("inf")), aq.PTGQ_EINVAL),
+    (dict(x=0), aq.PTGQ_EINVAL),
+    (dict(q=0), aq.PTGQ_EINVAL),
+    (dict(s=0), aq.PTGQ_EINVAL),
+    (dict(x=A16 + 8), aq.PTGQ_EALIGN),
+    (dict(q=A16 + 4), aq.PTGQ_EALIGN),
+    (dict(s=A16 + 2), aq.PTGQ_EALIGN),
+    (dict(M=0, x=0, q=0, s=0), aq.PTGQ_OK),   # nothing to do: no launch
+    (dict(K=0, x=0, q=0, s=0), aq.PTGQ_OK),
+])
+def test_ptgq_quant_validation(lib, kw, status):
+    assert quant(**kw) == status
+
+
+def masked(**kw):
+    args = dict(x=A16, in_dtype="bf16", E=4, tokens_pad=32, K=256, group_size=128,
+                fuse_silu_mul=True, masked_m=A16 * 4, expected_m=0, out_dtype="e4m3",
+                scale_fmt="ue8m0", scale_layout="col", eps=1e-10, q=A16 * 2, s=A16 * 3,
+                stream=0, check=False)
+    args.update(kw)
+    return aq.ptgq_quant_masked(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=-1), aq.PTGQ_EINVAL),
+    (dict(tokens_pad=-3), aq.PTGQ_EINVAL),
+    (dict(masked_m=0), aq.PTGQ_EINVAL),
+    (dict(masked_m=A16 + 2), aq.PTGQ_EALIGN),
+    (dict(group_size=8), aq.PTGQ_EINVAL),
+    (dict(x=A16 + 4), aq.PTGQ_EALIGN),
+    (dict(E=0, x=0, q=0, s=0, masked_m=0), aq.PTGQ_OK),
+    (dict(tokens_pad=0, x=0, q=0, s=0, masked_m=0), aq.PTGQ_OK),
+])
+def test_ptgq_quant_masked_validation(lib, kw, status):
+    assert masked(**kw) == status
+
+
+def per_token(**kw):
+    args = dict(x=A16, in_dtype="bf16", M=4, K=1076, q=A16 * 2, s=A16 * 3, stream=0, check=False)
+    args.update(kw)
+    return aq.ptq_quant_fp8(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=1074), aq.PTGQ_EINVAL),           # K % 4 != 0
+    (dict(in_dtype=5), aq.PTGQ_EINVAL),
+    (dict(M=-2), aq.PTGQ_EINVAL),
+    (dict(x=0), aq.PTGQ_EINVAL),
+    (dict(s=0), aq.PTGQ_EINVAL),
+    (dict(q=A16 + 1), aq.PTGQ_EALIGN),
+    (dict(s=A16 + 1), aq.PTGQ_EALIGN),
+    (dict(M=0, x=0, q=0, s=0), aq.PTGQ_OK),
+])
+def test_ptq_quant_fp8_validation(lib, kw, status):
+    assert per_token(**kw) == status
+
+
+def test_probe_validation(lib):
+    assert aq.ptgq_probe_e4m3(0, A16, 5, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_e4m3(A16, A16, -1, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_e4m3(0, 0, 0, stream=0, check=False) == aq.PTGQ_OK
+    assert aq.ptgq_probe_silu_mul(A16, A16, 2, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
+    with pytest.raises(aq.PtgqError):
+        aq.ptgq_set_tuning(9, 1)
+
+
+def test_binding_raises_on_error(lib):
+    with pytest.raises(aq.PtgqError) as ei:
+        aq.ptgq_quant(A16, "bf16", 4, 200, 128, False, "e4m3", "f32", "row", 1e-10, A16, A16,
+                      stream=0)
+    assert ei.value.status == aq.PTGQ_EINVAL
+
+
+def test_without_gpu_a_valid_call_reports_no_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert quant() == aq.PTGQ_EDEVICE
+    assert lib.ptgq_init(0) == aq.PTGQ_EDEVICE
+
+
+def test_binding_refuses_undersized_tensors(lib):
+    import torch
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    q = torch.zeros((4, 255), dtype=torch.uint8)
+    s = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        aq.ptgq_quant(x, "bf16", 4, 256, 128, False, "e4m3", "ue8m0", "col", 1e-10, q, s, stream=0)
+    with pytest.raises(ValueError):
+        aq.ptq_quant_fp8(x, "bf16", 5, 256, torch.zeros((5, 256), dtype=torch.uint8),
+                         torch.zeros(5), stream=0)

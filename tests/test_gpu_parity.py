@@ -1,0 +1,213 @@
+"""Bit-exact parity of the HIP path (through the C ABI) with the CPU oracle,
+on the five seeded workloads at their full sizes and on a sweep of every trait
+combination at small ragged shapes."""
+import numpy as np
+import pytest
+import torch
+
+import activation_quantization_amd as aq
+import oracle
+import workloads as W
+from gpu_util import compare, run_flat, run_masked, run_per_token, to_dev, DEV
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------ the workloads
+
+def test_cfg1_plain_fp32_rowmajor():
+    d = W.cfg1()
+    args = (d["x"], "bf16", d["M"], d["K"], d["G"], False, "e4m3", "f32", "row")
+    compare("cfg1", *run_flat(*args), *oracle.ptgq(*args, eps=d["eps"]))
+
+
+@pytest.mark.parametrize("M", W.CFG2_M)
+def test_cfg2_deepseek_shape_ue8m0_colmajor(M):
+    d = W.cfg2(M)
+    args = (d["x"], "bf16", M, d["K"], 128, False, "e4m3", "ue8m0", "col")
+    compare(f"cfg2 M={M}", *run_flat(*args), *oracle.ptgq(*args, eps=d["eps"]))
+
+
+@pytest.mark.parametrize("M", W.CFG3_M)
+def test_cfg3_fused_silu_mul(M):
+    d = W.cfg3(M)
+    args = (d["x"], "bf16", M, d["K"], 128, True, "e4m3", "ue8m0", "col")
+    compare(f"cfg3 M={M}", *run_flat(*args), *oracle.ptgq(*args, eps=d["eps"]))
+
+
+@pytest.mark.parametrize("expected_m", [0, 1, 64, 384])
+def test_cfg4_masked_moe(expected_m):
+    d = W.cfg4()
+    E, T, K, mm = d["E"], d["T"], d["K"], d["masked_m"]
+    gq, gs = run_masked(d["x"], "bf16", E, T, K, 128, True, mm, expected_m, "e4m3", "ue8m0", "col")
+    sb = aq.ptgq_scale_bytes(T, K, 128, "ue8m0", "col")
+    rq, rs = oracle.ptgq_masked(d["x"], "bf16", E, T, K, 128, True, mm, "e4m3", "ue8m0", "col",
+                                q_init=np.full((E, T, K), 0x7F, np.uint8),
+                                s_init=np.full(E * sb, 0xFF, np.uint8))
+    compare(f"cfg4 expected_m={expected_m} live={int(mm.sum())}", gq, gs, rq, rs)
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+def test_cfg5a_fp16_int8_group_sweep(G):
+    d = W.cfg5()
+    args = (d["x"], "fp16", d["M"], d["K"], G, False, "int8", "f32", "row")
+    compare(f"cfg5a G={G}", *run_flat(*args), *oracle.ptgq(*args, eps=d["eps"]))
+
+
+def test_cfg5b_per_token_fp8():
+    d = W.cfg5()
+    gq, gs = run_per_token(d["x"], "fp16", d["M"], d["K"])
+    rq, rs = oracle.ptq_fp8(d["x"], "fp16", d["M"], d["K"])
+    compare("cfg5b", gq, gs, rq, rs)
+
+
+@pytest.mark.parametrize("out_dtype", ["int8", "e4m3"])
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+def test_cfg5c_exactness_family(G, out_dtype):
+    d = W.cfg5c()
+    M, K = d["M"], d["K"]
+    args = (d["x"], "fp16", M, K, G, False, out_dtype, "ue8m0", "row")
+    gq, gs = run_flat(*args)
+    compare(f"cfg5c G={G} {out_dtype}", gq, gs, *oracle.ptgq(*args, eps=d["eps"]))
+    # implementation-independent: dequantized codes equal the integers exactly
+    scale = np.ldexp(1.0, gs.reshape(M, K // G).astype(np.int64) - 127)
+    if out_dtype == "int8":
+        deq = gq.view(np.int8).astype(np.float64)
+    else:
+        deq = torch.from_numpy(gq).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    deq = deq.reshape(M, K // G, G) * scale[:, :, None]
+    assert np.array_equal(deq.reshape(M, K), d["x"].view(np.float16).astype(np.float64))
+
+
+# ------------------------------------------------ every trait combination
+
+SHAPES = [(1, 128), (3, 640), (5, 2048 + 128), (37, 512), (6, 7168)]
+
+
+@pytest.mark.parametrize("fuse", [False, True])
+@pytest.mark.parametrize("layout", ["row", "col"])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+@pytest.mark.parametrize("out_dtype", ["e4m3", "int8"])
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+def test_trait_sweep(G, in_dtype, out_dtype, fmt, layout, fuse):
+    for i, (M, K) in enumerate(SHAPES):
+        if K % G:
+            continue
+        shape = (M, 2 * K if fuse else K)
+        seed = 100 * G + 10 * i + fuse
+        x = W.normal_bf16(seed, shape, factor_cols=[1, K - 1], factor=37.0) \
+            if in_dtype == "bf16" else W.normal_fp16(seed, shape)
+        args = (x, in_dtype, M, K, G, fuse, out_dtype, fmt, layout)
+        compare(f"sweep G={G} {in_dtype} {out_dtype} {fmt} {layout} fuse={fuse} M={M} K={K}",
+                *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
+
+
+@pytest.mark.parametrize("layout", ["row", "col"])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+@pytest.mark.parametrize("fuse", [False, True])
+def test_masked_sweep(fuse, fmt, layout):
+    d = W.cfg4(seed=4200 + fuse, E=5, T=45, K=640)
+    E, T, K = d["E"], d["T"], d["K"]
+    mm = d["masked_m"].copy()
+    mm[2], mm[3] = -7, T + 100
+    x = d["x"] if fuse else np.ascontiguousarray(d["x"][:, :, :K])
+    gq, gs = run_masked(x, "bf16", E, T, K, 64, fuse, mm, 16, "int8", fmt, layout)
+    sb = aq.ptgq_scale_bytes(T, K, 64, fmt, layout)
+    rq, rs = oracle.ptgq_masked(x, "bf16", E, T, K, 64, fuse, mm, "int8", fmt, layout,
+                                q_init=np.full((E, T, K), 0x7F, np.uint8),
+                                s_init=np.full(E * sb, 0xFF, np.uint8))
+    compare(f"masked fuse={fuse} {fmt} {layout} mm={list(mm)}", gq, gs, rq, rs)
+
+
+# --------------------------------------------------------------- per-token
+
+@pytest.mark.parametrize("mode", [-1, 0, 1, 2])
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp16", "fp32"])
+def test_per_token_modes(in_dtype, mode):
+    try:
+        aq.ptgq_set_tuning(3, mode)
+        for M, K in [(39, 1076), (39, 1368), (300, 4096), (7, 4), (2, 8192 * 3), (64, 3584)]:
+            seed = M * 7 + K
+            if in_dtype == "bf16":
+                x = W.normal_bf16(seed, (M, K))
+            elif in_dtype == "fp16":
+                x = W.normal_fp16(seed, (M, K))
+            else:
+                x = W.normal_f32(seed, (M, K))
+            x[M // 2] = 0          # a zero row: scale 0, codes 0
+            gq, gs = run_per_token(x, in_dtype, M, K)
+            rq, rs = oracle.ptq_fp8(x, in_dtype, M, K)
+            compare(f"per-token {in_dtype} mode={mode} M={M} K={K}", gq, gs, rq, rs)
+    finally:
+        aq.ptgq_set_tuning(3, -1)
+
+
+def test_per_token_many_rows_wave_dispatch():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    M, K = cus * 16, 1368
+    x = W.normal_bf16(31, (M, K))
+    gq, gs = run_per_token(x, "bf16", M, K)
+    compare(f"per-token wave-dispatch M={M}", gq, gs, *oracle.ptq_fp8(x, "bf16", M, K))
+
+
+# ---------------------------------------------------------------- edges
+
+def test_zero_rows_touch_nothing():
+    q = torch.full((4, 256), 0x5A, dtype=torch.uint8, device=DEV)
+    s = torch.full((64,), 0x5A, dtype=torch.uint8, device=DEV)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device=DEV)
+    aq.ptgq_quant(x, "bf16", 0, 256, 128, False, "e4m3", "ue8m0", "col", 1e-10, q, s)
+    aq.ptgq_quant_masked(x, "bf16", 0, 4, 256, 128, False, s, 0, "e4m3", "ue8m0", "col", 1e-10, q, s)
+    aq.ptq_quant_fp8(x, "bf16", 0, 256, q, s)
+    torch.cuda.synchronize()
+    assert bool((q == 0x5A).all()) and bool((s == 0x5A).all())
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-10, 1e-3])
+@pytest.mark.parametrize("fmt", ["f32", "ue8m0"])
+def test_special_values(eps, fmt):
+    """All-zero groups (eps floor; eps = 0 gives scale 0 / byte 0 and +-0
+    codes), signed zeros, bf16 subnormals, values near the bf16 maximum."""
+    M, K = 8, 1024
+    x = W.normal_bf16(55, (M, K))
+    x[0] = 0
+    x[1, :128] = 0x8000                      # -0
+    if eps > 0 or fmt == "ue8m0":
+        # bf16 subnormals: with eps = 0 an fp32 scale would be subnormal and its
+        # reciprocal infinite (0 * inf = NaN codes, unspecified), so that
+        # corner is left out
+        x[2] = (np.arange(K) % 128).astype(np.uint16)
+    x[3, :256] = 0x7F7F                      # largest finite bf16
+    x[3, 256:512] = 0xFF7F
+    x[4] = W.to_bf16_bits(np.full(K, 448.0))
+    x[5] = W.to_bf16_bits(np.linspace(-450.0, 450.0, K))
+    for out_dtype in ("e4m3", "int8"):
+        for layout in ("row", "col"):
+            args = (x, "bf16", M, K, 128, False, out_dtype, fmt, layout)
+            compare(f"special eps={eps} {fmt} {out_dtype} {layout}", *run_flat(*args, eps=eps),
+                    *oracle.ptgq(*args, eps=eps))
+
+
+def test_tuning_knobs_never_change_results():
+    d = W.cfg2(256)
+    args = (d["x"], "bf16", 256, d["K"], 128, False, "e4m3", "ue8m0", "col")
+    ref = oracle.ptgq(*args)
+    try:
+        for knob, values in ((0, [1, 2, 3, 4]), (1, [1, 2, 4]), (2, [1, 2, 64])):
+            for v in values:
+                aq.ptgq_set_tuning(knob, v)
+                compare(f"knob {knob}={v}", *run_flat(*args), *ref)
+                aq.ptgq_set_tuning(knob, -1)
+    finally:
+        for k in range(4):
+            aq.ptgq_set_tuning(k, -1)
+
+
+def test_runs_on_a_side_stream():
+    d = W.cfg2(16)
+    args = (d["x"], "bf16", 16, d["K"], 128, False, "e4m3", "ue8m0", "col")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        got = run_flat(*args, stream=st)
+    compare("side stream", *got, *oracle.ptgq(*args))
