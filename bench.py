@@ -1,0 +1,356 @@
+"""Benchmark: per-token-group 8-bit activation quantization on one MI355X.
+
+Headline workload: bf16 [16384, 7168] activations (the DeepSeek-V3 hidden
+size, synthetic N(0,1) with 1 % outlier channels x30), G = 128, e4m3 codes and
+UE8M0 scales packed column-major with M padded to 4.  A step is one
+ptgq_quant call over that batch.  Inputs are resident in HBM before timing;
+buffer sets totalling >= 1 GiB are rotated so that no set is still in the
+256 MB Infinity Cache when it is reused.
+
+Printed: one JSON line.  `value` = achieved GB/s at M = 16384, where bytes are
+the algorithmic bytes (bf16 read + codes written + one UE8M0 byte per group);
+`per_m` gives us/call, GB/s and fraction of the 8 TB/s HBM peak at every M of
+the workload; `variants` measures the fused, masked and per-token entry
+points the same way; `roofline` gives the dominant kernel's figures;
+`cpu_baseline` times the CPU oracle on one full step (single thread).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --profile-main   (only the headline loop, for rocprofv3)
+    python bench.py --calib-copy     (a plain device copy of known size, for
+                                      calibrating rocprofv3 byte counters)
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+GIB = 1 << 30
+METRIC = "achieved HBM GB/s and % of peak per M; us/call at M=1..16384, K=7168"
+
+
+def alg_bytes_flat(M, K, G, in_size, fuse, scale_bytes_per_group):
+    """Input read + codes written + real scale entries written (no pad slots)."""
+    return M * K * in_size * (2 if fuse else 1) + M * K + M * (K // G) * scale_bytes_per_group
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for rel in ("activation_quantization_amd/csrc/ptgq_kernels.hip",
+                "activation_quantization_amd/csrc/ptgq_api.cpp",
+                "activation_quantization_amd/csrc/ptgq_internal.h"):
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+class Timer:
+    """Times a list of zero-argument launch closures, cycled, on the current
+    stream: per-launch HIP events give the kernel's average duration, and one
+    event pair around the whole region gives the per-step time."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, calls, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        region0 = torch.cuda.Event(enable_timing=True)
+        region1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        region0.record()
+        for i in range(steps):
+            starts[i].record()
+            calls[i % len(calls)]()
+            ends[i].record()
+        region1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+        return {"region_ms": region0.elapsed_time(region1), "launch_ms_mean": float(np.mean(per)),
+                "launch_ms_median": float(np.median(per)), "wall_s": wall}
+
+    def graph(self, calls, per_graph, replays):
+        """Device time per call of `per_graph` back-to-back launches captured in
+        one HIP graph (launch overhead excluded): the latency-bound small-M
+        figure."""
+        torch = self.torch
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                for i in range(per_graph):
+                    calls[i % len(calls)]()
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (replays * per_graph)
+
+
+def rotation_sets(footprint, cap=64):
+    return int(max(2, min(cap, math.ceil(GIB / max(footprint, 1)))))
+
+
+def make_flat_sets(torch, aq, x_host, M, K, G, fuse, out_dtype, fmt, layout, in_dtype, nsets):
+    dev = "cuda"
+    xt = torch.from_numpy(np.ascontiguousarray(x_host).view(np.int16)).to(dev)
+    sets = []
+    sb = aq.ptgq_scale_bytes(M, K, G, fmt, layout)
+    for i in range(nsets):
+        xi = xt if i == 0 else xt.clone()
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        s = torch.empty((max(sb, 1),), dtype=torch.uint8, device=dev)
+        sets.append((xi, q, s))
+
+    def mk(xi, q, s):
+        return lambda: aq.ptgq_quant(xi, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, 1e-10,
+                                     q, s, check=False)
+    return sets, [mk(*st) for st in sets]
+
+
+def check_rows_cfg2(oracle, x_host, q_dev, s_dev, M, K, G, rows):
+    """Sampled parity at full size: the oracle quantizes the sampled rows alone
+    (row-major UE8M0 bytes); the GPU's packed column-major words are unpacked
+    for the same rows."""
+    ng = K // G
+    Mp = (M + 3) // 4 * 4
+    xs = np.ascontiguousarray(x_host[rows])
+    rq, rs = oracle.ptgq(xs, "bf16", len(rows), K, G, False, "e4m3", "ue8m0", "row")
+    gq = q_dev[rows].cpu().numpy()
+    words = s_dev.cpu().numpy().view(np.uint32).reshape((ng + 3) // 4, Mp)
+    gs = np.empty((len(rows), ng), dtype=np.uint8)
+    for g in range(ng):
+        gs[:, g] = (words[g // 4, rows] >> (8 * (g % 4))) & 0xFF
+    return int((gq != rq).sum()), int((gs != rs.reshape(len(rows), ng)).sum())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--profile-main", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this quantization path needs no exchange between "
+              f"GPUs (rows and experts are independent), and only --gpus 1 is supported "
+              f"(got --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import activation_quantization_amd as aq
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    aq.load_library()
+    aq.ptgq_init(0)
+    timer = Timer(torch)
+
+    if args.calib_copy:
+        # plain device-to-device copy of exactly 1 GiB, 5 times
+        a = torch.empty(GIB, dtype=torch.uint8, device="cuda")
+        b = torch.empty(GIB, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_each_way": GIB, "copies": 5}))
+        return
+
+    M, K, G = 16384, 7168, 128
+    d = W.cfg2(M)
+    x_host = d["x"]
+    foot = alg_bytes_flat(M, K, G, 2, False, 1)
+    nsets = rotation_sets(foot)
+    sets, calls = make_flat_sets(torch, aq, x_host, M, K, G, False, "e4m3", "ue8m0", "col",
+                                 "bf16", nsets)
+
+    if args.profile_main:
+        r = timer.run(calls, args.steps, args.warmup)
+        print(json.dumps({"profile_main": True, "steps": args.steps,
+                          "launch_us_mean": r["launch_ms_mean"] * 1e3}))
+        return
+
+    main_res = timer.run(calls, args.steps, args.warmup)
+    ms_per_step = main_res["region_ms"] / args.steps
+    value = foot / (ms_per_step * 1e-3) / 1e9
+    launch_s = main_res["launch_ms_mean"] * 1e-3
+    achieved = foot / launch_s / 1e9
+
+    # sampled parity of the timed output at full size
+    rows = sorted(set([0, 1, 2, M - 3, M - 2, M - 1] + list(range(5, M, 257))))
+    code_bad, scale_bad = check_rows_cfg2(__import__("oracle"), x_host, sets[0][1], sets[0][2],
+                                          M, K, G, np.array(rows))
+
+    # per-M sweep of the same workload
+    per_m = []
+    for Mi in W.CFG2_M:
+        di = x_host if Mi == M else W.cfg2(Mi)["x"]
+        fi = alg_bytes_flat(Mi, K, G, 2, False, 1)
+        ns = rotation_sets(fi)
+        _, ci = make_flat_sets(torch, aq, di, Mi, K, G, False, "e4m3", "ue8m0", "col", "bf16", ns)
+        per_graph = max(ns, min(200, max(8, int(2e8 // max(fi, 1)))))
+        t_cold = timer.graph(ci, per_graph, 5)
+        t_warm = timer.graph(ci[:1], min(per_graph, 100), 5) if Mi <= 256 else None
+        ent = {"M": Mi, "us_per_call": round(t_cold * 1e3, 3), "bytes": fi,
+               "GBps": round(fi / (t_cold * 1e-3) / 1e9, 1),
+               "frac_of_peak": round(fi / (t_cold * 1e-3) / 1e9 / PEAK_GBS, 4),
+               "buffer_sets": ns}
+        if t_warm is not None:
+            ent["us_per_call_warm"] = round(t_warm * 1e3, 3)
+        per_m.append(ent)
+        del ci
+        torch.cuda.empty_cache()
+
+    variants = {}
+    if not args.no_variants:
+        # fused silu(gate)*up, bf16 [8192, 2*4096]
+        d3 = W.cfg3(8192)
+        f3 = alg_bytes_flat(8192, 4096, 128, 2, True, 1)
+        _, c3 = make_flat_sets(torch, aq, d3["x"], 8192, 4096, 128, True, "e4m3", "ue8m0", "col",
+                               "bf16", rotation_sets(f3))
+        r3 = timer.run(c3, 100, 10)
+        variants["fused_silu_mul_M8192_K4096"] = {
+            "us_per_call": round(r3["launch_ms_mean"] * 1e3, 2), "bytes": f3,
+            "GBps": round(f3 / (r3["launch_ms_mean"] * 1e-3) / 1e9, 1)}
+        del c3
+        # masked MoE, E=32, tokens_pad=384, fused, K=2048
+        d4 = W.cfg4()
+        E, T, K4, mm = d4["E"], d4["T"], d4["K"], d4["masked_m"]
+        live = int(np.clip(mm, 0, T).sum())
+        f4 = live * (2 * K4 * 2 + K4 + K4 // 128) + 4 * E
+        x4 = torch.from_numpy(d4["x"].view(np.int16)).to("cuda")
+        mm_d = torch.from_numpy(mm).to("cuda")
+        sb4 = aq.ptgq_scale_bytes(T, K4, 128, "ue8m0", "col")
+        c4 = []
+        for i in range(rotation_sets(E * T * (4 * K4 + K4))):
+            xi = x4 if i == 0 else x4.clone()
+            q4 = torch.empty((E, T, K4), dtype=torch.uint8, device="cuda")
+            s4 = torch.empty((E * sb4,), dtype=torch.uint8, device="cuda")
+            c4.append((lambda xi=xi, q4=q4, s4=s4: aq.ptgq_quant_masked(
+                xi, "bf16", E, T, K4, 128, True, mm_d, int(live // E), "e4m3", "ue8m0", "col",
+                1e-10, q4, s4, check=False)))
+        r4 = timer.run(c4, 100, 10)
+        variants["masked_E32_T384_K2048_fused"] = {
+            "us_per_call": round(r4["launch_ms_mean"] * 1e3, 2), "bytes": f4, "live_rows": live,
+            "GBps": round(f4 / (r4["launch_ms_mean"] * 1e-3) / 1e9, 1)}
+        del c4
+        # fp16 [8192, 3584] -> int8, fp32 row-major scales, G = 128; per-token e4m3
+        d5 = W.cfg5()
+        f5 = alg_bytes_flat(8192, 3584, 128, 2, False, 4)
+        _, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, 128, False, "int8", "f32", "row",
+                               "fp16", rotation_sets(f5))
+        r5 = timer.run(c5, 100, 10)
+        variants["int8_fp16_M8192_K3584_G128"] = {
+            "us_per_call": round(r5["launch_ms_mean"] * 1e3, 2), "bytes": f5,
+            "GBps": round(f5 / (r5["launch_ms_mean"] * 1e-3) / 1e9, 1)}
+        del c5
+        f5b = 8192 * 3584 * 2 + 8192 * 3584 + 8192 * 4
+        x5 = torch.from_numpy(d5["x"].view(np.int16)).to("cuda")
+        c5b = []
+        for i in range(rotation_sets(f5b)):
+            xi = x5 if i == 0 else x5.clone()
+            q5 = torch.empty((8192, 3584), dtype=torch.uint8, device="cuda")
+            s5 = torch.empty((8192,), dtype=torch.float32, device="cuda")
+            c5b.append((lambda xi=xi, q5=q5, s5=s5: aq.ptq_quant_fp8(xi, "fp16", 8192, 3584, q5,
+                                                                    s5, check=False)))
+        r5b = timer.run(c5b, 100, 10)
+        variants["per_token_fp8_fp16_M8192_K3584"] = {
+            "us_per_call": round(r5b["launch_ms_mean"] * 1e3, 2), "bytes": f5b,
+            "GBps": round(f5b / (r5b["launch_ms_mean"] * 1e-3) / 1e9, 1)}
+        del c5b
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.ptgq(x_host, "bf16", M, K, G, False, "e4m3", "ue8m0", "col", eps=1e-10)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(foot / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"one full step: all {M} rows of the bf16 [{M},{K}] input "
+                         f"({M * K} elements), single-threaded, {dt:.1f} s"}
+
+    traffic = read_traffic("traffic_ptgq_flat_cfg2_M16384.md")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "bf16 [16384, 7168] -> e4m3, G=128, UE8M0 scales column-major "
+                               "(M padded to 4), N(0,1) with 1% outlier channels x30",
+                   "M": M, "K": K, "group_size": G, "eps": 1e-10, "buffer_sets": nsets,
+                   "algorithmic_bytes_per_step": foot},
+        "frac_of_peak": round(value / PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "ptgq_flat_kernel<bf16, G=128, no fuse, e4m3>",
+                     "avg_launch_us": round(main_res["launch_ms_mean"] * 1e3, 3),
+                     "kernel_source_digest": kernel_source_digest()},
+        "parity_sample": {"rows": len(rows), "code_mismatches": code_bad,
+                          "scale_mismatches": scale_bad},
+        "per_m": per_m,
+        "variants": variants,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(main_res["wall_s"], 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
