@@ -62,7 +62,7 @@ def load_library(path: str = LIB_PATH):
     lib.ptgq_init.restype = i32
     lib.ptgq_probe_e4m3.argtypes = [vp, vp, i64, vp]
     lib.ptgq_probe_e4m3.restype = i32
-    lib.ptgq_probe_silu_mul.argtypes = [vp, vp, i32, vp, i64, vp]
+    lib.ptgq_probe_silu_mul.argtypes = [vp, vp, i32, i32, vp, i64, vp]
     lib.ptgq_probe_silu_mul.restype = i32
     lib.ptgq_set_tuning.argtypes = [i32, i64]
     lib.ptgq_set_tuning.restype = i32
@@ -186,11 +186,11 @@ def ptgq_probe_e4m3(v, out, n, stream=None, check=True):
     return _check("ptgq_probe_e4m3", rc) if check else rc
 
 
-def ptgq_probe_silu_mul(g, u, in_dtype, out, n, stream=None, check=True):
+def ptgq_probe_silu_mul(g, u, in_dtype, path, out, n, stream=None, check=True):
     if n > 0:
         _need(g, 2 * n, "ptgq_probe_silu_mul", "g")
         _need(u, 2 * n, "ptgq_probe_silu_mul", "u")
         _need(out, 4 * n, "ptgq_probe_silu_mul", "out")
-    rc = load_library().ptgq_probe_silu_mul(_ptr(g), _ptr(u), _enum(in_dtype, IN_DTYPES), _ptr(out),
-                                            n, _stream(stream))
+    rc = load_library().ptgq_probe_silu_mul(_ptr(g), _ptr(u), _enum(in_dtype, IN_DTYPES),
+                                            int(path), _ptr(out), n, _stream(stream))
     return _check("ptgq_probe_silu_mul", rc) if check else rc

@@ -26,13 +26,19 @@ constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
 int g_dev_cus[kMaxDevices];            // compute units; 0 = query failed
 
+// Once per device: query the CU count and build the device's SiLU lookup table
+// (one small kernel and one host synchronization, never repeated).
 int device_cus(int dev)
 {
     if (dev < 0 || dev >= kMaxDevices) return 0;
     std::call_once(g_dev_once[dev], [dev] {
         int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        int prev = -1;
+        if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            launch_silu_table_init(nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
             cus = 0;
+        if (prev >= 0) (void)hipSetDevice(prev);
         g_dev_cus[dev] = cus;
     });
     return g_dev_cus[dev];
@@ -49,9 +55,10 @@ int current_cus(int *dev_out)
 // ------------------------------------------------------------ tuning knobs
 // Process-wide overrides of the geometry chooser (diagnostics and sweeps
 // only; -1 = automatic), set through ptgq_set_tuning.
-std::atomic<int64_t> g_knob[4] = {{-1}, {-1}, {-1}, {-1}};
+constexpr int kKnobs = 5;
+std::atomic<int64_t> g_knob[kKnobs] = {{-1}, {-1}, {-1}, {-1}, {-1}};
 enum { KNOB_SLABS_PER_TASK = 0, KNOB_WAVES_PER_BLOCK = 1, KNOB_BLOCKS_PER_CU = 2,
-       KNOB_TOKEN_MODE = 3 };
+       KNOB_TOKEN_MODE = 3, KNOB_SILU_TABLE = 4 };
 
 int64_t knob(int k) { return g_knob[k].load(std::memory_order_relaxed); }
 
@@ -77,6 +84,7 @@ int check_group_args(const void *x, int in_dtype, int64_t outer, int64_t rows, i
     if (outer < 0 || rows < 0 || K < 0 || K % G != 0) return PTGQ_EINVAL;
     if (!(std::isfinite(eps) && eps >= 0.0f)) return PTGQ_EINVAL;
     if (outer == 0 || rows == 0 || K == 0) return PTGQ_OK;
+    if (K >= (int64_t)1 << 29) return PTGQ_EUNSUPPORTED;   // rows are 32-bit buffer ranges
     if (!x || !q || !s) return PTGQ_EINVAL;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4)) return PTGQ_EALIGN;
     return PTGQ_OK;
@@ -87,38 +95,68 @@ int check_group_args(const void *x, int in_dtype, int64_t outer, int64_t rows, i
 struct GroupGeom {
     int U;          // slabs per task
     int wpb;        // waves per block
+    bool table;     // fused bf16: LDS SiLU table (16-wave blocks)
+    int64_t per_cu; // resident blocks per CU the grid is capped at
     unsigned grid;  // blocks
 };
 
-// Flat schedule.  Few tasks (decode-sized M): one slab per task and one-wave
-// blocks, so that the groups spread over as many CUs as possible.  Many tasks
-// (prefill-sized M): up to 4 slabs per task so each lane keeps 4 x 16 B (8 x
-// when fused) in flight, 4-wave blocks, and a grid capped at a few blocks per
-// CU that loops over the tasks (a multiple of 8 so each XCD gets the same
-// share).
-GroupGeom choose_flat(int64_t rows, int32_t spr, int cus)
+constexpr int kTableWaves = 16;       // 1024-thread blocks stage the 32 KiB table once
+constexpr int kTableBlocksPerCu = 1;  // one table block of 16 waves per CU
+
+// Loads in flight per CU that saturate HBM for this 2:1 read/write stream
+// (measured on MI355X: 48-64 KiB per CU, with every wave holding the next
+// task's loads while it processes the current one).
+constexpr int64_t kInflightBytesPerCu = 48 * 1024;
+
+// Slabs per task (1, 2 or 4; fused 1 or 2) and the SiLU path, for `slabs`
+// slabs of work in total.  Few slabs (decode-sized M): one slab per task so
+// the work spreads over as many waves and CUs as possible.  Many: two slabs
+// per task when a row has an even number of slabs (no task runs past a row),
+// else one; fused tasks hold one slab (gate and up already double the bytes).
+// Fused bf16 work large enough to amortize staging the 32 KiB table in LDS
+// reads the table.
+void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16, int cus)
 {
-    GroupGeom g;
-    const int64_t slabs = rows * spr;
     const int64_t wave_slots = (int64_t)cus * 4 * 8;   // 8 waves per SIMD
     int U = 1;
-    if (slabs >= 4 * wave_slots) U = 4;
-    else if (slabs >= 2 * wave_slots) U = 2;
-    if (knob(KNOB_SLABS_PER_TASK) > 0) U = (int)std::min<int64_t>(knob(KNOB_SLABS_PER_TASK), 4);
-    U = std::min(U, (int)spr);
-    g.U = U;
-    const int64_t tasks = rows * (((int64_t)spr + U - 1) / U);
-    int wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
-    if (knob(KNOB_WAVES_PER_BLOCK) > 0) wpb = (int)std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), 4);
-    g.wpb = wpb;
-    int64_t blocks = (tasks + wpb - 1) / wpb;
-    int64_t per_cu = 8;
+    if (!fuse && slabs >= 2 * wave_slots && spr % 2 == 0) U = 2;
+    if (knob(KNOB_SLABS_PER_TASK) > 0) {
+        const int64_t k = knob(KNOB_SLABS_PER_TASK);
+        U = k >= 4 ? 4 : (k >= 2 ? 2 : 1);
+    }
+    g.U = std::min(U, fuse ? kMaxSlabsPerFusedTask : kMaxSlabsPerTask);
+    g.table = fuse && bf16 && slabs >= (int64_t)cus * 4 * kTableWaves;
+    if (fuse && bf16 && knob(KNOB_SILU_TABLE) >= 0) g.table = knob(KNOB_SILU_TABLE) > 0;
+}
+
+// Blocks for `tasks` tasks.  Plain and direct-SiLU kernels: 4-wave blocks
+// (1-wave blocks for a handful of tasks), with the grid capped so that each
+// CU holds about kInflightBytesPerCu of loads (every wave keeps two tasks of
+// U slabs, 1 KiB per slab and input half); the grid then loops over the tasks.
+// Table kernels: one 16-wave block per CU.
+void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse)
+{
+    int wpb;
+    int64_t per_cu;
+    if (g.table) {
+        wpb = kTableWaves;
+        per_cu = kTableBlocksPerCu;
+    } else {
+        wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
+        if (knob(KNOB_WAVES_PER_BLOCK) > 0)
+            wpb = (int)std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), 4);
+        const int64_t wave_bytes = 2 * (int64_t)g.U * 1024 * (fuse ? 2 : 1);
+        const int64_t waves_per_cu = std::max<int64_t>(4, kInflightBytesPerCu / wave_bytes);
+        per_cu = std::max<int64_t>(1, waves_per_cu / wpb);
+    }
     if (knob(KNOB_BLOCKS_PER_CU) > 0) per_cu = knob(KNOB_BLOCKS_PER_CU);
-    const int64_t cap = (int64_t)cus * per_cu;
+    g.wpb = wpb;
+    g.per_cu = per_cu;
+    int64_t blocks = (tasks + wpb - 1) / wpb;
+    const int64_t cap = std::max<int64_t>(1, (int64_t)cus * per_cu);
     if (blocks > cap) blocks = cap;
     if (blocks >= 64) blocks = blocks / 8 * 8;
     g.grid = (unsigned)std::max<int64_t>(blocks, 1);
-    return g;
 }
 
 int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, int G, int fuse,
@@ -146,47 +184,39 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
     a.scale_fmt = scale_fmt;
     a.scale_layout = scale_layout;
     const bool masked = masked_m != nullptr;
+    const bool bf16 = in_dtype == PTGQ_BF16;
 
     GroupGeom geo;
     if (!masked) {
-        geo = choose_flat(rows, a.spr, cus);
+        choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
         const int64_t tasks = rows * (int64_t)a.tpr;
         if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.n_tasks = (int32_t)tasks;
+        choose_blocks(geo, tasks, cus, fuse != 0);
         if (scale_layout == PTGQ_COL_MAJOR && a.rows_pad > rows)
             a.pad_cols = (int32_t)(scale_fmt == PTGQ_SCALE_UE8M0 ? (a.ng + 3) / 4 : a.ng);
     } else {
-        // Masked schedule: each expert gets the blocks its expected live rows
-        // need (all tokens_pad rows when unknown); every block reads masked_m
-        // on the device and loops over the expert's live tasks.
+        // Masked schedule: the live rows of all experts form one task space,
+        // which the kernel splits evenly over the grid after reading masked_m
+        // on the device.  The grid is sized for the expected live rows (all
+        // tokens_pad rows of every expert when unknown); more live rows than
+        // expected only make each wave loop longer.
+        if (E > kMaxExperts) return PTGQ_EUNSUPPORTED;
         const int64_t hint = (expected_m > 0 && expected_m < rows) ? expected_m : rows;
-        const int64_t slabs = std::max<int64_t>(hint, 1) * a.spr * E;
-        int U = slabs >= (int64_t)cus * 4 * 8 * 4 ? 4 : 1;
-        if (knob(KNOB_SLABS_PER_TASK) > 0) U = (int)std::min<int64_t>(knob(KNOB_SLABS_PER_TASK), 4);
-        U = std::min(U, (int)a.spr);
-        a.U = U;
-        a.tpr = (a.spr + U - 1) / U;
-        if (rows * (int64_t)a.tpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
-        const int64_t tasks_hint = std::max<int64_t>(hint, 1) * a.tpr;
-        int wpb = tasks_hint * E >= (int64_t)cus * 4 ? 4 : 1;
-        if (knob(KNOB_WAVES_PER_BLOCK) > 0) wpb = (int)std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), 4);
-        int64_t bpe = (tasks_hint + wpb - 1) / wpb;
-        int64_t per_cu = knob(KNOB_BLOCKS_PER_CU) > 0 ? knob(KNOB_BLOCKS_PER_CU) : 8;
-        const int64_t cap = std::max<int64_t>(1, (int64_t)cus * per_cu / std::max<int64_t>(E, 1));
-        bpe = std::max<int64_t>(1, std::min(bpe, cap));
-        if (E * bpe >= INT32_MAX) return PTGQ_EUNSUPPORTED;
-        a.blocks_per_expert = (int32_t)bpe;
+        choose_task(geo, std::max<int64_t>(hint, 1) * a.spr * E, a.spr, fuse != 0, bf16, cus);
+        a.U = geo.U;
+        a.tpr = (a.spr + a.U - 1) / a.U;
+        if (E * rows * (int64_t)a.tpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+        choose_blocks(geo, std::max<int64_t>(hint, 1) * a.tpr * E, cus, fuse != 0);
+        a.num_experts = (int32_t)E;
         a.x_expert_stride = rows * a.in_stride;
         a.q_expert_stride = rows * K;
         a.s_expert_stride = (int64_t)ptgq_scale_bytes(rows, K, G, scale_fmt, scale_layout);
-        geo.U = U;
-        geo.wpb = wpb;
-        geo.grid = (unsigned)(E * bpe);
     }
-    const hipError_t err = launch_group(a, in_dtype, G, fuse != 0, out_dtype, masked, geo.grid,
-                                        (unsigned)(geo.wpb * 64),
+    const hipError_t err = launch_group(a, in_dtype, G, fuse != 0, out_dtype, geo.table, masked,
+                                        geo.grid, (unsigned)(geo.wpb * 64),
                                         static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
 }
@@ -254,6 +284,7 @@ int ptgq_quant_masked(const void *x, int in_dtype, int64_t E, int64_t tokens_pad
     if (E == 0 || tokens_pad == 0 || K == 0) return PTGQ_OK;
     if (!masked_m) return PTGQ_EINVAL;
     if (!aligned(masked_m, 4)) return PTGQ_EALIGN;
+    if (E > kMaxExperts) return PTGQ_EUNSUPPORTED;
     return launch_group_common(x, in_dtype, tokens_pad, K, group_size, fuse_silu_mul, out_dtype,
                                scale_fmt, scale_layout, eps, q, s, masked_m, E, expected_m,
                                stream);
@@ -328,22 +359,24 @@ int ptgq_probe_e4m3(const float *v, uint8_t *out, int64_t n, void *stream)
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
 }
 
-int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, float *out, int64_t n,
-                        void *stream)
+int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int path, float *out,
+                        int64_t n, void *stream)
 {
     if (in_dtype != PTGQ_BF16 && in_dtype != PTGQ_FP16) return PTGQ_EINVAL;
+    if (path != 0 && !(path == 1 && in_dtype == PTGQ_BF16)) return PTGQ_EINVAL;
     if (n < 0) return PTGQ_EINVAL;
     if (n == 0) return PTGQ_OK;
     if (!g || !u || !out) return PTGQ_EINVAL;
     if (n >= (int64_t)UINT32_MAX * 256) return PTGQ_EUNSUPPORTED;
-    const hipError_t err = launch_probe_silu(g, u, in_dtype, out, n,
+    if (current_cus(nullptr) <= 0) return PTGQ_EDEVICE;   // builds the lookup table
+    const hipError_t err = launch_probe_silu(g, u, in_dtype, path, out, n,
                                              static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
 }
 
 int ptgq_set_tuning(int which, int64_t value)
 {
-    if (which < 0 || which > 3) return PTGQ_EINVAL;
+    if (which < 0 || which >= kKnobs) return PTGQ_EINVAL;
     g_knob[which].store(value, std::memory_order_relaxed);
     return PTGQ_OK;
 }

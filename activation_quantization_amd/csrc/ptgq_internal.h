@@ -13,10 +13,14 @@ enum : int { SCALE_F32 = 0, SCALE_UE8M0 = 1 };
 enum : int { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
 
 // Elements of one "slab": one 16-byte load per lane across a 64-lane wave
-// (8 sixteen-bit elements per lane).  Every group-quant task is 1..4 slabs of
-// one row.
+// (8 sixteen-bit elements per lane).  Every group-quant task is U = 1, 2 or 4
+// consecutive slabs of one row (1 or 2 when fused); the last task of a row may
+// run past its end (those lanes read zeros and store nothing).
 constexpr int kSlab = 512;
 constexpr int kMaxSlabsPerTask = 4;
+constexpr int kMaxSlabsPerFusedTask = 2;
+// Masked calls keep a prefix sum of E ints in LDS.
+constexpr int kMaxExperts = 4096;
 
 // Arguments of the group-quantization kernels (flat and masked).  All shape
 // scalars are computed on the host; the device only indexes.
@@ -35,12 +39,12 @@ struct GroupArgs {
     int64_t s_expert_stride;  // masked: bytes per expert of s
     float eps;                // amax floor
     int32_t spr;              // slabs per row, ceil(K / kSlab)
-    int32_t U;                // slabs per task, 1..kMaxSlabsPerTask
+    int32_t U;                // slabs per task: 1, 2 or 4 (fused: 1 or 2)
     int32_t tpr;              // tasks per row, ceil(spr / U)
     int32_t n_tasks;          // flat: rows * tpr
     int32_t scale_fmt;        // SCALE_F32 / SCALE_UE8M0
     int32_t scale_layout;     // LAYOUT_ROW / LAYOUT_COL
-    int32_t blocks_per_expert;// masked: blocks given to each expert
+    int32_t num_experts;      // masked: E (1..kMaxExperts)
     int32_t pad_cols;         // flat column-major: 4-byte columns whose pad rows
                               // are zeroed (ceil(ng/4) or ng); 0 = none
 };
@@ -59,12 +63,17 @@ enum TokenMode : int { TOKEN_WAVE = 0, TOKEN_BLOCK = 1, TOKEN_BLOCK_LOOP = 2 };
 
 // Launchers (defined in ptgq_kernels.hip).  They return the hipError_t of the
 // launch.  `grid`/`block` are chosen by the caller.
+// `table`: fused bf16 kernels read g / (1 + e^-g) from the LDS-staged lookup
+// table (launch with 1024-thread blocks); it must have been built on the
+// device by launch_silu_table_init and synchronized before.
 hipError_t launch_group(const GroupArgs &a, int in_dtype, int G, bool fuse, int out_dtype,
-                        bool masked, unsigned grid, unsigned block, hipStream_t stream);
+                        bool table, bool masked, unsigned grid, unsigned block,
+                        hipStream_t stream);
+hipError_t launch_silu_table_init(hipStream_t stream);
 hipError_t launch_token(const TokenArgs &a, int in_dtype, int vec_bytes, TokenMode mode,
                         int nv_per_lane, unsigned grid, unsigned block, hipStream_t stream);
 hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_t stream);
-hipError_t launch_probe_silu(const void *g, const void *u, int in_dtype, float *out, int64_t n,
-                             hipStream_t stream);
+hipError_t launch_probe_silu(const void *g, const void *u, int in_dtype, int path, float *out,
+                             int64_t n, hipStream_t stream);
 
 }  // namespace ptgq

@@ -68,22 +68,6 @@ __device__ __forceinline__ void widen8(const uint4 r, float (&f)[8])
 }
 
 // --------------------------------------------------------------------------
-// Fused SiLU.  silu(g) * u = (g / (1 + e^-g)) * u with e^-g correctly
-// rounded to binary32: the double-precision exp is within about one double
-// ulp, far inside the distance of e^-g from any binary32 rounding boundary
-// for every 16-bit gate (checked exhaustively on the device against the
-// oracle).  Each other step is one IEEE fp32 operation.
-// --------------------------------------------------------------------------
-
-__device__ __forceinline__ float silu_mul(float g, float u)
-{
-    const float e = (float)exp(-(double)g);
-    const float d = 1.0f + e;
-    const float s = g / d;
-    return s * u;
-}
-
-// --------------------------------------------------------------------------
 // Cluster max with DPP.  All lanes of each aligned LANES-lane cluster end
 // with the cluster maximum.  Values are non-negative.
 // --------------------------------------------------------------------------
@@ -119,23 +103,57 @@ __device__ __forceinline__ float wave_max(float v)
 // r == 0), or UE8M0 byte e and exact multiplier 2^(127 - e).
 // --------------------------------------------------------------------------
 
+// UE8M0 without a division.  For a normal a with fl(a / qmax) normal (a at or
+// above qmax * 2^-126), write a = 1.f * 2^(E-127) and qmax = 1.q * 2^EQ: the
+// quotient's exponent field is E - EQ when 1.f >= 1.q and E - EQ - 1 when
+// 1.f < 1.q, its fraction is zero only when 1.f == 1.q, and rounding the
+// quotient to fp32 never carries it onto a power of two (no fp32 a lies within
+// half an ulp below a power-of-two multiple of qmax).  Hence
+//   e = E - EQ + (f > q).
+// Checked against the division for every fp32 a at or above the threshold.
+template <int OUT>
+struct Ue8m0Consts;
+template <>
+struct Ue8m0Consts<OUT_E4M3> {  // 448 = 1.75 * 2^8
+    static constexpr uint32_t EQ = 8, FQ = 0x600000u, THRESHOLD = 0x04E00000u;
+};
+template <>
+struct Ue8m0Consts<OUT_INT8> {  // 127 = 1.984375 * 2^6
+    static constexpr uint32_t EQ = 6, FQ = 0x7E0000u, THRESHOLD = 0x03FE0000u;
+};
+
+template <int OUT>
+__device__ __forceinline__ uint32_t ue8m0_byte(float a, float qmax)
+{
+    using C = Ue8m0Consts<OUT>;
+    const uint32_t b = __float_as_uint(a);
+    uint32_t e = (b >> 23) - C::EQ + ((b & 0x7FFFFFu) > C::FQ ? 1u : 0u);
+    if (b < C::THRESHOLD) {  // tiny a (eps below ~1e-35): exponent of the quotient
+        const uint32_t rb = __float_as_uint(a / qmax);
+        e = ((rb >> 23) & 0xFFu) + ((rb & 0x7FFFFFu) != 0u ? 1u : 0u);
+    }
+    return e;
+}
+
 struct Scale {
     float inv;       // multiplier applied to y
     float r;         // fp32 scale
     uint32_t e;      // UE8M0 byte
 };
 
-__device__ __forceinline__ Scale group_scale(float amax, float eps, float qmax, bool ue8m0)
+template <int OUT>
+__device__ __forceinline__ Scale group_scale(float amax, float eps, bool ue8m0)
 {
+    const float qmax = (OUT == OUT_E4M3) ? 448.0f : 127.0f;
     Scale sc;
     const float a = (amax > eps) ? amax : eps;
-    sc.r = a / qmax;
     if (!ue8m0) {
+        sc.r = a / qmax;
         sc.e = 0;
         sc.inv = (sc.r == 0.0f) ? 0.0f : 1.0f / sc.r;
     } else {
-        const uint32_t b = __float_as_uint(sc.r);
-        sc.e = ((b >> 23) & 0xFFu) + ((b & 0x7FFFFFu) != 0u ? 1u : 0u);
+        sc.r = 0.0f;
+        sc.e = ue8m0_byte<OUT>(a, qmax);
         sc.inv = __uint_as_float((254u - sc.e) << 23);
     }
     return sc;
@@ -145,15 +163,19 @@ __device__ __forceinline__ Scale group_scale(float amax, float eps, float qmax, 
 // Narrowing.
 // --------------------------------------------------------------------------
 
-// 4 floats -> 4 OCP e4m3 codes (byte i = code of value i).  The clamp makes
-// the conversion saturating; -0 and negative values that round to zero keep
-// the sign bit.
+// 4 floats -> 4 OCP e4m3 codes (byte i = code of value i), round to nearest
+// even.  CLAMP saturates to +-448 first; without it the caller guarantees
+// |v| <= 448 (true for UE8M0 scales: 2^(e-127) >= max(amax, eps) / 448
+// exactly).  -0 and negative values that round to zero keep the sign bit.
+template <bool CLAMP>
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
 {
-    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-    c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-    d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    if constexpr (CLAMP) {
+        a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+        b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+        c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+        d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    }
     int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
     return (uint32_t)p;
@@ -170,13 +192,13 @@ __device__ __forceinline__ uint32_t int8x4(float a, float b, float c, float d)
     return int8_1(a) | (int8_1(b) << 8) | (int8_1(c) << 16) | (int8_1(d) << 24);
 }
 
-template <int OUT>
+template <int OUT, bool CLAMP>
 __device__ __forceinline__ uint2 narrow8(const float (&v)[8])
 {
     uint2 o;
     if constexpr (OUT == OUT_E4M3) {
-        o.x = e4m3x4(v[0], v[1], v[2], v[3]);
-        o.y = e4m3x4(v[4], v[5], v[6], v[7]);
+        o.x = e4m3x4<CLAMP>(v[0], v[1], v[2], v[3]);
+        o.y = e4m3x4<CLAMP>(v[4], v[5], v[6], v[7]);
     } else {
         o.x = int8x4(v[0], v[1], v[2], v[3]);
         o.y = int8x4(v[4], v[5], v[6], v[7]);
@@ -185,85 +207,292 @@ __device__ __forceinline__ uint2 narrow8(const float (&v)[8])
 }
 
 // --------------------------------------------------------------------------
-// One task: slabs [j*U, min(j*U + U, spr)) of row m.
-//   xe, qe, se: bases of this expert (flat: the tensors themselves).
+// SiLU lookup for bf16 gates.  s(g) = g / (1 + exp_cr(-g)) depends on the 16
+// bits of g only.  Outside |g| in [2^-25, 2^7) it has a closed form that the
+// IEEE steps reach exactly: |g| < 2^-25 gives e^-g rounded to 1, so s = g/2;
+// g >= 2^7 gives e^-g rounded to 0, so s = g; g <= -2^7 gives e^-g = +inf, so
+// s = -0.  The 2 x 32 binades in between (8192 values) are tabulated by the
+// direct evaluation above, on the device, once per device.
 // --------------------------------------------------------------------------
 
-template <int IN, int G, bool FUSE, int OUT>
-__device__ __forceinline__ void group_task(const GroupArgs &a, const uint16_t *__restrict__ xe,
-                                           uint8_t *__restrict__ qe, uint8_t *__restrict__ se,
-                                           int64_t m, int j, int lane)
+constexpr uint32_t kTabElo = 127 - 25;   // biased exponent of 2^-25
+constexpr uint32_t kTabEhi = 127 + 6;    // biased exponent of [2^6, 2^7)
+constexpr uint32_t kTabNE = kTabEhi - kTabElo + 1;
+constexpr int kSiluTab = 2 * kTabNE * 128;   // 8192 floats = 32 KiB
+
+__device__ float g_silu_table[kSiluTab];
+
+__device__ __forceinline__ float silu_s(float g)
+{
+    const float e = (float)exp(-(double)g);
+    const float d = 1.0f + e;
+    return g / d;
+}
+
+__global__ __launch_bounds__(256) void silu_table_init_kernel()
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < kSiluTab) {
+        const uint32_t sign = (uint32_t)i / (kTabNE * 128);
+        const uint32_t E = kTabElo + ((uint32_t)i / 128) % kTabNE;
+        const uint32_t h = (sign << 15) | (E << 7) | ((uint32_t)i & 127u);
+        g_silu_table[i] = silu_s(__uint_as_float(h << 16));
+    }
+}
+
+__device__ __forceinline__ float silu_s_lookup(uint32_t h, const float *tab)
+{
+    const uint32_t E = (h >> 7) & 0xFFu;
+    const uint32_t sign = (h >> 15) & 1u;
+    const float g = __uint_as_float(h << 16);
+    const uint32_t Ec = E < kTabElo ? kTabElo : (E > kTabEhi ? kTabEhi : E);
+    const float t = tab[((sign * kTabNE + (Ec - kTabElo)) << 7) | (h & 0x7Fu)];
+    const float big = sign ? -0.0f : g;
+    return E < kTabElo ? g * 0.5f : (E > kTabEhi ? big : t);
+}
+
+// --------------------------------------------------------------------------
+// Group quantization tasks.
+//   A task is UMAX consecutive slabs of one row: slabs [j*UMAX, j*UMAX+UMAX)
+//   of row m; a slab is 512 consecutive elements of the row, one 16-byte load
+//   per lane.  Loads and code stores go through per-row buffer resources, so
+//   a slab or lane past the end of the row reads zeros without touching
+//   memory and its code store is dropped by the hardware range check: a task
+//   has no branches.  The next task's loads are issued before the current
+//   task is processed (two buffers), so each wave keeps its loads in flight
+//   while it computes and stores.
+// --------------------------------------------------------------------------
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Cache policy of the streaming accesses: non-temporal ("nt"), since every
+// input byte is read once and every code byte written once.  Measured on
+// MI355X for this 2:1 read/write mix: 6.4 TB/s non-temporal against 5.9 TB/s
+// with the default policy.  Scale words keep the default policy so that the
+// partial lines of neighbouring rows merge in L2.
+constexpr int kStreamPolicy = 2;
+
+// Raw (unstructured) buffer resource over [base, base + bytes); the third
+// dword selects 32-bit data format, as gfx9 raw buffers expect.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int UMAX>
+struct TaskBuf {
+    u32x4 g[UMAX];
+    u32x4 u[UMAX];
+};
+
+// Where a task lives: its row of input and codes, the scale tensor its row
+// belongs to (flat: the whole tensor; masked: the expert's), the row index in
+// that scale tensor, and the task index within the row.
+struct TaskLoc {
+    const uint16_t *xrow;
+    uint8_t *qrow;
+    uint8_t *sbase;
+    int64_t m;
+    int j;
+};
+
+// `live` false: the loads are issued over an empty range (zeros, no memory
+// traffic), so that every path through the task loop issues the same loads
+// and the wait counts stay exact.
+template <bool FUSE, int UMAX>
+__device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, int lane,
+                                          bool live, TaskBuf<UMAX> &b)
+{
+    const uint32_t row_bytes = live ? (uint32_t)(a.K * 2) : 0u;
+    const rsrc_t rg = make_rsrc(t.xrow, row_bytes);
+    const uint32_t off = (uint32_t)t.j * (UMAX * kSlab * 2) + (uint32_t)lane * 16;
+#pragma unroll
+    for (int s = 0; s < UMAX; ++s)
+        b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * 2, 0,
+                                                       kStreamPolicy);
+    if constexpr (FUSE) {
+        const rsrc_t ru = make_rsrc(t.xrow + a.K, row_bytes);
+#pragma unroll
+        for (int s = 0; s < UMAX; ++s)
+            b.u[s] = __builtin_amdgcn_raw_buffer_load_b128(ru, off + s * kSlab * 2, 0,
+                                                           kStreamPolicy);
+    }
+}
+
+__device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
+__device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &t, int lane,
+                                             const TaskBuf<UMAX> &b, const float *tab)
 {
     constexpr int LPG = G / 8;          // lanes per group
     constexpr int GPS = kSlab / G;      // groups per slab (>= 4)
-    const float qmax = (OUT == OUT_E4M3) ? 448.0f : 127.0f;
-    const int s_begin = j * a.U;
-    const int ns = min(a.U, a.spr - s_begin);   // wave-uniform, >= 1
-    const uint16_t *xr = xe + m * a.in_stride;
-    uint8_t *qr = qe + m * a.K;
-
-    uint4 rg[kMaxSlabsPerTask], ru[kMaxSlabsPerTask];
+    const rsrc_t rq = make_rsrc(t.qrow, (uint32_t)a.K);
+    uint8_t *se = t.sbase;
+    const int64_t m = t.m;
+    const bool ue8m0 = a.scale_fmt == SCALE_UE8M0;
 #pragma unroll
-    for (int s = 0; s < kMaxSlabsPerTask; ++s) {
-        rg[s] = make_uint4(0, 0, 0, 0);
-        ru[s] = make_uint4(0, 0, 0, 0);
-        if (s < ns) {
-            const int64_t col = (int64_t)(s_begin + s) * kSlab + lane * 8;
-            if (col < a.K) {
-                rg[s] = *reinterpret_cast<const uint4 *>(xr + col);
-                if constexpr (FUSE) ru[s] = *reinterpret_cast<const uint4 *>(xr + a.K + col);
-            }
-        }
-    }
-
-#pragma unroll
-    for (int s = 0; s < kMaxSlabsPerTask; ++s) {
-        if (s < ns) {
-            const int64_t col = (int64_t)(s_begin + s) * kSlab + lane * 8;
-            const bool valid = col < a.K;
-            float y[8];
-            widen8<IN>(rg[s], y);
+    for (int s = 0; s < UMAX; ++s) {
+        const int slab = t.j * UMAX + s;                            // slab within row
+        const uint32_t col = (uint32_t)slab * kSlab + (uint32_t)lane * 8;
+        const bool valid = (int64_t)col < a.K;
+        float y[8];
+        if constexpr (FUSE && TABLE) {
+            const u32x4 w = b.g[s];
+            float u[8];
+            widen8<IN>(as_uint4(b.u[s]), u);
+            y[0] = silu_s_lookup(w.x & 0xFFFFu, tab) * u[0];
+            y[1] = silu_s_lookup(w.x >> 16, tab) * u[1];
+            y[2] = silu_s_lookup(w.y & 0xFFFFu, tab) * u[2];
+            y[3] = silu_s_lookup(w.y >> 16, tab) * u[3];
+            y[4] = silu_s_lookup(w.z & 0xFFFFu, tab) * u[4];
+            y[5] = silu_s_lookup(w.z >> 16, tab) * u[5];
+            y[6] = silu_s_lookup(w.w & 0xFFFFu, tab) * u[6];
+            y[7] = silu_s_lookup(w.w >> 16, tab) * u[7];
+        } else {
+            widen8<IN>(as_uint4(b.g[s]), y);
             if constexpr (FUSE) {
                 float u[8];
-                widen8<IN>(ru[s], u);
+                widen8<IN>(as_uint4(b.u[s]), u);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) y[k] = silu_mul(y[k], u[k]);
+                for (int k = 0; k < 8; ++k) y[k] = silu_s(y[k]) * u[k];
             }
-            float amax = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(y[k]));
-            amax = cluster_max<LPG>(amax);
+        }
+        float amax = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fabsf(y[2]));
+        amax = fmaxf(fmaxf(amax, fabsf(y[3])), fabsf(y[4]));
+        amax = fmaxf(fmaxf(amax, fabsf(y[5])), fabsf(y[6]));
+        amax = fmaxf(amax, fabsf(y[7]));
+        amax = cluster_max<LPG>(amax);
 
-            const bool ue8m0 = a.scale_fmt == SCALE_UE8M0;
-            const Scale sc = group_scale(amax, a.eps, qmax, ue8m0);
-            float v[8];
+        const Scale sc = group_scale<OUT>(amax, a.eps, ue8m0);
+        float v[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) v[k] = y[k] * sc.inv;
-            const uint2 codes = narrow8<OUT>(v);
-            if (valid) *reinterpret_cast<uint2 *>(qr + col) = codes;
+        for (int k = 0; k < 8; ++k) v[k] = y[k] * sc.inv;
+        const uint2 codes = ue8m0 ? narrow8<OUT, false>(v) : narrow8<OUT, true>(v);
+        u32x2 c2;
+        c2.x = codes.x;
+        c2.y = codes.y;
+        __builtin_amdgcn_raw_buffer_store_b64(c2, rq, col, 0, kStreamPolicy);  // dropped past the row
 
-            // scales
-            const int lg = lane / LPG;                        // group within slab
-            const int64_t gi = (int64_t)(s_begin + s) * GPS + lg;  // group within row
-            const bool leader = (lane % LPG) == 0;
-            if (ue8m0 && a.scale_layout == LAYOUT_COL) {
-                const uint32_t byte = valid ? sc.e : 0u;
+        // scales of the slab's groups
+        const int lg = lane / LPG;                                  // group within slab
+        const int64_t g0 = (int64_t)slab * GPS;                     // first group of slab
+        const bool leader = (lane % LPG) == 0;
+        if (ue8m0 && a.scale_layout == LAYOUT_COL) {
+            const uint32_t byte = valid ? sc.e : 0u;
+            if constexpr (G >= 64) {
+                // G/8 >= 8 lanes per group: read the bytes into scalars
+#pragma unroll
+                for (int w = 0; w < GPS / 4; ++w) {
+                    const uint32_t word =
+                        (uint32_t)__builtin_amdgcn_readlane((int)byte, (4 * w + 0) * LPG) |
+                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, (4 * w + 1) * LPG) << 8) |
+                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, (4 * w + 2) * LPG) << 16) |
+                        ((uint32_t)__builtin_amdgcn_readlane((int)byte, (4 * w + 3) * LPG) << 24);
+                    const int64_t gw = g0 + 4 * w;
+                    if (lane == 0 && gw < a.ng)
+                        reinterpret_cast<uint32_t *>(se)[(gw >> 2) * a.rows_pad + m] = word;
+                }
+            } else {
                 const uint32_t b1 = (uint32_t)__shfl((int)byte, lane + LPG);
                 const uint32_t b2 = (uint32_t)__shfl((int)byte, lane + 2 * LPG);
                 const uint32_t b3 = (uint32_t)__shfl((int)byte, lane + 3 * LPG);
                 if (leader && (lg & 3) == 0 && valid) {
                     const uint32_t word = byte | (b1 << 8) | (b2 << 16) | (b3 << 24);
-                    reinterpret_cast<uint32_t *>(se)[(gi >> 2) * a.rows_pad + m] = word;
+                    reinterpret_cast<uint32_t *>(se)[((g0 + lg) >> 2) * a.rows_pad + m] = word;
                 }
-            } else if (leader && valid) {
-                if (ue8m0)
-                    se[m * a.ng + gi] = (uint8_t)sc.e;
-                else if (a.scale_layout == LAYOUT_ROW)
-                    reinterpret_cast<float *>(se)[m * a.ng + gi] = sc.r;
-                else
-                    reinterpret_cast<float *>(se)[gi * a.rows_pad + m] = sc.r;
+            }
+        } else if (leader && valid) {
+            const int64_t gi = g0 + lg;
+            if (ue8m0)
+                se[m * a.ng + gi] = (uint8_t)sc.e;
+            else if (a.scale_layout == LAYOUT_ROW)
+                reinterpret_cast<float *>(se)[m * a.ng + gi] = sc.r;
+            else
+                reinterpret_cast<float *>(se)[gi * a.rows_pad + m] = sc.r;
+        }
+    }
+}
+
+// Flat schedule: task t is task t % tpr of row t / tpr.
+struct FlatMap {
+    __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int /*lane*/)
+    {
+        const int m = t / a.tpr;
+        TaskLoc l;
+        l.xrow = static_cast<const uint16_t *>(a.x) + (int64_t)m * a.in_stride;
+        l.qrow = a.q + (int64_t)m * a.K;
+        l.sbase = static_cast<uint8_t *>(a.s);
+        l.m = m;
+        l.j = t - m * a.tpr;
+        return l;
+    }
+};
+
+// Masked schedule: the live rows of all experts, back to back, are one task
+// space.  `scan` (LDS) holds the inclusive prefix sum of the experts' live row
+// counts, so live row R belongs to the first expert e with scan[e] > R and is
+// row R - scan[e-1] of that expert.  A wave's tasks only move forward, so the
+// 64-expert window of the search only moves forward too.
+struct MaskedMap {
+    const int *scan;
+    int E;
+    int chunk;
+    __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int lane)
+    {
+        const int R = t / a.tpr;
+        int e = E - 1;
+        for (; chunk < E; chunk += 64) {
+            const int idx = chunk + lane;
+            const int v = idx < E ? scan[idx] : INT32_MAX;
+            const unsigned long long hit = __ballot(v > R);
+            if (hit) {
+                e = chunk + (int)__builtin_ctzll(hit);
+                break;
             }
         }
+        const int r = R - (e == 0 ? 0 : scan[e - 1]);
+        TaskLoc l;
+        l.xrow = static_cast<const uint16_t *>(a.x) + (int64_t)e * a.x_expert_stride +
+                 (int64_t)r * a.in_stride;
+        l.qrow = a.q + (int64_t)e * a.q_expert_stride + (int64_t)r * a.K;
+        l.sbase = static_cast<uint8_t *>(a.s) + (int64_t)e * a.s_expert_stride;
+        l.m = r;
+        l.j = t - R * a.tpr;
+        return l;
+    }
+};
+
+// Tasks first, first + stride, ... < n, two at a time in flight.  A task
+// index past n is clamped for address arithmetic and loaded over an empty
+// range.
+template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE, class Map>
+__device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
+                                          int stride, int lane, const float *tab)
+{
+    int t = first;
+    if (t >= n) return;
+    TaskBuf<UMAX> A, B;
+    TaskLoc lA = map(a, t, lane);
+    load_task<FUSE, UMAX>(a, lA, lane, true, A);
+    while (true) {
+        const int tB = t + stride;
+        const bool hasB = tB < n;
+        const TaskLoc lB = map(a, hasB ? tB : t, lane);
+        load_task<FUSE, UMAX>(a, lB, lane, hasB, B);
+        process_task<IN, G, FUSE, OUT, UMAX, TABLE>(a, lA, lane, A, tab);
+        if (!hasB) break;
+        t = tB;
+        const int tA = t + stride;
+        const bool hasA = tA < n;
+        lA = map(a, hasA ? tA : t, lane);
+        load_task<FUSE, UMAX>(a, lA, lane, hasA, A);
+        process_task<IN, G, FUSE, OUT, UMAX, TABLE>(a, lB, lane, B, tab);
+        if (!hasA) break;
+        t = tA;
     }
 }
 
@@ -275,52 +504,79 @@ __device__ __forceinline__ int logical_block(int b, int nb)
     return (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
 }
 
-template <int IN, int G, bool FUSE, int OUT>
-__global__ __launch_bounds__(256) void ptgq_flat_kernel(GroupArgs a)
+// Copy the SiLU table into LDS (whole block; call before any early exit that
+// is not block-uniform).
+template <bool TABLE>
+__device__ __forceinline__ void stage_table(float *tab)
 {
+    if constexpr (TABLE) {
+        const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
+        float4 *dst = reinterpret_cast<float4 *>(tab);
+        for (int i = threadIdx.x; i < kSiluTab / 4; i += blockDim.x) dst[i] = src[i];
+        __syncthreads();
+    }
+}
+
+template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
+__global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs a)
+{
+    __shared__ float tab[TABLE ? kSiluTab : 1];
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x);
-    const int total = gridDim.x * wpb;
-    const uint16_t *x = static_cast<const uint16_t *>(a.x);
-    uint8_t *s = static_cast<uint8_t *>(a.s);
-    for (int t = lb * wpb + wib; t < a.n_tasks; t += total) {
-        const int m = t / a.tpr;
-        const int j = t - m * a.tpr;
-        group_task<IN, G, FUSE, OUT>(a, x, a.q, s, m, j, lane);
-    }
+    stage_table<TABLE>(tab);
+    run_tasks<IN, G, FUSE, OUT, UMAX, TABLE>(a, FlatMap{}, lb * wpb + wib, a.n_tasks,
+                                             gridDim.x * wpb, lane, tab);
     // column-major pad slots (rows M .. rows_pad-1) are zero
     if (a.pad_cols > 0 && lb == 0 && wib == 0) {
+        uint32_t *s = static_cast<uint32_t *>(a.s);
         const int64_t npad = (a.rows_pad - a.rows) * (int64_t)a.pad_cols;
         for (int64_t i = lane; i < npad; i += 64) {
             const int64_t r = a.rows + i / a.pad_cols;
             const int64_t c = i % a.pad_cols;
-            reinterpret_cast<uint32_t *>(s)[c * a.rows_pad + r] = 0u;
+            s[c * a.rows_pad + r] = 0u;
         }
     }
 }
 
-template <int IN, int G, bool FUSE, int OUT>
-__global__ __launch_bounds__(256) void ptgq_masked_kernel(GroupArgs a)
+// Masked layout, balanced over experts: every block reads masked_m (E values,
+// clamped to [0, tokens_pad]) into an LDS prefix sum, and the grid walks the
+// live rows of all experts as one task space.  Rows at or past masked_m are
+// never read or written.  Dynamic LDS: E ints.
+template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
+__global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupArgs a)
 {
+    __shared__ float tab[TABLE ? kSiluTab : 1];
+    extern __shared__ int scan[];
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
-    const int e = blockIdx.x / a.blocks_per_expert;
-    const int lb = blockIdx.x - e * a.blocks_per_expert;
-    int live = a.masked_m[e];
-    live = live < 0 ? 0 : (live > a.rows ? (int)a.rows : live);
-    const int n = live * a.tpr;
-    const uint16_t *xe = static_cast<const uint16_t *>(a.x) + e * a.x_expert_stride;
-    uint8_t *qe = a.q + e * a.q_expert_stride;
-    uint8_t *se = static_cast<uint8_t *>(a.s) + e * a.s_expert_stride;
-    const int stride = a.blocks_per_expert * wpb;
-    for (int t = lb * wpb + wib; t < n; t += stride) {
-        const int m = t / a.tpr;
-        const int j = t - m * a.tpr;
-        group_task<IN, G, FUSE, OUT>(a, xe, qe, se, m, j, lane);
+    const int lb = logical_block(blockIdx.x, gridDim.x);
+    const int E = a.num_experts;
+    if (wib == 0) {
+        int carry = 0;
+        for (int c = 0; c < E; c += 64) {
+            int v = 0;
+            if (c + lane < E) {
+                v = a.masked_m[c + lane];
+                v = v < 0 ? 0 : (v > a.rows ? (int)a.rows : v);
+            }
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(v, d);
+                if (lane >= d) v += y;
+            }
+            if (c + lane < E) scan[c + lane] = v + carry;
+            carry += __shfl(v, 63);
+        }
     }
+    __syncthreads();
+    const int n = scan[E - 1] * a.tpr;
+    if (lb * wpb >= n) return;                    // block-uniform: nothing to do
+    stage_table<TABLE>(tab);
+    run_tasks<IN, G, FUSE, OUT, UMAX, TABLE>(a, MaskedMap{scan, E, 0}, lb * wpb + wib, n,
+                                             gridDim.x * wpb, lane, tab);
 }
 
 // --------------------------------------------------------------------------
@@ -337,9 +593,18 @@ struct TokVec {
     static constexpr int EV = VB / insz;    // elements per vector
     using raw_t = typename std::conditional<VB == 16, uint4, uint2>::type;
 
+    // non-temporal, like the group kernels' streaming accesses
     __device__ static __forceinline__ raw_t load(const uint8_t *p)
     {
-        return *reinterpret_cast<const raw_t *>(p);
+        raw_t r;
+        if constexpr (VB == 16) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+            r = make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+            r = make_uint2(v.x, v.y);
+        }
+        return r;
     }
     __device__ static __forceinline__ raw_t zero()
     {
@@ -372,12 +637,13 @@ struct TokVec {
     __device__ static __forceinline__ void store_codes(uint8_t *p, const float (&v)[EV])
     {
         if constexpr (EV == 8) {
-            uint2 o;
-            o.x = e4m3x4(v[0], v[1], v[2], v[3]);
-            o.y = e4m3x4(v[4], v[5], v[6], v[7]);
-            *reinterpret_cast<uint2 *>(p) = o;
+            u32x2 o;
+            o.x = e4m3x4<true>(v[0], v[1], v[2], v[3]);
+            o.y = e4m3x4<true>(v[4], v[5], v[6], v[7]);
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(p));
         } else {
-            *reinterpret_cast<uint32_t *>(p) = e4m3x4(v[0], v[1], v[2], v[3]);
+            __builtin_nontemporal_store(e4m3x4<true>(v[0], v[1], v[2], v[3]),
+                                        reinterpret_cast<uint32_t *>(p));
         }
     }
 };
@@ -520,25 +786,29 @@ __global__ __launch_bounds__(256) void probe_e4m3_kernel(const float *__restrict
                                                          uint8_t *__restrict__ out, int64_t n)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) out[i] = (uint8_t)(e4m3x4(v[i], 0.0f, 0.0f, 0.0f) & 0xFFu);
+    if (i < n) out[i] = (uint8_t)(e4m3x4<true>(v[i], 0.0f, 0.0f, 0.0f) & 0xFFu);
 }
 
+// path 0: direct evaluation; path 1: the bf16 lookup (global-memory copy of
+// the table the fused kernels stage in LDS).
 template <int IN>
 __global__ __launch_bounds__(256) void probe_silu_kernel(const uint16_t *__restrict__ g,
                                                          const uint16_t *__restrict__ u,
-                                                         float *__restrict__ out, int64_t n)
+                                                         float *__restrict__ out, int64_t n,
+                                                         int path)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) {
-        float gf, uf;
+        float s, uf;
         if constexpr (IN == IN_BF16) {
-            gf = __uint_as_float((uint32_t)g[i] << 16);
             uf = __uint_as_float((uint32_t)u[i] << 16);
+            s = path == 1 ? silu_s_lookup(g[i], g_silu_table)
+                          : silu_s(__uint_as_float((uint32_t)g[i] << 16));
         } else {
-            gf = fp16_to_f32(g[i]);
             uf = fp16_to_f32(u[i]);
+            s = silu_s(fp16_to_f32(g[i]));
         }
-        out[i] = silu_mul(gf, uf);
+        out[i] = s * uf;
     }
 }
 
@@ -546,53 +816,90 @@ __global__ __launch_bounds__(256) void probe_silu_kernel(const uint16_t *__restr
 // Launchers: runtime traits -> template instantiation.
 // --------------------------------------------------------------------------
 
-template <int IN, int G, bool FUSE, int OUT>
+hipError_t launch_silu_table_init(hipStream_t stream)
+{
+    silu_table_init_kernel<<<kSiluTab / 256, 256, 0, stream>>>();
+    return hipGetLastError();
+}
+
+template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
 static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid, unsigned block,
                                  hipStream_t st)
 {
     if (masked)
-        ptgq_masked_kernel<IN, G, FUSE, OUT><<<grid, block, 0, st>>>(a);
+        ptgq_masked_kernel<IN, G, FUSE, OUT, UMAX, TABLE>
+            <<<grid, block, (size_t)a.num_experts * sizeof(int), st>>>(a);
     else
-        ptgq_flat_kernel<IN, G, FUSE, OUT><<<grid, block, 0, st>>>(a);
+        ptgq_flat_kernel<IN, G, FUSE, OUT, UMAX, TABLE><<<grid, block, 0, st>>>(a);
     return hipGetLastError();
 }
 
-template <int IN, int G, bool FUSE>
-static hipError_t launch_group_o(const GroupArgs &a, int out, bool masked, unsigned grid,
+// Task sizes: plain tasks 1, 2 or 4 slabs; fused tasks 1 or 2 (gate and up
+// double the registers).  The LDS SiLU table exists for bf16 gates only.
+template <int IN, int G, bool FUSE, int OUT>
+static hipError_t launch_group_u(const GroupArgs &a, bool table, bool masked, unsigned grid,
                                  unsigned block, hipStream_t st)
 {
-    return out == OUT_E4M3 ? launch_group_t<IN, G, FUSE, OUT_E4M3>(a, masked, grid, block, st)
-                           : launch_group_t<IN, G, FUSE, OUT_INT8>(a, masked, grid, block, st);
+    if constexpr (!FUSE) {
+        switch (a.U) {
+        case 1: return launch_group_t<IN, G, false, OUT, 1, false>(a, masked, grid, block, st);
+        case 2: return launch_group_t<IN, G, false, OUT, 2, false>(a, masked, grid, block, st);
+        case 4: return launch_group_t<IN, G, false, OUT, 4, false>(a, masked, grid, block, st);
+        default: return hipErrorInvalidValue;
+        }
+    } else if constexpr (IN == IN_BF16) {
+        if (table)
+            return a.U == 1 ? launch_group_t<IN, G, true, OUT, 1, true>(a, masked, grid, block, st)
+                 : a.U == 2 ? launch_group_t<IN, G, true, OUT, 2, true>(a, masked, grid, block, st)
+                            : hipErrorInvalidValue;
+        return a.U == 1 ? launch_group_t<IN, G, true, OUT, 1, false>(a, masked, grid, block, st)
+             : a.U == 2 ? launch_group_t<IN, G, true, OUT, 2, false>(a, masked, grid, block, st)
+                        : hipErrorInvalidValue;
+    } else {
+        return a.U == 1 ? launch_group_t<IN, G, true, OUT, 1, false>(a, masked, grid, block, st)
+             : a.U == 2 ? launch_group_t<IN, G, true, OUT, 2, false>(a, masked, grid, block, st)
+                        : hipErrorInvalidValue;
+    }
+}
+
+template <int IN, int G, bool FUSE>
+static hipError_t launch_group_o(const GroupArgs &a, int out, bool table, bool masked,
+                                 unsigned grid, unsigned block, hipStream_t st)
+{
+    return out == OUT_E4M3
+               ? launch_group_u<IN, G, FUSE, OUT_E4M3>(a, table, masked, grid, block, st)
+               : launch_group_u<IN, G, FUSE, OUT_INT8>(a, table, masked, grid, block, st);
 }
 
 template <int IN, int G>
-static hipError_t launch_group_f(const GroupArgs &a, bool fuse, int out, bool masked,
+static hipError_t launch_group_f(const GroupArgs &a, bool fuse, int out, bool table, bool masked,
                                  unsigned grid, unsigned block, hipStream_t st)
 {
-    return fuse ? launch_group_o<IN, G, true>(a, out, masked, grid, block, st)
-                : launch_group_o<IN, G, false>(a, out, masked, grid, block, st);
+    return fuse ? launch_group_o<IN, G, true>(a, out, table, masked, grid, block, st)
+                : launch_group_o<IN, G, false>(a, out, table, masked, grid, block, st);
 }
 
 template <int IN>
-static hipError_t launch_group_g(const GroupArgs &a, int G, bool fuse, int out, bool masked,
-                                 unsigned grid, unsigned block, hipStream_t st)
+static hipError_t launch_group_g(const GroupArgs &a, int G, bool fuse, int out, bool table,
+                                 bool masked, unsigned grid, unsigned block, hipStream_t st)
 {
     switch (G) {
-    case 16: return launch_group_f<IN, 16>(a, fuse, out, masked, grid, block, st);
-    case 32: return launch_group_f<IN, 32>(a, fuse, out, masked, grid, block, st);
-    case 64: return launch_group_f<IN, 64>(a, fuse, out, masked, grid, block, st);
-    case 128: return launch_group_f<IN, 128>(a, fuse, out, masked, grid, block, st);
+    case 16: return launch_group_f<IN, 16>(a, fuse, out, table, masked, grid, block, st);
+    case 32: return launch_group_f<IN, 32>(a, fuse, out, table, masked, grid, block, st);
+    case 64: return launch_group_f<IN, 64>(a, fuse, out, table, masked, grid, block, st);
+    case 128: return launch_group_f<IN, 128>(a, fuse, out, table, masked, grid, block, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_group(const GroupArgs &a, int in_dtype, int G, bool fuse, int out_dtype,
-                        bool masked, unsigned grid, unsigned block, hipStream_t stream)
+                        bool table, bool masked, unsigned grid, unsigned block,
+                        hipStream_t stream)
 {
     if (in_dtype == IN_BF16)
-        return launch_group_g<IN_BF16>(a, G, fuse, out_dtype, masked, grid, block, stream);
+        return launch_group_g<IN_BF16>(a, G, fuse, out_dtype, table, masked, grid, block, stream);
     if (in_dtype == IN_FP16)
-        return launch_group_g<IN_FP16>(a, G, fuse, out_dtype, masked, grid, block, stream);
+        return launch_group_g<IN_FP16>(a, G, fuse, out_dtype, false, masked, grid, block, stream);
     return hipErrorInvalidValue;
 }
 
@@ -647,16 +954,16 @@ hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_probe_silu(const void *g, const void *u, int in_dtype, float *out, int64_t n,
-                             hipStream_t stream)
+hipError_t launch_probe_silu(const void *g, const void *u, int in_dtype, int path, float *out,
+                             int64_t n, hipStream_t stream)
 {
     const unsigned grid = (unsigned)((n + 255) / 256);
     const uint16_t *gg = static_cast<const uint16_t *>(g);
     const uint16_t *uu = static_cast<const uint16_t *>(u);
     if (in_dtype == IN_BF16)
-        probe_silu_kernel<IN_BF16><<<grid, 256, 0, stream>>>(gg, uu, out, n);
+        probe_silu_kernel<IN_BF16><<<grid, 256, 0, stream>>>(gg, uu, out, n, path);
     else
-        probe_silu_kernel<IN_FP16><<<grid, 256, 0, stream>>>(gg, uu, out, n);
+        probe_silu_kernel<IN_FP16><<<grid, 256, 0, stream>>>(gg, uu, out, n, path);
     return hipGetLastError();
 }
 

@@ -76,24 +76,29 @@ class Timer:
         self.torch = torch
 
     def run(self, calls, steps, warmup):
+        """Two timed passes over `steps` launches: one HIP event pair around the
+        whole region (the per-step time, with nothing between launches), then
+        an event pair around every launch (the kernel's average duration)."""
         torch = self.torch
         for i in range(warmup):
             calls[i % len(calls)]()
         torch.cuda.synchronize()
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         region0 = torch.cuda.Event(enable_timing=True)
         region1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         wall0 = time.perf_counter()
         region0.record()
+        for i in range(steps):
+            calls[i % len(calls)]()
+        region1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         for i in range(steps):
             starts[i].record()
             calls[i % len(calls)]()
             ends[i].record()
-        region1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
         per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
         return {"region_ms": region0.elapsed_time(region1), "launch_ms_mean": float(np.mean(per)),
                 "launch_ms_median": float(np.median(per)), "wall_s": wall}

@@ -31,7 +31,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous on that stream and never synchronize the host, so they may
  *     be captured into a HIP graph.  The first call on a device (or ptgq_init)
- *     queries the device's compute-unit count; no other host work happens.
+ *     queries the device's compute-unit count and builds the device's SiLU
+ *     lookup table (one small kernel and one host synchronization, never
+ *     repeated); no other host work happens.
  *   - Arguments are validated on the host before anything is launched.  A
  *     negative return value means nothing was launched and nothing written.
  *   - Sizes are int64.  A call with zero rows (M == 0, E == 0, or K == 0)
@@ -122,13 +124,15 @@ PTGQ_API int ptgq_quant(const void *x, int in_dtype, int64_t M, int64_t K, int g
  *              ptgq_scale_bytes(tokens_pad, K, G, fmt, layout) bytes (so the
  *              column-major form is [E][ng or ceil(ng/4)][pad4(tokens_pad)]).
  *   Rows at or past masked_m are neither read nor written, in q or in s
- *   (column-major pad slots included): the caller's contents stay.
+ *   (column-major pad slots included): the caller's contents stay.  The live
+ *   rows of all experts are spread evenly over the launch, whatever their
+ *   distribution over experts.
  * Sources: sglang #30924 review page, implementation breakdown (masked_m and
  * expected_m); sglang #27449 PR body, summary and validation (masked layout
  * scheduler, [num_experts, tokens_pad, hidden*2] with silu+mul); sglang
  * #35593 review page, key source snippets (rows past masked_m untouched).
  * Errors: as ptgq_quant, plus PTGQ_EINVAL for E < 0, tokens_pad < 0 or a NULL
- * masked_m with E > 0.
+ * masked_m with E > 0, and PTGQ_EUNSUPPORTED for E > 4096.
  */
 PTGQ_API int ptgq_quant_masked(const void *x, int in_dtype, int64_t E, int64_t tokens_pad, int64_t K,
                       int group_size, int fuse_silu_mul, const int32_t *masked_m,
@@ -165,10 +169,11 @@ PTGQ_API size_t ptgq_scale_bytes(int64_t rows, int64_t K, int group_size, int sc
 PTGQ_API const char *ptgq_status_string(int status);
 
 /*
- * ptgq_init - optional: make `device` (a HIP ordinal) ready, querying its
- * compute-unit count now rather than at the first call on it.  Calls that
- * are captured into a HIP graph should follow one ptgq_init (or one ordinary
- * call) on their device.  Returns PTGQ_OK or PTGQ_EDEVICE.
+ * ptgq_init - optional: make `device` (a HIP ordinal) ready now rather than
+ * at the first call on it: query its compute-unit count and build its SiLU
+ * lookup table (this synchronizes the device once).  Calls that are captured
+ * into a HIP graph must follow one ptgq_init (or one ordinary call) on their
+ * device.  Returns PTGQ_OK or PTGQ_EDEVICE.
  */
 PTGQ_API int ptgq_init(int device);
 
@@ -182,20 +187,25 @@ PTGQ_API int ptgq_init(int device);
  *   uint8 [n]; both 4-byte aligned.
  * ptgq_probe_silu_mul: out[i] = silu(g[i]) * u[i] in fp32, where g, u are
  *   device arrays of in_dtype (PTGQ_BF16 or PTGQ_FP16) bit patterns [n]
- *   and out is device float [n].
- * Errors: PTGQ_EINVAL (n < 0, NULL pointer, bad dtype), PTGQ_ELAUNCH.
+ *   and out is device float [n].  path 0: the direct evaluation (e^-g in
+ *   double precision rounded to fp32, then fp32 add, divide, multiply);
+ *   path 1 (bf16 only): the lookup of g / (1 + e^-g) that large fused calls
+ *   use, followed by the multiply.
+ * Errors: PTGQ_EINVAL (n < 0, NULL pointer, bad dtype or path), PTGQ_ELAUNCH,
+ * PTGQ_EDEVICE.
  */
 PTGQ_API int ptgq_probe_e4m3(const float *v, uint8_t *out, int64_t n, void *stream);
-PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, float *out, int64_t n,
-                        void *stream);
+PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int path,
+                                 float *out, int64_t n, void *stream);
 
 /*
  * ptgq_set_tuning - diagnostics only: override one decision of the launch
  * geometry chooser for the whole process (value -1 restores the automatic
- * choice).  Knobs: 0 slabs per task (1..4; one slab = 512 elements of a row),
- * 1 waves per block (1..4), 2 resident blocks per compute unit (grid cap),
- * 3 per-token mode (0 one wave per row, 1 one block per row, 2 two-pass
- * block).  Results never depend on these; only speed does.  Not synchronized
+ * choice).  Knobs: 0 slabs per task (1..4, at most 2 when fused; one slab
+ * = 512 elements of a row), 1 waves per block (1..4), 2 resident blocks per
+ * compute unit (grid cap), 3 per-token mode (0 one wave per row, 1 one block
+ * per row, 2 two-pass block), 4 fused bf16 SiLU path (0 direct evaluation, 1
+ * LDS lookup table).  Results never depend on these; only speed does.  Not synchronized
  * with calls running on other host threads.  Returns PTGQ_OK or PTGQ_EINVAL.
  */
 PTGQ_API int ptgq_set_tuning(int knob, int64_t value);

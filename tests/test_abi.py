@@ -116,6 +116,7 @@ def masked(**kw):
     (dict(masked_m=A16 + 2), aq.PTGQ_EALIGN),
     (dict(group_size=8), aq.PTGQ_EINVAL),
     (dict(x=A16 + 4), aq.PTGQ_EALIGN),
+    (dict(E=4097), aq.PTGQ_EUNSUPPORTED),
     (dict(E=0, x=0, q=0, s=0, masked_m=0), aq.PTGQ_OK),
     (dict(tokens_pad=0, x=0, q=0, s=0, masked_m=0), aq.PTGQ_OK),
 ])
@@ -147,7 +148,9 @@ def test_probe_validation(lib):
     assert aq.ptgq_probe_e4m3(0, A16, 5, stream=0, check=False) == aq.PTGQ_EINVAL
     assert aq.ptgq_probe_e4m3(A16, A16, -1, stream=0, check=False) == aq.PTGQ_EINVAL
     assert aq.ptgq_probe_e4m3(0, 0, 0, stream=0, check=False) == aq.PTGQ_OK
-    assert aq.ptgq_probe_silu_mul(A16, A16, 2, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_silu_mul(A16, A16, 2, 0, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_silu_mul(A16, A16, "fp16", 1, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_silu_mul(A16, A16, "bf16", 2, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
     with pytest.raises(aq.PtgqError):
         aq.ptgq_set_tuning(9, 1)
 

@@ -120,6 +120,40 @@ def test_masked_sweep(fuse, fmt, layout):
     compare(f"masked fuse={fuse} {fmt} {layout} mm={list(mm)}", gq, gs, rq, rs)
 
 
+@pytest.mark.parametrize("dist", ["one_expert", "alternating", "many_experts", "single",
+                                  "all_empty", "all_full"])
+def test_masked_balanced_schedule(dist):
+    """The balanced masked schedule under skewed live-row distributions, more
+    than 64 experts (several search windows) and degenerate cases."""
+    rng = np.random.default_rng(abs(hash(dist)) % 1000)
+    if dist == "one_expert":
+        E, T, K, mm = 16, 200, 1024, np.zeros(16, np.int32)
+        mm[11] = 200
+    elif dist == "alternating":
+        E, T, K = 12, 96, 2048
+        mm = np.array([0, 96] * 6, np.int32)
+    elif dist == "many_experts":
+        E, T, K = 150, 9, 512
+        mm = rng.integers(-2, 12, E).astype(np.int32)
+    elif dist == "single":
+        E, T, K, mm = 1, 77, 1536, np.array([77], np.int32)
+    elif dist == "all_empty":
+        E, T, K, mm = 8, 40, 512, np.zeros(8, np.int32)
+    else:
+        E, T, K = 8, 33, 640
+        mm = np.full(8, 33, np.int32)
+    x = W.normal_bf16(E * 1000 + T, (E, T, 2 * K))
+    for fuse in (False, True):
+        xi = x if fuse else np.ascontiguousarray(x[:, :, :K])
+        for exp_m in (0, 3):
+            gq, gs = run_masked(xi, "bf16", E, T, K, 128, fuse, mm, exp_m, "e4m3", "ue8m0", "col")
+            sb = aq.ptgq_scale_bytes(T, K, 128, "ue8m0", "col")
+            rq, rs = oracle.ptgq_masked(xi, "bf16", E, T, K, 128, fuse, mm, "e4m3", "ue8m0", "col",
+                                        q_init=np.full((E, T, K), 0x7F, np.uint8),
+                                        s_init=np.full(E * sb, 0xFF, np.uint8))
+            compare(f"masked {dist} fuse={fuse} expected_m={exp_m}", gq, gs, rq, rs)
+
+
 # --------------------------------------------------------------- per-token
 
 @pytest.mark.parametrize("mode", [-1, 0, 1, 2])
@@ -189,19 +223,66 @@ def test_special_values(eps, fmt):
                     *oracle.ptgq(*args, eps=eps))
 
 
-def test_tuning_knobs_never_change_results():
-    d = W.cfg2(256)
-    args = (d["x"], "bf16", 256, d["K"], 128, False, "e4m3", "ue8m0", "col")
+def reset_knobs():
+    for k in range(5):
+        aq.ptgq_set_tuning(k, -1)
+
+
+@pytest.mark.parametrize("fuse", [False, True])
+def test_tuning_knobs_never_change_results(fuse):
+    M, K = 300, 7168 if not fuse else 3584
+    x = W.normal_bf16(808 + fuse, (M, 2 * K if fuse else K), factor_cols=[7, 99], factor=30.0)
+    args = (x, "bf16", M, K, 128, fuse, "e4m3", "ue8m0", "col")
     ref = oracle.ptgq(*args)
     try:
-        for knob, values in ((0, [1, 2, 3, 4]), (1, [1, 2, 4]), (2, [1, 2, 64])):
+        for knob, values in ((0, [1, 2, 4]), (1, [1, 2, 4]), (2, [1, 2, 64]), (4, [0, 1])):
             for v in values:
                 aq.ptgq_set_tuning(knob, v)
-                compare(f"knob {knob}={v}", *run_flat(*args), *ref)
+                compare(f"fuse={fuse} knob {knob}={v}", *run_flat(*args), *ref)
                 aq.ptgq_set_tuning(knob, -1)
     finally:
-        for k in range(4):
-            aq.ptgq_set_tuning(k, -1)
+        reset_knobs()
+
+
+@pytest.mark.parametrize("table", [0, 1])
+@pytest.mark.parametrize("U", [1, 2])
+def test_fused_paths_ragged(U, table):
+    """Both SiLU paths and both fused task sizes, rows whose last task runs past
+    the row (K = 640: 2 slabs, second one ragged), masked and flat."""
+    try:
+        aq.ptgq_set_tuning(0, U)
+        aq.ptgq_set_tuning(4, table)
+        for M, K in ((7, 640), (33, 1664), (2, 4096)):
+            x = W.normal_bf16(M * 10 + K, (M, 2 * K), factor_cols=[0, K + 3], factor=9.0)
+            for fmt, lay in (("ue8m0", "col"), ("f32", "row")):
+                args = (x, "bf16", M, K, 128, True, "e4m3", fmt, lay)
+                compare(f"fused U={U} table={table} M={M} K={K} {fmt} {lay}", *run_flat(*args),
+                        *oracle.ptgq(*args))
+        d = W.cfg4(seed=4300, E=6, T=50, K=640)
+        gq, gs = run_masked(d["x"], "bf16", 6, 50, 640, 128, True, d["masked_m"], 0, "e4m3",
+                            "ue8m0", "col")
+        sb = aq.ptgq_scale_bytes(50, 640, 128, "ue8m0", "col")
+        rq, rs = oracle.ptgq_masked(d["x"], "bf16", 6, 50, 640, 128, True, d["masked_m"], "e4m3",
+                                    "ue8m0", "col", q_init=np.full((6, 50, 640), 0x7F, np.uint8),
+                                    s_init=np.full(6 * sb, 0xFF, np.uint8))
+        compare(f"masked fused U={U} table={table}", gq, gs, rq, rs)
+    finally:
+        reset_knobs()
+
+
+@pytest.mark.parametrize("U", [1, 2, 4])
+def test_plain_task_sizes_ragged(U):
+    try:
+        aq.ptgq_set_tuning(0, U)
+        for M, K, G in ((5, 7168, 128), (9, 3584, 64), (3, 640, 32), (4, 128, 16), (17, 2560, 128)):
+            x = W.normal_fp16(M + K + G, (M, K))
+            for out_dtype, fmt, lay in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row"),
+                                        ("e4m3", "f32", "col"), ("int8", "ue8m0", "row")):
+                args = (x, "fp16", M, K, G, False, out_dtype, fmt, lay)
+                compare(f"U={U} M={M} K={K} G={G} {out_dtype} {fmt} {lay}", *run_flat(*args),
+                        *oracle.ptgq(*args))
+    finally:
+        reset_knobs()
 
 
 def test_runs_on_a_side_stream():

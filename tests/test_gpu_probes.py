@@ -49,8 +49,8 @@ def test_e4m3_narrowing_every_fp32_in_range():
     assert np.array_equal(got, oracle.e4m3(v))
 
 
-@pytest.mark.parametrize("in_dtype", ["bf16", "fp16"])
-def test_silu_mul_every_16bit_gate(in_dtype):
+@pytest.mark.parametrize("in_dtype,path", [("bf16", 0), ("bf16", 1), ("fp16", 0)])
+def test_silu_mul_every_16bit_gate(in_dtype, path):
     g_bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
     gf = oracle.decode(g_bits, in_dtype)
     keep = np.isfinite(gf)
@@ -61,12 +61,12 @@ def test_silu_mul_every_16bit_gate(in_dtype):
         gd = torch.from_numpy(g_bits.view(np.int16)).to(DEV)
         ud = torch.from_numpy(u_bits.view(np.int16)).to(DEV)
         out = torch.empty(g_bits.size, dtype=torch.float32, device=DEV)
-        aq.ptgq_probe_silu_mul(gd, ud, in_dtype, out, g_bits.size)
+        aq.ptgq_probe_silu_mul(gd, ud, in_dtype, path, out, g_bits.size)
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         ref = oracle.silu_mul(gf, oracle.decode(u_bits, in_dtype))
         bad = (got.view(np.uint32) != ref.view(np.uint32)) & keep
-        print(f"silu probe {in_dtype} u={u}: {int(bad.sum())} mismatches over {int(keep.sum())} "
+        print(f"silu probe {in_dtype} path {path} u={u}: {int(bad.sum())} mismatches over {int(keep.sum())} "
               f"finite gates", flush=True)
         if bad.any():
             i = int(np.flatnonzero(bad)[0])
