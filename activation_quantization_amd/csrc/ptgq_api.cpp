@@ -112,14 +112,14 @@ constexpr int64_t kInflightBytesPerCu = 48 * 1024;
 // slabs of work in total.  Few slabs (decode-sized M): one slab per task so
 // the work spreads over as many waves and CUs as possible.  Many: two slabs
 // per task when a row has an even number of slabs (no task runs past a row),
-// else one; fused tasks hold one slab (gate and up already double the bytes).
+// else one (plain and fused alike: measured best on MI355X).
 // Fused bf16 work large enough to amortize staging the 32 KiB table in LDS
 // reads the table.
 void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16, int cus)
 {
     const int64_t wave_slots = (int64_t)cus * 4 * 8;   // 8 waves per SIMD
     int U = 1;
-    if (!fuse && slabs >= 2 * wave_slots && spr % 2 == 0) U = 2;
+    if (slabs >= 2 * wave_slots && spr % 2 == 0) U = 2;
     if (knob(KNOB_SLABS_PER_TASK) > 0) {
         const int64_t k = knob(KNOB_SLABS_PER_TASK);
         U = k >= 4 ? 4 : (k >= 2 ? 2 : 1);

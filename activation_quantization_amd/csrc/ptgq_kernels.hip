@@ -251,6 +251,37 @@ __device__ __forceinline__ float silu_s_lookup(uint32_t h, const float *tab)
     return E < kTabElo ? g * 0.5f : (E > kTabEhi ? big : t);
 }
 
+// Two bf16 gates packed in a dword -> LDS byte offsets of their table entries
+// (valid when both gates' magnitudes lie in the tabulated binades; `in_range`
+// says whether they do).  The table index of a gate is
+// (|bits| - Elo*128) + sign*NE*128 with NE*128 = 4096 = (bit 15) >> 3, so the
+// two 16-bit halves are clamped with packed u16 min/max and the rest is done
+// on the whole dword without any carry crossing the halves.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void silu_pair_offsets(uint32_t w, uint32_t &off_lo, uint32_t &off_hi,
+                                                  bool &in_range)
+{
+    constexpr uint32_t lo = kTabElo << 7;
+    constexpr uint32_t hi = ((kTabEhi + 1) << 7) - 1;
+    static_assert(kTabNE * 128 == 4096, "sign offset is bit 15 >> 3");
+    const uint32_t mag = w & 0x7FFF7FFFu;
+    const u16x2 lo2 = {(unsigned short)lo, (unsigned short)lo};
+    const u16x2 hi2 = {(unsigned short)hi, (unsigned short)hi};
+    const uint32_t c = __builtin_bit_cast(
+        uint32_t, __builtin_elementwise_min(__builtin_elementwise_max(
+                                                __builtin_bit_cast(u16x2, mag), lo2), hi2));
+    in_range = c == mag;
+    const uint32_t idx = ((c - lo * 0x10001u) | ((w & 0x80008000u) >> 3)) << 2;
+    off_lo = idx & 0xFFFFu;
+    off_hi = idx >> 16;
+}
+
+__device__ __forceinline__ float lds_f32_at(const float *tab, uint32_t byte_off)
+{
+    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(tab) + byte_off);
+}
+
 // --------------------------------------------------------------------------
 // Group quantization tasks.
 //   A task is UMAX consecutive slabs of one row: slabs [j*UMAX, j*UMAX+UMAX)
@@ -344,14 +375,22 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
             const u32x4 w = b.g[s];
             float u[8];
             widen8<IN>(as_uint4(b.u[s]), u);
-            y[0] = silu_s_lookup(w.x & 0xFFFFu, tab) * u[0];
-            y[1] = silu_s_lookup(w.x >> 16, tab) * u[1];
-            y[2] = silu_s_lookup(w.y & 0xFFFFu, tab) * u[2];
-            y[3] = silu_s_lookup(w.y >> 16, tab) * u[3];
-            y[4] = silu_s_lookup(w.z & 0xFFFFu, tab) * u[4];
-            y[5] = silu_s_lookup(w.z >> 16, tab) * u[5];
-            y[6] = silu_s_lookup(w.w & 0xFFFFu, tab) * u[6];
-            y[7] = silu_s_lookup(w.w >> 16, tab) * u[7];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            uint32_t off[8];
+            bool in[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) silu_pair_offsets(ww[k], off[2 * k], off[2 * k + 1], in[k]);
+            if (__all(in[0] && in[1] && in[2] && in[3])) {
+                // every gate of the wave is tabulated: plain lookups
+#pragma unroll
+                for (int k = 0; k < 8; ++k) y[k] = lds_f32_at(tab, off[k]) * u[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    y[2 * k] = silu_s_lookup(ww[k] & 0xFFFFu, tab) * u[2 * k];
+                    y[2 * k + 1] = silu_s_lookup(ww[k] >> 16, tab) * u[2 * k + 1];
+                }
+            }
         } else {
             widen8<IN>(as_uint4(b.g[s]), y);
             if constexpr (FUSE) {
@@ -436,25 +475,37 @@ struct FlatMap {
 // space.  `scan` (LDS) holds the inclusive prefix sum of the experts' live row
 // counts, so live row R belongs to the first expert e with scan[e] > R and is
 // row R - scan[e-1] of that expert.  A wave's tasks only move forward, so the
-// 64-expert window of the search only moves forward too.
+// wave keeps the current 64-expert window of the prefix sum in a register
+// (lane l holds scan[chunk + l]) and searches it with one ballot; the window
+// only moves forward, re-read from LDS when a search runs off its end.
 struct MaskedMap {
     const int *scan;
     int E;
-    int chunk;
+    int chunk;    // first expert of the window
+    int base;     // scan[chunk - 1] (0 for the first window)
+    int win;      // this lane's scan[chunk + lane], INT32_MAX past E
+
+    __device__ __forceinline__ MaskedMap(const int *scan_, int E_, int lane)
+        : scan(scan_), E(E_), chunk(0), base(0), win(lane < E_ ? scan_[lane] : INT32_MAX)
+    {
+    }
+
     __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int lane)
     {
         const int R = t / a.tpr;
-        int e = E - 1;
-        for (; chunk < E; chunk += 64) {
-            const int idx = chunk + lane;
-            const int v = idx < E ? scan[idx] : INT32_MAX;
-            const unsigned long long hit = __ballot(v > R);
-            if (hit) {
-                e = chunk + (int)__builtin_ctzll(hit);
-                break;
-            }
+        unsigned long long hit = __ballot(win > R);
+        while (!hit && chunk + 64 < E) {                 // wave-uniform; rare
+            base = __builtin_amdgcn_readlane(win, 63);
+            chunk += 64;
+            win = chunk + lane < E ? scan[chunk + lane] : INT32_MAX;
+            hit = __ballot(win > R);
         }
-        const int r = R - (e == 0 ? 0 : scan[e - 1]);
+        // R is below the total live rows, so the last window always hits; the
+        // clamp only keeps a miss inside the experts
+        const int k = hit ? (int)__builtin_ctzll(hit) : min(63, E - 1 - chunk);
+        const int e = chunk + k;
+        const int prev = __builtin_amdgcn_readlane(win, k > 0 ? k - 1 : 0);
+        const int r = R - (k == 0 ? base : prev);
         TaskLoc l;
         l.xrow = static_cast<const uint16_t *>(a.x) + (int64_t)e * a.x_expert_stride +
                  (int64_t)r * a.in_stride;
@@ -466,18 +517,35 @@ struct MaskedMap {
     }
 };
 
+// Copy the SiLU table into LDS (whole block; call before any early exit that
+// is not block-uniform).
+template <bool TABLE>
+__device__ __forceinline__ void stage_table(float *tab)
+{
+    if constexpr (TABLE) {
+        const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
+        float4 *dst = reinterpret_cast<float4 *>(tab);
+        for (int i = threadIdx.x; i < kSiluTab / 4; i += blockDim.x) dst[i] = src[i];
+        __syncthreads();
+    }
+}
+
 // Tasks first, first + stride, ... < n, two at a time in flight.  A task
 // index past n is clamped for address arithmetic and loaded over an empty
-// range.
-template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE, class Map>
+// range.  Table kernels stage the SiLU table into LDS after the first task's
+// loads are issued (every wave of the block reaches that barrier, with or
+// without a task), so the table copy overlaps the first HBM reads.  n >= 1.
+template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE, bool STAGE, class Map>
 __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
-                                          int stride, int lane, const float *tab)
+                                          int stride, int lane, float *tab)
 {
     int t = first;
-    if (t >= n) return;
+    const bool hasA0 = t < n;
     TaskBuf<UMAX> A, B;
-    TaskLoc lA = map(a, t, lane);
-    load_task<FUSE, UMAX>(a, lA, lane, true, A);
+    TaskLoc lA = map(a, hasA0 ? t : 0, lane);
+    load_task<FUSE, UMAX>(a, lA, lane, hasA0, A);
+    if constexpr (STAGE) stage_table<TABLE>(tab);
+    if (!hasA0) return;
     while (true) {
         const int tB = t + stride;
         const bool hasB = tB < n;
@@ -504,19 +572,6 @@ __device__ __forceinline__ int logical_block(int b, int nb)
     return (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
 }
 
-// Copy the SiLU table into LDS (whole block; call before any early exit that
-// is not block-uniform).
-template <bool TABLE>
-__device__ __forceinline__ void stage_table(float *tab)
-{
-    if constexpr (TABLE) {
-        const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
-        float4 *dst = reinterpret_cast<float4 *>(tab);
-        for (int i = threadIdx.x; i < kSiluTab / 4; i += blockDim.x) dst[i] = src[i];
-        __syncthreads();
-    }
-}
-
 template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs a)
 {
@@ -525,8 +580,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x);
-    stage_table<TABLE>(tab);
-    run_tasks<IN, G, FUSE, OUT, UMAX, TABLE>(a, FlatMap{}, lb * wpb + wib, a.n_tasks,
+    run_tasks<IN, G, FUSE, OUT, UMAX, TABLE, true>(a, FlatMap{}, lb * wpb + wib, a.n_tasks,
                                              gridDim.x * wpb, lane, tab);
     // column-major pad slots (rows M .. rows_pad-1) are zero
     if (a.pad_cols > 0 && lb == 0 && wib == 0) {
@@ -554,6 +608,15 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x);
     const int E = a.num_experts;
+    // The table copy (all waves; table kernels always run 1024-lane blocks, 2
+    // float4 per lane) and the prefix sum of masked_m (wave 0) run side by
+    // side, behind one barrier.
+    float4 staged[TABLE ? kSiluTab / 4 / 1024 : 1];
+    if constexpr (TABLE) {
+        const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
+#pragma unroll
+        for (int i = 0; i < kSiluTab / 4 / 1024; ++i) staged[i] = src[threadIdx.x + 1024 * i];
+    }
     if (wib == 0) {
         int carry = 0;
         for (int c = 0; c < E; c += 64) {
@@ -568,15 +631,19 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
                 if (lane >= d) v += y;
             }
             if (c + lane < E) scan[c + lane] = v + carry;
-            carry += __shfl(v, 63);
+            carry += __builtin_amdgcn_readlane(v, 63);
         }
+    }
+    if constexpr (TABLE) {
+        float4 *dst = reinterpret_cast<float4 *>(tab);
+#pragma unroll
+        for (int i = 0; i < kSiluTab / 4 / 1024; ++i) dst[threadIdx.x + 1024 * i] = staged[i];
     }
     __syncthreads();
     const int n = scan[E - 1] * a.tpr;
     if (lb * wpb >= n) return;                    // block-uniform: nothing to do
-    stage_table<TABLE>(tab);
-    run_tasks<IN, G, FUSE, OUT, UMAX, TABLE>(a, MaskedMap{scan, E, 0}, lb * wpb + wib, n,
-                                             gridDim.x * wpb, lane, tab);
+    run_tasks<IN, G, FUSE, OUT, UMAX, TABLE, false>(a, MaskedMap(scan, E, lane), lb * wpb + wib,
+                                                    n, gridDim.x * wpb, lane, tab);
 }
 
 // --------------------------------------------------------------------------
@@ -802,8 +869,28 @@ __global__ __launch_bounds__(256) void probe_silu_kernel(const uint16_t *__restr
         float s, uf;
         if constexpr (IN == IN_BF16) {
             uf = __uint_as_float((uint32_t)u[i] << 16);
-            s = path == 1 ? silu_s_lookup(g[i], g_silu_table)
-                          : silu_s(__uint_as_float((uint32_t)g[i] << 16));
+            if (path == 1) {
+                // the fused kernels' lookup: the packed-pair offsets (gate i in
+                // the low half, then in the high half, beside another gate)
+                // when the gate is tabulated, else the per-gate form
+                const uint32_t other = g[(i + 12345) % n];
+                uint32_t lo0, hi0, lo1, hi1;
+                bool in0, in1;
+                silu_pair_offsets((uint32_t)g[i] | (other << 16), lo0, hi0, in0);
+                silu_pair_offsets(other | ((uint32_t)g[i] << 16), lo1, hi1, in1);
+                const uint32_t E = (g[i] >> 7) & 0xFFu, Eo = (other >> 7) & 0xFFu;
+                const bool tabulated = E >= kTabElo && E <= kTabEhi;
+                const bool both = tabulated && Eo >= kTabElo && Eo <= kTabEhi;
+                if (in0 != both || in1 != both || (tabulated && lo0 != hi1))
+                    s = __uint_as_float(0x7FC00000u);            // NaN: never equal
+                else if (tabulated)
+                    s = lds_f32_at(g_silu_table, lo0);
+                else
+                    s = silu_s_lookup(g[i], g_silu_table);
+                (void)hi0; (void)lo1;
+            } else {
+                s = silu_s(__uint_as_float((uint32_t)g[i] << 16));
+            }
         } else {
             uf = fp16_to_f32(u[i]);
             s = silu_s(fp16_to_f32(g[i]));

@@ -131,6 +131,15 @@ class Timer:
         return e0.elapsed_time(e1) / (replays * per_graph)
 
 
+def variant_entry(r, steps, nbytes):
+    """us/call and GB/s of a variant from the region timing (back-to-back
+    launches), with the per-launch event mean beside it."""
+    us = r["region_ms"] * 1e3 / steps
+    return {"us_per_call": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+            "frac_of_peak": round(nbytes / us / 1e3 / PEAK_GBS, 4),
+            "us_per_launch_events": round(r["launch_ms_mean"] * 1e3, 2)}
+
+
 def rotation_sets(footprint, cap=64):
     return int(max(2, min(cap, math.ceil(GIB / max(footprint, 1)))))
 
@@ -261,9 +270,7 @@ def main():
         _, c3 = make_flat_sets(torch, aq, d3["x"], 8192, 4096, 128, True, "e4m3", "ue8m0", "col",
                                "bf16", rotation_sets(f3))
         r3 = timer.run(c3, 100, 10)
-        variants["fused_silu_mul_M8192_K4096"] = {
-            "us_per_call": round(r3["launch_ms_mean"] * 1e3, 2), "bytes": f3,
-            "GBps": round(f3 / (r3["launch_ms_mean"] * 1e-3) / 1e9, 1)}
+        variants["fused_silu_mul_M8192_K4096"] = variant_entry(r3, 100, f3)
         del c3
         # masked MoE, E=32, tokens_pad=384, fused, K=2048
         d4 = W.cfg4()
@@ -282,9 +289,7 @@ def main():
                 xi, "bf16", E, T, K4, 128, True, mm_d, int(live // E), "e4m3", "ue8m0", "col",
                 1e-10, q4, s4, check=False)))
         r4 = timer.run(c4, 100, 10)
-        variants["masked_E32_T384_K2048_fused"] = {
-            "us_per_call": round(r4["launch_ms_mean"] * 1e3, 2), "bytes": f4, "live_rows": live,
-            "GBps": round(f4 / (r4["launch_ms_mean"] * 1e-3) / 1e9, 1)}
+        variants["masked_E32_T384_K2048_fused"] = dict(variant_entry(r4, 100, f4), live_rows=live)
         del c4
         # fp16 [8192, 3584] -> int8, fp32 row-major scales, G = 128; per-token e4m3
         d5 = W.cfg5()
@@ -292,9 +297,7 @@ def main():
         _, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, 128, False, "int8", "f32", "row",
                                "fp16", rotation_sets(f5))
         r5 = timer.run(c5, 100, 10)
-        variants["int8_fp16_M8192_K3584_G128"] = {
-            "us_per_call": round(r5["launch_ms_mean"] * 1e3, 2), "bytes": f5,
-            "GBps": round(f5 / (r5["launch_ms_mean"] * 1e-3) / 1e9, 1)}
+        variants["int8_fp16_M8192_K3584_G128"] = variant_entry(r5, 100, f5)
         del c5
         f5b = 8192 * 3584 * 2 + 8192 * 3584 + 8192 * 4
         x5 = torch.from_numpy(d5["x"].view(np.int16)).to("cuda")
@@ -306,9 +309,7 @@ def main():
             c5b.append((lambda xi=xi, q5=q5, s5=s5: aq.ptq_quant_fp8(xi, "fp16", 8192, 3584, q5,
                                                                     s5, check=False)))
         r5b = timer.run(c5b, 100, 10)
-        variants["per_token_fp8_fp16_M8192_K3584"] = {
-            "us_per_call": round(r5b["launch_ms_mean"] * 1e3, 2), "bytes": f5b,
-            "GBps": round(f5b / (r5b["launch_ms_mean"] * 1e-3) / 1e9, 1)}
+        variants["per_token_fp8_fp16_M8192_K3584"] = variant_entry(r5b, 100, f5b)
         del c5b
         torch.cuda.empty_cache()
 
