@@ -150,12 +150,27 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse)
         per_cu = std::max<int64_t>(1, waves_per_cu / wpb);
     }
     if (knob(KNOB_BLOCKS_PER_CU) > 0) per_cu = knob(KNOB_BLOCKS_PER_CU);
+    // The capped grid loops over the tasks, so it must give every CU the same
+    // number of blocks (a CU with one block more finishes last).  Its waves
+    // run ceil(tasks / waves) tasks at most: when that tail costs more than 5 %
+    // at per_cu blocks per CU, a third more blocks per CU is used if it
+    // divides the tasks better.
+    if (!g.table && knob(KNOB_BLOCKS_PER_CU) <= 0) {
+        const int64_t w0 = (int64_t)cus * per_cu * wpb;
+        const int64_t alt = per_cu + std::max<int64_t>(1, per_cu / 3);
+        const int64_t w1 = (int64_t)cus * alt * wpb;
+        const double loss0 = (double)((tasks + w0 - 1) / w0) * w0 / tasks;
+        const double loss1 = (double)((tasks + w1 - 1) / w1) * w1 / tasks;
+        if (tasks > w0 && loss0 > 1.05 && loss1 < loss0) per_cu = alt;
+    }
     g.wpb = wpb;
     g.per_cu = per_cu;
     int64_t blocks = (tasks + wpb - 1) / wpb;
     const int64_t cap = std::max<int64_t>(1, (int64_t)cus * per_cu);
-    if (blocks > cap) blocks = cap;
-    if (blocks >= 64) blocks = blocks / 8 * 8;
+    if (blocks > cap)
+        blocks = cap;                                  // a multiple of the CU count
+    else if (blocks >= 64)
+        blocks = (blocks + 7) / 8 * 8;                 // spare waves find no task
     g.grid = (unsigned)std::max<int64_t>(blocks, 1);
 }
 
