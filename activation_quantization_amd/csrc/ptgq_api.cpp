@@ -82,7 +82,7 @@ int check_group_args(const void *x, int in_dtype, int64_t outer, int64_t rows, i
     if (scale_layout != PTGQ_ROW_MAJOR && scale_layout != PTGQ_COL_MAJOR) return PTGQ_EINVAL;
     if (!valid_group_size(G)) return PTGQ_EINVAL;
     if (outer < 0 || rows < 0 || K < 0 || K % G != 0) return PTGQ_EINVAL;
-    if (!(std::isfinite(eps) && eps >= 0.0f)) return PTGQ_EINVAL;
+    if (!(std::isfinite(eps) && eps >= 0.0f) || std::signbit(eps)) return PTGQ_EINVAL;
     if (outer == 0 || rows == 0 || K == 0) return PTGQ_OK;
     if (K >= (int64_t)1 << 29) return PTGQ_EUNSUPPORTED;   // rows are 32-bit buffer ranges
     if (!x || !q || !s) return PTGQ_EINVAL;
@@ -108,7 +108,7 @@ constexpr int kTableBlocksPerCu = 1;  // one table block of 16 waves per CU
 // task's loads while it processes the current one).
 constexpr int64_t kInflightBytesPerCu = 48 * 1024;
 
-// Slabs per task (1, 2 or 4; fused 1 or 2) and the SiLU path, for `slabs`
+// Slabs per task (1 or 2) and the SiLU path, for `slabs`
 // slabs of work in total.  Few slabs (decode-sized M): one slab per task so
 // the work spreads over as many waves and CUs as possible.  Many: two slabs
 // per task when a row has an even number of slabs (no task runs past a row),
@@ -120,11 +120,8 @@ void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16,
     const int64_t wave_slots = (int64_t)cus * 4 * 8;   // 8 waves per SIMD
     int U = 1;
     if (slabs >= 2 * wave_slots && spr % 2 == 0) U = 2;
-    if (knob(KNOB_SLABS_PER_TASK) > 0) {
-        const int64_t k = knob(KNOB_SLABS_PER_TASK);
-        U = k >= 4 ? 4 : (k >= 2 ? 2 : 1);
-    }
-    g.U = std::min(U, fuse ? kMaxSlabsPerFusedTask : kMaxSlabsPerTask);
+    if (knob(KNOB_SLABS_PER_TASK) > 0) U = knob(KNOB_SLABS_PER_TASK) >= 2 ? 2 : 1;
+    g.U = std::min(U, kMaxSlabsPerTask);
     g.table = fuse && bf16 && slabs >= (int64_t)cus * 4 * kTableWaves;
     if (fuse && bf16 && knob(KNOB_SILU_TABLE) >= 0) g.table = knob(KNOB_SILU_TABLE) > 0;
 }
@@ -334,9 +331,10 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
     a.nv = (int32_t)nv;
 
     // Token-count dispatch (the analogue of the warp/CTA threshold of the
-    // sglang #34257 page): with enough rows to fill the chip, one wave per row;
-    // otherwise one 256-lane block per row; rows too long for registers take
-    // the two-pass loop.
+    // sglang #34257 page): with enough rows to fill the chip and rows of at
+    // most 8 KiB (8 vectors per lane), one wave per row; otherwise one 256-lane
+    // block per row (measured faster for 14 KiB rows); rows too long for
+    // registers take the two-pass loop.
     const int64_t per_wave = (nv + 63) / 64;
     const int64_t per_block = (nv + 255) / 256;
     TokenMode mode;
@@ -344,7 +342,7 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
     if (forced == TOKEN_WAVE && per_wave <= 16) mode = TOKEN_WAVE;
     else if (forced == TOKEN_BLOCK && per_block <= 16) mode = TOKEN_BLOCK;
     else if (forced == TOKEN_BLOCK_LOOP) mode = TOKEN_BLOCK_LOOP;
-    else if (M >= (int64_t)cus * 8 && per_wave <= 16) mode = TOKEN_WAVE;
+    else if (M >= (int64_t)cus * 8 && per_wave <= 8) mode = TOKEN_WAVE;
     else if (per_block <= 16) mode = TOKEN_BLOCK;
     else mode = TOKEN_BLOCK_LOOP;
 

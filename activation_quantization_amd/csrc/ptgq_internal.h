@@ -13,12 +13,11 @@ enum : int { SCALE_F32 = 0, SCALE_UE8M0 = 1 };
 enum : int { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
 
 // Elements of one "slab": one 16-byte load per lane across a 64-lane wave
-// (8 sixteen-bit elements per lane).  Every group-quant task is U = 1, 2 or 4
-// consecutive slabs of one row (1 or 2 when fused); the last task of a row may
-// run past its end (those lanes read zeros and store nothing).
+// (8 sixteen-bit elements per lane).  Every group-quant task is U = 1 or 2
+// consecutive slabs of one row; the last task of a row may run past its end
+// (those lanes read zeros and store nothing).
 constexpr int kSlab = 512;
-constexpr int kMaxSlabsPerTask = 4;
-constexpr int kMaxSlabsPerFusedTask = 2;
+constexpr int kMaxSlabsPerTask = 2;
 // Masked calls keep a prefix sum of E ints in LDS.
 constexpr int kMaxExperts = 4096;
 
@@ -39,7 +38,7 @@ struct GroupArgs {
     int64_t s_expert_stride;  // masked: bytes per expert of s
     float eps;                // amax floor
     int32_t spr;              // slabs per row, ceil(K / kSlab)
-    int32_t U;                // slabs per task: 1, 2 or 4 (fused: 1 or 2)
+    int32_t U;                // slabs per task: 1 or 2
     int32_t tpr;              // tasks per row, ceil(spr / U)
     int32_t n_tasks;          // flat: rows * tpr
     int32_t scale_fmt;        // SCALE_F32 / SCALE_UE8M0

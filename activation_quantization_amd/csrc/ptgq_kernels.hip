@@ -68,34 +68,74 @@ __device__ __forceinline__ void widen8(const uint4 r, float (&f)[8])
 }
 
 // --------------------------------------------------------------------------
-// Cluster max with DPP.  All lanes of each aligned LANES-lane cluster end
-// with the cluster maximum.  Values are non-negative.
+// Maxima of non-negative floats, taken on their bit patterns (which order
+// exactly like the values), so no NaN canonicalization is needed and each
+// DPP step folds into one v_max_u32_dpp (old value 0, the identity).
 // --------------------------------------------------------------------------
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v)
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v)
 {
-    const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF,
-                                              0xF, false);
-    return fmaxf(v, __int_as_float(o));
+    const uint32_t o =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+    return v > o ? v : o;
 }
 
+// All lanes of each aligned LANES-lane cluster end with the cluster maximum.
 template <int LANES>
-__device__ __forceinline__ float cluster_max(float v)
+__device__ __forceinline__ uint32_t cluster_max_bits(uint32_t v)
 {
-    if constexpr (LANES >= 2) v = dpp_max<0xB1>(v);    // quad_perm [1,0,3,2]
-    if constexpr (LANES >= 4) v = dpp_max<0x4E>(v);    // quad_perm [2,3,0,1]
-    if constexpr (LANES >= 8) v = dpp_max<0x141>(v);   // row_half_mirror
-    if constexpr (LANES >= 16) v = dpp_max<0x140>(v);  // row_mirror
+    if constexpr (LANES >= 2) v = dpp_umax<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (LANES >= 4) v = dpp_umax<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (LANES >= 8) v = dpp_umax<0x141>(v);   // row_half_mirror
+    if constexpr (LANES >= 16) v = dpp_umax<0x140>(v);  // row_mirror
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v)
+// Wave maximum, returned wave-uniform: row maxima, then row_bcast:15 into
+// rows 1 and 3 and row_bcast:31 into rows 2 and 3, so lane 63 holds the lot.
+__device__ __forceinline__ uint32_t wave_max_bits(uint32_t v)
 {
-    v = cluster_max<16>(v);
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    v = cluster_max_bits<16>(v);
+    v = dpp_umax<0x142, 0xA>(v);                        // row_bcast:15
+    v = dpp_umax<0x143, 0xC>(v);                        // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// |x| maximum of 8 sixteen-bit floats (bf16 or fp16) held in 4 dwords, as the
+// fp32 bit pattern of that maximum: magnitudes of both formats order like
+// their bit patterns, so packed u16 maxima of (bits & 0x7FFF) suffice.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_umax16(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+template <int IN>
+__device__ __forceinline__ uint32_t absmax8_bits(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3)
+{
+    const uint32_t m = pk_umax16(pk_umax16(w0 & 0x7FFF7FFFu, w1 & 0x7FFF7FFFu),
+                                 pk_umax16(w2 & 0x7FFF7FFFu, w3 & 0x7FFF7FFFu));
+    const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    const uint32_t h = lo > hi ? lo : hi;
+    if constexpr (IN == IN_BF16)
+        return h << 16;
+    else
+        return __float_as_uint(fp16_to_f32(h));
+}
+
+// |x| maximum of fp32 values, as a bit pattern.
+__device__ __forceinline__ uint32_t absmax_bits(const float (&y)[8])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t b = __float_as_uint(y[k]) & 0x7FFFFFFFu;
+        m = m > b ? m : b;
+    }
+    return m;
 }
 
 // --------------------------------------------------------------------------
@@ -141,12 +181,13 @@ struct Scale {
     uint32_t e;      // UE8M0 byte
 };
 
+// `amax_bits` and `eps_bits`: bit patterns of non-negative floats (eps >= +0).
 template <int OUT>
-__device__ __forceinline__ Scale group_scale(float amax, float eps, bool ue8m0)
+__device__ __forceinline__ Scale group_scale(uint32_t amax_bits, uint32_t eps_bits, bool ue8m0)
 {
     const float qmax = (OUT == OUT_E4M3) ? 448.0f : 127.0f;
     Scale sc;
-    const float a = (amax > eps) ? amax : eps;
+    const float a = __uint_as_float(amax_bits > eps_bits ? amax_bits : eps_bits);
     if (!ue8m0) {
         sc.r = a / qmax;
         sc.e = 0;
@@ -355,7 +396,7 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
 
 __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
-template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
 __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &t, int lane,
                                              const TaskBuf<UMAX> &b, const float *tab)
 {
@@ -364,7 +405,7 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
     const rsrc_t rq = make_rsrc(t.qrow, (uint32_t)a.K);
     uint8_t *se = t.sbase;
     const int64_t m = t.m;
-    const bool ue8m0 = a.scale_fmt == SCALE_UE8M0;
+    constexpr bool ue8m0 = SF == SCALE_UE8M0;
 #pragma unroll
     for (int s = 0; s < UMAX; ++s) {
         const int slab = t.j * UMAX + s;                            // slab within row
@@ -400,17 +441,18 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
                 for (int k = 0; k < 8; ++k) y[k] = silu_s(y[k]) * u[k];
             }
         }
-        float amax = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fabsf(y[2]));
-        amax = fmaxf(fmaxf(amax, fabsf(y[3])), fabsf(y[4]));
-        amax = fmaxf(fmaxf(amax, fabsf(y[5])), fabsf(y[6]));
-        amax = fmaxf(amax, fabsf(y[7]));
-        amax = cluster_max<LPG>(amax);
+        uint32_t amax;
+        if constexpr (FUSE)
+            amax = absmax_bits(y);
+        else
+            amax = absmax8_bits<IN>(b.g[s].x, b.g[s].y, b.g[s].z, b.g[s].w);
+        amax = cluster_max_bits<LPG>(amax);
 
-        const Scale sc = group_scale<OUT>(amax, a.eps, ue8m0);
+        const Scale sc = group_scale<OUT>(amax, __float_as_uint(a.eps), ue8m0);
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = y[k] * sc.inv;
-        const uint2 codes = ue8m0 ? narrow8<OUT, false>(v) : narrow8<OUT, true>(v);
+        const uint2 codes = narrow8<OUT, !ue8m0>(v);
         u32x2 c2;
         c2.x = codes.x;
         c2.y = codes.y;
@@ -420,7 +462,8 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
         const int lg = lane / LPG;                                  // group within slab
         const int64_t g0 = (int64_t)slab * GPS;                     // first group of slab
         const bool leader = (lane % LPG) == 0;
-        if (ue8m0 && a.scale_layout == LAYOUT_COL) {
+        if constexpr (ue8m0) {
+          if (a.scale_layout == LAYOUT_COL) {
             const uint32_t byte = valid ? sc.e : 0u;
             if constexpr (G >= 64) {
                 // G/8 >= 8 lanes per group: read the bytes into scalars
@@ -444,11 +487,12 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
                     reinterpret_cast<uint32_t *>(se)[((g0 + lg) >> 2) * a.rows_pad + m] = word;
                 }
             }
+          } else if (leader && valid) {
+            se[m * a.ng + g0 + lg] = (uint8_t)sc.e;
+          }
         } else if (leader && valid) {
             const int64_t gi = g0 + lg;
-            if (ue8m0)
-                se[m * a.ng + gi] = (uint8_t)sc.e;
-            else if (a.scale_layout == LAYOUT_ROW)
+            if (a.scale_layout == LAYOUT_ROW)
                 reinterpret_cast<float *>(se)[m * a.ng + gi] = sc.r;
             else
                 reinterpret_cast<float *>(se)[gi * a.rows_pad + m] = sc.r;
@@ -535,7 +579,8 @@ __device__ __forceinline__ void stage_table(float *tab)
 // range.  Table kernels stage the SiLU table into LDS after the first task's
 // loads are issued (every wave of the block reaches that barrier, with or
 // without a task), so the table copy overlaps the first HBM reads.  n >= 1.
-template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE, bool STAGE, class Map>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, bool STAGE,
+          class Map>
 __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
                                           int stride, int lane, float *tab)
 {
@@ -551,14 +596,14 @@ __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first
         const bool hasB = tB < n;
         const TaskLoc lB = map(a, hasB ? tB : t, lane);
         load_task<FUSE, UMAX>(a, lB, lane, hasB, B);
-        process_task<IN, G, FUSE, OUT, UMAX, TABLE>(a, lA, lane, A, tab);
+        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lA, lane, A, tab);
         if (!hasB) break;
         t = tB;
         const int tA = t + stride;
         const bool hasA = tA < n;
         lA = map(a, hasA ? tA : t, lane);
         load_task<FUSE, UMAX>(a, lA, lane, hasA, A);
-        process_task<IN, G, FUSE, OUT, UMAX, TABLE>(a, lB, lane, B, tab);
+        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lB, lane, B, tab);
         if (!hasA) break;
         t = tA;
     }
@@ -572,7 +617,7 @@ __device__ __forceinline__ int logical_block(int b, int nb)
     return (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
 }
 
-template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs a)
 {
     __shared__ float tab[TABLE ? kSiluTab : 1];
@@ -580,7 +625,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x);
-    run_tasks<IN, G, FUSE, OUT, UMAX, TABLE, true>(a, FlatMap{}, lb * wpb + wib, a.n_tasks,
+    run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, true>(a, FlatMap{}, lb * wpb + wib, a.n_tasks,
                                              gridDim.x * wpb, lane, tab);
     // column-major pad slots (rows M .. rows_pad-1) are zero
     if (a.pad_cols > 0 && lb == 0 && wib == 0) {
@@ -598,7 +643,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
 // clamped to [0, tokens_pad]) into an LDS prefix sum, and the grid walks the
 // live rows of all experts as one task space.  Rows at or past masked_m are
 // never read or written.  Dynamic LDS: E ints.
-template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupArgs a)
 {
     __shared__ float tab[TABLE ? kSiluTab : 1];
@@ -642,7 +687,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
     __syncthreads();
     const int n = scan[E - 1] * a.tpr;
     if (lb * wpb >= n) return;                    // block-uniform: nothing to do
-    run_tasks<IN, G, FUSE, OUT, UMAX, TABLE, false>(a, MaskedMap(scan, E, lane), lb * wpb + wib,
+    run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, false>(a, MaskedMap(scan, E, lane), lb * wpb + wib,
                                                     n, gridDim.x * wpb, lane, tab);
 }
 
@@ -701,6 +746,23 @@ struct TokVec {
             }
         }
     }
+    // |x| maximum of the vector, as an fp32 bit pattern
+    __device__ static __forceinline__ uint32_t absmax(const raw_t r)
+    {
+        if constexpr (IN == IN_FP32) {
+            const uint4 w = r;
+            const uint32_t a = (w.x & 0x7FFFFFFFu) > (w.y & 0x7FFFFFFFu) ? (w.x & 0x7FFFFFFFu)
+                                                                          : (w.y & 0x7FFFFFFFu);
+            const uint32_t b = (w.z & 0x7FFFFFFFu) > (w.w & 0x7FFFFFFFu) ? (w.z & 0x7FFFFFFFu)
+                                                                          : (w.w & 0x7FFFFFFFu);
+            return a > b ? a : b;
+        } else if constexpr (VB == 16) {
+            return absmax8_bits<IN>(r.x, r.y, r.z, r.w);
+        } else {
+            return absmax8_bits<IN>(r.x, r.y, 0u, 0u);
+        }
+    }
+
     __device__ static __forceinline__ void store_codes(uint8_t *p, const float (&v)[EV])
     {
         if constexpr (EV == 8) {
@@ -738,17 +800,14 @@ __global__ __launch_bounds__(256) void ptq_wave_kernel(TokenArgs a)
         const int i = lane + 64 * k;
         raw[k] = (i < a.nv) ? TV::load(xr + (int64_t)i * VB) : TV::zero();
     }
-    float amax = 0.0f;
+    uint32_t amax = 0;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-        float f[EV];
-        TV::widen(raw[k], f);
-#pragma unroll
-        for (int e = 0; e < EV; ++e) amax = fmaxf(amax, fabsf(f[e]));
+        const uint32_t m = TV::absmax(raw[k]);
+        amax = amax > m ? amax : m;
     }
-    amax = wave_max(amax);
     float r;
-    const float inv = token_inv(amax, r);
+    const float inv = token_inv(__uint_as_float(wave_max_bits(amax)), r);
     if (lane == 0) a.s[m] = r;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -763,14 +822,14 @@ __global__ __launch_bounds__(256) void ptq_wave_kernel(TokenArgs a)
     }
 }
 
-__device__ __forceinline__ float block_max(float v, float *red)
+__device__ __forceinline__ uint32_t block_max_bits(uint32_t v, uint32_t *red)
 {
-    v = wave_max(v);
+    v = wave_max_bits(v);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[w] = v;
     __syncthreads();
-    float m = red[0];
-    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, red[i]);
+    uint32_t m = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = m > red[i] ? m : red[i];
     return m;
 }
 
@@ -779,7 +838,7 @@ __global__ __launch_bounds__(256) void ptq_block_kernel(TokenArgs a)
 {
     using TV = TokVec<IN, VB>;
     constexpr int EV = TV::EV;
-    __shared__ float red[4];
+    __shared__ uint32_t red[4];
     const int tid = threadIdx.x;
     const int64_t m = blockIdx.x;
     const uint8_t *xr = static_cast<const uint8_t *>(a.x) + m * a.K * TV::insz;
@@ -790,17 +849,14 @@ __global__ __launch_bounds__(256) void ptq_block_kernel(TokenArgs a)
         const int i = tid + 256 * k;
         raw[k] = (i < a.nv) ? TV::load(xr + (int64_t)i * VB) : TV::zero();
     }
-    float amax = 0.0f;
+    uint32_t amax = 0;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-        float f[EV];
-        TV::widen(raw[k], f);
-#pragma unroll
-        for (int e = 0; e < EV; ++e) amax = fmaxf(amax, fabsf(f[e]));
+        const uint32_t mk = TV::absmax(raw[k]);
+        amax = amax > mk ? amax : mk;
     }
-    amax = block_max(amax, red);
     float r;
-    const float inv = token_inv(amax, r);
+    const float inv = token_inv(__uint_as_float(block_max_bits(amax, red)), r);
     if (tid == 0) a.s[m] = r;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -820,21 +876,18 @@ __global__ __launch_bounds__(256) void ptq_block_loop_kernel(TokenArgs a)
 {
     using TV = TokVec<IN, VB>;
     constexpr int EV = TV::EV;
-    __shared__ float red[4];
+    __shared__ uint32_t red[4];
     const int tid = threadIdx.x;
     const int64_t m = blockIdx.x;
     const uint8_t *xr = static_cast<const uint8_t *>(a.x) + m * a.K * TV::insz;
     uint8_t *qr = a.q + m * a.K;
-    float amax = 0.0f;
+    uint32_t amax = 0;
     for (int i = tid; i < a.nv; i += 256) {
-        float f[EV];
-        TV::widen(TV::load(xr + (int64_t)i * VB), f);
-#pragma unroll
-        for (int e = 0; e < EV; ++e) amax = fmaxf(amax, fabsf(f[e]));
+        const uint32_t mk = TV::absmax(TV::load(xr + (int64_t)i * VB));
+        amax = amax > mk ? amax : mk;
     }
-    amax = block_max(amax, red);
     float r;
-    const float inv = token_inv(amax, r);
+    const float inv = token_inv(__uint_as_float(block_max_bits(amax, red)), r);
     if (tid == 0) a.s[m] = r;
     for (int i = tid; i < a.nv; i += 256) {
         float f[EV];
@@ -909,44 +962,39 @@ hipError_t launch_silu_table_init(hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int IN, int G, bool FUSE, int OUT, int UMAX, bool TABLE>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
 static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid, unsigned block,
                                  hipStream_t st)
 {
     if (masked)
-        ptgq_masked_kernel<IN, G, FUSE, OUT, UMAX, TABLE>
+        ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE>
             <<<grid, block, (size_t)a.num_experts * sizeof(int), st>>>(a);
     else
-        ptgq_flat_kernel<IN, G, FUSE, OUT, UMAX, TABLE><<<grid, block, 0, st>>>(a);
+        ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE><<<grid, block, 0, st>>>(a);
     return hipGetLastError();
 }
 
-// Task sizes: plain tasks 1, 2 or 4 slabs; fused tasks 1 or 2 (gate and up
-// double the registers).  The LDS SiLU table exists for bf16 gates only.
-template <int IN, int G, bool FUSE, int OUT>
+// Task sizes: 1 or 2 slabs.  The LDS SiLU table exists for bf16 gates only.
+template <int IN, int G, bool FUSE, int OUT, int SF>
 static hipError_t launch_group_u(const GroupArgs &a, bool table, bool masked, unsigned grid,
                                  unsigned block, hipStream_t st)
 {
-    if constexpr (!FUSE) {
-        switch (a.U) {
-        case 1: return launch_group_t<IN, G, false, OUT, 1, false>(a, masked, grid, block, st);
-        case 2: return launch_group_t<IN, G, false, OUT, 2, false>(a, masked, grid, block, st);
-        case 4: return launch_group_t<IN, G, false, OUT, 4, false>(a, masked, grid, block, st);
-        default: return hipErrorInvalidValue;
-        }
-    } else if constexpr (IN == IN_BF16) {
-        if (table)
-            return a.U == 1 ? launch_group_t<IN, G, true, OUT, 1, true>(a, masked, grid, block, st)
-                 : a.U == 2 ? launch_group_t<IN, G, true, OUT, 2, true>(a, masked, grid, block, st)
-                            : hipErrorInvalidValue;
-        return a.U == 1 ? launch_group_t<IN, G, true, OUT, 1, false>(a, masked, grid, block, st)
-             : a.U == 2 ? launch_group_t<IN, G, true, OUT, 2, false>(a, masked, grid, block, st)
-                        : hipErrorInvalidValue;
-    } else {
-        return a.U == 1 ? launch_group_t<IN, G, true, OUT, 1, false>(a, masked, grid, block, st)
-             : a.U == 2 ? launch_group_t<IN, G, true, OUT, 2, false>(a, masked, grid, block, st)
-                        : hipErrorInvalidValue;
-    }
+    constexpr bool T = FUSE && IN == IN_BF16;
+    if (a.U != 1 && a.U != 2) return hipErrorInvalidValue;
+    if (T && table)
+        return a.U == 1 ? launch_group_t<IN, G, FUSE, OUT, SF, 1, T>(a, masked, grid, block, st)
+                        : launch_group_t<IN, G, FUSE, OUT, SF, 2, T>(a, masked, grid, block, st);
+    return a.U == 1 ? launch_group_t<IN, G, FUSE, OUT, SF, 1, false>(a, masked, grid, block, st)
+                    : launch_group_t<IN, G, FUSE, OUT, SF, 2, false>(a, masked, grid, block, st);
+}
+
+template <int IN, int G, bool FUSE, int OUT>
+static hipError_t launch_group_s(const GroupArgs &a, bool table, bool masked, unsigned grid,
+                                 unsigned block, hipStream_t st)
+{
+    return a.scale_fmt == SCALE_UE8M0
+               ? launch_group_u<IN, G, FUSE, OUT, SCALE_UE8M0>(a, table, masked, grid, block, st)
+               : launch_group_u<IN, G, FUSE, OUT, SCALE_F32>(a, table, masked, grid, block, st);
 }
 
 template <int IN, int G, bool FUSE>
@@ -954,8 +1002,8 @@ static hipError_t launch_group_o(const GroupArgs &a, int out, bool table, bool m
                                  unsigned grid, unsigned block, hipStream_t st)
 {
     return out == OUT_E4M3
-               ? launch_group_u<IN, G, FUSE, OUT_E4M3>(a, table, masked, grid, block, st)
-               : launch_group_u<IN, G, FUSE, OUT_INT8>(a, table, masked, grid, block, st);
+               ? launch_group_s<IN, G, FUSE, OUT_E4M3>(a, table, masked, grid, block, st)
+               : launch_group_s<IN, G, FUSE, OUT_INT8>(a, table, masked, grid, block, st);
 }
 
 template <int IN, int G>

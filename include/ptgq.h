@@ -95,14 +95,15 @@ enum ptgq_scale_layout { PTGQ_ROW_MAJOR = 0, PTGQ_COL_MAJOR = 1 };
  *   group_size G in {16, 32, 64, 128}; K % G == 0.
  *   out_dtype  PTGQ_E4M3 (OCP e4m3fn codes) or PTGQ_INT8 (two's complement).
  *   scale_fmt, scale_layout  see the layouts above.
- *   eps        floor of the group absmax (finite, >= 0; e.g. 1e-10).
+ *   eps        floor of the group absmax (finite, >= +0.0; -0.0 is rejected;
+ *              e.g. 1e-10).
  *   q          device uint8 [M, K] codes; 16-byte aligned.
  *   s          device scale tensor of ptgq_scale_bytes(M, K, G, fmt, layout)
  *              bytes; 4-byte aligned.
  * Sources: sglang #30924 review page, implementation breakdown (flat
  * schedule); sglang #27449 PR body, summary (naive scheduler over [M, K]).
  * Errors: PTGQ_EINVAL (M < 0, K < 0, G not allowed, K % G, bad enum, NULL
- * pointer with M*K > 0, eps not finite or negative), PTGQ_EALIGN,
+ * pointer with M*K > 0, eps not finite, negative or -0.0), PTGQ_EALIGN,
  * PTGQ_ELAUNCH, PTGQ_EDEVICE.
  */
 PTGQ_API int ptgq_quant(const void *x, int in_dtype, int64_t M, int64_t K, int group_size,
@@ -201,8 +202,8 @@ PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int
 /*
  * ptgq_set_tuning - diagnostics only: override one decision of the launch
  * geometry chooser for the whole process (value -1 restores the automatic
- * choice).  Knobs: 0 slabs per task (1..4, at most 2 when fused; one slab
- * = 512 elements of a row), 1 waves per block (1..4), 2 resident blocks per
+ * choice).  Knobs: 0 slabs per task (1 or 2; one slab = 512 elements of a
+ * row), 1 waves per block (1..4), 2 resident blocks per
  * compute unit (grid cap), 3 per-token mode (0 one wave per row, 1 one block
  * per row, 2 two-pass block), 4 fused bf16 SiLU path (0 direct evaluation, 1
  * LDS lookup table).  Results never depend on these; only speed does.  Not synchronized

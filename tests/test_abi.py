@@ -87,6 +87,7 @@ def quant(**kw):
     (dict(eps=float("nan")), aq.PTGQ_EINVAL),
     (dict(eps=-1.0), aq.PTGQ_EINVAL),
     (dict(eps=float("inf")), aq.PTGQ_EINVAL),
+    (dict(eps=-0.0), aq.PTGQ_EINVAL),
     (dict(x=0), aq.PTGQ_EINVAL),
     (dict(q=0), aq.PTGQ_EINVAL),
     (dict(s=0), aq.PTGQ_EINVAL),
