@@ -47,6 +47,10 @@ def _load():
         lib.oracle_silu_mul_vec.restype = None
         lib.oracle_decode_vec.argtypes = [vp, i32, vp, i64]
         lib.oracle_decode_vec.restype = None
+        lib.oracle_requant_fp8.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, f32, vp]
+        lib.oracle_requant_fp8.restype = i32
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = f32
         _lib = lib
     return _lib
 
@@ -113,6 +117,32 @@ def ptq_fp8(x, in_dtype, M, K):
     if rc != 0:
         raise ValueError("oracle_ptq_fp8 rejected its arguments")
     return q, s
+
+
+def requant_fp8(x, E, T, K, G, x_scale, strides, masked_m, output_scale, out_init=None):
+    """Per-token-group fp8 -> per-tensor fp8 requantization of x [E, T, K]
+    (uint8 e4m3 codes) with group scales x_scale (float32, element (e, t, g) at
+    e*strides[0] + t*strides[1] + g*strides[2]); rows past masked_m keep
+    out_init (None: every row is live when masked_m is None)."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    assert x.size == E * T * K
+    xs = np.ascontiguousarray(x_scale, dtype=np.float32)
+    out = np.array(out_init, dtype=np.uint8, copy=True).reshape(E, T, K) if out_init is not None \
+        else np.zeros((E, T, K), dtype=np.uint8)
+    mm = None if masked_m is None else np.ascontiguousarray(masked_m, dtype=np.int32)
+    rc = _load().oracle_requant_fp8(_ptr(x), E, T, K, G, _ptr(xs), int(strides[0]),
+                                    int(strides[1]), int(strides[2]),
+                                    None if mm is None else _ptr(mm), float(output_scale),
+                                    _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_requant_fp8 rejected its arguments")
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    table = np.array([lib.oracle_e4m3_decode(c) for c in range(256)], dtype=np.float32)
+    return table[np.asarray(codes, dtype=np.uint8)]
 
 
 # ---- element helpers (for pinning single steps) ----

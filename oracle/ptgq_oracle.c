@@ -370,6 +370,51 @@ int oracle_ptq_fp8(const void *x, int in_dtype, int64_t M, int64_t K, uint8_t *q
 }
 
 /* ------------------------------------------------------------------------ */
+/* Per-token-group fp8 -> per-tensor fp8 requantization (masked layout).     */
+/* ------------------------------------------------------------------------ */
+
+/* Value of an e4m3 code (finite codes; 0x7F / 0xFF are NaN). */
+static float e4m3_decode(uint8_t c)
+{
+    if (!e4m3_table_ready) e4m3_build_table();
+    if ((c & 0x7F) == 0x7F) return NAN;
+    const float mag = (float)e4m3_table[c & 0x7F];
+    return (c & 0x80) ? -mag : mag;
+}
+
+/* For expert e and rows t < min(max(masked_m[e], 0), T) (every row when
+ * masked_m is NULL): out[e][t][k] = e4m3_sat((dec(x[e][t][k]) * s) * inv) with
+ * s = x_scale[e*se + t*st + (k/G)*sg] and inv = 1 / output_scale, each product
+ * one fp32 rounding; rows past masked_m keep out's contents.
+ * ([sglang #35593] key source snippets: dequantize by the group scale, then
+ * multiply by the reciprocal of the per-tensor output scale, saturating RN
+ * narrowing; implementation breakdown: 128-wide scale groups, column-major
+ * [E, M, hidden/128] scales, rows past masked_m untouched.) */
+int oracle_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int G,
+                       const float *x_scale, int64_t se, int64_t st, int64_t sg,
+                       const int32_t *masked_m, float output_scale, uint8_t *out)
+{
+    if (E < 0 || T < 0 || K < 0 || G <= 0 || K % G != 0) return -1;
+    const float inv = 1.0f / output_scale;
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t live = masked_m ? masked_m[e] : T;
+        if (live < 0) live = 0;
+        if (live > T) live = T;
+        for (int64_t t = 0; t < live; ++t) {
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t i = (e * T + t) * K + k;
+                const float s = x_scale[e * se + t * st + (k / G) * sg];
+                const float h = e4m3_decode(x[i]) * s;
+                out[i] = e4m3_rne_sat(h * inv);
+            }
+        }
+    }
+    return 0;
+}
+
+float oracle_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
+
+/* ------------------------------------------------------------------------ */
 /* Element helpers, exported so that the tests can pin each step alone.      */
 /* ------------------------------------------------------------------------ */
 
