@@ -24,9 +24,9 @@ OUT_DTYPES = {"e4m3": PTGQ_E4M3, "int8": PTGQ_INT8}
 SCALE_FMTS = {"f32": PTGQ_SCALE_F32, "ue8m0": PTGQ_SCALE_UE8M0}
 SCALE_LAYOUTS = {"row": PTGQ_ROW_MAJOR, "col": PTGQ_COL_MAJOR}
 
-EXPORTS = ("ptgq_quant", "ptgq_quant_masked", "ptq_quant_fp8", "ptgq_scale_bytes",
-           "ptgq_status_string", "ptgq_init", "ptgq_probe_e4m3", "ptgq_probe_silu_mul",
-           "ptgq_set_tuning")
+EXPORTS = ("ptgq_quant", "ptgq_quant_masked", "ptq_quant_fp8", "ptgq_requant_fp8",
+           "ptgq_scale_bytes", "ptgq_status_string", "ptgq_init", "ptgq_probe_e4m3",
+           "ptgq_probe_silu_mul", "ptgq_set_tuning")
 
 
 class PtgqError(RuntimeError):
@@ -54,6 +54,9 @@ def load_library(path: str = LIB_PATH):
     lib.ptgq_quant_masked.restype = i32
     lib.ptq_quant_fp8.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     lib.ptq_quant_fp8.restype = i32
+    lib.ptgq_requant_fp8.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, i64, vp, vp,
+                                     vp]
+    lib.ptgq_requant_fp8.restype = i32
     lib.ptgq_scale_bytes.argtypes = [i64, i64, i32, i32, i32]
     lib.ptgq_scale_bytes.restype = ctypes.c_size_t
     lib.ptgq_status_string.argtypes = [i32]
@@ -176,6 +179,25 @@ def ptq_quant_fp8(x, in_dtype, M, K, q, s, stream=None, check=True):
     rc = load_library().ptq_quant_fp8(_ptr(x), _enum(in_dtype, IN_DTYPES), M, K, _ptr(q), _ptr(s),
                                       _stream(stream))
     return _check("ptq_quant_fp8", rc) if check else rc
+
+
+def ptgq_requant_fp8(x, E, T, K, group_size, x_scale, scale_strides, masked_m, expected_m,
+                     output_scale, out, stream=None, check=True):
+    """scale_strides = (stride_e, stride_t, stride_g) in elements."""
+    se, st, sg = (int(v) for v in scale_strides)
+    if E > 0 and T > 0 and K > 0 and group_size > 0 and K % group_size == 0 and min(se, st, sg) >= 0:
+        fn = "ptgq_requant_fp8"
+        _need(x, E * T * K, fn, "x")
+        _need(out, E * T * K, fn, "out")
+        _need(x_scale, 4 * ((E - 1) * se + (T - 1) * st + (K // group_size - 1) * sg + 1), fn,
+              "x_scale")
+        _need(output_scale, 4, fn, "output_scale")
+        if masked_m is not None:
+            _need(masked_m, 4 * E, fn, "masked_m")
+    rc = load_library().ptgq_requant_fp8(_ptr(x), E, T, K, group_size, _ptr(x_scale), se, st, sg,
+                                         _ptr(masked_m), int(expected_m), _ptr(output_scale),
+                                         _ptr(out), _stream(stream))
+    return _check("ptgq_requant_fp8", rc) if check else rc
 
 
 def ptgq_probe_e4m3(v, out, n, stream=None, check=True):

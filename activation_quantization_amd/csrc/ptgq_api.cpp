@@ -362,6 +362,56 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
 }
 
+int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int group_size,
+                     const float *x_scale, int64_t scale_stride_e, int64_t scale_stride_t,
+                     int64_t scale_stride_g, const int32_t *masked_m, int64_t expected_m,
+                     const float *output_scale, uint8_t *out, void *stream)
+{
+    if (E < 0 || T < 0 || K < 0 || !valid_group_size(group_size) || K % group_size != 0)
+        return PTGQ_EINVAL;
+    if (scale_stride_e < 0 || scale_stride_t < 0 || scale_stride_g < 0) return PTGQ_EINVAL;
+    if (E == 0 || T == 0 || K == 0) return PTGQ_OK;
+    if (!x || !x_scale || !output_scale || !out || x == out) return PTGQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(x_scale, 4) || !aligned(output_scale, 4) ||
+        (masked_m && !aligned(masked_m, 4)))
+        return PTGQ_EALIGN;
+    if (E > kMaxExperts || K >= ((int64_t)1 << 30)) return PTGQ_EUNSUPPORTED;
+    // a row's scales are read through a 32-bit buffer range
+    if (((K / group_size - 1) * scale_stride_g + 1) * 4 >= ((int64_t)1 << 32) - 16)
+        return PTGQ_EUNSUPPORTED;
+    const int64_t spr = (K + 1023) / 1024;
+    if (E * T * spr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+    const int cus = current_cus(nullptr);
+    if (cus <= 0) return PTGQ_EDEVICE;
+
+    RequantArgs a;
+    a.x = x;
+    a.x_scale = x_scale;
+    a.masked_m = masked_m;
+    a.output_scale = output_scale;
+    a.out = out;
+    a.T = T;
+    a.K = K;
+    a.se = scale_stride_e;
+    a.st = scale_stride_t;
+    a.sg = scale_stride_g;
+    a.E = (int32_t)E;
+    a.G = group_size;
+    a.spr = (int32_t)spr;
+    // Grid: every wave keeps two 1 KiB tasks in flight; ~48 KiB per CU is 24
+    // waves (6 four-wave blocks) per CU, capped by the expected tasks.
+    const int64_t hint = masked_m ? ((expected_m > 0 && expected_m < T) ? expected_m : T) : T;
+    const int64_t tasks = std::max<int64_t>(hint, 1) * spr * E;
+    const int wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
+    int64_t blocks = (tasks + wpb - 1) / wpb;
+    const int64_t cap = (int64_t)cus * (knob(KNOB_BLOCKS_PER_CU) > 0 ? knob(KNOB_BLOCKS_PER_CU) : 6);
+    if (blocks > cap) blocks = cap;
+    else if (blocks >= 64) blocks = (blocks + 7) / 8 * 8;
+    const hipError_t err = launch_requant(a, (unsigned)std::max<int64_t>(blocks, 1),
+                                          (unsigned)(wpb * 64), static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
+}
+
 int ptgq_probe_e4m3(const float *v, uint8_t *out, int64_t n, void *stream)
 {
     if (n < 0) return PTGQ_EINVAL;

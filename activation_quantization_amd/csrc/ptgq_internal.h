@@ -60,6 +60,21 @@ struct TokenArgs {
 
 enum TokenMode : int { TOKEN_WAVE = 0, TOKEN_BLOCK = 1, TOKEN_BLOCK_LOOP = 2 };
 
+// Arguments of the fp8 requantization kernel.
+struct RequantArgs {
+    const uint8_t *x;         // e4m3 codes [E, T, K]
+    const float *x_scale;     // group scales, element (e, t, g) at e*se + t*st + g*sg
+    const int32_t *masked_m;  // live rows per expert; nullptr: all T rows
+    const float *output_scale;// device scalar
+    uint8_t *out;             // e4m3 codes [E, T, K]
+    int64_t T;
+    int64_t K;
+    int64_t se, st, sg;
+    int32_t E;
+    int32_t G;
+    int32_t spr;              // 1024-code slabs per row
+};
+
 // Launchers (defined in ptgq_kernels.hip).  They return the hipError_t of the
 // launch.  `grid`/`block` are chosen by the caller.
 // `table`: fused bf16 kernels read g / (1 + e^-g) from the LDS-staged lookup
@@ -71,6 +86,7 @@ hipError_t launch_group(const GroupArgs &a, int in_dtype, int G, bool fuse, int 
 hipError_t launch_silu_table_init(hipStream_t stream);
 hipError_t launch_token(const TokenArgs &a, int in_dtype, int vec_bytes, TokenMode mode,
                         int nv_per_lane, unsigned grid, unsigned block, hipStream_t stream);
+hipError_t launch_requant(const RequantArgs &a, unsigned grid, unsigned block, hipStream_t stream);
 hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_t stream);
 hipError_t launch_probe_silu(const void *g, const void *u, int in_dtype, int path, float *out,
                              int64_t n, hipStream_t stream);

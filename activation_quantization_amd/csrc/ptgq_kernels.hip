@@ -518,25 +518,25 @@ struct FlatMap {
 // Masked schedule: the live rows of all experts, back to back, are one task
 // space.  `scan` (LDS) holds the inclusive prefix sum of the experts' live row
 // counts, so live row R belongs to the first expert e with scan[e] > R and is
-// row R - scan[e-1] of that expert.  A wave's tasks only move forward, so the
+// row R - scan[e-1] of that expert.  A wave's rows only move forward, so the
 // wave keeps the current 64-expert window of the prefix sum in a register
 // (lane l holds scan[chunk + l]) and searches it with one ballot; the window
 // only moves forward, re-read from LDS when a search runs off its end.
-struct MaskedMap {
+struct MaskedRows {
     const int *scan;
     int E;
     int chunk;    // first expert of the window
     int base;     // scan[chunk - 1] (0 for the first window)
     int win;      // this lane's scan[chunk + lane], INT32_MAX past E
 
-    __device__ __forceinline__ MaskedMap(const int *scan_, int E_, int lane)
+    __device__ __forceinline__ MaskedRows(const int *scan_, int E_, int lane)
         : scan(scan_), E(E_), chunk(0), base(0), win(lane < E_ ? scan_[lane] : INT32_MAX)
     {
     }
 
-    __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int lane)
+    // live row R (< total live rows) -> expert e and row r within it
+    __device__ __forceinline__ void locate(int R, int lane, int &e, int &r)
     {
-        const int R = t / a.tpr;
         unsigned long long hit = __ballot(win > R);
         while (!hit && chunk + 64 < E) {                 // wave-uniform; rare
             base = __builtin_amdgcn_readlane(win, 63);
@@ -547,9 +547,45 @@ struct MaskedMap {
         // R is below the total live rows, so the last window always hits; the
         // clamp only keeps a miss inside the experts
         const int k = hit ? (int)__builtin_ctzll(hit) : min(63, E - 1 - chunk);
-        const int e = chunk + k;
         const int prev = __builtin_amdgcn_readlane(win, k > 0 ? k - 1 : 0);
-        const int r = R - (k == 0 ? base : prev);
+        e = chunk + k;
+        r = R - (k == 0 ? base : prev);
+    }
+};
+
+// Inclusive prefix sum of clamp(masked_m[e], 0, rows) over e < E into LDS
+// `scan` (masked_m NULL: every row of every expert is live).  Wave 0 only;
+// the caller synchronizes.
+__device__ __forceinline__ void masked_prefix_sum(const int32_t *masked_m, int E, int64_t rows,
+                                                  int lane, int *scan)
+{
+    int carry = 0;
+    for (int c = 0; c < E; c += 64) {
+        int v = 0;
+        if (c + lane < E) {
+            v = masked_m ? masked_m[c + lane] : (int)rows;
+            v = v < 0 ? 0 : (v > rows ? (int)rows : v);
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(v, d);
+            if (lane >= d) v += y;
+        }
+        if (c + lane < E) scan[c + lane] = v + carry;
+        carry += __builtin_amdgcn_readlane(v, 63);
+    }
+}
+
+struct MaskedMap {
+    MaskedRows rows;
+
+    __device__ __forceinline__ MaskedMap(const int *scan, int E, int lane) : rows(scan, E, lane) {}
+
+    __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int lane)
+    {
+        const int R = t / a.tpr;
+        int e, r;
+        rows.locate(R, lane, e, r);
         TaskLoc l;
         l.xrow = static_cast<const uint16_t *>(a.x) + (int64_t)e * a.x_expert_stride +
                  (int64_t)r * a.in_stride;
@@ -662,23 +698,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
 #pragma unroll
         for (int i = 0; i < kSiluTab / 4 / 1024; ++i) staged[i] = src[threadIdx.x + 1024 * i];
     }
-    if (wib == 0) {
-        int carry = 0;
-        for (int c = 0; c < E; c += 64) {
-            int v = 0;
-            if (c + lane < E) {
-                v = a.masked_m[c + lane];
-                v = v < 0 ? 0 : (v > a.rows ? (int)a.rows : v);
-            }
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int y = __shfl_up(v, d);
-                if (lane >= d) v += y;
-            }
-            if (c + lane < E) scan[c + lane] = v + carry;
-            carry += __builtin_amdgcn_readlane(v, 63);
-        }
-    }
+    if (wib == 0) masked_prefix_sum(a.masked_m, E, a.rows, lane, scan);
     if constexpr (TABLE) {
         float4 *dst = reinterpret_cast<float4 *>(tab);
 #pragma unroll
@@ -899,6 +919,127 @@ __global__ __launch_bounds__(256) void ptq_block_loop_kernel(TokenArgs a)
 }
 
 // --------------------------------------------------------------------------
+// Per-token-group fp8 -> per-tensor fp8 requantization on the masked layout
+// (sglang #35593 review page, key source snippets): each e4m3 code is decoded,
+// multiplied by its group scale, then by 1 / output_scale (two fp32
+// roundings), and narrowed with saturation.  A slab here is 1024 codes of a
+// row (16 per lane, one 16-byte load); tasks are one slab of one live row,
+// balanced over all experts like the masked quantizer, two in flight per wave.
+// --------------------------------------------------------------------------
+
+constexpr int kRqSlab = 1024;
+
+__device__ __forceinline__ void decode4_e4m3(uint32_t w, float (&f)[4])
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = lo.x;
+    f[1] = lo.y;
+    f[2] = hi.x;
+    f[3] = hi.y;
+}
+
+struct RqLoc {
+    const uint8_t *xrow;
+    uint8_t *orow;
+    const float *srow;    // x_scale + e*se + r*st
+    int j;                // slab within row
+};
+
+__global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
+{
+    extern __shared__ int scan[];
+    const int lane = threadIdx.x & 63;
+    const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wpb = blockDim.x >> 6;
+    const int lb = logical_block(blockIdx.x, gridDim.x);
+    const int E = a.E;
+    if (wib == 0) masked_prefix_sum(a.masked_m, E, a.T, lane, scan);
+    __syncthreads();
+    const int n = scan[E - 1] * a.spr;
+    if (lb * wpb >= n) return;                              // block-uniform
+    MaskedRows rows(scan, E, lane);
+    const float inv = 1.0f / a.output_scale[0];
+    const uint32_t row_bytes = (uint32_t)a.K;
+
+    auto locate = [&](int t) {
+        const int R = t / a.spr;
+        int e, r;
+        rows.locate(R, lane, e, r);
+        RqLoc l;
+        const int64_t row = (int64_t)e * a.T + r;
+        l.xrow = a.x + row * a.K;
+        l.orow = a.out + row * a.K;
+        l.srow = a.x_scale + (int64_t)e * a.se + (int64_t)r * a.st;
+        l.j = t - R * a.spr;
+        return l;
+    };
+    // A task's loads: its 16 codes per lane and the lane's group scale, both
+    // through per-row buffer resources (the scale resource spans this row's
+    // scales), so lanes past the row read zeros and an empty task reads nothing.
+    const int64_t ng = a.K / a.G;
+    const uint32_t srow_bytes = (uint32_t)(((ng - 1) * a.sg + 1) * 4);
+    struct RqBuf {
+        u32x4 w;
+        float s;
+    };
+    auto load = [&](const RqLoc &l, bool live) {
+        RqBuf b;
+        const uint32_t col = (uint32_t)l.j * kRqSlab + lane * 16;
+        const rsrc_t rx = make_rsrc(l.xrow, live ? row_bytes : 0u);
+        b.w = __builtin_amdgcn_raw_buffer_load_b128(rx, col, 0, kStreamPolicy);
+        const rsrc_t rs = make_rsrc(l.srow, live ? srow_bytes : 0u);
+        const uint32_t soff = col < row_bytes ? (uint32_t)((col / a.G) * a.sg * 4) : 0xFFFFFFF0u;
+        b.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
+        return b;
+    };
+    auto process = [&](const RqLoc &l, const RqBuf &b) {
+        const uint32_t col = (uint32_t)l.j * kRqSlab + lane * 16;
+        const u32x4 w = b.w;
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float f[4];
+            decode4_e4m3(ww[k], f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[i] = (f[i] * b.s) * inv;
+            o[k] = e4m3x4<true>(f[0], f[1], f[2], f[3]);
+        }
+        const rsrc_t ro = make_rsrc(l.orow, row_bytes);
+        u32x4 ov;
+        ov.x = o[0];
+        ov.y = o[1];
+        ov.z = o[2];
+        ov.w = o[3];
+        __builtin_amdgcn_raw_buffer_store_b128(ov, ro, col, 0, kStreamPolicy);
+    };
+
+    const int stride = gridDim.x * wpb;
+    int t = lb * wpb + wib;
+    if (t >= n) return;
+    RqLoc lA = locate(t);
+    RqBuf A = load(lA, true), B;
+    while (true) {
+        const int tB = t + stride;
+        const bool hasB = tB < n;
+        const RqLoc lB = locate(hasB ? tB : t);
+        B = load(lB, hasB);
+        process(lA, A);
+        if (!hasB) break;
+        t = tB;
+        const int tA = t + stride;
+        const bool hasA = tA < n;
+        lA = locate(hasA ? tA : t);
+        A = load(lA, hasA);
+        process(lB, B);
+        if (!hasA) break;
+        t = tA;
+    }
+}
+
+// --------------------------------------------------------------------------
 // Probes: one step of the device arithmetic over arbitrary inputs.
 // --------------------------------------------------------------------------
 
@@ -1080,6 +1221,12 @@ hipError_t launch_token(const TokenArgs &a, int in_dtype, int vec_bytes, TokenMo
                    ? launch_token_v<IN_FP16, 16>(a, mode, nv_per_lane, grid, block, stream)
                    : launch_token_v<IN_FP16, 8>(a, mode, nv_per_lane, grid, block, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_requant(const RequantArgs &a, unsigned grid, unsigned block, hipStream_t stream)
+{
+    requant_fp8_kernel<<<grid, block, (size_t)a.E * sizeof(int), stream>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_t stream)

@@ -131,13 +131,17 @@ class Timer:
         return e0.elapsed_time(e1) / (replays * per_graph)
 
 
-def variant_entry(r, steps, nbytes):
-    """us/call and GB/s of a variant from the region timing (back-to-back
-    launches), with the per-launch event mean beside it."""
-    us = r["region_ms"] * 1e3 / steps
+def variant_entry(timer, calls, nbytes, steps=100):
+    """us/call and GB/s of a variant: device time per call of back-to-back
+    launches captured in a HIP graph (the pages time their kernels inside
+    graphs too), with the eager back-to-back figure beside it."""
+    r = timer.run(calls, steps, 10)
+    per_graph = max(len(calls), min(200, max(8, int(2e8 // max(nbytes, 1)))))
+    ms = timer.graph(calls, per_graph, 5)
+    us = ms * 1e3
     return {"us_per_call": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
             "frac_of_peak": round(nbytes / us / 1e3 / PEAK_GBS, 4),
-            "us_per_launch_events": round(r["launch_ms_mean"] * 1e3, 2)}
+            "us_per_call_eager": round(r["region_ms"] * 1e3 / steps, 2)}
 
 
 def rotation_sets(footprint, cap=64):
@@ -269,8 +273,7 @@ def main():
         f3 = alg_bytes_flat(8192, 4096, 128, 2, True, 1)
         _, c3 = make_flat_sets(torch, aq, d3["x"], 8192, 4096, 128, True, "e4m3", "ue8m0", "col",
                                "bf16", rotation_sets(f3))
-        r3 = timer.run(c3, 100, 10)
-        variants["fused_silu_mul_M8192_K4096"] = variant_entry(r3, 100, f3)
+        variants["fused_silu_mul_M8192_K4096"] = variant_entry(timer, c3, f3)
         del c3
         # masked MoE, E=32, tokens_pad=384, fused, K=2048
         d4 = W.cfg4()
@@ -288,16 +291,14 @@ def main():
             c4.append((lambda xi=xi, q4=q4, s4=s4: aq.ptgq_quant_masked(
                 xi, "bf16", E, T, K4, 128, True, mm_d, int(live // E), "e4m3", "ue8m0", "col",
                 1e-10, q4, s4, check=False)))
-        r4 = timer.run(c4, 100, 10)
-        variants["masked_E32_T384_K2048_fused"] = dict(variant_entry(r4, 100, f4), live_rows=live)
+        variants["masked_E32_T384_K2048_fused"] = dict(variant_entry(timer, c4, f4), live_rows=live)
         del c4
         # fp16 [8192, 3584] -> int8, fp32 row-major scales, G = 128; per-token e4m3
         d5 = W.cfg5()
         f5 = alg_bytes_flat(8192, 3584, 128, 2, False, 4)
         _, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, 128, False, "int8", "f32", "row",
                                "fp16", rotation_sets(f5))
-        r5 = timer.run(c5, 100, 10)
-        variants["int8_fp16_M8192_K3584_G128"] = variant_entry(r5, 100, f5)
+        variants["int8_fp16_M8192_K3584_G128"] = variant_entry(timer, c5, f5)
         del c5
         f5b = 8192 * 3584 * 2 + 8192 * 3584 + 8192 * 4
         x5 = torch.from_numpy(d5["x"].view(np.int16)).to("cuda")
@@ -308,9 +309,32 @@ def main():
             s5 = torch.empty((8192,), dtype=torch.float32, device="cuda")
             c5b.append((lambda xi=xi, q5=q5, s5=s5: aq.ptq_quant_fp8(xi, "fp16", 8192, 3584, q5,
                                                                     s5, check=False)))
-        r5b = timer.run(c5b, 100, 10)
-        variants["per_token_fp8_fp16_M8192_K3584"] = variant_entry(r5b, 100, f5b)
+        variants["per_token_fp8_fp16_M8192_K3584"] = variant_entry(timer, c5b, f5b)
         del c5b
+        torch.cuda.empty_cache()
+        # fp8 requantization, the sglang #35593 page's timed shape: K = 3584,
+        # 8 experts, 1024 live rows -- read both as 1024 rows in total (128 per
+        # expert) and as 1024 rows per expert; tokens_pad 1024, DeepEP
+        # column-major group scales, output scale 2
+        E8, T8, K8 = 8, 1024, 3584
+        rng = np.random.default_rng(35593)
+        xq = torch.from_numpy(rng.integers(0, 127, (E8, T8, K8)).astype(np.uint8)).to("cuda")
+        xs = torch.from_numpy(rng.uniform(0.5, 2.0, E8 * T8 * (K8 // 128)).astype(np.float32)).to("cuda")
+        osd = torch.tensor([2.0], dtype=torch.float32, device="cuda")
+        strides = (T8 * (K8 // 128), 1, T8)
+        for label, live in (("total", 128), ("per_expert", 1024)):
+            mmq = torch.full((E8,), live, dtype=torch.int32, device="cuda")
+            nsets = rotation_sets(E8 * live * 7280)
+            outs = [torch.empty((E8, T8, K8), dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+            ins = [xq] + [xq.clone() for _ in range(nsets - 1)]
+            cq = [(lambda xi=ins[i], oi=outs[i]: aq.ptgq_requant_fp8(
+                xi, E8, T8, K8, 128, xs, strides, mmq, live, osd, oi, check=False))
+                for i in range(nsets)]
+            fq = E8 * live * (K8 + K8 + (K8 // 128) * 4) + 4 * E8 + 4
+            variants[f"requant_fp8_E8_K3584_live1024_{label}"] = dict(
+                variant_entry(timer, cq, fq), live_rows=E8 * live,
+                pages_context_us={"H200": 25.4, "B200": 14.6})
+            del cq, outs, ins
         torch.cuda.empty_cache()
 
     cpu = None

@@ -158,6 +158,38 @@ PTGQ_API int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, vo
                   void *stream);
 
 /*
+ * ptgq_requant_fp8 - per-token-group fp8 -> per-tensor fp8 requantization
+ * on the masked layout: for expert e and rows t < min(max(masked_m[e], 0), T)
+ * (every row when masked_m is NULL),
+ *   out[e][t][k] = e4m3_sat((decode(x[e][t][k]) * s) * (1 / output_scale[0]))
+ * with s = x_scale[e*scale_stride_e + t*scale_stride_t + (k/G)*scale_stride_g],
+ * each product one fp32 rounding (1 / output_scale is an IEEE division),
+ * narrowed round-to-nearest-even with saturation to +-448.  Rows past
+ * masked_m keep out's contents.
+ *
+ *   x             device uint8 [E, T, K] e4m3 codes; 16-byte aligned.
+ *   group_size    G in {16, 32, 64, 128} (the pages use 128); K % G == 0, so
+ *                 K need only be G-aligned (e.g. 3584, 1152).
+ *   x_scale       device float group scales; strides in elements, >= 0 (the
+ *                 DeepEP layout [E, T, K/128] with its last two dims
+ *                 column-major is se = T*(K/128), st = 1, sg = T).
+ *   masked_m      device int32 [E] or NULL; expected_m: launch hint (<= 0:
+ *                 unknown), never changes results.
+ *   output_scale  device float [1], the per-tensor output scale.
+ *   out           device uint8 [E, T, K]; 16-byte aligned; must not be x.
+ * Source: sglang #35593 review page (key source snippets: the requant kernel
+ * and its test; implementation breakdown: 128-aligned hidden sizes).
+ * Errors: PTGQ_EINVAL (negative sizes or strides, G, K % G, NULL pointer,
+ * out == x), PTGQ_EALIGN, PTGQ_EUNSUPPORTED (E > 4096 or sizes beyond 32-bit
+ * task counts), PTGQ_ELAUNCH, PTGQ_EDEVICE.
+ */
+PTGQ_API int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int group_size,
+                              const float *x_scale, int64_t scale_stride_e,
+                              int64_t scale_stride_t, int64_t scale_stride_g,
+                              const int32_t *masked_m, int64_t expected_m,
+                              const float *output_scale, uint8_t *out, void *stream);
+
+/*
  * ptgq_scale_bytes - size in bytes of the scale tensor for `rows` rows of K
  * elements in groups of group_size, in the given format and layout (see the
  * layout table above).  Returns 0 for invalid arguments.  Host only; no

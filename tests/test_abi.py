@@ -181,3 +181,29 @@ def test_binding_refuses_undersized_tensors(lib):
     with pytest.raises(ValueError):
         aq.ptq_quant_fp8(x, "bf16", 5, 256, torch.zeros((5, 256), dtype=torch.uint8),
                          torch.zeros(5), stream=0)
+
+
+def requant(**kw):
+    args = dict(x=A16, E=4, T=48, K=3584, group_size=128, x_scale=A16 * 5,
+                scale_strides=(28 * 48, 1, 48), masked_m=A16 * 4, expected_m=0,
+                output_scale=A16 * 6, out=A16 * 2, stream=0, check=False)
+    args.update(kw)
+    return aq.ptgq_requant_fp8(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=3500), aq.PTGQ_EINVAL),
+    (dict(group_size=96), aq.PTGQ_EINVAL),
+    (dict(E=-1), aq.PTGQ_EINVAL),
+    (dict(scale_strides=(1, -1, 1)), aq.PTGQ_EINVAL),
+    (dict(x=0), aq.PTGQ_EINVAL),
+    (dict(output_scale=0), aq.PTGQ_EINVAL),
+    (dict(out=A16), aq.PTGQ_EINVAL),                # in place is refused
+    (dict(x=A16 + 8), aq.PTGQ_EALIGN),
+    (dict(x_scale=A16 + 2), aq.PTGQ_EALIGN),
+    (dict(masked_m=A16 + 2), aq.PTGQ_EALIGN),
+    (dict(E=5000), aq.PTGQ_EUNSUPPORTED),
+    (dict(E=0, x=0, out=0, x_scale=0, output_scale=0), aq.PTGQ_OK),
+])
+def test_ptgq_requant_fp8_validation(lib, kw, status):
+    assert requant(**kw) == status
