@@ -51,6 +51,11 @@ def _load():
         lib.oracle_requant_fp8.restype = i32
         lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_decode.restype = f32
+        lib.oracle_dequant.argtypes = [vp, i32, i64, i64, i32, vp, i32, i32, i32, vp]
+        lib.oracle_dequant.restype = i32
+        for name in ("oracle_bf16_rne_vec", "oracle_fp16_rne_vec"):
+            getattr(lib, name).argtypes = [vp, vp, i64]
+            getattr(lib, name).restype = None
         _lib = lib
     return _lib
 
@@ -143,6 +148,34 @@ def e4m3_decode(codes) -> np.ndarray:
     lib = _load()
     table = np.array([lib.oracle_e4m3_decode(c) for c in range(256)], dtype=np.float32)
     return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def dequant(q, code_dtype, M, K, G, s, scale_fmt, scale_layout, out_dtype):
+    """codes [M, K] (uint8, e4m3 or int8) x group scales -> y [M, K] as bf16 /
+    fp16 bit patterns (uint16) or float32."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    assert q.size == M * K
+    s = np.ascontiguousarray(s).view(np.uint8)
+    y = np.empty((M, K), dtype=np.float32 if out_dtype == "fp32" else np.uint16)
+    rc = _load().oracle_dequant(_ptr(q), _OUT[code_dtype], M, K, G, _ptr(s), _FMT[scale_fmt],
+                                _LAY[scale_layout], _IN[out_dtype], _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_dequant rejected its arguments")
+    return y
+
+
+def bf16_rne(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_bf16_rne_vec(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def fp16_rne(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().oracle_fp16_rne_vec(_ptr(v), _ptr(out), v.size)
+    return out
 
 
 # ---- element helpers (for pinning single steps) ----

@@ -415,6 +415,104 @@ int oracle_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int G,
 float oracle_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
 
 /* ------------------------------------------------------------------------ */
+/* Dequantization: codes x group scales -> bf16 / fp16 / fp32.               */
+/* ------------------------------------------------------------------------ */
+
+/* Round a finite or infinite fp32 to the nearest bf16 (ties to even),
+ * overflowing to infinity from the midpoint above the largest finite value. */
+static uint16_t bf16_rne(float v)
+{
+    uint32_t b = bits_from_f32(v);
+    if (isnan(v)) return (uint16_t)((b >> 16) | 0x40);
+    uint16_t lo = (uint16_t)(b >> 16);                 /* truncated magnitude */
+    uint16_t hi = (uint16_t)(lo + 1);
+    double a = fabs((double)v);
+    double alo = fabs((double)decode_bf16(lo));
+    double ahi = fabs((double)decode_bf16(hi));
+    /* Past the largest finite bf16 the next step up is infinity; IEEE rounds
+     * as if the exponent range went on, i.e. towards 2^128. */
+    if (isinf(ahi) && !isinf(alo)) ahi = ldexp(1.0, 128);
+    if ((b & 0xFFFFu) == 0) return lo;
+    double dlo = a - alo, dhi = ahi - a;
+    if (dlo < dhi) return lo;
+    if (dhi < dlo) return hi;
+    return (lo & 1) ? hi : lo;
+}
+
+/* Round a finite fp32 to the nearest IEEE binary16 (ties to even),
+ * overflowing to infinity from 65520 up. */
+static uint16_t fp16_rne(float v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs((double)v);
+    if (isnan(v)) return 0x7E00;
+    if (a >= 65520.0) return sign | 0x7C00;
+    int e = (a > 0) ? (int)floor(log2(a)) : -14;
+    if (e < -14) e = -14;
+    if (a >= ldexp(1.0, e + 1)) e += 1;             /* guard the log2 rounding */
+    if (e > -14 && a < ldexp(1.0, e)) e -= 1;
+    double ulp = ldexp(1.0, e - 10);
+    double n = a / ulp;                             /* exact: a has <= 24 bits */
+    double f = floor(n), frac = n - f;
+    double r = (frac > 0.5) ? f + 1 : (frac < 0.5) ? f : (fmod(f, 2.0) == 0 ? f : f + 1);
+    /* r * ulp, re-encoded: subnormals have exponent field 0 */
+    double val = r * ulp;
+    if (val == 0) return sign;
+    int E = (int)floor(log2(val));
+    if (val < ldexp(1.0, E)) E -= 1;
+    if (E < -14) return sign | (uint16_t)(val / ldexp(1.0, -24));
+    uint16_t m = (uint16_t)(val / ldexp(1.0, E - 10) - 1024.0);
+    return sign | (uint16_t)((E + 15) << 10) | m;
+}
+
+static float scale_of(const void *s, int64_t rows, int64_t ng, int64_t m, int64_t g,
+                      int scale_fmt, int scale_layout)
+{
+    if (scale_fmt == OR_SCALE_F32) {
+        const float *f = (const float *)s;
+        return scale_layout == OR_ROW_MAJOR ? f[m * ng + g] : f[g * pad4(rows) + m];
+    }
+    const uint8_t *b = (const uint8_t *)s;
+    uint8_t e = scale_layout == OR_ROW_MAJOR ? b[m * ng + g]
+                                             : b[((g / 4) * pad4(rows) + m) * 4 + (g % 4)];
+    return f32_from_bits(e == 0 ? 0x00400000u : (uint32_t)e << 23);   /* 2^(e-127) */
+}
+
+/* y[m][k] = round_out(fl(decode(q[m][k]) * scale(m, k/G))): the product is one
+ * fp32 rounding (exact for UE8M0 scales unless it underflows), then rounded
+ * to the output dtype (round-to-nearest-even).  ([sglang #35593] key source
+ * snippets, the test's reference: codes as float times the repeated group
+ * scales; [sglang #30924] implementation breakdown: fp32-scale results are
+ * checked by their dequantization.) */
+int oracle_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int G, const void *s,
+                   int scale_fmt, int scale_layout, int out_dtype, void *y)
+{
+    if (M < 0 || K < 0 || G <= 0 || K % G != 0) return -1;
+    if (code_dtype != OR_E4M3 && code_dtype != OR_INT8) return -1;
+    const int64_t ng = K / G;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t c = q[m * K + k];
+            const float d = code_dtype == OR_E4M3 ? e4m3_decode(c) : (float)(int8_t)c;
+            const float v = d * scale_of(s, M, ng, m, k / G, scale_fmt, scale_layout);
+            if (out_dtype == OR_BF16) ((uint16_t *)y)[m * K + k] = bf16_rne(v);
+            else if (out_dtype == OR_FP16) ((uint16_t *)y)[m * K + k] = fp16_rne(v);
+            else ((float *)y)[m * K + k] = v;
+        }
+    }
+    return 0;
+}
+
+void oracle_bf16_rne_vec(const float *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_rne(v[i]);
+}
+void oracle_fp16_rne_vec(const float *v, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = fp16_rne(v[i]);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Element helpers, exported so that the tests can pin each step alone.      */
 /* ------------------------------------------------------------------------ */
 
