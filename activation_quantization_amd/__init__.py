@@ -25,7 +25,7 @@ SCALE_FMTS = {"f32": PTGQ_SCALE_F32, "ue8m0": PTGQ_SCALE_UE8M0}
 SCALE_LAYOUTS = {"row": PTGQ_ROW_MAJOR, "col": PTGQ_COL_MAJOR}
 
 EXPORTS = ("ptgq_quant", "ptgq_quant_masked", "ptq_quant_fp8", "ptgq_requant_fp8",
-           "ptgq_scale_bytes", "ptgq_status_string", "ptgq_init", "ptgq_probe_e4m3",
+           "ptgq_dequant", "ptgq_scale_bytes", "ptgq_status_string", "ptgq_init", "ptgq_probe_e4m3",
            "ptgq_probe_silu_mul", "ptgq_set_tuning")
 
 
@@ -57,6 +57,8 @@ def load_library(path: str = LIB_PATH):
     lib.ptgq_requant_fp8.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, i64, vp, vp,
                                      vp]
     lib.ptgq_requant_fp8.restype = i32
+    lib.ptgq_dequant.argtypes = [vp, i32, i64, i64, i32, vp, i32, i32, i32, vp, vp]
+    lib.ptgq_dequant.restype = i32
     lib.ptgq_scale_bytes.argtypes = [i64, i64, i32, i32, i32]
     lib.ptgq_scale_bytes.restype = ctypes.c_size_t
     lib.ptgq_status_string.argtypes = [i32]
@@ -198,6 +200,20 @@ def ptgq_requant_fp8(x, E, T, K, group_size, x_scale, scale_strides, masked_m, e
                                          _ptr(masked_m), int(expected_m), _ptr(output_scale),
                                          _ptr(out), _stream(stream))
     return _check("ptgq_requant_fp8", rc) if check else rc
+
+
+def ptgq_dequant(q, code_dtype, M, K, group_size, s, scale_fmt, scale_layout, out_dtype, y,
+                 stream=None, check=True):
+    fmt, lay = _enum(scale_fmt, SCALE_FMTS), _enum(scale_layout, SCALE_LAYOUTS)
+    outd = _enum(out_dtype, IN_DTYPES)
+    if M > 0 and K > 0 and outd in _IN_SIZE:
+        fn = "ptgq_dequant"
+        _need(q, M * K, fn, "q")
+        _need(s, ptgq_scale_bytes(M, K, group_size, fmt, lay), fn, "s")
+        _need(y, M * K * _IN_SIZE[outd], fn, "y")
+    rc = load_library().ptgq_dequant(_ptr(q), _enum(code_dtype, OUT_DTYPES), M, K, group_size,
+                                     _ptr(s), fmt, lay, outd, _ptr(y), _stream(stream))
+    return _check("ptgq_dequant", rc) if check else rc
 
 
 def ptgq_probe_e4m3(v, out, n, stream=None, check=True):

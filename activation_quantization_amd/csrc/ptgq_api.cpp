@@ -412,6 +412,61 @@ int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int grou
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
 }
 
+int ptgq_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int group_size,
+                 const void *s, int scale_fmt, int scale_layout, int out_dtype, void *y,
+                 void *stream)
+{
+    if (code_dtype != PTGQ_E4M3 && code_dtype != PTGQ_INT8) return PTGQ_EINVAL;
+    if (scale_fmt != PTGQ_SCALE_F32 && scale_fmt != PTGQ_SCALE_UE8M0) return PTGQ_EINVAL;
+    if (scale_layout != PTGQ_ROW_MAJOR && scale_layout != PTGQ_COL_MAJOR) return PTGQ_EINVAL;
+    if (out_dtype != PTGQ_BF16 && out_dtype != PTGQ_FP16 && out_dtype != PTGQ_FP32)
+        return PTGQ_EINVAL;
+    if (!valid_group_size(group_size) || M < 0 || K < 0 || K % group_size != 0)
+        return PTGQ_EINVAL;
+    if (M == 0 || K == 0) return PTGQ_OK;
+    if (!q || !s || !y) return PTGQ_EINVAL;
+    if (static_cast<const void *>(q) == y || s == y) return PTGQ_EINVAL;
+    if (!aligned(q, 16) || !aligned(y, 16) || (scale_fmt == PTGQ_SCALE_F32 && !aligned(s, 4)))
+        return PTGQ_EALIGN;
+    if (K >= (int64_t)1 << 29) return PTGQ_EUNSUPPORTED;   // fp32 rows are 32-bit buffer ranges
+    const int64_t ng = K / group_size;
+    const int64_t rows_pad = pad4(M);
+    DequantArgs a;
+    a.q = q;
+    a.s = s;
+    a.y = y;
+    a.K = K;
+    a.ng = ng;
+    a.rows_pad = rows_pad;
+    a.st = scale_layout == PTGQ_ROW_MAJOR ? ng : 1;
+    a.sg = scale_layout == PTGQ_ROW_MAJOR ? 1 : rows_pad;
+    int64_t span;   // bytes from a row's first scale to the end of its last
+    if (scale_fmt == PTGQ_SCALE_F32) span = ((ng - 1) * a.sg + 1) * 4;
+    else if (scale_layout == PTGQ_ROW_MAJOR) span = ng;
+    else span = (ng - 1) / 4 * rows_pad * 4 + 4;
+    if (span >= ((int64_t)1 << 32) - 16) return PTGQ_EUNSUPPORTED;
+    a.srow_bytes = (uint32_t)span;
+    const int64_t spr = (K + 1023) / 1024;
+    if (M * spr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+    a.spr = (int32_t)spr;
+    a.n_tasks = (int32_t)(M * spr);
+    a.log2g = __builtin_ctz((unsigned)group_size);
+    const int cus = current_cus(nullptr);
+    if (cus <= 0) return PTGQ_EDEVICE;
+    // Grid: as the requantizer (1 KiB of codes per task, two tasks in flight
+    // per wave), capped at a whole number of blocks per CU.
+    const int64_t tasks = a.n_tasks;
+    const int wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
+    int64_t blocks = (tasks + wpb - 1) / wpb;
+    const int64_t cap = (int64_t)cus * (knob(KNOB_BLOCKS_PER_CU) > 0 ? knob(KNOB_BLOCKS_PER_CU) : 6);
+    if (blocks > cap) blocks = cap;
+    else if (blocks >= 64) blocks = (blocks + 7) / 8 * 8;
+    const hipError_t err = launch_dequant(a, code_dtype, scale_fmt, scale_layout, out_dtype,
+                                          (unsigned)blocks, (unsigned)(wpb * 64),
+                                          static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
+}
+
 int ptgq_probe_e4m3(const float *v, uint8_t *out, int64_t n, void *stream)
 {
     if (n < 0) return PTGQ_EINVAL;

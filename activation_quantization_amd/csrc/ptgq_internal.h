@@ -75,6 +75,23 @@ struct RequantArgs {
     int32_t spr;              // 1024-code slabs per row
 };
 
+// Arguments of the dequantization kernel.  Group g of row m has its scale at
+// element (fp32) or byte (UE8M0 row-major) m*st + g*sg of s; packed UE8M0
+// column-major words are addressed by the kernel from rows_pad.
+struct DequantArgs {
+    const uint8_t *q;         // codes [M, K]
+    const void *s;            // scales
+    void *y;                  // output [M, K]
+    int64_t K;
+    int64_t ng;               // groups per row
+    int64_t st, sg;           // fp32 / row-major UE8M0 scale strides
+    int64_t rows_pad;         // packed UE8M0 column-major: rows per word column
+    uint32_t srow_bytes;      // bytes of one row's scale span (buffer range)
+    int32_t spr;              // 1024-code slabs per row
+    int32_t n_tasks;          // M * spr
+    int32_t log2g;            // log2(G)
+};
+
 // Launchers (defined in ptgq_kernels.hip).  They return the hipError_t of the
 // launch.  `grid`/`block` are chosen by the caller.
 // `table`: fused bf16 kernels read g / (1 + e^-g) from the LDS-staged lookup
@@ -87,6 +104,8 @@ hipError_t launch_silu_table_init(hipStream_t stream);
 hipError_t launch_token(const TokenArgs &a, int in_dtype, int vec_bytes, TokenMode mode,
                         int nv_per_lane, unsigned grid, unsigned block, hipStream_t stream);
 hipError_t launch_requant(const RequantArgs &a, unsigned grid, unsigned block, hipStream_t stream);
+hipError_t launch_dequant(const DequantArgs &a, int code_dtype, int scale_fmt, int scale_layout,
+                          int out_dtype, unsigned grid, unsigned block, hipStream_t stream);
 hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_t stream);
 hipError_t launch_probe_silu(const void *g, const void *u, int in_dtype, int path, float *out,
                              int64_t n, hipStream_t stream);

@@ -1040,6 +1040,178 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
 }
 
 // --------------------------------------------------------------------------
+// Dequantization: y = round_out(decode(code) * scale) per element, the
+// inverse step the pages check quantized activations with (sglang #35593
+// review page, key source snippets: codes as float times the group scales
+// repeated over each group; sglang #30924 review page, implementation
+// breakdown: fp32-scale results are checked by their dequantization).
+//
+// HBM-bound (1 code byte in, 2 or 4 bytes out per element).  A task is one
+// 1024-code slab of one row, two tasks in flight per wave.  Each lane takes
+// W consecutive codes per sub-slab (W = 4 for fp32 output, 8 for 16-bit), so
+// that every store instruction of the wave writes one contiguous 1 KiB run
+// (16 bytes per lane) and every code load reads a contiguous 256 or 512 B.
+// W divides every group size, so one scale covers a lane's sub-slab.
+// --------------------------------------------------------------------------
+
+constexpr int kDqSlab = 1024;
+
+template <int OUTD>
+struct DqShape {
+    static constexpr int W = OUTD == IN_FP32 ? 4 : 8;   // codes per lane per sub-slab
+    static constexpr int NK = kDqSlab / (64 * W);        // sub-slabs per slab
+    static constexpr int OSZ = OUTD == IN_FP32 ? 4 : 2;  // output bytes per element
+};
+
+template <int CODE>
+__device__ __forceinline__ void decode_codes4(uint32_t w, float (&f)[4])
+{
+    if constexpr (CODE == OUT_E4M3) {
+        decode4_e4m3(w, f);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = (float)(int32_t)(int8_t)(uint8_t)(w >> (8 * i));
+    }
+}
+
+// Two fp32 values to a packed pair of 16-bit values, round-to-nearest-even
+// (one v_cvt_pk_bf16_f32 for bf16).
+__device__ __forceinline__ uint32_t pack2_out_bf16(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ uint32_t pack2_out_fp16(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+template <int CODE, int SF, int SL, int OUTD>
+__global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a)
+{
+    using Sh = DqShape<OUTD>;
+    constexpr int W = Sh::W, NK = Sh::NK, OSZ = Sh::OSZ;
+    const int lane = threadIdx.x & 63;
+    const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wpb = blockDim.x >> 6;
+    const int lb = logical_block(blockIdx.x, gridDim.x);
+    const uint32_t row_bytes = (uint32_t)a.K;
+
+    struct Loc {
+        int64_t m;
+        uint32_t col0;   // first code of this lane's first sub-slab
+    };
+    struct Buf {
+        uint32_t c[NK][W / 4];
+        uint32_t s[NK];  // fp32 scale bits, or the UE8M0 exponent byte
+    };
+    auto locate = [&](int t) {
+        const int m = t / a.spr;
+        Loc l;
+        l.m = m;
+        l.col0 = (uint32_t)(t - m * a.spr) * kDqSlab + lane * W;
+        return l;
+    };
+    // Scale byte offset of group g within the row's scale span.
+    auto scale_off = [&](uint32_t g) -> uint32_t {
+        if constexpr (SF == SCALE_F32) return (uint32_t)(g * a.sg * 4);
+        else if constexpr (SL == LAYOUT_ROW) return g;
+        else return (uint32_t)((g >> 2) * a.rows_pad * 4 + (g & 3));
+    };
+    auto load = [&](const Loc &l, bool live) {
+        Buf b;
+        const rsrc_t rq = make_rsrc(a.q + l.m * a.K, live ? row_bytes : 0u);
+        const char *sbase = (const char *)a.s;
+        if constexpr (SF == SCALE_F32) sbase += l.m * a.st * 4;
+        else if constexpr (SL == LAYOUT_ROW) sbase += l.m * a.ng;
+        else sbase += l.m * 4;
+        const rsrc_t rs = make_rsrc(sbase, live ? a.srow_bytes : 0u);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            const uint32_t col = l.col0 + k * 64 * W;
+            if constexpr (W == 4) {
+                b.c[k][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, col, 0, kStreamPolicy);
+            } else {
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rq, col, 0, kStreamPolicy);
+                b.c[k][0] = v.x;
+                b.c[k][1] = v.y;
+            }
+            const uint32_t soff = col < row_bytes ? scale_off(col >> a.log2g) : 0xFFFFFFF0u;
+            if constexpr (SF == SCALE_F32)
+                b.s[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0);
+            else
+                b.s[k] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff, 0, 0);
+        }
+        return b;
+    };
+    auto process = [&](const Loc &l, const Buf &b) {
+        const rsrc_t ry = make_rsrc((char *)a.y + l.m * a.K * OSZ, row_bytes * OSZ);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            float sc;
+            if constexpr (SF == SCALE_F32) sc = __uint_as_float(b.s[k]);
+            else sc = __uint_as_float(b.s[k] == 0 ? 0x00400000u : b.s[k] << 23);   // 2^(e-127)
+            float f[W];
+#pragma unroll
+            for (int i = 0; i < W / 4; ++i) {
+                float d[4];
+                decode_codes4<CODE>(b.c[k][i], d);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[4 * i + j] = d[j] * sc;
+            }
+            u32x4 o;
+            if constexpr (OUTD == IN_FP32) {
+                o.x = __float_as_uint(f[0]);
+                o.y = __float_as_uint(f[1]);
+                o.z = __float_as_uint(f[2]);
+                o.w = __float_as_uint(f[3]);
+            } else if constexpr (OUTD == IN_BF16) {
+                o.x = pack2_out_bf16(f[0], f[1]);
+                o.y = pack2_out_bf16(f[2], f[3]);
+                o.z = pack2_out_bf16(f[4], f[5]);
+                o.w = pack2_out_bf16(f[6], f[7]);
+            } else {
+                o.x = pack2_out_fp16(f[0], f[1]);
+                o.y = pack2_out_fp16(f[2], f[3]);
+                o.z = pack2_out_fp16(f[4], f[5]);
+                o.w = pack2_out_fp16(f[6], f[7]);
+            }
+            const uint32_t col = l.col0 + k * 64 * W;
+            __builtin_amdgcn_raw_buffer_store_b128(o, ry, col * OSZ, 0, kStreamPolicy);
+        }
+    };
+
+    const int n = a.n_tasks;
+    const int stride = gridDim.x * wpb;
+    int t = lb * wpb + wib;
+    if (t >= n) return;
+    Loc lA = locate(t);
+    Buf A = load(lA, true), B;
+    while (true) {
+        const int tB = t + stride;
+        const bool hasB = tB < n;
+        const Loc lB = locate(hasB ? tB : t);
+        B = load(lB, hasB);
+        process(lA, A);
+        if (!hasB) break;
+        t = tB;
+        const int tA = t + stride;
+        const bool hasA = tA < n;
+        lA = locate(hasA ? tA : t);
+        A = load(lA, hasA);
+        process(lB, B);
+        if (!hasA) break;
+        t = tA;
+    }
+}
+
+// --------------------------------------------------------------------------
 // Probes: one step of the device arithmetic over arbitrary inputs.
 // --------------------------------------------------------------------------
 
@@ -1227,6 +1399,42 @@ hipError_t launch_requant(const RequantArgs &a, unsigned grid, unsigned block, h
 {
     requant_fp8_kernel<<<grid, block, (size_t)a.E * sizeof(int), stream>>>(a);
     return hipGetLastError();
+}
+
+template <int CODE, int SF, int SL>
+static hipError_t launch_dequant_o(const DequantArgs &a, int out_dtype, unsigned grid,
+                                   unsigned block, hipStream_t stream)
+{
+    switch (out_dtype) {
+    case IN_BF16: dequant_kernel<CODE, SF, SL, IN_BF16><<<grid, block, 0, stream>>>(a); break;
+    case IN_FP16: dequant_kernel<CODE, SF, SL, IN_FP16><<<grid, block, 0, stream>>>(a); break;
+    case IN_FP32: dequant_kernel<CODE, SF, SL, IN_FP32><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int CODE>
+static hipError_t launch_dequant_c(const DequantArgs &a, int scale_fmt, int scale_layout,
+                                   int out_dtype, unsigned grid, unsigned block, hipStream_t stream)
+{
+    if (scale_fmt == SCALE_F32)   // fp32 layouts differ only in strides
+        return launch_dequant_o<CODE, SCALE_F32, LAYOUT_ROW>(a, out_dtype, grid, block, stream);
+    if (scale_layout == LAYOUT_ROW)
+        return launch_dequant_o<CODE, SCALE_UE8M0, LAYOUT_ROW>(a, out_dtype, grid, block, stream);
+    return launch_dequant_o<CODE, SCALE_UE8M0, LAYOUT_COL>(a, out_dtype, grid, block, stream);
+}
+
+hipError_t launch_dequant(const DequantArgs &a, int code_dtype, int scale_fmt, int scale_layout,
+                          int out_dtype, unsigned grid, unsigned block, hipStream_t stream)
+{
+    if (code_dtype == OUT_E4M3)
+        return launch_dequant_c<OUT_E4M3>(a, scale_fmt, scale_layout, out_dtype, grid, block,
+                                          stream);
+    if (code_dtype == OUT_INT8)
+        return launch_dequant_c<OUT_INT8>(a, scale_fmt, scale_layout, out_dtype, grid, block,
+                                          stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_t stream)

@@ -10,8 +10,8 @@ buffer sets totalling >= 1 GiB are rotated so that no set is still in the
 Printed: one JSON line.  `value` = achieved GB/s at M = 16384, where bytes are
 the algorithmic bytes (bf16 read + codes written + one UE8M0 byte per group);
 `per_m` gives us/call, GB/s and fraction of the 8 TB/s HBM peak at every M of
-the workload; `variants` measures the fused, masked and per-token entry
-points the same way; `roofline` gives the dominant kernel's figures;
+the workload; `variants` measures the fused, masked, per-token,
+requantization and dequantization entry points the same way; `roofline` gives the dominant kernel's figures;
 `cpu_baseline` times the CPU oracle on one full step (single thread).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -335,6 +335,25 @@ def main():
                 variant_entry(timer, cq, fq), live_rows=E8 * live,
                 pages_context_us={"H200": 25.4, "B200": 14.6})
             del cq, outs, ins
+        torch.cuda.empty_cache()
+        # dequantization of the headline output: e4m3 codes [16384, 7168] with
+        # packed column-major UE8M0 scales back to bf16
+        Md, Kd = 16384, 7168
+        rng = np.random.default_rng(7168)
+        qh = rng.integers(0, 256, (Md, Kd), dtype=np.uint8)
+        qh[(qh & 0x7F) == 0x7F] = 0x38
+        sbd = aq.ptgq_scale_bytes(Md, Kd, 128, "ue8m0", "col")
+        sd = torch.from_numpy(rng.integers(110, 135, sbd, dtype=np.uint8)).to("cuda")
+        qd = torch.from_numpy(qh).to("cuda")
+        fd = Md * Kd * (1 + 2) + Md * (Kd // 128)
+        cd = []
+        for i in range(rotation_sets(fd)):
+            qi = qd if i == 0 else qd.clone()
+            yi = torch.empty((Md, Kd), dtype=torch.bfloat16, device="cuda")
+            cd.append((lambda qi=qi, yi=yi: aq.ptgq_dequant(qi, "e4m3", Md, Kd, 128, sd, "ue8m0",
+                                                            "col", "bf16", yi, check=False)))
+        variants["dequant_e4m3_to_bf16_M16384_K7168"] = variant_entry(timer, cd, fd)
+        del cd, qd
         torch.cuda.empty_cache()
 
     cpu = None

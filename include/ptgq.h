@@ -190,6 +190,36 @@ PTGQ_API int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K,
                               const float *output_scale, uint8_t *out, void *stream);
 
 /*
+ * ptgq_dequant - group dequantization, the inverse of ptgq_quant:
+ *   y[m][k] = round_out(decode(q[m][k]) * scale(m, k / G))
+ * decode is the e4m3 value of the code (OCP e4m3fn; 0x7F / 0xFF are NaN) or
+ * the int8 value; the product is one fp32 rounding (exact for UE8M0 scales
+ * unless it falls below the normal range); round_out is round-to-nearest-even
+ * to bf16 / fp16 (overflowing to infinity) or nothing for fp32.  A UE8M0
+ * scale byte e stands for 2^(e - 127) (e == 0: 2^-127, e == 255: infinity).
+ *
+ *   q             device uint8 [M, K] codes of code_dtype (PTGQ_E4M3 or
+ *                 PTGQ_INT8); row-major; 16-byte aligned.
+ *   group_size    G in {16, 32, 64, 128}; K % G == 0.
+ *   s             device scales of M rows in scale_fmt / scale_layout, exactly
+ *                 as ptgq_quant writes them (layout table above; pad slots are
+ *                 not read); fp32 scales 4-byte aligned.
+ *   out_dtype     PTGQ_BF16, PTGQ_FP16 or PTGQ_FP32.
+ *   y             device [M, K] of out_dtype; 16-byte aligned; must not alias
+ *                 q or s.
+ * Sources: sglang #35593 review page, key source snippets (the test's
+ * reference multiplies the codes, as float, by the group scales repeated over
+ * each group); sglang #30924 review page, implementation breakdown (fp32-scale
+ * results are verified through their dequantization).
+ * Errors: PTGQ_EINVAL (M < 0, K < 0, G not allowed, K % G, bad enum, NULL
+ * pointer, y aliasing q or s), PTGQ_EALIGN, PTGQ_EUNSUPPORTED (K >= 2^29,
+ * sizes beyond 32-bit task counts or scale spans), PTGQ_ELAUNCH, PTGQ_EDEVICE.
+ */
+PTGQ_API int ptgq_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int group_size,
+                          const void *s, int scale_fmt, int scale_layout, int out_dtype, void *y,
+                          void *stream);
+
+/*
  * ptgq_scale_bytes - size in bytes of the scale tensor for `rows` rows of K
  * elements in groups of group_size, in the given format and layout (see the
  * layout table above).  Returns 0 for invalid arguments.  Host only; no

@@ -207,3 +207,41 @@ def requant(**kw):
 ])
 def test_ptgq_requant_fp8_validation(lib, kw, status):
     assert requant(**kw) == status
+
+
+def dequant(**kw):
+    args = dict(q=A16, code_dtype="e4m3", M=8, K=1024, group_size=128, s=A16 * 3,
+                scale_fmt="f32", scale_layout="col", out_dtype="bf16", y=A16 * 5, stream=0,
+                check=False)
+    args.update(kw)
+    return aq.ptgq_dequant(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=1000), aq.PTGQ_EINVAL),
+    (dict(group_size=256), aq.PTGQ_EINVAL),
+    (dict(M=-1), aq.PTGQ_EINVAL),
+    (dict(code_dtype=2), aq.PTGQ_EINVAL),
+    (dict(out_dtype=3), aq.PTGQ_EINVAL),
+    (dict(scale_fmt=2), aq.PTGQ_EINVAL),
+    (dict(scale_layout=2), aq.PTGQ_EINVAL),
+    (dict(q=0), aq.PTGQ_EINVAL),
+    (dict(s=0), aq.PTGQ_EINVAL),
+    (dict(y=A16), aq.PTGQ_EINVAL),                  # y aliasing q
+    (dict(y=A16 * 3), aq.PTGQ_EINVAL),              # y aliasing s
+    (dict(q=A16 + 8), aq.PTGQ_EALIGN),
+    (dict(y=A16 * 5 + 4), aq.PTGQ_EALIGN),
+    (dict(s=A16 * 3 + 2), aq.PTGQ_EALIGN),
+    (dict(K=1 << 29), aq.PTGQ_EUNSUPPORTED),
+    (dict(M=0, q=0, s=0, y=0), aq.PTGQ_OK),
+    (dict(K=0, q=0, s=0, y=0), aq.PTGQ_OK),
+])
+def test_ptgq_dequant_validation(lib, kw, status):
+    assert dequant(**kw) == status
+
+
+def test_dequant_ue8m0_scales_need_no_alignment(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert dequant(s=A16 * 3 + 1, scale_fmt="ue8m0") == aq.PTGQ_EDEVICE
