@@ -428,39 +428,56 @@ int ptgq_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int gro
     if (static_cast<const void *>(q) == y || s == y) return PTGQ_EINVAL;
     if (!aligned(q, 16) || !aligned(y, 16) || (scale_fmt == PTGQ_SCALE_F32 && !aligned(s, 4)))
         return PTGQ_EALIGN;
-    if (K >= (int64_t)1 << 29) return PTGQ_EUNSUPPORTED;   // fp32 rows are 32-bit buffer ranges
+    if (K >= (int64_t)1 << 29 || M >= ((int64_t)1 << 31)) return PTGQ_EUNSUPPORTED;
     const int64_t ng = K / group_size;
-    const int64_t rows_pad = pad4(M);
+    const size_t s_bytes = ptgq_scale_bytes(M, K, group_size, scale_fmt, scale_layout);
+    if (s_bytes == 0 || s_bytes >= ((size_t)1 << 32) - (1 << 20)) return PTGQ_EUNSUPPORTED;
+    const int cus = current_cus(nullptr);
+    if (cus <= 0) return PTGQ_EDEVICE;
+    // Tasks of ns sub-slabs (a sub-slab is 512 codes for 16-bit outputs, 256
+    // for fp32), contiguous so that a wave's loads in flight stay within a few
+    // pages, grid-strided over the waves for as many full rounds as fit; the
+    // remainder is one last round in which every wave takes an equal share
+    // (whole sub-slabs).  Four sub-slabs per task with four four-wave blocks
+    // per CU (two for fp32 outputs, whose stores are twice as wide) measured
+    // best on MI355X; problems too small to give every wave a few tasks use
+    // one sub-slab per task.
+    const int64_t total = M * K;
+    const int64_t sub = out_dtype == PTGQ_FP32 ? 256 : 512;
+    const int64_t subs = (total + sub - 1) / sub;
+    if (subs >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+    int ns = subs >= (int64_t)cus * 16 * 8 ? 4 : 1;
+    if (knob(KNOB_SLABS_PER_TASK) > 0) ns = knob(KNOB_SLABS_PER_TASK) >= 4 ? 4 : 1;
+    const int64_t ts = ns * sub;
+    const int64_t tasks = (subs + ns - 1) / ns;
+    const int wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
+    int64_t blocks = (tasks + wpb - 1) / wpb;
+    int64_t per_cu = out_dtype == PTGQ_FP32 ? 2 : 4;
+    if (knob(KNOB_BLOCKS_PER_CU) > 0) per_cu = knob(KNOB_BLOCKS_PER_CU);
+    if (blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
+    else if (blocks >= 64) blocks = (blocks + 7) / 8 * 8;
+    const int64_t waves = blocks * wpb;
     DequantArgs a;
+    a.step = waves * ts;
+    a.full = (int32_t)(total / a.step);
+    a.full_end = a.full * a.step;
+    const int64_t rem = total - a.full_end;
+    a.last = (rem + waves * sub - 1) / (waves * sub) * sub;
     a.q = q;
     a.s = s;
     a.y = y;
+    a.M = M;
     a.K = K;
     a.ng = ng;
-    a.rows_pad = rows_pad;
+    a.rows_pad = pad4(M);
     a.st = scale_layout == PTGQ_ROW_MAJOR ? ng : 1;
-    a.sg = scale_layout == PTGQ_ROW_MAJOR ? 1 : rows_pad;
-    int64_t span;   // bytes from a row's first scale to the end of its last
-    if (scale_fmt == PTGQ_SCALE_F32) span = ((ng - 1) * a.sg + 1) * 4;
-    else if (scale_layout == PTGQ_ROW_MAJOR) span = ng;
-    else span = (ng - 1) / 4 * rows_pad * 4 + 4;
-    if (span >= ((int64_t)1 << 32) - 16) return PTGQ_EUNSUPPORTED;
-    a.srow_bytes = (uint32_t)span;
-    const int64_t spr = (K + 1023) / 1024;
-    if (M * spr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
-    a.spr = (int32_t)spr;
-    a.n_tasks = (int32_t)(M * spr);
+    a.sg = scale_layout == PTGQ_ROW_MAJOR ? 1 : a.rows_pad;
+    a.dm = a.step / K;
+    a.dc = (uint32_t)(a.step % K);
+    a.s_bytes = (uint32_t)s_bytes;
+    a.inv_k = 1.0f / (float)K;
+    a.ns = ns;
     a.log2g = __builtin_ctz((unsigned)group_size);
-    const int cus = current_cus(nullptr);
-    if (cus <= 0) return PTGQ_EDEVICE;
-    // Grid: as the requantizer (1 KiB of codes per task, two tasks in flight
-    // per wave), capped at a whole number of blocks per CU.
-    const int64_t tasks = a.n_tasks;
-    const int wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
-    int64_t blocks = (tasks + wpb - 1) / wpb;
-    const int64_t cap = (int64_t)cus * (knob(KNOB_BLOCKS_PER_CU) > 0 ? knob(KNOB_BLOCKS_PER_CU) : 6);
-    if (blocks > cap) blocks = cap;
-    else if (blocks >= 64) blocks = (blocks + 7) / 8 * 8;
     const hipError_t err = launch_dequant(a, code_dtype, scale_fmt, scale_layout, out_dtype,
                                           (unsigned)blocks, (unsigned)(wpb * 64),
                                           static_cast<hipStream_t>(stream));

@@ -75,20 +75,30 @@ struct RequantArgs {
     int32_t spr;              // 1024-code slabs per row
 };
 
-// Arguments of the dequantization kernel.  Group g of row m has its scale at
-// element (fp32) or byte (UE8M0 row-major) m*st + g*sg of s; packed UE8M0
-// column-major words are addressed by the kernel from rows_pad.
+// Arguments of the dequantization kernel.  Codes and outputs are contiguous
+// [M, K]; the work is cut into flat tasks of ns sub-slabs (a sub-slab is 64
+// lanes x 8 codes for 16-bit outputs, 64 x 4 for fp32), grid-strided over
+// `full` rounds, then one last round of `last` codes per wave.
+// fp32 scale of (row m, group g) is element m*st + g*sg; UE8M0 row-major byte
+// m*ng + g; packed UE8M0 column-major byte ((g/4)*rows_pad + m)*4 + g%4.
 struct DequantArgs {
     const uint8_t *q;         // codes [M, K]
     const void *s;            // scales
     void *y;                  // output [M, K]
+    int64_t M;
     int64_t K;
     int64_t ng;               // groups per row
-    int64_t st, sg;           // fp32 / row-major UE8M0 scale strides
-    int64_t rows_pad;         // packed UE8M0 column-major: rows per word column
-    uint32_t srow_bytes;      // bytes of one row's scale span (buffer range)
-    int32_t spr;              // 1024-code slabs per row
-    int32_t n_tasks;          // M * spr
+    int64_t st, sg;           // fp32 scale strides (elements)
+    int64_t rows_pad;         // packed UE8M0 column-major: words per word column
+    int64_t step;             // codes per round: waves * task codes
+    int64_t dm;               // step / K
+    int64_t full_end;         // full * step: first code of the last round
+    int64_t last;             // codes per wave in the last round (whole sub-slabs)
+    uint32_t dc;              // step % K
+    uint32_t s_bytes;         // bytes of the scale tensor (buffer range)
+    float inv_k;              // 1 / K, for the quotient estimate when K < a task
+    int32_t full;             // rounds of full tasks
+    int32_t ns;               // sub-slabs per task: 1 or 4
     int32_t log2g;            // log2(G)
 };
 

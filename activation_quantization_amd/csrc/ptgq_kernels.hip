@@ -1046,20 +1046,22 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
 // repeated over each group; sglang #30924 review page, implementation
 // breakdown: fp32-scale results are checked by their dequantization).
 //
-// HBM-bound (1 code byte in, 2 or 4 bytes out per element).  A task is one
-// 1024-code slab of one row, two tasks in flight per wave.  Each lane takes
-// W consecutive codes per sub-slab (W = 4 for fp32 output, 8 for 16-bit), so
-// that every store instruction of the wave writes one contiguous 1 KiB run
-// (16 bytes per lane) and every code load reads a contiguous 256 or 512 B.
-// W divides every group size, so one scale covers a lane's sub-slab.
+// HBM-bound (1 code byte in, 2 or 4 bytes out per element).  Codes and
+// outputs are contiguous [M, K], so the work is cut into flat tasks of
+// NS sub-slabs that cross row ends freely; only the scale lookup needs the
+// row.  A sub-slab is 64 lanes x W consecutive codes (W = 8 for 16-bit
+// output, 4 for fp32), so every store instruction of the wave writes one
+// contiguous 1 KiB run (16 bytes per lane).  W divides every group size and K
+// is a multiple of the group size, so a lane's W codes share one row and one
+// scale.  Each wave keeps two tasks in flight and walks the grid-stride
+// sequence of tasks with an incremental (row, column) cursor, so no division
+// happens per task.
 // --------------------------------------------------------------------------
-
-constexpr int kDqSlab = 1024;
 
 template <int OUTD>
 struct DqShape {
     static constexpr int W = OUTD == IN_FP32 ? 4 : 8;   // codes per lane per sub-slab
-    static constexpr int NK = kDqSlab / (64 * W);        // sub-slabs per slab
+    static constexpr int SUB = 64 * W;                    // codes per sub-slab
     static constexpr int OSZ = OUTD == IN_FP32 ? 4 : 2;  // output bytes per element
 };
 
@@ -1075,7 +1077,7 @@ __device__ __forceinline__ void decode_codes4(uint32_t w, float (&f)[4])
 }
 
 // Two fp32 values to a packed pair of 16-bit values, round-to-nearest-even
-// (one v_cvt_pk_bf16_f32 for bf16).
+// (one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t pack2_out_bf16(float a, float b)
 {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -1092,76 +1094,135 @@ __device__ __forceinline__ uint32_t pack2_out_fp16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
-template <int CODE, int SF, int SL, int OUTD>
+// Position of a task: its round, first code's flat index and (row, column).
+struct DqCursor {
+    int32_t i;
+    int64_t e;
+    int64_t m;
+    uint32_t c;
+};
+
+template <int CODE, int SF, int SL, int OUTD, int NS>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a)
 {
     using Sh = DqShape<OUTD>;
-    constexpr int W = Sh::W, NK = Sh::NK, OSZ = Sh::OSZ;
+    constexpr int W = Sh::W, SUB = Sh::SUB, OSZ = Sh::OSZ;
+    constexpr int TS = NS * SUB;
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x);
-    const uint32_t row_bytes = (uint32_t)a.K;
+    const uint32_t K = (uint32_t)a.K;
+    const int64_t total = a.M * a.K;
+    const rsrc_t rs = make_rsrc(a.s, a.s_bytes);
 
-    struct Loc {
-        int64_t m;
-        uint32_t col0;   // first code of this lane's first sub-slab
+    // Wave w's tasks: rounds 0 .. full-1 take TS codes at (i * waves + w) * TS;
+    // the last round takes `last` codes (whole sub-slabs, < TS) at
+    // full * waves * TS + w * last, so no wave does more than one sub-slab
+    // beyond any other.
+    const int64_t w = (int64_t)lb * wpb + wib;
+    const int64_t e2 = a.full_end + w * a.last;   // this wave's last-round task
+    auto at = [&](int32_t i, int64_t e) {
+        DqCursor u;
+        u.i = i;
+        u.e = e;
+        u.m = e / a.K;
+        u.c = (uint32_t)(e - u.m * a.K);
+        return u;
     };
-    struct Buf {
-        uint32_t c[NK][W / 4];
-        uint32_t s[NK];  // fp32 scale bits, or the UE8M0 exponent byte
+    auto size_of = [&](const DqCursor &u) -> uint32_t {
+        const int64_t cap = u.i < a.full ? TS : u.i == a.full ? a.last : 0;
+        const int64_t left = total - u.e;
+        return left <= 0 ? 0u : left < cap ? (uint32_t)left : (uint32_t)cap;
     };
-    auto locate = [&](int t) {
-        const int m = t / a.spr;
-        Loc l;
-        l.m = m;
-        l.col0 = (uint32_t)(t - m * a.spr) * kDqSlab + lane * W;
-        return l;
-    };
-    // Scale byte offset of group g within the row's scale span.
-    auto scale_off = [&](uint32_t g) -> uint32_t {
-        if constexpr (SF == SCALE_F32) return (uint32_t)(g * a.sg * 4);
-        else if constexpr (SL == LAYOUT_ROW) return g;
-        else return (uint32_t)((g >> 2) * a.rows_pad * 4 + (g & 3));
-    };
-    auto load = [&](const Loc &l, bool live) {
-        Buf b;
-        const rsrc_t rq = make_rsrc(a.q + l.m * a.K, live ? row_bytes : 0u);
-        const char *sbase = (const char *)a.s;
-        if constexpr (SF == SCALE_F32) sbase += l.m * a.st * 4;
-        else if constexpr (SL == LAYOUT_ROW) sbase += l.m * a.ng;
-        else sbase += l.m * 4;
-        const rsrc_t rs = make_rsrc(sbase, live ? a.srow_bytes : 0u);
-#pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            const uint32_t col = l.col0 + k * 64 * W;
-            if constexpr (W == 4) {
-                b.c[k][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, col, 0, kStreamPolicy);
-            } else {
-                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rq, col, 0, kStreamPolicy);
-                b.c[k][0] = v.x;
-                b.c[k][1] = v.y;
+    auto advance = [&](DqCursor u) {
+        if (u.i + 1 < a.full) {
+            u.i += 1;
+            u.e += a.step;
+            u.m += a.dm;
+            u.c += a.dc;
+            if (u.c >= K) {
+                u.c -= K;
+                u.m += 1;
             }
-            const uint32_t soff = col < row_bytes ? scale_off(col >> a.log2g) : 0xFFFFFFF0u;
-            if constexpr (SF == SCALE_F32)
-                b.s[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0);
-            else
-                b.s[k] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff, 0, 0);
+            return u;
         }
-        return b;
+        if (u.i + 1 == a.full) return at(a.full, e2);
+        u.i = a.full + 1;   // past the last round: empty
+        return u;
     };
-    auto process = [&](const Loc &l, const Buf &b) {
-        const rsrc_t ry = make_rsrc((char *)a.y + l.m * a.K * OSZ, row_bytes * OSZ);
+    DqCursor cur = a.full > 0 ? at(0, w * TS) : at(0, e2);
+    if (size_of(cur) == 0) return;
+
+    struct Task {
+        DqCursor u;
+        uint32_t c[NS][W / 4];
+        uint32_t s[NS];  // fp32 scale bits, or the UE8M0 exponent byte
+    };
+    auto load = [&](Task &T) {
+        T.u = cur;
+        cur = advance(cur);
+        const DqCursor &u = T.u;
+        const uint32_t range = size_of(u);
+        const rsrc_t rq = make_rsrc(a.q + (range ? u.e : 0), range);
 #pragma unroll
-        for (int k = 0; k < NK; ++k) {
+        for (int k = 0; k < NS; ++k) {
+            const uint32_t off = k * SUB + lane * W;
+            if constexpr (W == 4) {
+                T.c[k][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, kStreamPolicy);
+            } else {
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, kStreamPolicy);
+                T.c[k][0] = v.x;
+                T.c[k][1] = v.y;
+            }
+            // row and column of this lane's codes
+            uint32_t col = u.c + off;
+            uint32_t m = (uint32_t)u.m;
+            if (K >= (uint32_t)TS) {
+                if (col >= K) {
+                    col -= K;
+                    m += 1;
+                }
+            } else {
+                // quotient from an fp32 estimate (exact operands), off by at most one
+                uint32_t d = (uint32_t)((float)col * a.inv_k);
+                int32_t r = (int32_t)(col - d * K);
+                if (r < 0) {
+                    d -= 1;
+                    r += (int32_t)K;
+                } else if (r >= (int32_t)K) {
+                    d += 1;
+                    r -= (int32_t)K;
+                }
+                col = (uint32_t)r;
+                m += d;
+            }
+            const uint32_t g = col >> a.log2g;
+            uint32_t soff;
+            if constexpr (SF == SCALE_F32) soff = (m * (uint32_t)a.st + g * (uint32_t)a.sg) * 4;
+            else if constexpr (SL == LAYOUT_ROW) soff = m * (uint32_t)a.ng + g;
+            else soff = ((g >> 2) * (uint32_t)a.rows_pad + m) * 4 + (g & 3);
+            if (off >= range) soff = 0xFFFFFFF0u;   // past the end: read nothing
+            if constexpr (SF == SCALE_F32)
+                T.s[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0);
+            else
+                T.s[k] = __builtin_amdgcn_raw_buffer_load_b8(rs, soff, 0, 0);
+        }
+    };
+    auto process = [&](const Task &T) {
+        const DqCursor &u = T.u;
+        const uint32_t range = size_of(u);
+        const rsrc_t ry = make_rsrc((char *)a.y + (range ? u.e * OSZ : 0), range * OSZ);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
             float sc;
-            if constexpr (SF == SCALE_F32) sc = __uint_as_float(b.s[k]);
-            else sc = __uint_as_float(b.s[k] == 0 ? 0x00400000u : b.s[k] << 23);   // 2^(e-127)
+            if constexpr (SF == SCALE_F32) sc = __uint_as_float(T.s[k]);
+            else sc = __uint_as_float(T.s[k] == 0 ? 0x00400000u : T.s[k] << 23);   // 2^(e-127)
             float f[W];
 #pragma unroll
             for (int i = 0; i < W / 4; ++i) {
                 float d[4];
-                decode_codes4<CODE>(b.c[k][i], d);
+                decode_codes4<CODE>(T.c[k][i], d);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) f[4 * i + j] = d[j] * sc;
             }
@@ -1182,32 +1243,25 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a)
                 o.z = pack2_out_fp16(f[4], f[5]);
                 o.w = pack2_out_fp16(f[6], f[7]);
             }
-            const uint32_t col = l.col0 + k * 64 * W;
-            __builtin_amdgcn_raw_buffer_store_b128(o, ry, col * OSZ, 0, kStreamPolicy);
+            __builtin_amdgcn_raw_buffer_store_b128(o, ry, (k * SUB + lane * W) * OSZ, 0,
+                                                   kStreamPolicy);
         }
     };
 
-    const int n = a.n_tasks;
-    const int stride = gridDim.x * wpb;
-    int t = lb * wpb + wib;
-    if (t >= n) return;
-    Loc lA = locate(t);
-    Buf A = load(lA, true), B;
+    // Two tasks in flight: the next task's loads are issued before the
+    // current one is converted and stored.  An empty task loads nothing
+    // (empty ranges) and ends the loop.
+    Task A, B;
+    load(A);
     while (true) {
-        const int tB = t + stride;
-        const bool hasB = tB < n;
-        const Loc lB = locate(hasB ? tB : t);
-        B = load(lB, hasB);
-        process(lA, A);
+        const bool hasB = size_of(cur) != 0;
+        load(B);
+        process(A);
         if (!hasB) break;
-        t = tB;
-        const int tA = t + stride;
-        const bool hasA = tA < n;
-        lA = locate(hasA ? tA : t);
-        A = load(lA, hasA);
-        process(lB, B);
+        const bool hasA = size_of(cur) != 0;
+        load(A);
+        process(B);
         if (!hasA) break;
-        t = tA;
     }
 }
 
@@ -1401,17 +1455,28 @@ hipError_t launch_requant(const RequantArgs &a, unsigned grid, unsigned block, h
     return hipGetLastError();
 }
 
+template <int CODE, int SF, int SL, int OUTD>
+static hipError_t launch_dequant_n(const DequantArgs &a, unsigned grid, unsigned block,
+                                   hipStream_t stream)
+{
+    switch (a.ns) {
+    case 1: dequant_kernel<CODE, SF, SL, OUTD, 1><<<grid, block, 0, stream>>>(a); break;
+    case 4: dequant_kernel<CODE, SF, SL, OUTD, 4><<<grid, block, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int CODE, int SF, int SL>
 static hipError_t launch_dequant_o(const DequantArgs &a, int out_dtype, unsigned grid,
                                    unsigned block, hipStream_t stream)
 {
     switch (out_dtype) {
-    case IN_BF16: dequant_kernel<CODE, SF, SL, IN_BF16><<<grid, block, 0, stream>>>(a); break;
-    case IN_FP16: dequant_kernel<CODE, SF, SL, IN_FP16><<<grid, block, 0, stream>>>(a); break;
-    case IN_FP32: dequant_kernel<CODE, SF, SL, IN_FP32><<<grid, block, 0, stream>>>(a); break;
+    case IN_BF16: return launch_dequant_n<CODE, SF, SL, IN_BF16>(a, grid, block, stream);
+    case IN_FP16: return launch_dequant_n<CODE, SF, SL, IN_FP16>(a, grid, block, stream);
+    case IN_FP32: return launch_dequant_n<CODE, SF, SL, IN_FP32>(a, grid, block, stream);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int CODE>

@@ -264,11 +264,11 @@ PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int
 /*
  * ptgq_set_tuning - diagnostics only: override one decision of the launch
  * geometry chooser for the whole process (value -1 restores the automatic
- * choice).  Knobs: 0 slabs per task (1 or 2; one slab = 512 elements of a
- * row), 1 waves per block (1..4), 2 resident blocks per
- * compute unit (grid cap), 3 per-token mode (0 one wave per row, 1 one block
- * per row, 2 two-pass block), 4 fused bf16 SiLU path (0 direct evaluation, 1
- * LDS lookup table).  Results never depend on these; only speed does.  Not synchronized
+ * choice).  Knobs: 0 slabs per task (quantization: 1 or 2, one slab = 512
+ * elements of a row; dequantization: 1 or 4 sub-slabs), 1 waves per block
+ * (1..4), 2 resident blocks per compute unit (grid cap), 3 per-token mode (0
+ * one wave per row, 1 one block per row, 2 two-pass block), 4 fused bf16 SiLU
+ * path (0 direct evaluation, 1 LDS lookup table).  Results never depend on these; only speed does.  Not synchronized
  * with calls running on other host threads.  Returns PTGQ_OK or PTGQ_EINVAL.
  */
 PTGQ_API int ptgq_set_tuning(int knob, int64_t value);
