@@ -292,7 +292,7 @@ static void quant_row(const void *x, int in_dtype, int64_t row_in, int64_t K, in
 static int check_common(int in_dtype, int64_t K, int G, int out_dtype, int scale_fmt,
                         int scale_layout)
 {
-    if (in_dtype != OR_BF16 && in_dtype != OR_FP16) return -1;
+    if (in_dtype != OR_BF16 && in_dtype != OR_FP16 && in_dtype != OR_FP32) return -1;
     if (G != 16 && G != 32 && G != 64 && G != 128) return -1;
     if (K < 0 || K % G != 0) return -1;
     if (out_dtype != OR_E4M3 && out_dtype != OR_INT8) return -1;
@@ -310,6 +310,7 @@ int oracle_ptgq(const void *x, int in_dtype, int64_t M, int64_t K, int G, int fu
                 uint8_t *q, void *s)
 {
     if (check_common(in_dtype, K, G, out_dtype, scale_fmt, scale_layout) || M < 0) return -1;
+    if (fuse && in_dtype == OR_FP32) return -1;   /* fused calls take 16-bit inputs */
     if (scale_layout == OR_COL_MAJOR)
         memset(s, 0, oracle_scale_bytes(M, K, G, scale_fmt, scale_layout));
     for (int64_t m = 0; m < M; ++m)
@@ -330,6 +331,7 @@ int oracle_ptgq_masked(const void *x, int in_dtype, int64_t E, int64_t T, int64_
 {
     if (check_common(in_dtype, K, G, out_dtype, scale_fmt, scale_layout) || E < 0 || T < 0)
         return -1;
+    if (fuse && in_dtype == OR_FP32) return -1;
     const size_t sb = oracle_scale_bytes(T, K, G, scale_fmt, scale_layout);
     const int64_t in_width = fuse ? 2 * K : K;
     const size_t in_elem = 2;

@@ -180,3 +180,40 @@ def test_rejects_bad_arguments():
     x = np.zeros((2, 96), np.uint16)
     with pytest.raises(ValueError):
         oracle.ptgq(x, "bf16", 2, 96, 48, False, "e4m3", "f32", "row")    # G not a power of 2
+
+
+@pytest.mark.parametrize("fmt,layout", [("f32", "row"), ("ue8m0", "col")])
+@pytest.mark.parametrize("out_dtype", ["e4m3", "int8"])
+def test_fp32_input_equals_16bit_input_on_the_same_values(out_dtype, fmt, layout):
+    """Decoding is the only step that depends on the input dtype: fp32 inputs
+    holding bf16 (or fp16) values give the bf16 (fp16) results byte for byte."""
+    M, K, G = 9, 640, 64
+    xb = W.normal_bf16(91, (M, K), factor_cols=[3], factor=40.0)
+    xh = W.normal_fp16(92, (M, K))
+    for x, dt in ((xb, "bf16"), (xh, "fp16")):
+        xf = oracle.decode(x, dt).reshape(M, K)
+        assert np.array_equal(np.asarray(oracle.ptgq(xf, "fp32", M, K, G, False, out_dtype, fmt,
+                                                     layout)[0]),
+                              oracle.ptgq(x, dt, M, K, G, False, out_dtype, fmt, layout)[0])
+        assert np.array_equal(oracle.ptgq(xf, "fp32", M, K, G, False, out_dtype, fmt, layout)[1],
+                              oracle.ptgq(x, dt, M, K, G, False, out_dtype, fmt, layout)[1])
+
+
+def test_fp32_input_keeps_what_16bit_inputs_cannot_hold():
+    """An fp32 value between two bf16 values is quantized from its own value:
+    with a unit UE8M0 scale (amax 448) 1.0625 (e4m3 tie between 1.0 and
+    1.125 -> even 1.0) and the next fp32 above it (-> 1.125, no bf16 or fp16
+    holds it) give different codes."""
+    x = np.zeros((1, 128), np.float32)
+    x[0, 0] = 448.0
+    x[0, 1] = 1.0625
+    x[0, 2] = np.nextafter(np.float32(1.0625), np.float32(2))
+    q, s = oracle.ptgq(x, "fp32", 1, 128, 128, False, "e4m3", "ue8m0", "row")
+    assert s[0] == 0x7F
+    assert list(q[0, :3]) == [0x7E, 0x38, 0x39]
+
+
+def test_fused_fp32_is_rejected():
+    with pytest.raises(ValueError):
+        oracle.ptgq(np.zeros((1, 256), np.float32), "fp32", 1, 128, 128, True, "e4m3", "f32",
+                    "row")
