@@ -334,7 +334,7 @@ int oracle_ptgq_masked(const void *x, int in_dtype, int64_t E, int64_t T, int64_
     if (fuse && in_dtype == OR_FP32) return -1;
     const size_t sb = oracle_scale_bytes(T, K, G, scale_fmt, scale_layout);
     const int64_t in_width = fuse ? 2 * K : K;
-    const size_t in_elem = 2;
+    const size_t in_elem = in_dtype == OR_FP32 ? 4 : 2;
     for (int64_t e = 0; e < E; ++e) {
         int64_t live = masked_m[e];
         if (live < 0) live = 0;

@@ -217,3 +217,30 @@ def test_fused_fp32_is_rejected():
     with pytest.raises(ValueError):
         oracle.ptgq(np.zeros((1, 256), np.float32), "fp32", 1, 128, 128, True, "e4m3", "f32",
                     "row")
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp16", "fp32"])
+def test_masked_expert_equals_flat_call_on_its_rows(in_dtype):
+    """Each expert's live rows are a flat call on that expert's slice (its own
+    scale tensor of tokens_pad rows); other rows keep the sentinels."""
+    E, T, K, G = 4, 9, 384, 128
+    if in_dtype == "fp32":
+        x = W.normal_f32(61, (E, T, K))
+    elif in_dtype == "fp16":
+        x = W.normal_fp16(62, (E, T, K))
+    else:
+        x = W.normal_bf16(63, (E, T, K))
+    mm = np.array([9, 0, 4, 12], np.int32)
+    sb = oracle.scale_bytes(T, K, G, "f32", "row")
+    q, s = oracle.ptgq_masked(x, in_dtype, E, T, K, G, False, mm, "e4m3", "f32", "row",
+                              q_init=np.full((E, T, K), 0x7F, np.uint8),
+                              s_init=np.full(E * sb, 0xFF, np.uint8))
+    for e in range(E):
+        live = int(min(max(mm[e], 0), T))
+        if live:
+            fq, fs = oracle.ptgq(np.ascontiguousarray(x[e, :live]), in_dtype, live, K, G, False,
+                                 "e4m3", "f32", "row")
+            assert np.array_equal(q[e, :live], fq)
+            assert np.array_equal(s[e * sb:e * sb + fs.size], fs)
+        assert np.all(q[e, live:] == 0x7F)
+        assert np.all(s[e * sb + live * (K // G) * 4:(e + 1) * sb] == 0xFF)
