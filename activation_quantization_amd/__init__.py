@@ -24,7 +24,7 @@ OUT_DTYPES = {"e4m3": PTGQ_E4M3, "int8": PTGQ_INT8}
 SCALE_FMTS = {"f32": PTGQ_SCALE_F32, "ue8m0": PTGQ_SCALE_UE8M0}
 SCALE_LAYOUTS = {"row": PTGQ_ROW_MAJOR, "col": PTGQ_COL_MAJOR}
 
-EXPORTS = ("ptgq_quant", "ptgq_quant_masked", "ptq_quant_fp8", "ptgq_requant_fp8",
+EXPORTS = ("ptgq_quant", "ptgq_quant_padded", "ptgq_quant_masked", "ptq_quant_fp8", "ptgq_requant_fp8",
            "ptgq_dequant", "ptgq_scale_bytes", "ptgq_status_string", "ptgq_init", "ptgq_probe_e4m3",
            "ptgq_probe_silu_mul", "ptgq_set_tuning")
 
@@ -49,6 +49,9 @@ def load_library(path: str = LIB_PATH):
     i32, i64, f32, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
     lib.ptgq_quant.argtypes = [vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, vp, vp, vp]
     lib.ptgq_quant.restype = i32
+    lib.ptgq_quant_padded.argtypes = [vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, vp, i64,
+                                      vp, vp]
+    lib.ptgq_quant_padded.restype = i32
     lib.ptgq_quant_masked.argtypes = [vp, i32, i64, i64, i64, i32, i32, vp, i64, i32, i32, i32,
                                       f32, vp, vp, vp]
     lib.ptgq_quant_masked.restype = i32
@@ -152,6 +155,21 @@ def ptgq_quant(x, in_dtype, M, K, group_size, fuse_silu_mul, out_dtype, scale_fm
                                    _enum(scale_fmt, SCALE_FMTS), _enum(scale_layout, SCALE_LAYOUTS),
                                    float(eps), _ptr(q), _ptr(s), _stream(stream))
     return _check("ptgq_quant", rc) if check else rc
+
+
+def ptgq_quant_padded(x, in_dtype, M, K, group_size, fuse_silu_mul, out_dtype, scale_fmt,
+                      scale_layout, eps, q, q_rows, s, stream=None, check=True):
+    ind, fmt, lay = _enum(in_dtype, IN_DTYPES), _enum(scale_fmt, SCALE_FMTS), _enum(scale_layout, SCALE_LAYOUTS)
+    if K > 0 and q_rows >= M >= 0:
+        fn = "ptgq_quant_padded"
+        _need(q, q_rows * K, fn, "q")
+        if M > 0 and ind in _IN_SIZE:
+            _need(x, M * K * (2 if fuse_silu_mul else 1) * _IN_SIZE[ind], fn, "x")
+            _need(s, ptgq_scale_bytes(M, K, group_size, fmt, lay), fn, "s")
+    rc = load_library().ptgq_quant_padded(_ptr(x), ind, M, K, group_size, int(bool(fuse_silu_mul)),
+                                          _enum(out_dtype, OUT_DTYPES), fmt, lay, float(eps),
+                                          _ptr(q), int(q_rows), _ptr(s), _stream(stream))
+    return _check("ptgq_quant_padded", rc) if check else rc
 
 
 def ptgq_quant_masked(x, in_dtype, E, tokens_pad, K, group_size, fuse_silu_mul, masked_m,

@@ -72,17 +72,19 @@ int64_t pad4(int64_t n) { return (n + 3) / 4 * 4; }
 
 // `outer` multiplies the rows (number of experts for the masked layout, 1
 // for flat calls); an empty problem needs no pointers.
-int check_group_args(const void *x, int in_dtype, int64_t outer, int64_t rows, int64_t K, int G,
-                     int out_dtype, int scale_fmt, int scale_layout, float eps, const void *q,
-                     const void *s)
+int check_group_args(const void *x, int in_dtype, int fuse, int64_t outer, int64_t rows,
+                     int64_t K, int G, int out_dtype, int scale_fmt, int scale_layout, float eps,
+                     const void *q, const void *s)
 {
-    if (in_dtype != PTGQ_BF16 && in_dtype != PTGQ_FP16) return PTGQ_EINVAL;
+    if (in_dtype != PTGQ_BF16 && in_dtype != PTGQ_FP16 && in_dtype != PTGQ_FP32)
+        return PTGQ_EINVAL;
     if (out_dtype != PTGQ_E4M3 && out_dtype != PTGQ_INT8) return PTGQ_EINVAL;
     if (scale_fmt != PTGQ_SCALE_F32 && scale_fmt != PTGQ_SCALE_UE8M0) return PTGQ_EINVAL;
     if (scale_layout != PTGQ_ROW_MAJOR && scale_layout != PTGQ_COL_MAJOR) return PTGQ_EINVAL;
     if (!valid_group_size(G)) return PTGQ_EINVAL;
     if (outer < 0 || rows < 0 || K < 0 || K % G != 0) return PTGQ_EINVAL;
     if (!(std::isfinite(eps) && eps >= 0.0f) || std::signbit(eps)) return PTGQ_EINVAL;
+    if (fuse && in_dtype == PTGQ_FP32) return PTGQ_EUNSUPPORTED;   // fused: 16-bit inputs
     if (outer == 0 || rows == 0 || K == 0) return PTGQ_OK;
     if (K >= (int64_t)1 << 29) return PTGQ_EUNSUPPORTED;   // rows are 32-bit buffer ranges
     if (!x || !q || !s) return PTGQ_EINVAL;
@@ -129,9 +131,10 @@ void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16,
 // Blocks for `tasks` tasks.  Plain and direct-SiLU kernels: 4-wave blocks
 // (1-wave blocks for a handful of tasks), with the grid capped so that each
 // CU holds about kInflightBytesPerCu of loads (every wave keeps two tasks of
-// U slabs, 1 KiB per slab and input half); the grid then loops over the tasks.
+// U slabs, 1 KiB per slab and input half, 2 KiB for fp32 input); the grid
+// then loops over the tasks.
 // Table kernels: one 16-wave block per CU.
-void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse)
+void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es)
 {
     int wpb;
     int64_t per_cu;
@@ -142,7 +145,7 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse)
         wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
         if (knob(KNOB_WAVES_PER_BLOCK) > 0)
             wpb = (int)std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), 4);
-        const int64_t wave_bytes = 2 * (int64_t)g.U * 1024 * (fuse ? 2 : 1);
+        const int64_t wave_bytes = 2 * (int64_t)g.U * kSlab * es * (fuse ? 2 : 1);
         const int64_t waves_per_cu = std::max<int64_t>(4, kInflightBytesPerCu / wave_bytes);
         per_cu = std::max<int64_t>(1, waves_per_cu / wpb);
     }
@@ -171,10 +174,12 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse)
     g.grid = (unsigned)std::max<int64_t>(blocks, 1);
 }
 
+// `q_rows` (flat only): rows of the q buffer, >= rows; the extra rows are
+// written as zero.
 int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, int G, int fuse,
                         int out_dtype, int scale_fmt, int scale_layout, float eps, void *q,
                         void *s, const int32_t *masked_m, int64_t E, int64_t expected_m,
-                        void *stream)
+                        int64_t q_rows, void *stream)
 {
     int dev = 0;
     const int cus = current_cus(&dev);
@@ -188,7 +193,8 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
     a.masked_m = masked_m;
     a.rows = rows;
     a.K = K;
-    a.in_stride = fuse ? 2 * K : K;
+    const int64_t es = in_dtype == PTGQ_FP32 ? 4 : 2;   // input element bytes
+    a.in_stride = (fuse ? 2 * K : K) * es;
     a.ng = K / G;
     a.rows_pad = pad4(rows);
     a.eps = eps;
@@ -206,7 +212,10 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         const int64_t tasks = rows * (int64_t)a.tpr;
         if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.n_tasks = (int32_t)tasks;
-        choose_blocks(geo, tasks, cus, fuse != 0);
+        a.q_pad_bytes = (q_rows - rows) * K;
+        // a large zero-filled tail also needs waves: one 1 KiB wave store each
+        choose_blocks(geo, std::max<int64_t>(tasks, (a.q_pad_bytes + 1023) / 1024), cus,
+                      fuse != 0, es);
         if (scale_layout == PTGQ_COL_MAJOR && a.rows_pad > rows)
             a.pad_cols = (int32_t)(scale_fmt == PTGQ_SCALE_UE8M0 ? (a.ng + 3) / 4 : a.ng);
     } else {
@@ -221,7 +230,7 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
         if (E * rows * (int64_t)a.tpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
-        choose_blocks(geo, std::max<int64_t>(hint, 1) * a.tpr * E, cus, fuse != 0);
+        choose_blocks(geo, std::max<int64_t>(hint, 1) * a.tpr * E, cus, fuse != 0, es);
         a.num_experts = (int32_t)E;
         a.x_expert_stride = rows * a.in_stride;
         a.q_expert_stride = rows * K;
@@ -278,11 +287,31 @@ int ptgq_quant(const void *x, int in_dtype, int64_t M, int64_t K, int group_size
                int fuse_silu_mul, int out_dtype, int scale_fmt, int scale_layout, float eps,
                void *q, void *s, void *stream)
 {
-    const int rc = check_group_args(x, in_dtype, 1, M, K, group_size, out_dtype, scale_fmt,
-                                    scale_layout, eps, q, s);
+    const int rc = check_group_args(x, in_dtype, fuse_silu_mul, 1, M, K, group_size, out_dtype,
+                                    scale_fmt, scale_layout, eps, q, s);
     if (rc != PTGQ_OK || M == 0 || K == 0) return rc;
     return launch_group_common(x, in_dtype, M, K, group_size, fuse_silu_mul, out_dtype,
-                               scale_fmt, scale_layout, eps, q, s, nullptr, 1, 0, stream);
+                               scale_fmt, scale_layout, eps, q, s, nullptr, 1, 0, M, stream);
+}
+
+int ptgq_quant_padded(const void *x, int in_dtype, int64_t M, int64_t K, int group_size,
+                      int fuse_silu_mul, int out_dtype, int scale_fmt, int scale_layout,
+                      float eps, void *q, int64_t q_rows, void *s, void *stream)
+{
+    if (q_rows < M) return PTGQ_EINVAL;
+    const int rc = check_group_args(x, in_dtype, fuse_silu_mul, 1, M, K, group_size, out_dtype,
+                                    scale_fmt, scale_layout, eps, q, s);
+    if (rc != PTGQ_OK || q_rows == 0 || K == 0) return rc;
+    if (M == 0) {   // only the zero fill: no input or scales are touched
+        if (!q) return PTGQ_EINVAL;
+        if (!aligned(q, 16)) return PTGQ_EALIGN;
+        x = q;      // never read (no tasks), but a valid base for the
+        s = q;      // empty-range loads every wave issues
+    }
+    if (q_rows >= ((int64_t)1 << 31)) return PTGQ_EUNSUPPORTED;
+    return launch_group_common(x, in_dtype, M, K, group_size, fuse_silu_mul, out_dtype,
+                               scale_fmt, scale_layout, eps, q, s, nullptr, 1, 0, q_rows,
+                               stream);
 }
 
 int ptgq_quant_masked(const void *x, int in_dtype, int64_t E, int64_t tokens_pad, int64_t K,
@@ -290,8 +319,8 @@ int ptgq_quant_masked(const void *x, int in_dtype, int64_t E, int64_t tokens_pad
                       int64_t expected_m, int out_dtype, int scale_fmt, int scale_layout,
                       float eps, void *q, void *s, void *stream)
 {
-    const int rc = check_group_args(x, in_dtype, E, tokens_pad, K, group_size, out_dtype,
-                                    scale_fmt, scale_layout, eps, q, s);
+    const int rc = check_group_args(x, in_dtype, fuse_silu_mul, E, tokens_pad, K, group_size,
+                                    out_dtype, scale_fmt, scale_layout, eps, q, s);
     if (rc != PTGQ_OK) return rc;
     if (E == 0 || tokens_pad == 0 || K == 0) return PTGQ_OK;
     if (!masked_m) return PTGQ_EINVAL;
@@ -299,7 +328,7 @@ int ptgq_quant_masked(const void *x, int in_dtype, int64_t E, int64_t tokens_pad
     if (E > kMaxExperts) return PTGQ_EUNSUPPORTED;
     return launch_group_common(x, in_dtype, tokens_pad, K, group_size, fuse_silu_mul, out_dtype,
                                scale_fmt, scale_layout, eps, q, s, masked_m, E, expected_m,
-                               stream);
+                               tokens_pad, stream);
 }
 
 int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, float *s,

@@ -12,8 +12,8 @@ enum : int { OUT_E4M3 = 0, OUT_INT8 = 1 };
 enum : int { SCALE_F32 = 0, SCALE_UE8M0 = 1 };
 enum : int { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
 
-// Elements of one "slab": one 16-byte load per lane across a 64-lane wave
-// (8 sixteen-bit elements per lane).  Every group-quant task is U = 1 or 2
+// Elements of one "slab": 8 elements per lane across a 64-lane wave (one
+// 16-byte load per lane for 16-bit inputs, two for fp32).  Every group-quant task is U = 1 or 2
 // consecutive slabs of one row; the last task of a row may run past its end
 // (those lanes read zeros and store nothing).
 constexpr int kSlab = 512;
@@ -24,16 +24,16 @@ constexpr int kMaxExperts = 4096;
 // Arguments of the group-quantization kernels (flat and masked).  All shape
 // scalars are computed on the host; the device only indexes.
 struct GroupArgs {
-    const void *x;            // input base (16-bit patterns)
+    const void *x;            // input base (bf16 / fp16 / fp32)
     uint8_t *q;               // codes base
     void *s;                  // scale tensor base
     const int32_t *masked_m;  // masked: live rows per expert; flat: nullptr
     int64_t rows;             // flat: M; masked: tokens_pad
     int64_t K;                // output row width
-    int64_t in_stride;        // input row stride in elements (K, or 2K when fused)
+    int64_t in_stride;        // input row stride in bytes (K, or 2K when fused, elements)
     int64_t ng;               // groups per row, K / G
     int64_t rows_pad;         // ceil(rows / 4) * 4 (column-major scales)
-    int64_t x_expert_stride;  // masked: elements per expert of x
+    int64_t x_expert_stride;  // masked: bytes per expert of x
     int64_t q_expert_stride;  // masked: bytes per expert of q
     int64_t s_expert_stride;  // masked: bytes per expert of s
     float eps;                // amax floor
@@ -46,6 +46,7 @@ struct GroupArgs {
     int32_t num_experts;      // masked: E (1..kMaxExperts)
     int32_t pad_cols;         // flat column-major: 4-byte columns whose pad rows
                               // are zeroed (ceil(ng/4) or ng); 0 = none
+    int64_t q_pad_bytes;      // flat: bytes of q past row M written as zero
 };
 
 // Arguments of the whole-row per-token kernels.

@@ -354,9 +354,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
                                              0x00020000);
 }
 
+// A task's loads: per slab, 16 bytes per lane of the input (gate) half and,
+// when fused, of the up half; fp32 input takes 32 bytes per lane (g, then gh).
 template <int UMAX>
 struct TaskBuf {
     u32x4 g[UMAX];
+    u32x4 gh[UMAX];
     u32x4 u[UMAX];
 };
 
@@ -364,7 +367,7 @@ struct TaskBuf {
 // belongs to (flat: the whole tensor; masked: the expert's), the row index in
 // that scale tensor, and the task index within the row.
 struct TaskLoc {
-    const uint16_t *xrow;
+    const char *xrow;
     uint8_t *qrow;
     uint8_t *sbase;
     int64_t m;
@@ -374,19 +377,25 @@ struct TaskLoc {
 // `live` false: the loads are issued over an empty range (zeros, no memory
 // traffic), so that every path through the task loop issues the same loads
 // and the wait counts stay exact.
-template <bool FUSE, int UMAX>
+template <int IN, bool FUSE, int UMAX>
 __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, int lane,
                                           bool live, TaskBuf<UMAX> &b)
 {
-    const uint32_t row_bytes = live ? (uint32_t)(a.K * 2) : 0u;
+    constexpr int ES = IN == IN_FP32 ? 4 : 2;   // input element bytes
+    const uint32_t row_bytes = live ? (uint32_t)(a.K * ES) : 0u;
     const rsrc_t rg = make_rsrc(t.xrow, row_bytes);
-    const uint32_t off = (uint32_t)t.j * (UMAX * kSlab * 2) + (uint32_t)lane * 16;
+    const uint32_t off = (uint32_t)t.j * (UMAX * kSlab * ES) + (uint32_t)lane * (8 * ES);
 #pragma unroll
-    for (int s = 0; s < UMAX; ++s)
-        b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * 2, 0,
+    for (int s = 0; s < UMAX; ++s) {
+        b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES, 0,
                                                        kStreamPolicy);
+        if constexpr (IN == IN_FP32)
+            b.gh[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES + 16, 0,
+                                                            kStreamPolicy);
+    }
     if constexpr (FUSE) {
-        const rsrc_t ru = make_rsrc(t.xrow + a.K, row_bytes);
+        static_assert(IN != IN_FP32, "fused calls take 16-bit inputs");
+        const rsrc_t ru = make_rsrc(t.xrow + a.K * ES, row_bytes);
 #pragma unroll
         for (int s = 0; s < UMAX; ++s)
             b.u[s] = __builtin_amdgcn_raw_buffer_load_b128(ru, off + s * kSlab * 2, 0,
@@ -432,6 +441,11 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
                     y[2 * k + 1] = silu_s_lookup(ww[k] >> 16, tab) * u[2 * k + 1];
                 }
             }
+        } else if constexpr (IN == IN_FP32) {
+            const uint32_t w[8] = {b.g[s].x, b.g[s].y, b.g[s].z, b.g[s].w,
+                                   b.gh[s].x, b.gh[s].y, b.gh[s].z, b.gh[s].w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) y[k] = __uint_as_float(w[k]);
         } else {
             widen8<IN>(as_uint4(b.g[s]), y);
             if constexpr (FUSE) {
@@ -442,7 +456,7 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
             }
         }
         uint32_t amax;
-        if constexpr (FUSE)
+        if constexpr (FUSE || IN == IN_FP32)
             amax = absmax_bits(y);
         else
             amax = absmax8_bits<IN>(b.g[s].x, b.g[s].y, b.g[s].z, b.g[s].w);
@@ -506,7 +520,7 @@ struct FlatMap {
     {
         const int m = t / a.tpr;
         TaskLoc l;
-        l.xrow = static_cast<const uint16_t *>(a.x) + (int64_t)m * a.in_stride;
+        l.xrow = static_cast<const char *>(a.x) + (int64_t)m * a.in_stride;
         l.qrow = a.q + (int64_t)m * a.K;
         l.sbase = static_cast<uint8_t *>(a.s);
         l.m = m;
@@ -587,7 +601,7 @@ struct MaskedMap {
         int e, r;
         rows.locate(R, lane, e, r);
         TaskLoc l;
-        l.xrow = static_cast<const uint16_t *>(a.x) + (int64_t)e * a.x_expert_stride +
+        l.xrow = static_cast<const char *>(a.x) + (int64_t)e * a.x_expert_stride +
                  (int64_t)r * a.in_stride;
         l.qrow = a.q + (int64_t)e * a.q_expert_stride + (int64_t)r * a.K;
         l.sbase = static_cast<uint8_t *>(a.s) + (int64_t)e * a.s_expert_stride;
@@ -624,21 +638,21 @@ __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first
     const bool hasA0 = t < n;
     TaskBuf<UMAX> A, B;
     TaskLoc lA = map(a, hasA0 ? t : 0, lane);
-    load_task<FUSE, UMAX>(a, lA, lane, hasA0, A);
+    load_task<IN, FUSE, UMAX>(a, lA, lane, hasA0, A);
     if constexpr (STAGE) stage_table<TABLE>(tab);
     if (!hasA0) return;
     while (true) {
         const int tB = t + stride;
         const bool hasB = tB < n;
         const TaskLoc lB = map(a, hasB ? tB : t, lane);
-        load_task<FUSE, UMAX>(a, lB, lane, hasB, B);
+        load_task<IN, FUSE, UMAX>(a, lB, lane, hasB, B);
         process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lA, lane, A, tab);
         if (!hasB) break;
         t = tB;
         const int tA = t + stride;
         const bool hasA = tA < n;
         lA = map(a, hasA ? tA : t, lane);
-        load_task<FUSE, UMAX>(a, lA, lane, hasA, A);
+        load_task<IN, FUSE, UMAX>(a, lA, lane, hasA, A);
         process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lB, lane, B, tab);
         if (!hasA) break;
         t = tA;
@@ -663,6 +677,16 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     const int lb = logical_block(blockIdx.x, gridDim.x);
     run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, true>(a, FlatMap{}, lb * wpb + wib, a.n_tasks,
                                              gridDim.x * wpb, lane, tab);
+    // code rows past M (a padded q buffer) are zero: 16 bytes per lane,
+    // grid-strided over all waves
+    if (a.q_pad_bytes > 0) {
+        u32x4 *qp = reinterpret_cast<u32x4 *>(a.q + a.rows * a.K);
+        const int64_t n16 = a.q_pad_bytes / 16;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        const int64_t nl = (int64_t)gridDim.x * wpb * 64;
+        for (int64_t i = ((int64_t)lb * wpb + wib) * 64 + lane; i < n16; i += nl)
+            __builtin_nontemporal_store(zero, qp + i);
+    }
     // column-major pad slots (rows M .. rows_pad-1) are zero
     if (a.pad_cols > 0 && lb == 0 && wib == 0) {
         uint32_t *s = static_cast<uint32_t *>(a.s);
@@ -1377,8 +1401,13 @@ template <int IN, int G>
 static hipError_t launch_group_f(const GroupArgs &a, bool fuse, int out, bool table, bool masked,
                                  unsigned grid, unsigned block, hipStream_t st)
 {
-    return fuse ? launch_group_o<IN, G, true>(a, out, table, masked, grid, block, st)
-                : launch_group_o<IN, G, false>(a, out, table, masked, grid, block, st);
+    if constexpr (IN == IN_FP32) {   // fused calls take 16-bit inputs
+        if (fuse) return hipErrorInvalidValue;
+        return launch_group_o<IN, G, false>(a, out, table, masked, grid, block, st);
+    } else {
+        return fuse ? launch_group_o<IN, G, true>(a, out, table, masked, grid, block, st)
+                    : launch_group_o<IN, G, false>(a, out, table, masked, grid, block, st);
+    }
 }
 
 template <int IN>
@@ -1402,6 +1431,8 @@ hipError_t launch_group(const GroupArgs &a, int in_dtype, int G, bool fuse, int 
         return launch_group_g<IN_BF16>(a, G, fuse, out_dtype, table, masked, grid, block, stream);
     if (in_dtype == IN_FP16)
         return launch_group_g<IN_FP16>(a, G, fuse, out_dtype, false, masked, grid, block, stream);
+    if (in_dtype == IN_FP32)
+        return launch_group_g<IN_FP32>(a, G, fuse, out_dtype, false, masked, grid, block, stream);
     return hipErrorInvalidValue;
 }
 

@@ -90,8 +90,11 @@ enum ptgq_scale_layout { PTGQ_ROW_MAJOR = 0, PTGQ_COL_MAJOR = 1 };
  * ptgq_quant - flat per-token-group quantization of x [M, K] (or of
  * silu(gate) * up for x = [M, 2K] = gate | up when fuse_silu_mul != 0).
  *
- *   x          device, in_dtype (PTGQ_BF16 or PTGQ_FP16), row-major contiguous
- *              [M, K] or [M, 2K]; 16-byte aligned.
+ *   x          device, in_dtype (PTGQ_BF16, PTGQ_FP16, or PTGQ_FP32 when not
+ *              fused), row-major contiguous [M, K] or [M, 2K]; 16-byte
+ *              aligned.  fp32 input is the trait the pages list beside the
+ *              16-bit ones (sglang #34257 review page, key source snippets:
+ *              float, half and bfloat16 instantiations).
  *   group_size G in {16, 32, 64, 128}; K % G == 0.
  *   out_dtype  PTGQ_E4M3 (OCP e4m3fn codes) or PTGQ_INT8 (two's complement).
  *   scale_fmt, scale_layout  see the layouts above.
@@ -104,11 +107,30 @@ enum ptgq_scale_layout { PTGQ_ROW_MAJOR = 0, PTGQ_COL_MAJOR = 1 };
  * schedule); sglang #27449 PR body, summary (naive scheduler over [M, K]).
  * Errors: PTGQ_EINVAL (M < 0, K < 0, G not allowed, K % G, bad enum, NULL
  * pointer with M*K > 0, eps not finite, negative or -0.0), PTGQ_EALIGN,
- * PTGQ_ELAUNCH, PTGQ_EDEVICE.
+ * PTGQ_EUNSUPPORTED (fp32 input with fuse_silu_mul, K >= 2^29, sizes beyond
+ * 32-bit task counts), PTGQ_ELAUNCH, PTGQ_EDEVICE.
  */
 PTGQ_API int ptgq_quant(const void *x, int in_dtype, int64_t M, int64_t K, int group_size,
                int fuse_silu_mul, int out_dtype, int scale_fmt, int scale_layout, float eps,
                void *q, void *s, void *stream);
+
+/*
+ * ptgq_quant_padded - ptgq_quant into a padded code buffer: q holds q_rows >=
+ * M rows of K bytes, as consumers that load q in 4-row-aligned tiles allocate
+ * it; rows M .. q_rows-1 are written as zero in the same launch (so they hold
+ * no stale bytes).  Rows 0 .. M-1 and the scales are exactly ptgq_quant's
+ * (scale layouts still use rows = M).  With M == 0 only the zero fill runs, and
+ * x and s are not used.
+ * Source: vllm #41326 review page, implementation breakdown (zero-filling the
+ * TMA-aligned extra rows of output_q after quantization) and key source
+ * snippets (the kernel's output_q extent beside tma_aligned_mn).
+ * Errors: as ptgq_quant, plus PTGQ_EINVAL for q_rows < M and
+ * PTGQ_EUNSUPPORTED for q_rows >= 2^31.
+ */
+PTGQ_API int ptgq_quant_padded(const void *x, int in_dtype, int64_t M, int64_t K,
+                               int group_size, int fuse_silu_mul, int out_dtype, int scale_fmt,
+                               int scale_layout, float eps, void *q, int64_t q_rows, void *s,
+                               void *stream);
 
 /*
  * ptgq_quant_masked - the masked expert-parallel MoE layout.

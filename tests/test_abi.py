@@ -79,7 +79,7 @@ def quant(**kw):
     (dict(K=200), aq.PTGQ_EINVAL),
     (dict(M=-1), aq.PTGQ_EINVAL),
     (dict(K=-128), aq.PTGQ_EINVAL),
-    (dict(in_dtype=2), aq.PTGQ_EINVAL),       # fp32 input only for per-token
+    (dict(in_dtype=2, fuse_silu_mul=True), aq.PTGQ_EUNSUPPORTED),   # fused: 16-bit only
     (dict(in_dtype=9), aq.PTGQ_EINVAL),
     (dict(out_dtype=3), aq.PTGQ_EINVAL),
     (dict(scale_fmt=2), aq.PTGQ_EINVAL),
@@ -101,6 +101,46 @@ def test_ptgq_quant_validation(lib, kw, status):
     assert quant(**kw) == status
 
 
+def test_fp32_group_input_passes_validation(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert quant(in_dtype="fp32") == aq.PTGQ_EDEVICE
+    assert quant(in_dtype="fp32", scale_fmt="f32", scale_layout="row") == aq.PTGQ_EDEVICE
+
+
+def padded(**kw):
+    args = dict(x=A16, in_dtype="bf16", M=5, K=256, group_size=128, fuse_silu_mul=False,
+                out_dtype="e4m3", scale_fmt="ue8m0", scale_layout="col", eps=1e-10, q=A16 * 2,
+                q_rows=8, s=A16 * 3, stream=0, check=False)
+    args.update(kw)
+    return aq.ptgq_quant_padded(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_rows=4), aq.PTGQ_EINVAL),               # fewer q rows than M
+    (dict(q_rows=-1, M=0), aq.PTGQ_EINVAL),
+    (dict(group_size=96), aq.PTGQ_EINVAL),
+    (dict(x=0), aq.PTGQ_EINVAL),
+    (dict(q=A16 + 8), aq.PTGQ_EALIGN),
+    (dict(M=0, x=0, s=0, q=0), aq.PTGQ_EINVAL),     # zero fill still needs q
+    (dict(M=0, x=0, s=0, q=A16 + 4), aq.PTGQ_EALIGN),
+    (dict(q_rows=1 << 31), aq.PTGQ_EUNSUPPORTED),
+    (dict(in_dtype="fp32", fuse_silu_mul=True), aq.PTGQ_EUNSUPPORTED),
+    (dict(M=0, q_rows=0, x=0, s=0, q=0), aq.PTGQ_OK),
+    (dict(K=0, x=0, s=0, q=0), aq.PTGQ_OK),
+])
+def test_ptgq_quant_padded_validation(lib, kw, status):
+    assert padded(**kw) == status
+
+
+def test_padded_zero_fill_alone_needs_no_input(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert padded(M=0, x=0, s=0) == aq.PTGQ_EDEVICE
+
+
 def masked(**kw):
     args = dict(x=A16, in_dtype="bf16", E=4, tokens_pad=32, K=256, group_size=128,
                 fuse_silu_mul=True, masked_m=A16 * 4, expected_m=0, out_dtype="e4m3",
@@ -118,6 +158,7 @@ def masked(**kw):
     (dict(group_size=8), aq.PTGQ_EINVAL),
     (dict(x=A16 + 4), aq.PTGQ_EALIGN),
     (dict(E=4097), aq.PTGQ_EUNSUPPORTED),
+    (dict(in_dtype="fp32"), aq.PTGQ_EUNSUPPORTED),  # fused fp32
     (dict(E=0, x=0, q=0, s=0, masked_m=0), aq.PTGQ_OK),
     (dict(tokens_pad=0, x=0, q=0, s=0, masked_m=0), aq.PTGQ_OK),
 ])
