@@ -16,6 +16,7 @@ requantization and dequantization entry points the same way; `roofline` gives th
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --profile-main   (only the headline loop, for rocprofv3)
+    python bench.py --profile-dequant / --profile-requant  (only that loop)
     python bench.py --calib-copy     (a plain device copy of known size, for
                                       calibrating rocprofv3 byte counters)
 """
@@ -181,6 +182,47 @@ def check_rows_cfg2(oracle, x_host, q_dev, s_dev, M, K, G, rows):
     return int((gq != rq).sum()), int((gs != rs.reshape(len(rows), ng)).sum())
 
 
+def dequant_calls(torch, aq):
+    """Dequantization of the headline output: e4m3 codes [16384, 7168] with
+    packed column-major UE8M0 scales back to bf16, over rotated buffer sets."""
+    Md, Kd = 16384, 7168
+    rng = np.random.default_rng(7168)
+    qh = rng.integers(0, 256, (Md, Kd), dtype=np.uint8)
+    qh[(qh & 0x7F) == 0x7F] = 0x38
+    sbd = aq.ptgq_scale_bytes(Md, Kd, 128, "ue8m0", "col")
+    sd = torch.from_numpy(rng.integers(110, 135, sbd, dtype=np.uint8)).to("cuda")
+    qd = torch.from_numpy(qh).to("cuda")
+    fd = Md * Kd * (1 + 2) + Md * (Kd // 128)
+    cd = []
+    for i in range(rotation_sets(fd)):
+        qi = qd if i == 0 else qd.clone()
+        yi = torch.empty((Md, Kd), dtype=torch.bfloat16, device="cuda")
+        cd.append((lambda qi=qi, yi=yi: aq.ptgq_dequant(qi, "e4m3", Md, Kd, 128, sd, "ue8m0",
+                                                        "col", "bf16", yi, check=False)))
+    return cd, fd
+
+
+def requant_calls(torch, aq, live):
+    """fp8 requantization at the sglang #35593 page's timed shape: K = 3584,
+    8 experts, tokens_pad 1024, `live` rows per expert, DeepEP column-major
+    group scales, output scale 2."""
+    E8, T8, K8 = 8, 1024, 3584
+    rng = np.random.default_rng(35593)
+    xq = torch.from_numpy(rng.integers(0, 127, (E8, T8, K8)).astype(np.uint8)).to("cuda")
+    xs = torch.from_numpy(rng.uniform(0.5, 2.0, E8 * T8 * (K8 // 128)).astype(np.float32)).to("cuda")
+    osd = torch.tensor([2.0], dtype=torch.float32, device="cuda")
+    strides = (T8 * (K8 // 128), 1, T8)
+    mmq = torch.full((E8,), live, dtype=torch.int32, device="cuda")
+    nsets = rotation_sets(E8 * live * 7280)
+    outs = [torch.empty((E8, T8, K8), dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    ins = [xq] + [xq.clone() for _ in range(nsets - 1)]
+    cq = [(lambda xi=ins[i], oi=outs[i]: aq.ptgq_requant_fp8(
+        xi, E8, T8, K8, 128, xs, strides, mmq, live, osd, oi, check=False))
+        for i in range(nsets)]
+    fq = E8 * live * (K8 + K8 + (K8 // 128) * 4) + 4 * E8 + 4
+    return cq, fq
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +231,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--profile-main", action="store_true")
+    ap.add_argument("--profile-dequant", action="store_true")
+    ap.add_argument("--profile-requant", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
 
@@ -219,6 +263,15 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes_each_way": GIB, "copies": 5}))
+        return
+
+    if args.profile_dequant or args.profile_requant:
+        calls, nbytes = dequant_calls(torch, aq) if args.profile_dequant else \
+            requant_calls(torch, aq, 1024)
+        r = timer.run(calls, args.steps, args.warmup)
+        print(json.dumps({"profile": "dequant" if args.profile_dequant else "requant",
+                          "steps": args.steps, "bytes": nbytes,
+                          "launch_us_mean": r["launch_ms_mean"] * 1e3}))
         return
 
     M, K, G = 16384, 7168, 128
@@ -268,6 +321,28 @@ def main():
 
     variants = {}
     if not args.no_variants:
+        # the headline input to int8 codes with the same UE8M0 scales
+        fi8 = alg_bytes_flat(M, K, G, 2, False, 1)
+        _, ci8 = make_flat_sets(torch, aq, x_host, M, K, G, False, "int8", "ue8m0", "col",
+                                "bf16", rotation_sets(fi8))
+        variants["int8_ue8m0_bf16_M16384_K7168"] = variant_entry(timer, ci8, fi8)
+        del ci8
+        # fp32 input [8192, 7168] -> e4m3, packed column-major UE8M0 scales
+        M32 = 8192
+        x32 = torch.from_numpy(W.normal_f32(32, (M32, K))).to("cuda")
+        f32b = alg_bytes_flat(M32, K, G, 4, False, 1)
+        sb32 = aq.ptgq_scale_bytes(M32, K, G, "ue8m0", "col")
+        c32 = []
+        for i in range(rotation_sets(f32b)):
+            xi = x32 if i == 0 else x32.clone()
+            qi = torch.empty((M32, K), dtype=torch.uint8, device="cuda")
+            si = torch.empty((sb32,), dtype=torch.uint8, device="cuda")
+            c32.append((lambda xi=xi, qi=qi, si=si: aq.ptgq_quant(
+                xi, "fp32", M32, K, G, False, "e4m3", "ue8m0", "col", 1e-10, qi, si,
+                check=False)))
+        variants["fp32_input_M8192_K7168"] = variant_entry(timer, c32, f32b)
+        del c32, x32
+        torch.cuda.empty_cache()
         # fused silu(gate)*up, bf16 [8192, 2*4096]
         d3 = W.cfg3(8192)
         f3 = alg_bytes_flat(8192, 4096, 128, 2, True, 1)
@@ -316,44 +391,16 @@ def main():
         # 8 experts, 1024 live rows -- read both as 1024 rows in total (128 per
         # expert) and as 1024 rows per expert; tokens_pad 1024, DeepEP
         # column-major group scales, output scale 2
-        E8, T8, K8 = 8, 1024, 3584
-        rng = np.random.default_rng(35593)
-        xq = torch.from_numpy(rng.integers(0, 127, (E8, T8, K8)).astype(np.uint8)).to("cuda")
-        xs = torch.from_numpy(rng.uniform(0.5, 2.0, E8 * T8 * (K8 // 128)).astype(np.float32)).to("cuda")
-        osd = torch.tensor([2.0], dtype=torch.float32, device="cuda")
-        strides = (T8 * (K8 // 128), 1, T8)
         for label, live in (("total", 128), ("per_expert", 1024)):
-            mmq = torch.full((E8,), live, dtype=torch.int32, device="cuda")
-            nsets = rotation_sets(E8 * live * 7280)
-            outs = [torch.empty((E8, T8, K8), dtype=torch.uint8, device="cuda") for _ in range(nsets)]
-            ins = [xq] + [xq.clone() for _ in range(nsets - 1)]
-            cq = [(lambda xi=ins[i], oi=outs[i]: aq.ptgq_requant_fp8(
-                xi, E8, T8, K8, 128, xs, strides, mmq, live, osd, oi, check=False))
-                for i in range(nsets)]
-            fq = E8 * live * (K8 + K8 + (K8 // 128) * 4) + 4 * E8 + 4
+            cq, fq = requant_calls(torch, aq, live)
             variants[f"requant_fp8_E8_K3584_live1024_{label}"] = dict(
-                variant_entry(timer, cq, fq), live_rows=E8 * live,
+                variant_entry(timer, cq, fq), live_rows=8 * live,
                 pages_context_us={"H200": 25.4, "B200": 14.6})
-            del cq, outs, ins
+            del cq
         torch.cuda.empty_cache()
-        # dequantization of the headline output: e4m3 codes [16384, 7168] with
-        # packed column-major UE8M0 scales back to bf16
-        Md, Kd = 16384, 7168
-        rng = np.random.default_rng(7168)
-        qh = rng.integers(0, 256, (Md, Kd), dtype=np.uint8)
-        qh[(qh & 0x7F) == 0x7F] = 0x38
-        sbd = aq.ptgq_scale_bytes(Md, Kd, 128, "ue8m0", "col")
-        sd = torch.from_numpy(rng.integers(110, 135, sbd, dtype=np.uint8)).to("cuda")
-        qd = torch.from_numpy(qh).to("cuda")
-        fd = Md * Kd * (1 + 2) + Md * (Kd // 128)
-        cd = []
-        for i in range(rotation_sets(fd)):
-            qi = qd if i == 0 else qd.clone()
-            yi = torch.empty((Md, Kd), dtype=torch.bfloat16, device="cuda")
-            cd.append((lambda qi=qi, yi=yi: aq.ptgq_dequant(qi, "e4m3", Md, Kd, 128, sd, "ue8m0",
-                                                            "col", "bf16", yi, check=False)))
+        cd, fd = dequant_calls(torch, aq)
         variants["dequant_e4m3_to_bf16_M16384_K7168"] = variant_entry(timer, cd, fd)
-        del cd, qd
+        del cd
         torch.cuda.empty_cache()
 
     cpu = None
