@@ -405,11 +405,13 @@ int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int grou
         (masked_m && !aligned(masked_m, 4)))
         return PTGQ_EALIGN;
     if (E > kMaxExperts || K >= ((int64_t)1 << 30)) return PTGQ_EUNSUPPORTED;
-    // a row's scales are read through a 32-bit buffer range
-    if (((K / group_size - 1) * scale_stride_g + 1) * 4 >= ((int64_t)1 << 32) - 16)
-        return PTGQ_EUNSUPPORTED;
-    const int64_t spr = (K + 1023) / 1024;
-    if (E * T * spr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+    // an expert's codes are addressed with 32-bit offsets, the scales through
+    // one 32-bit buffer range
+    if (T * K >= ((int64_t)1 << 31)) return PTGQ_EUNSUPPORTED;
+    const int64_t ng = K / group_size;
+    const int64_t smax = (E - 1) * scale_stride_e + (T - 1) * scale_stride_t +
+                         (ng - 1) * scale_stride_g;
+    if (smax >= ((int64_t)1 << 30) - 4) return PTGQ_EUNSUPPORTED;
     const int cus = current_cus(nullptr);
     if (cus <= 0) return PTGQ_EDEVICE;
 
@@ -424,16 +426,39 @@ int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int grou
     a.se = scale_stride_e;
     a.st = scale_stride_t;
     a.sg = scale_stride_g;
+    a.s_bytes = (uint32_t)((smax + 1) * 4);
+    a.inv_k = 1.0f / (float)K;
     a.E = (int32_t)E;
-    a.G = group_size;
-    a.spr = (int32_t)spr;
-    // Grid: every wave keeps two 1 KiB tasks in flight; ~48 KiB per CU is 24
-    // waves (6 four-wave blocks) per CU, capped by the expected tasks.
+    a.log2g = __builtin_ctz((unsigned)group_size);
+    // Tasks of 2048 contiguous codes unless there are too few of them to
+    // spread over the CUs; the grid is sized for the expected live rows.  When
+    // it is capped, the blocks per CU (2, 3, 4 or 6 four-wave blocks, every
+    // wave keeping two tasks in flight) are chosen so that the expected tasks
+    // fill the rounds of the grid-stride loop most evenly (measured on MI355X:
+    // a partial last round costs up to 20 %; fewer blocks break ties).
     const int64_t hint = masked_m ? ((expected_m > 0 && expected_m < T) ? expected_m : T) : T;
-    const int64_t tasks = std::max<int64_t>(hint, 1) * spr * E;
+    const int64_t live_codes = std::max<int64_t>(hint, 1) * K;
+    int64_t tcodes = E * ((live_codes + 2047) / 2048) >= (int64_t)cus * 2 ? 2048 : 1024;
+    if (knob(KNOB_SLABS_PER_TASK) > 0) tcodes = knob(KNOB_SLABS_PER_TASK) >= 2 ? 2048 : 1024;
+    a.tcodes = tcodes;
+    if (E * ((T * K + tcodes - 1) / tcodes) >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+    const int64_t tasks = E * ((live_codes + tcodes - 1) / tcodes);
     const int wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
     int64_t blocks = (tasks + wpb - 1) / wpb;
-    const int64_t cap = (int64_t)cus * (knob(KNOB_BLOCKS_PER_CU) > 0 ? knob(KNOB_BLOCKS_PER_CU) : 6);
+    int64_t per_cu = knob(KNOB_BLOCKS_PER_CU);
+    if (per_cu <= 0 && blocks > (int64_t)cus * 2) {
+        double best = 0.0;
+        for (const int64_t c : {2, 3, 4, 6}) {
+            const int64_t waves = (int64_t)cus * c * wpb;
+            const double eff = (double)tasks / (double)(((tasks + waves - 1) / waves) * waves);
+            if (eff > best + 1e-9) {
+                best = eff;
+                per_cu = c;
+            }
+        }
+    }
+    if (per_cu <= 0) per_cu = 2;
+    const int64_t cap = (int64_t)cus * per_cu;
     if (blocks > cap) blocks = cap;
     else if (blocks >= 64) blocks = (blocks + 7) / 8 * 8;
     const hipError_t err = launch_requant(a, (unsigned)std::max<int64_t>(blocks, 1),

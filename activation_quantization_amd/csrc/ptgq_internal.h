@@ -61,7 +61,9 @@ struct TokenArgs {
 
 enum TokenMode : int { TOKEN_WAVE = 0, TOKEN_BLOCK = 1, TOKEN_BLOCK_LOOP = 2 };
 
-// Arguments of the fp8 requantization kernel.
+// Arguments of the fp8 requantization kernel.  Expert e's live codes are the
+// flat region x + e*T*K .. + live_e*K; tasks are `tcodes` contiguous codes of
+// one region (1024 or 2048).
 struct RequantArgs {
     const uint8_t *x;         // e4m3 codes [E, T, K]
     const float *x_scale;     // group scales, element (e, t, g) at e*se + t*st + g*sg
@@ -71,9 +73,11 @@ struct RequantArgs {
     int64_t T;
     int64_t K;
     int64_t se, st, sg;
+    int64_t tcodes;           // codes per task
+    uint32_t s_bytes;         // bytes spanned by x_scale (buffer range)
+    float inv_k;              // 1 / K, for the row estimate when K < a task
     int32_t E;
-    int32_t G;
-    int32_t spr;              // 1024-code slabs per row
+    int32_t log2g;            // log2(group size)
 };
 
 // Arguments of the dequantization kernel.  Codes and outputs are contiguous

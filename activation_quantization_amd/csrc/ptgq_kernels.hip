@@ -946,12 +946,19 @@ __global__ __launch_bounds__(256) void ptq_block_loop_kernel(TokenArgs a)
 // Per-token-group fp8 -> per-tensor fp8 requantization on the masked layout
 // (sglang #35593 review page, key source snippets): each e4m3 code is decoded,
 // multiplied by its group scale, then by 1 / output_scale (two fp32
-// roundings), and narrowed with saturation.  A slab here is 1024 codes of a
-// row (16 per lane, one 16-byte load); tasks are one slab of one live row,
-// balanced over all experts like the masked quantizer, two in flight per wave.
+// roundings), and narrowed with saturation.
+//
+// The live rows of an expert are contiguous in memory (rows 0 .. live-1 of
+// its [T, K] block), so each expert's live codes form one flat region; a task
+// is NS contiguous 1024-code sub-slabs of one region (16 codes per lane per
+// sub-slab, one 16-byte load and store), crossing row ends freely: no lane idles
+// on a row's ragged tail.  Tasks of all experts form one space, split over the
+// grid through an LDS prefix sum of the experts' task counts (read from
+// masked_m on the device); two tasks are in flight per wave.  A lane's row and
+// group (hence its scale) follow from the task's first row and column.
 // --------------------------------------------------------------------------
 
-constexpr int kRqSlab = 1024;
+constexpr int kRqSub = 1024;
 
 __device__ __forceinline__ void decode4_e4m3(uint32_t w, float (&f)[4])
 {
@@ -964,91 +971,142 @@ __device__ __forceinline__ void decode4_e4m3(uint32_t w, float (&f)[4])
     f[3] = hi.y;
 }
 
-struct RqLoc {
-    const uint8_t *xrow;
-    uint8_t *orow;
-    const float *srow;    // x_scale + e*se + r*st
-    int j;                // slab within row
-};
+// Wave 0: live[e] = clamp(masked_m[e], 0, T) (T for every expert without
+// masked_m) and scan[e] = inclusive prefix sum of ceil(live[e] * K / tcodes).
+__device__ __forceinline__ void requant_task_scan(const RequantArgs &a, int lane, int *scan,
+                                                  int *live)
+{
+    int carry = 0;
+    for (int c = 0; c < a.E; c += 64) {
+        int v = 0;
+        if (c + lane < a.E) {
+            int r = a.masked_m ? a.masked_m[c + lane] : (int)a.T;
+            r = r < 0 ? 0 : (r > a.T ? (int)a.T : r);
+            live[c + lane] = r;
+            v = (int)(((int64_t)r * a.K + a.tcodes - 1) / a.tcodes);
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(v, d);
+            if (lane >= d) v += y;
+        }
+        if (c + lane < a.E) scan[c + lane] = v + carry;
+        carry += __builtin_amdgcn_readlane(v, 63);
+    }
+}
 
+template <int NS>
 __global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
 {
-    extern __shared__ int scan[];
+    extern __shared__ int lds[];
+    int *scan = lds;
+    int *live = lds + a.E;
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x);
-    const int E = a.E;
-    if (wib == 0) masked_prefix_sum(a.masked_m, E, a.T, lane, scan);
+    if (wib == 0) requant_task_scan(a, lane, scan, live);
     __syncthreads();
-    const int n = scan[E - 1] * a.spr;
+    const int n = scan[a.E - 1];
     if (lb * wpb >= n) return;                              // block-uniform
-    MaskedRows rows(scan, E, lane);
+    MaskedRows tasks(scan, a.E, lane);
     const float inv = 1.0f / a.output_scale[0];
-    const uint32_t row_bytes = (uint32_t)a.K;
+    const uint32_t K = (uint32_t)a.K;
+    constexpr uint32_t TS = NS * kRqSub;
+    const rsrc_t rs = make_rsrc(a.x_scale, a.s_bytes);
 
+    struct Loc {
+        int64_t base;     // code offset of the task in x and out
+        uint32_t len;     // codes in the task (<= TS)
+        uint32_t row0;    // row (within the expert) of the first code
+        uint32_t c0;      // column of the first code
+        uint32_t sexp;    // e * se: the expert's first scale element
+    };
+    struct Buf {
+        u32x4 w[NS];
+        float s[NS];
+    };
     auto locate = [&](int t) {
-        const int R = t / a.spr;
         int e, r;
-        rows.locate(R, lane, e, r);
-        RqLoc l;
-        const int64_t row = (int64_t)e * a.T + r;
-        l.xrow = a.x + row * a.K;
-        l.orow = a.out + row * a.K;
-        l.srow = a.x_scale + (int64_t)e * a.se + (int64_t)r * a.st;
-        l.j = t - R * a.spr;
+        tasks.locate(t, lane, e, r);
+        Loc l;
+        const uint32_t off0 = (uint32_t)r * TS;               // < T * K < 2^31
+        const uint32_t region = (uint32_t)live[e] * K;
+        l.len = region - off0 < TS ? region - off0 : TS;
+        l.row0 = off0 / K;
+        l.c0 = off0 - l.row0 * K;
+        l.base = (int64_t)e * a.T * a.K + off0;
+        l.sexp = (uint32_t)e * (uint32_t)a.se;
         return l;
     };
-    // A task's loads: its 16 codes per lane and the lane's group scale, both
-    // through per-row buffer resources (the scale resource spans this row's
-    // scales), so lanes past the row read zeros and an empty task reads nothing.
-    const int64_t ng = a.K / a.G;
-    const uint32_t srow_bytes = (uint32_t)(((ng - 1) * a.sg + 1) * 4);
-    struct RqBuf {
-        u32x4 w;
-        float s;
-    };
-    auto load = [&](const RqLoc &l, bool live) {
-        RqBuf b;
-        const uint32_t col = (uint32_t)l.j * kRqSlab + lane * 16;
-        const rsrc_t rx = make_rsrc(l.xrow, live ? row_bytes : 0u);
-        b.w = __builtin_amdgcn_raw_buffer_load_b128(rx, col, 0, kStreamPolicy);
-        const rsrc_t rs = make_rsrc(l.srow, live ? srow_bytes : 0u);
-        const uint32_t soff = col < row_bytes ? (uint32_t)((col / a.G) * a.sg * 4) : 0xFFFFFFF0u;
-        b.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
+    auto load = [&](const Loc &l, bool alive) {
+        Buf b;
+        const uint32_t range = alive ? l.len : 0u;
+        const rsrc_t rx = make_rsrc(a.x + l.base, range);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const uint32_t off = k * kRqSub + lane * 16;
+            b.w[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, kStreamPolicy);
+            uint32_t col = l.c0 + off;
+            uint32_t row = l.row0;
+            if (K >= TS) {
+                if (col >= K) {
+                    col -= K;
+                    row += 1;
+                }
+            } else {
+                // quotient from an fp32 estimate (exact operands), off by at most one
+                uint32_t d = (uint32_t)((float)col * a.inv_k);
+                int32_t rem = (int32_t)(col - d * K);
+                if (rem < 0) {
+                    d -= 1;
+                    rem += (int32_t)K;
+                } else if (rem >= (int32_t)K) {
+                    d += 1;
+                    rem -= (int32_t)K;
+                }
+                col = (uint32_t)rem;
+                row += d;
+            }
+            const uint32_t sidx = l.sexp + row * (uint32_t)a.st + (col >> a.log2g) * (uint32_t)a.sg;
+            const uint32_t soff = off < range ? sidx * 4 : 0xFFFFFFF0u;
+            b.s[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
+        }
         return b;
     };
-    auto process = [&](const RqLoc &l, const RqBuf &b) {
-        const uint32_t col = (uint32_t)l.j * kRqSlab + lane * 16;
-        const u32x4 w = b.w;
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-        uint32_t o[4];
+    auto process = [&](const Loc &l, const Buf &b) {
+        const rsrc_t ro = make_rsrc(a.out + l.base, l.len);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float f[4];
-            decode4_e4m3(ww[k], f);
+        for (int k = 0; k < NS; ++k) {
+            const uint32_t ww[4] = {b.w[k].x, b.w[k].y, b.w[k].z, b.w[k].w};
+            u32x4 o;
+            uint32_t oo[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) f[i] = (f[i] * b.s) * inv;
-            o[k] = e4m3x4<true>(f[0], f[1], f[2], f[3]);
+            for (int i = 0; i < 4; ++i) {
+                float f[4];
+                decode4_e4m3(ww[i], f);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[j] = (f[j] * b.s[k]) * inv;
+                oo[i] = e4m3x4<true>(f[0], f[1], f[2], f[3]);
+            }
+            o.x = oo[0];
+            o.y = oo[1];
+            o.z = oo[2];
+            o.w = oo[3];
+            __builtin_amdgcn_raw_buffer_store_b128(o, ro, k * kRqSub + lane * 16, 0,
+                                                   kStreamPolicy);
         }
-        const rsrc_t ro = make_rsrc(l.orow, row_bytes);
-        u32x4 ov;
-        ov.x = o[0];
-        ov.y = o[1];
-        ov.z = o[2];
-        ov.w = o[3];
-        __builtin_amdgcn_raw_buffer_store_b128(ov, ro, col, 0, kStreamPolicy);
     };
 
     const int stride = gridDim.x * wpb;
     int t = lb * wpb + wib;
     if (t >= n) return;
-    RqLoc lA = locate(t);
-    RqBuf A = load(lA, true), B;
+    Loc lA = locate(t);
+    Buf A = load(lA, true), B;
     while (true) {
         const int tB = t + stride;
         const bool hasB = tB < n;
-        const RqLoc lB = locate(hasB ? tB : t);
+        const Loc lB = locate(hasB ? tB : t);
         B = load(lB, hasB);
         process(lA, A);
         if (!hasB) break;
@@ -1482,7 +1540,13 @@ hipError_t launch_token(const TokenArgs &a, int in_dtype, int vec_bytes, TokenMo
 
 hipError_t launch_requant(const RequantArgs &a, unsigned grid, unsigned block, hipStream_t stream)
 {
-    requant_fp8_kernel<<<grid, block, (size_t)a.E * sizeof(int), stream>>>(a);
+    const size_t lds = 2 * (size_t)a.E * sizeof(int);
+    if (a.tcodes == kRqSub)
+        requant_fp8_kernel<1><<<grid, block, lds, stream>>>(a);
+    else if (a.tcodes == 2 * kRqSub)
+        requant_fp8_kernel<2><<<grid, block, lds, stream>>>(a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

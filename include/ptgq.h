@@ -202,8 +202,9 @@ PTGQ_API int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, vo
  * Source: sglang #35593 review page (key source snippets: the requant kernel
  * and its test; implementation breakdown: 128-aligned hidden sizes).
  * Errors: PTGQ_EINVAL (negative sizes or strides, G, K % G, NULL pointer,
- * out == x), PTGQ_EALIGN, PTGQ_EUNSUPPORTED (E > 4096 or sizes beyond 32-bit
- * task counts), PTGQ_ELAUNCH, PTGQ_EDEVICE.
+ * out == x), PTGQ_EALIGN, PTGQ_EUNSUPPORTED (E > 4096, T*K >= 2^31, a scale
+ * span of 2^30 elements or more, sizes beyond 32-bit task counts),
+ * PTGQ_ELAUNCH, PTGQ_EDEVICE.
  */
 PTGQ_API int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int group_size,
                               const float *x_scale, int64_t scale_stride_e,
