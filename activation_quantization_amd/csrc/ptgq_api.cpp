@@ -135,7 +135,13 @@ void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16,
 // U slabs, 1 KiB per slab and input half, 2 KiB for fp32 input); the grid
 // then loops over the tasks.
 // Table kernels: one 16-wave block per CU.
-void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es)
+// `uncapped`: one wave per task, the grid as large as the task count (no
+// grid-stride loop); the hardware dispatcher then balances the short-lived
+// blocks over the CUs.  Measured on MI355X for plain 16-bit inputs with
+// two-slab tasks: 6.3 TB/s against 5.9 for the capped persistent grid at
+// bf16 [16384, 7168] (the fused, fp32-input and masked kernels are faster
+// capped).
+void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es, bool uncapped)
 {
     int wpb;
     int64_t per_cu;
@@ -167,7 +173,9 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es)
     g.wpb = wpb;
     g.per_cu = per_cu;
     int64_t blocks = (tasks + wpb - 1) / wpb;
-    const int64_t cap = std::max<int64_t>(1, (int64_t)cus * per_cu);
+    const int64_t cap = uncapped && knob(KNOB_BLOCKS_PER_CU) <= 0
+                            ? blocks
+                            : std::max<int64_t>(1, (int64_t)cus * per_cu);
     if (blocks > cap)
         blocks = cap;                                  // a multiple of the CU count
     else if (blocks >= 64)
@@ -215,8 +223,9 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         a.n_tasks = (int32_t)tasks;
         a.q_pad_bytes = (q_rows - rows) * K;
         // a large zero-filled tail also needs waves: one 1 KiB wave store each
+        const bool uncapped = !fuse && es == 2 && geo.U == 2;
         choose_blocks(geo, std::max<int64_t>(tasks, (a.q_pad_bytes + 1023) / 1024), cus,
-                      fuse != 0, es);
+                      fuse != 0, es, uncapped);
         if (scale_layout == PTGQ_COL_MAJOR && a.rows_pad > rows)
             a.pad_cols = (int32_t)(scale_fmt == PTGQ_SCALE_UE8M0 ? (a.ng + 3) / 4 : a.ng);
     } else {
@@ -231,7 +240,7 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
         if (E * rows * (int64_t)a.tpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
-        choose_blocks(geo, std::max<int64_t>(hint, 1) * a.tpr * E, cus, fuse != 0, es);
+        choose_blocks(geo, std::max<int64_t>(hint, 1) * a.tpr * E, cus, fuse != 0, es, false);
         a.num_experts = (int32_t)E;
         a.x_expert_stride = rows * a.in_stride;
         a.q_expert_stride = rows * K;
@@ -362,17 +371,19 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
 
     // Token-count dispatch (the analogue of the warp/CTA threshold of the
     // sglang #34257 page): with enough rows to fill the chip and rows of at
-    // most 8 KiB (8 vectors per lane), one wave per row; otherwise one 256-lane
-    // block per row (measured faster for 14 KiB rows); rows too long for
-    // registers take the two-pass loop.
+    // most 8 KiB (8 vectors per lane), persistent waves that each walk rows
+    // (one wave per row at a time); otherwise one 256-lane block per row
+    // (measured faster for 14 KiB rows); rows too long for registers take the
+    // two-pass loop.
     const int64_t per_wave = (nv + 63) / 64;
     const int64_t per_block = (nv + 255) / 256;
     TokenMode mode;
     const int64_t forced = knob(KNOB_TOKEN_MODE);
     if (forced == TOKEN_WAVE && per_wave <= 16) mode = TOKEN_WAVE;
+    else if (forced == TOKEN_WAVE_LOOP && per_wave <= 8) mode = TOKEN_WAVE_LOOP;
     else if (forced == TOKEN_BLOCK && per_block <= 16) mode = TOKEN_BLOCK;
     else if (forced == TOKEN_BLOCK_LOOP) mode = TOKEN_BLOCK_LOOP;
-    else if (M >= (int64_t)cus * 8 && per_wave <= 8) mode = TOKEN_WAVE;
+    else if (M >= (int64_t)cus * 8 && per_wave <= 8) mode = TOKEN_WAVE_LOOP;
     else if (per_block <= 16) mode = TOKEN_BLOCK;
     else mode = TOKEN_BLOCK_LOOP;
 
@@ -382,6 +393,15 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
         nvl = next_pow2(per_wave);
         block = 256;
         grid = (unsigned)((M + 3) / 4);
+    } else if (mode == TOKEN_WAVE_LOOP) {
+        // persistent waves, two rows in flight each: one four-wave block per
+        // CU measured best (fp16 [8192, 3584]: 16.1 us against 16.7 for one
+        // wave per row and 17.4 with four blocks per CU); the grid never
+        // exceeds one wave per row
+        nvl = next_pow2(per_wave);
+        block = 256;
+        const int64_t per_cu = knob(KNOB_BLOCKS_PER_CU) > 0 ? knob(KNOB_BLOCKS_PER_CU) : 1;
+        grid = (unsigned)std::min<int64_t>((M + 3) / 4, (int64_t)cus * per_cu);
     } else {
         nvl = mode == TOKEN_BLOCK ? next_pow2(per_block) : 0;
         block = 256;

@@ -59,7 +59,7 @@ struct TokenArgs {
     int32_t nv;               // vectors per row (row bytes / vector bytes)
 };
 
-enum TokenMode : int { TOKEN_WAVE = 0, TOKEN_BLOCK = 1, TOKEN_BLOCK_LOOP = 2 };
+enum TokenMode : int { TOKEN_WAVE = 0, TOKEN_BLOCK = 1, TOKEN_BLOCK_LOOP = 2, TOKEN_WAVE_LOOP = 3 };
 
 // Arguments of the fp8 requantization kernel.  Expert e's live codes are the
 // flat region x + e*T*K .. + live_e*K; tasks are `tcodes` contiguous codes of

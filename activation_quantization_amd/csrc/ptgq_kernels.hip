@@ -866,6 +866,90 @@ __global__ __launch_bounds__(256) void ptq_wave_kernel(TokenArgs a)
     }
 }
 
+// Persistent form of the wave-per-row kernel: a grid of a few blocks per CU
+// whose waves walk the rows grid-strided, keeping the next row's loads in
+// flight while they quantize the current one (so reads and writes overlap for
+// the whole call instead of all rows loading first and storing last).  Loads
+// and code stores go through per-row buffer resources (lanes past the row read
+// zeros and store nothing).
+template <int IN, int VB, int NV>
+__global__ __launch_bounds__(256) void ptq_wave_loop_kernel(TokenArgs a)
+{
+    using TV = TokVec<IN, VB>;
+    using raw_t = typename TV::raw_t;
+    constexpr int EV = TV::EV;
+    const int lane = threadIdx.x & 63;
+    const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wpb = blockDim.x >> 6;
+    const int lb = logical_block(blockIdx.x, gridDim.x);
+    const uint32_t row_bytes = (uint32_t)(a.K * TV::insz);
+    const int64_t W = (int64_t)gridDim.x * wpb;
+    int64_t m = (int64_t)lb * wpb + wib;
+    if (m >= a.M) return;                                   // wave-uniform
+
+    auto load = [&](int64_t row, bool live, raw_t (&r)[NV]) {
+        const rsrc_t rx =
+            make_rsrc(static_cast<const uint8_t *>(a.x) + row * row_bytes, live ? row_bytes : 0u);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const uint32_t off = (uint32_t)(lane + 64 * k) * VB;
+            if constexpr (VB == 16) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, kStreamPolicy);
+                r[k] = make_uint4(v.x, v.y, v.z, v.w);
+            } else {
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rx, off, 0, kStreamPolicy);
+                r[k] = make_uint2(v.x, v.y);
+            }
+        }
+    };
+    auto process = [&](int64_t row, const raw_t (&r)[NV]) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const uint32_t mk = TV::absmax(r[k]);
+            amax = amax > mk ? amax : mk;
+        }
+        float rs;
+        const float inv = token_inv(__uint_as_float(wave_max_bits(amax)), rs);
+        if (lane == 0) a.s[row] = rs;
+        const rsrc_t rq = make_rsrc(a.q + row * a.K, (uint32_t)a.K);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            float f[EV];
+            TV::widen(r[k], f);
+#pragma unroll
+            for (int e = 0; e < EV; ++e) f[e] = f[e] * inv;
+            const uint32_t off = (uint32_t)(lane + 64 * k) * EV;
+            if constexpr (EV == 8) {
+                u32x2 o;
+                o.x = e4m3x4<true>(f[0], f[1], f[2], f[3]);
+                o.y = e4m3x4<true>(f[4], f[5], f[6], f[7]);
+                __builtin_amdgcn_raw_buffer_store_b64(o, rq, off, 0, kStreamPolicy);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b32(e4m3x4<true>(f[0], f[1], f[2], f[3]), rq,
+                                                      off, 0, kStreamPolicy);
+            }
+        }
+    };
+
+    raw_t A[NV], B[NV];
+    load(m, true, A);
+    while (true) {
+        const int64_t mB = m + W;
+        const bool hasB = mB < a.M;
+        load(hasB ? mB : m, hasB, B);
+        process(m, A);
+        if (!hasB) break;
+        m = mB;
+        const int64_t mA = m + W;
+        const bool hasA = mA < a.M;
+        load(hasA ? mA : m, hasA, A);
+        process(m, B);
+        if (!hasA) break;
+        m = mA;
+    }
+}
+
 __device__ __forceinline__ uint32_t block_max_bits(uint32_t v, uint32_t *red)
 {
     v = wave_max_bits(v);
@@ -1506,6 +1590,8 @@ static hipError_t launch_token_v(const TokenArgs &a, TokenMode mode, int nvl, un
     case NVV:                                                                  \
         if (mode == TOKEN_WAVE)                                                \
             ptq_wave_kernel<IN, VB, NVV><<<grid, block, 0, st>>>(a);           \
+        else if (mode == TOKEN_WAVE_LOOP)                                      \
+            ptq_wave_loop_kernel<IN, VB, NVV><<<grid, block, 0, st>>>(a);      \
         else                                                                   \
             ptq_block_kernel<IN, VB, NVV><<<grid, block, 0, st>>>(a);          \
         return hipGetLastError();

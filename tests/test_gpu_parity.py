@@ -156,7 +156,7 @@ def test_masked_balanced_schedule(dist):
 
 # --------------------------------------------------------------- per-token
 
-@pytest.mark.parametrize("mode", [-1, 0, 1, 2])
+@pytest.mark.parametrize("mode", [-1, 0, 1, 2, 3])
 @pytest.mark.parametrize("in_dtype", ["bf16", "fp16", "fp32"])
 def test_per_token_modes(in_dtype, mode):
     try:
@@ -177,12 +177,16 @@ def test_per_token_modes(in_dtype, mode):
         aq.ptgq_set_tuning(3, -1)
 
 
-def test_per_token_many_rows_wave_dispatch():
+@pytest.mark.parametrize("K", [1368, 3584, 1076, 4096])
+def test_per_token_many_rows_wave_dispatch(K):
+    """Enough rows for the persistent wave loop (several rows per wave, an odd
+    count for some waves), each row length class."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    M, K = cus * 16, 1368
-    x = W.normal_bf16(31, (M, K))
+    M = cus * 16 + 37
+    x = W.normal_bf16(31 + K, (M, K))
+    x[5] = 0
     gq, gs = run_per_token(x, "bf16", M, K)
-    compare(f"per-token wave-dispatch M={M}", gq, gs, *oracle.ptq_fp8(x, "bf16", M, K))
+    compare(f"per-token wave-dispatch M={M} K={K}", gq, gs, *oracle.ptq_fp8(x, "bf16", M, K))
 
 
 # ---------------------------------------------------------------- edges
