@@ -369,21 +369,23 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
     a.K = K;
     a.nv = (int32_t)nv;
 
-    // Token-count dispatch (the analogue of the warp/CTA threshold of the
-    // sglang #34257 page): with enough rows to fill the chip and rows of at
-    // most 8 KiB (8 vectors per lane), persistent waves that each walk rows
-    // (one wave per row at a time); otherwise one 256-lane block per row
-    // (measured faster for 14 KiB rows); rows too long for registers take the
-    // two-pass loop.
+    // Dispatch (the analogue of the warp/CTA threshold of the sglang #34257
+    // page, by row length here): one block per row, of one wave per ~4 KiB of
+    // row, for rows that fit in registers (16 vectors per lane); longer rows
+    // take the two-pass loop.  Measured on MI355X against one wave per row and
+    // persistent waves: equal or faster for 2, 7, 8 and 14 KiB rows (bf16
+    // [16384, 7168]: 6.4 TB/s).  The other modes stay selectable for tests.
     const int64_t per_wave = (nv + 63) / 64;
-    const int64_t per_block = (nv + 255) / 256;
+    // block mode: one block per row with one wave per ~4 KiB of row (1..4)
+    int64_t tw = std::min<int64_t>(4, std::max<int64_t>(1, (row_bytes + 4095) / 4096));
+    if (knob(KNOB_WAVES_PER_BLOCK) > 0) tw = std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), 4);
+    const int64_t per_block = (nv + 64 * tw - 1) / (64 * tw);
     TokenMode mode;
     const int64_t forced = knob(KNOB_TOKEN_MODE);
     if (forced == TOKEN_WAVE && per_wave <= 16) mode = TOKEN_WAVE;
     else if (forced == TOKEN_WAVE_LOOP && per_wave <= 8) mode = TOKEN_WAVE_LOOP;
     else if (forced == TOKEN_BLOCK && per_block <= 16) mode = TOKEN_BLOCK;
     else if (forced == TOKEN_BLOCK_LOOP) mode = TOKEN_BLOCK_LOOP;
-    else if (M >= (int64_t)cus * 8 && per_wave <= 8) mode = TOKEN_WAVE_LOOP;
     else if (per_block <= 16) mode = TOKEN_BLOCK;
     else mode = TOKEN_BLOCK_LOOP;
 
@@ -404,7 +406,7 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
         grid = (unsigned)std::min<int64_t>((M + 3) / 4, (int64_t)cus * per_cu);
     } else {
         nvl = mode == TOKEN_BLOCK ? next_pow2(per_block) : 0;
-        block = 256;
+        block = mode == TOKEN_BLOCK ? (unsigned)(64 * tw) : 256;
         grid = (unsigned)M;
     }
     const hipError_t err = launch_token(a, in_dtype, vb, mode, nvl, grid, block,

@@ -972,9 +972,10 @@ __global__ __launch_bounds__(256) void ptq_block_kernel(TokenArgs a)
     const uint8_t *xr = static_cast<const uint8_t *>(a.x) + m * a.K * TV::insz;
     uint8_t *qr = a.q + m * a.K;
     typename TV::raw_t raw[NV];
+    const int nt = blockDim.x;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-        const int i = tid + 256 * k;
+        const int i = tid + nt * k;
         raw[k] = (i < a.nv) ? TV::load(xr + (int64_t)i * VB) : TV::zero();
     }
     uint32_t amax = 0;
@@ -988,7 +989,7 @@ __global__ __launch_bounds__(256) void ptq_block_kernel(TokenArgs a)
     if (tid == 0) a.s[m] = r;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-        const int i = tid + 256 * k;
+        const int i = tid + nt * k;
         if (i < a.nv) {
             float f[EV];
             TV::widen(raw[k], f);
