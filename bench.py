@@ -199,7 +199,16 @@ def dequant_calls(torch, aq):
         yi = torch.empty((Md, Kd), dtype=torch.bfloat16, device="cuda")
         cd.append((lambda qi=qi, yi=yi: aq.ptgq_dequant(qi, "e4m3", Md, Kd, 128, sd, "ue8m0",
                                                         "col", "bf16", yi, check=False)))
-    return cd, fd
+
+    def parity(oracle):
+        """Sampled rows of set 0's output against the oracle."""
+        rows = np.unique(np.linspace(0, Md - 1, 24).astype(np.int64))
+        srow = np.ascontiguousarray(rows_of_scales(sd, Md, Kd, 128, "ue8m0", "col", rows))
+        ref = oracle.dequant(np.ascontiguousarray(qh[rows]), "e4m3", len(rows), Kd, 128, srow,
+                             "ue8m0", "row", "bf16")
+        got = cd[0].__defaults__[1][rows].view(torch.int16).cpu().numpy().view(np.uint16)
+        return {"rows": int(len(rows)), "mismatches": int((got != ref).sum())}
+    return cd, fd, parity
 
 
 def requant_calls(torch, aq, live):
@@ -220,7 +229,55 @@ def requant_calls(torch, aq, live):
         xi, E8, T8, K8, 128, xs, strides, mmq, live, osd, oi, check=False))
         for i in range(nsets)]
     fq = E8 * live * (K8 + K8 + (K8 // 128) * 4) + 4 * E8 + 4
-    return cq, fq
+
+    def parity(oracle):
+        """Sampled live rows of three experts of set 0's output against the
+        oracle, each row's group scales gathered from the column-major layout."""
+        xh = xq.cpu().numpy()
+        sh = xs.cpu().numpy()
+        ng = K8 // 128
+        bad = n = 0
+        for e in (0, 3, E8 - 1):
+            rows = np.unique(np.linspace(0, live - 1, 8).astype(np.int64))
+            srow = np.stack([sh[e * strides[0] + t * strides[1] + np.arange(ng) * strides[2]]
+                             for t in rows])
+            ref = oracle.requant_fp8(xh[e, rows][None], 1, len(rows), K8, 128, srow,
+                                     (len(rows) * ng, ng, 1), None, 2.0)
+            bad += int((outs[0][e, rows].cpu().numpy() != ref[0]).sum())
+            n += len(rows)
+        return {"rows": n, "mismatches": bad}
+    return cq, fq, parity
+
+
+def rows_of_scales(s_dev, M, K, G, fmt, layout, rows):
+    """The scales of `rows` from a device scale tensor, as a row-major array
+    ([len(rows), ng] float32 or uint8)."""
+    ng = K // G
+    Mp = (M + 3) // 4 * 4
+    b = s_dev.cpu().numpy().view(np.uint8)
+    if fmt == "f32":
+        f = b.view(np.float32)
+        return f.reshape(M, ng)[rows] if layout == "row" else f[:ng * Mp].reshape(ng, Mp)[:, rows].T
+    if layout == "row":
+        return b[:M * ng].reshape(M, ng)[rows]
+    words = b.view(np.uint32)[:((ng + 3) // 4) * Mp].reshape((ng + 3) // 4, Mp)
+    out = np.empty((len(rows), ng), dtype=np.uint8)
+    for g in range(ng):
+        out[:, g] = (words[g // 4, rows] >> (8 * (g % 4))) & 0xFF
+    return out
+
+
+def sample_flat(oracle, x_host, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, q_dev, s_dev,
+                nrows=24):
+    """Mismatch counts of sampled rows of a timed flat call against the oracle."""
+    rows = np.unique(np.linspace(0, M - 1, nrows).astype(np.int64))
+    xs = np.ascontiguousarray(x_host[rows])
+    rq, rs = oracle.ptgq(xs, in_dtype, len(rows), K, G, fuse, out_dtype, fmt, "row", eps=1e-10)
+    gq = q_dev[rows].cpu().numpy()
+    gs = rows_of_scales(s_dev, M, K, G, fmt, layout, rows)
+    rs = rs.view(np.float32 if fmt == "f32" else np.uint8).reshape(len(rows), K // G)
+    return {"rows": int(len(rows)), "code_mismatches": int((gq != rq).sum()),
+            "scale_mismatches": int((gs.view(np.uint8) != rs.view(np.uint8)).sum())}
 
 
 def main():
@@ -266,7 +323,7 @@ def main():
         return
 
     if args.profile_dequant or args.profile_requant:
-        calls, nbytes = dequant_calls(torch, aq) if args.profile_dequant else \
+        calls, nbytes, _ = dequant_calls(torch, aq) if args.profile_dequant else \
             requant_calls(torch, aq, 1024)
         r = timer.run(calls, args.steps, args.warmup)
         print(json.dumps({"profile": "dequant" if args.profile_dequant else "requant",
@@ -321,15 +378,20 @@ def main():
 
     variants = {}
     if not args.no_variants:
+        import oracle as oracle_mod
         # the headline input to int8 codes with the same UE8M0 scales
         fi8 = alg_bytes_flat(M, K, G, 2, False, 1)
-        _, ci8 = make_flat_sets(torch, aq, x_host, M, K, G, False, "int8", "ue8m0", "col",
-                                "bf16", rotation_sets(fi8))
-        variants["int8_ue8m0_bf16_M16384_K7168"] = variant_entry(timer, ci8, fi8)
-        del ci8
+        si8, ci8 = make_flat_sets(torch, aq, x_host, M, K, G, False, "int8", "ue8m0", "col",
+                                  "bf16", rotation_sets(fi8))
+        variants["int8_ue8m0_bf16_M16384_K7168"] = dict(
+            variant_entry(timer, ci8, fi8),
+            parity=sample_flat(oracle_mod, x_host, "bf16", M, K, G, False, "int8", "ue8m0", "col",
+                               si8[0][1], si8[0][2]))
+        del ci8, si8
         # fp32 input [8192, 7168] -> e4m3, packed column-major UE8M0 scales
         M32 = 8192
-        x32 = torch.from_numpy(W.normal_f32(32, (M32, K))).to("cuda")
+        x32h = W.normal_f32(32, (M32, K))
+        x32 = torch.from_numpy(x32h).to("cuda")
         f32b = alg_bytes_flat(M32, K, G, 4, False, 1)
         sb32 = aq.ptgq_scale_bytes(M32, K, G, "ue8m0", "col")
         c32 = []
@@ -340,16 +402,22 @@ def main():
             c32.append((lambda xi=xi, qi=qi, si=si: aq.ptgq_quant(
                 xi, "fp32", M32, K, G, False, "e4m3", "ue8m0", "col", 1e-10, qi, si,
                 check=False)))
-        variants["fp32_input_M8192_K7168"] = variant_entry(timer, c32, f32b)
+        variants["fp32_input_M8192_K7168"] = dict(
+            variant_entry(timer, c32, f32b),
+            parity=sample_flat(oracle_mod, x32h, "fp32", M32, K, G, False, "e4m3", "ue8m0", "col",
+                               c32[0].__defaults__[1], c32[0].__defaults__[2]))
         del c32, x32
         torch.cuda.empty_cache()
         # fused silu(gate)*up, bf16 [8192, 2*4096]
         d3 = W.cfg3(8192)
         f3 = alg_bytes_flat(8192, 4096, 128, 2, True, 1)
-        _, c3 = make_flat_sets(torch, aq, d3["x"], 8192, 4096, 128, True, "e4m3", "ue8m0", "col",
-                               "bf16", rotation_sets(f3))
-        variants["fused_silu_mul_M8192_K4096"] = variant_entry(timer, c3, f3)
-        del c3
+        s3, c3 = make_flat_sets(torch, aq, d3["x"], 8192, 4096, 128, True, "e4m3", "ue8m0",
+                                "col", "bf16", rotation_sets(f3))
+        variants["fused_silu_mul_M8192_K4096"] = dict(
+            variant_entry(timer, c3, f3),
+            parity=sample_flat(oracle_mod, d3["x"], "bf16", 8192, 4096, 128, True, "e4m3", "ue8m0",
+                               "col", s3[0][1], s3[0][2]))
+        del c3, s3
         # masked MoE, E=32, tokens_pad=384, fused, K=2048
         d4 = W.cfg4()
         E, T, K4, mm = d4["E"], d4["T"], d4["K"], d4["masked_m"]
@@ -366,15 +434,35 @@ def main():
             c4.append((lambda xi=xi, q4=q4, s4=s4: aq.ptgq_quant_masked(
                 xi, "bf16", E, T, K4, 128, True, mm_d, int(live // E), "e4m3", "ue8m0", "col",
                 1e-10, q4, s4, check=False)))
-        variants["masked_E32_T384_K2048_fused"] = dict(variant_entry(timer, c4, f4), live_rows=live)
+        ent4 = dict(variant_entry(timer, c4, f4), live_rows=live)
+        # live rows of four experts of set 0 (the rest of its rows hold whatever
+        # the buffer held: only live rows are checked)
+        bad_q = bad_s = nrow = 0
+        q40, s40 = c4[0].__defaults__[1], c4[0].__defaults__[2]
+        for e in (0, 1, 7, E - 1):
+            lv = int(np.clip(mm[e], 0, T))
+            if lv == 0:
+                continue
+            rq, rs = oracle_mod.ptgq(np.ascontiguousarray(d4["x"][e, :lv]), "bf16", lv, K4, 128,
+                                     True, "e4m3", "ue8m0", "row", eps=1e-10)
+            bad_q += int((q40[e, :lv].cpu().numpy() != rq).sum())
+            gs = rows_of_scales(s40[e * sb4:(e + 1) * sb4], T, K4, 128, "ue8m0", "col",
+                                np.arange(lv))
+            bad_s += int((gs != rs.reshape(lv, K4 // 128)).sum())
+            nrow += lv
+        ent4["parity"] = {"rows": nrow, "code_mismatches": bad_q, "scale_mismatches": bad_s}
+        variants["masked_E32_T384_K2048_fused"] = ent4
         del c4
         # fp16 [8192, 3584] -> int8, fp32 row-major scales, G = 128; per-token e4m3
         d5 = W.cfg5()
         f5 = alg_bytes_flat(8192, 3584, 128, 2, False, 4)
-        _, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, 128, False, "int8", "f32", "row",
-                               "fp16", rotation_sets(f5))
-        variants["int8_fp16_M8192_K3584_G128"] = variant_entry(timer, c5, f5)
-        del c5
+        s5s, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, 128, False, "int8", "f32", "row",
+                                 "fp16", rotation_sets(f5))
+        variants["int8_fp16_M8192_K3584_G128"] = dict(
+            variant_entry(timer, c5, f5),
+            parity=sample_flat(oracle_mod, d5["x"], "fp16", 8192, 3584, 128, False, "int8", "f32",
+                               "row", s5s[0][1], s5s[0][2]))
+        del c5, s5s
         f5b = 8192 * 3584 * 2 + 8192 * 3584 + 8192 * 4
         x5 = torch.from_numpy(d5["x"].view(np.int16)).to("cuda")
         c5b = []
@@ -384,7 +472,16 @@ def main():
             s5 = torch.empty((8192,), dtype=torch.float32, device="cuda")
             c5b.append((lambda xi=xi, q5=q5, s5=s5: aq.ptq_quant_fp8(xi, "fp16", 8192, 3584, q5,
                                                                     s5, check=False)))
-        variants["per_token_fp8_fp16_M8192_K3584"] = variant_entry(timer, c5b, f5b)
+        ent5 = variant_entry(timer, c5b, f5b)
+        rows5 = np.unique(np.linspace(0, 8191, 24).astype(np.int64))
+        rq5, rs5 = oracle_mod.ptq_fp8(np.ascontiguousarray(d5["x"][rows5]), "fp16", len(rows5),
+                                      3584)
+        q50, s50 = c5b[0].__defaults__[1], c5b[0].__defaults__[2]
+        ent5["parity"] = {"rows": int(len(rows5)),
+                          "code_mismatches": int((q50[rows5].cpu().numpy() != rq5).sum()),
+                          "scale_mismatches": int((s50[rows5].cpu().numpy().view(np.uint32) !=
+                                                   rs5.view(np.uint32)).sum())}
+        variants["per_token_fp8_fp16_M8192_K3584"] = ent5
         del c5b
         torch.cuda.empty_cache()
         # fp8 requantization, the sglang #35593 page's timed shape: K = 3584,
@@ -392,15 +489,16 @@ def main():
         # expert) and as 1024 rows per expert; tokens_pad 1024, DeepEP
         # column-major group scales, output scale 2
         for label, live in (("total", 128), ("per_expert", 1024)):
-            cq, fq = requant_calls(torch, aq, live)
+            cq, fq, pq = requant_calls(torch, aq, live)
             variants[f"requant_fp8_E8_K3584_live1024_{label}"] = dict(
                 variant_entry(timer, cq, fq), live_rows=8 * live,
-                pages_context_us={"H200": 25.4, "B200": 14.6})
-            del cq
+                pages_context_us={"H200": 25.4, "B200": 14.6}, parity=pq(oracle_mod))
+            del cq, pq
         torch.cuda.empty_cache()
-        cd, fd = dequant_calls(torch, aq)
-        variants["dequant_e4m3_to_bf16_M16384_K7168"] = variant_entry(timer, cd, fd)
-        del cd
+        cd, fd, pd = dequant_calls(torch, aq)
+        variants["dequant_e4m3_to_bf16_M16384_K7168"] = dict(variant_entry(timer, cd, fd),
+                                                             parity=pd(oracle_mod))
+        del cd, pd
         torch.cuda.empty_cache()
 
     cpu = None
