@@ -55,10 +55,10 @@ int current_cus(int *dev_out)
 // ------------------------------------------------------------ tuning knobs
 // Process-wide overrides of the geometry chooser (diagnostics and sweeps
 // only; -1 = automatic), set through ptgq_set_tuning.
-constexpr int kKnobs = 5;
-std::atomic<int64_t> g_knob[kKnobs] = {{-1}, {-1}, {-1}, {-1}, {-1}};
+constexpr int kKnobs = 6;
+std::atomic<int64_t> g_knob[kKnobs] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
 enum { KNOB_SLABS_PER_TASK = 0, KNOB_WAVES_PER_BLOCK = 1, KNOB_BLOCKS_PER_CU = 2,
-       KNOB_TOKEN_MODE = 3, KNOB_SILU_TABLE = 4 };
+       KNOB_TOKEN_MODE = 3, KNOB_SILU_TABLE = 4, KNOB_XCD_CHUNK = 5 };
 
 int64_t knob(int k) { return g_knob[k].load(std::memory_order_relaxed); }
 
@@ -109,6 +109,8 @@ constexpr int kTableBlocksPerCu = 1;  // one table block of 16 waves per CU
 // (measured on MI355X: 48-64 KiB per CU, with every wave holding the next
 // task's loads while it processes the current one).
 constexpr int64_t kInflightBytesPerCu = 48 * 1024;
+// Blocks per XCD chunk of the uncapped flat grid's block -> task mapping.
+constexpr int64_t kXcdChunk = 64;
 
 // Slabs per task (1 or 2) and the SiLU path, for `slabs` slabs of work in
 // total.  Fused bf16 work large enough to amortize staging the 32 KiB table in
@@ -116,7 +118,13 @@ constexpr int64_t kInflightBytesPerCu = 48 * 1024;
 // work spreads over as many waves and CUs as possible.  Many: two slabs per
 // task for the plain and direct-SiLU kernels when a row has an even number of
 // slabs (no task runs past a row), else one (measured best on MI355X).
-void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16, int cus)
+// `flat16`: an unfused flat call on 16-bit input, which runs the uncapped
+// grid with two-slab tasks also when a row has an odd number (>= 3) of slabs:
+// its last task per row holds one slab (measured on MI355X, fp16 rows of 3, 5
+// and 7 slabs: 2-10 % faster than capped one-slab tasks; one-slab rows stay
+// one-slab).
+void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16, bool flat16,
+                 int cus)
 {
     const int64_t wave_slots = (int64_t)cus * 4 * 8;   // 8 waves per SIMD
     g.table = fuse && bf16 && slabs >= (int64_t)cus * 4 * kTableWaves;
@@ -124,7 +132,7 @@ void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16,
     // Table kernels (16 waves per CU) run one-slab tasks: measured 6-8 % faster
     // than two-slab tasks for the fused flat and masked workloads.
     int U = 1;
-    if (!g.table && slabs >= 2 * wave_slots && spr % 2 == 0) U = 2;
+    if (!g.table && slabs >= 2 * wave_slots && (spr % 2 == 0 || (flat16 && spr >= 3))) U = 2;
     if (knob(KNOB_SLABS_PER_TASK) > 0) U = knob(KNOB_SLABS_PER_TASK) >= 2 ? 2 : 1;
     g.U = std::min(U, kMaxSlabsPerTask);
 }
@@ -215,7 +223,7 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
 
     GroupGeom geo;
     if (!masked) {
-        choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, cus);
+        choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, !fuse && es == 2, cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
         const int64_t tasks = rows * (int64_t)a.tpr;
@@ -226,6 +234,15 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         const bool uncapped = !fuse && es == 2 && geo.U == 2;
         choose_blocks(geo, std::max<int64_t>(tasks, (a.q_pad_bytes + 1023) / 1024), cus,
                       fuse != 0, es, uncapped);
+        // Block -> task mapping of a grid far larger than the chip: chunks of
+        // 64 blocks per XCD (measured on MI355X, bf16 [M, 7168]: M = 4096
+        // 16.4 -> 15.4 us, M = 16384 55.9 -> 53.4 us against one contiguous
+        // range per XCD; chunks of 32..256 blocks within 1 %; fp16 [16384,
+        // 3584]: 30.3 -> 28.6 us).  Rows of fewer than 4 tasks (fp16 K =
+        // 1536, 2560: 3-7 % slower chunked) and grids of fewer than 4 spans
+        // (M = 256 here: 3.1 us against 3.3-3.6) keep the contiguous ranges.
+        if (uncapped && a.tpr >= 4 && geo.grid >= 4 * 8 * kXcdChunk) a.xcd_chunk = kXcdChunk;
+        if (knob(KNOB_XCD_CHUNK) >= 0) a.xcd_chunk = (int32_t)std::min<int64_t>(knob(KNOB_XCD_CHUNK), 1 << 20);
         if (scale_layout == PTGQ_COL_MAJOR && a.rows_pad > rows)
             a.pad_cols = (int32_t)(scale_fmt == PTGQ_SCALE_UE8M0 ? (a.ng + 3) / 4 : a.ng);
     } else {
@@ -236,7 +253,8 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         // expected only make each wave loop longer.
         if (E > kMaxExperts) return PTGQ_EUNSUPPORTED;
         const int64_t hint = (expected_m > 0 && expected_m < rows) ? expected_m : rows;
-        choose_task(geo, std::max<int64_t>(hint, 1) * a.spr * E, a.spr, fuse != 0, bf16, cus);
+        choose_task(geo, std::max<int64_t>(hint, 1) * a.spr * E, a.spr, fuse != 0, bf16, false,
+                    cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
         if (E * rows * (int64_t)a.tpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;

@@ -47,6 +47,8 @@ struct GroupArgs {
     int32_t pad_cols;         // flat column-major: 4-byte columns whose pad rows
                               // are zeroed (ceil(ng/4) or ng); 0 = none
     int64_t q_pad_bytes;      // flat: bytes of q past row M written as zero
+    int32_t xcd_chunk;        // flat: blocks per XCD chunk of the block -> task
+                              // mapping; 0 = one contiguous range per XCD
 };
 
 // Arguments of the whole-row per-token kernels.

@@ -659,12 +659,23 @@ __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first
     }
 }
 
-// XCD-aware logical block id: blocks are dealt to the 8 XCDs round-robin, so
-// with a grid that is a multiple of 8, XCD x gets logical ids
-// [x * nb/8, (x+1) * nb/8), a contiguous range of tasks.
-__device__ __forceinline__ int logical_block(int b, int nb)
+// XCD-aware logical block id.  Blocks are dealt to the 8 XCDs round-robin
+// (block b runs on XCD b % 8).  With chunk == 0 and a grid that is a multiple
+// of 8, XCD x gets the logical ids [x * nb/8, (x+1) * nb/8): one contiguous
+// range of tasks, the right mapping for a capped grid whose waves loop (all
+// XCDs then sweep one grid-stride window together).  With chunk C > 0 the
+// ids are dealt in spans of 8C blocks, XCD x taking C consecutive ids of each
+// span: for a grid much larger than the chip, the XCDs stream neighbouring
+// regions of memory instead of eight far-apart ones, and the scale words of
+// neighbouring rows are still written from one L2.  Ids in a last, partial
+// span map to themselves.
+__device__ __forceinline__ int logical_block(int b, int nb, int chunk = 0)
 {
-    return (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+    if (chunk <= 0) return (nb & 7) == 0 ? (b & 7) * (nb >> 3) + (b >> 3) : b;
+    const int span = 8 * chunk;
+    if (b >= nb / span * span) return b;
+    const int r = b % span;
+    return (b - r) + (r & 7) * chunk + (r >> 3);
 }
 
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
@@ -674,7 +685,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
-    const int lb = logical_block(blockIdx.x, gridDim.x);
+    const int lb = logical_block(blockIdx.x, gridDim.x, a.xcd_chunk);
     run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, true>(a, FlatMap{}, lb * wpb + wib, a.n_tasks,
                                              gridDim.x * wpb, lane, tab);
     // code rows past M (a padded q buffer) are zero: 16 bytes per lane,

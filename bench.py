@@ -76,10 +76,12 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def run(self, calls, steps, warmup):
-        """Two timed passes over `steps` launches: one HIP event pair around the
-        whole region (the per-step time, with nothing between launches), then
-        an event pair around every launch (the kernel's average duration)."""
+    def run(self, calls, steps, warmup, per_launch=True):
+        """Timed passes over `steps` launches: one HIP event pair around the
+        whole region (launches back to back, nothing between them: the average
+        launch duration, inter-launch gaps included), then, with `per_launch`,
+        an event pair around every launch (each launch then starts from a
+        drained queue; the events themselves add about 2 us)."""
         torch = self.torch
         for i in range(warmup):
             calls[i % len(calls)]()
@@ -93,6 +95,8 @@ class Timer:
         region1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
+        if not per_launch:
+            return {"region_ms": region0.elapsed_time(region1), "wall_s": wall}
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         for i in range(steps):
@@ -104,10 +108,12 @@ class Timer:
         return {"region_ms": region0.elapsed_time(region1), "launch_ms_mean": float(np.mean(per)),
                 "launch_ms_median": float(np.median(per)), "wall_s": wall}
 
-    def graph(self, calls, per_graph, replays):
+    def graph(self, calls, per_graph, replays, min_ms=50.0):
         """Device time per call of `per_graph` back-to-back launches captured in
         one HIP graph (launch overhead excluded): the latency-bound small-M
-        figure."""
+        figure.  The graph is replayed at least `replays` times and for at
+        least `min_ms` of device time, so that short windows of a GPU that is
+        still changing clocks do not decide the figure."""
         torch = self.torch
         for c in calls:
             c()
@@ -125,6 +131,13 @@ class Timer:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        replays = max(replays, math.ceil(min_ms / max(e0.elapsed_time(e1), 1e-3)))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(replays):
             g.replay()
         e1.record()
@@ -137,7 +150,7 @@ def variant_entry(timer, calls, nbytes, steps=100):
     launches captured in a HIP graph (the pages time their kernels inside
     graphs too), with the eager back-to-back figure beside it."""
     r = timer.run(calls, steps, 10)
-    per_graph = max(len(calls), min(200, max(8, int(2e8 // max(nbytes, 1)))))
+    per_graph = max(len(calls), min(200, max(8, math.ceil(1.2e10 / max(nbytes, 1)))))
     ms = timer.graph(calls, per_graph, 5)
     us = ms * 1e3
     return {"us_per_call": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
@@ -283,11 +296,13 @@ def sample_flat(oracle, x_host, in_dtype, M, K, G, fuse, out_dtype, fmt, layout,
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--profile-main", action="store_true")
+    ap.add_argument("--profile-m", type=int, default=16384,
+                    help="rows of the workload that --profile-main launches")
     ap.add_argument("--profile-dequant", action="store_true")
     ap.add_argument("--profile-requant", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
@@ -325,13 +340,15 @@ def main():
     if args.profile_dequant or args.profile_requant:
         calls, nbytes, _ = dequant_calls(torch, aq) if args.profile_dequant else \
             requant_calls(torch, aq, 1024)
-        r = timer.run(calls, args.steps, args.warmup)
+        r = timer.run(calls, args.steps, args.warmup, per_launch=False)
         print(json.dumps({"profile": "dequant" if args.profile_dequant else "requant",
                           "steps": args.steps, "bytes": nbytes,
-                          "launch_us_mean": r["launch_ms_mean"] * 1e3}))
+                          "us_per_launch": r["region_ms"] * 1e3 / args.steps}))
         return
 
     M, K, G = 16384, 7168, 128
+    if args.profile_main:
+        M = args.profile_m
     d = W.cfg2(M)
     x_host = d["x"]
     foot = alg_bytes_flat(M, K, G, 2, False, 1)
@@ -340,16 +357,18 @@ def main():
                                  "bf16", nsets)
 
     if args.profile_main:
-        r = timer.run(calls, args.steps, args.warmup)
+        r = timer.run(calls, args.steps, args.warmup, per_launch=False)
         print(json.dumps({"profile_main": True, "steps": args.steps,
-                          "launch_us_mean": r["launch_ms_mean"] * 1e3}))
+                          "us_per_launch": r["region_ms"] * 1e3 / args.steps}))
         return
 
     main_res = timer.run(calls, args.steps, args.warmup)
     ms_per_step = main_res["region_ms"] / args.steps
     value = foot / (ms_per_step * 1e-3) / 1e9
-    launch_s = main_res["launch_ms_mean"] * 1e-3
-    achieved = foot / launch_s / 1e9
+    # the kernel's average launch duration: the event pair around the K
+    # back-to-back launches on the stream they run on (gaps included, so a
+    # lower bound on the kernel's own rate); one launch per step
+    achieved = foot / (ms_per_step * 1e-3) / 1e9
 
     # sampled parity of the timed output at full size
     rows = sorted(set([0, 1, 2, M - 3, M - 2, M - 1] + list(range(5, M, 257))))
@@ -363,7 +382,7 @@ def main():
         fi = alg_bytes_flat(Mi, K, G, 2, False, 1)
         ns = rotation_sets(fi)
         _, ci = make_flat_sets(torch, aq, di, Mi, K, G, False, "e4m3", "ue8m0", "col", "bf16", ns)
-        per_graph = max(ns, min(200, max(8, int(2e8 // max(fi, 1)))))
+        per_graph = max(ns, min(200, max(8, math.ceil(1.2e10 / max(fi, 1)))))
         t_cold = timer.graph(ci, per_graph, 5)
         t_warm = timer.graph(ci[:1], min(per_graph, 100), 5) if Mi <= 256 else None
         ent = {"M": Mi, "us_per_call": round(t_cold * 1e3, 3), "bytes": fi,
@@ -537,7 +556,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": "ptgq_flat_kernel<bf16, G=128, no fuse, e4m3>",
-                     "avg_launch_us": round(main_res["launch_ms_mean"] * 1e3, 3),
+                     "avg_launch_us": round(ms_per_step * 1e3, 3),
+                     "avg_launch_us_isolated": round(main_res["launch_ms_mean"] * 1e3, 3),
                      "kernel_source_digest": kernel_source_digest()},
         "parity_sample": {"rows": len(rows), "code_mismatches": code_bad,
                           "scale_mismatches": scale_bad},

@@ -228,7 +228,7 @@ def test_special_values(eps, fmt):
 
 
 def reset_knobs():
-    for k in range(5):
+    for k in range(6):
         aq.ptgq_set_tuning(k, -1)
 
 
@@ -239,7 +239,9 @@ def test_tuning_knobs_never_change_results(fuse):
     args = (x, "bf16", M, K, 128, fuse, "e4m3", "ue8m0", "col")
     ref = oracle.ptgq(*args)
     try:
-        for knob, values in ((0, [1, 2, 4]), (1, [1, 2, 4]), (2, [1, 2, 64]), (4, [0, 1])):
+        # knob 5 (XCD chunk): 1, 3 and 64 leave a ragged last span of blocks
+        for knob, values in ((0, [1, 2, 4]), (1, [1, 2, 4]), (2, [1, 2, 64]), (4, [0, 1]),
+                             (5, [0, 1, 3, 64])):
             for v in values:
                 aq.ptgq_set_tuning(knob, v)
                 compare(f"fuse={fuse} knob {knob}={v}", *run_flat(*args), *ref)
