@@ -109,8 +109,9 @@ constexpr int kTableBlocksPerCu = 1;  // one table block of 16 waves per CU
 // (measured on MI355X: 48-64 KiB per CU, with every wave holding the next
 // task's loads while it processes the current one).
 constexpr int64_t kInflightBytesPerCu = 48 * 1024;
-// Blocks per XCD chunk of the uncapped flat grid's block -> task mapping.
+// Blocks per XCD chunk of the uncapped grids' block -> task mappings.
 constexpr int64_t kXcdChunk = 64;
+constexpr int64_t kDequantXcdChunk = 16;
 
 // Slabs per task (1 or 2) and the SiLU path, for `slabs` slabs of work in
 // total.  Fused bf16 work large enough to amortize staging the 32 KiB table in
@@ -533,10 +534,15 @@ int ptgq_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int gro
     // for fp32), contiguous so that a wave's loads in flight stay within a few
     // pages, grid-strided over the waves for as many full rounds as fit; the
     // remainder is one last round in which every wave takes an equal share
-    // (whole sub-slabs).  Four sub-slabs per task with four four-wave blocks
-    // per CU (two for fp32 outputs, whose stores are twice as wide) measured
-    // best on MI355X; problems too small to give every wave a few tasks use
-    // one sub-slab per task.
+    // (whole sub-slabs).  Problems too small to give every wave a few tasks
+    // use one sub-slab per task.  With at least as many tasks as the chip
+    // holds waves, the grid is uncapped (one task per wave) and its blocks are
+    // dealt to the XCDs in chunks of 16 (measured on MI355X, e4m3 [M, 7168] ->
+    // bf16: M = 16384 63.7 -> 57.0 us, M = 4096 17.4 -> 16.6 us; fp32 out
+    // [8192, 7168] 52.5 -> 48.3 us; chunks of 2..32 blocks within 1 %, one
+    // contiguous range per XCD 62.6 us).  Fewer tasks: four four-wave blocks
+    // per CU (two for fp32 outputs, whose stores are twice as wide), which
+    // measured best there (M = 1024: 6.9 us against 7.7 uncapped).
     const int64_t total = M * K;
     const int64_t sub = out_dtype == PTGQ_FP32 ? 256 : 512;
     const int64_t subs = (total + sub - 1) / sub;
@@ -548,9 +554,11 @@ int ptgq_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int gro
     const int wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
     int64_t blocks = (tasks + wpb - 1) / wpb;
     int64_t per_cu = out_dtype == PTGQ_FP32 ? 2 : 4;
+    const bool uncapped = tasks >= (int64_t)cus * 32 && knob(KNOB_BLOCKS_PER_CU) <= 0;
     if (knob(KNOB_BLOCKS_PER_CU) > 0) per_cu = knob(KNOB_BLOCKS_PER_CU);
-    if (blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
+    if (!uncapped && blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
     else if (blocks >= 64) blocks = (blocks + 7) / 8 * 8;
+    if (blocks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
     const int64_t waves = blocks * wpb;
     DequantArgs a;
     a.step = waves * ts;
@@ -573,6 +581,9 @@ int ptgq_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int gro
     a.inv_k = 1.0f / (float)K;
     a.ns = ns;
     a.log2g = __builtin_ctz((unsigned)group_size);
+    a.xcd_chunk = uncapped ? (int32_t)kDequantXcdChunk : 0;
+    if (knob(KNOB_XCD_CHUNK) >= 0)
+        a.xcd_chunk = (int32_t)std::min<int64_t>(knob(KNOB_XCD_CHUNK), 1 << 20);
     const hipError_t err = launch_dequant(a, code_dtype, scale_fmt, scale_layout, out_dtype,
                                           (unsigned)blocks, (unsigned)(wpb * 64),
                                           static_cast<hipStream_t>(stream));

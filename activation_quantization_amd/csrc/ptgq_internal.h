@@ -107,6 +107,7 @@ struct DequantArgs {
     int32_t full;             // rounds of full tasks
     int32_t ns;               // sub-slabs per task: 1 or 4
     int32_t log2g;            // log2(G)
+    int32_t xcd_chunk;        // blocks per XCD chunk (0: one contiguous range per XCD)
 };
 
 // Launchers (defined in ptgq_kernels.hip).  They return the hipError_t of the

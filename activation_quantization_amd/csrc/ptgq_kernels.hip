@@ -1289,7 +1289,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a)
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
-    const int lb = logical_block(blockIdx.x, gridDim.x);
+    const int lb = logical_block(blockIdx.x, gridDim.x, a.xcd_chunk);
     const uint32_t K = (uint32_t)a.K;
     const int64_t total = a.M * a.K;
     const rsrc_t rs = make_rsrc(a.s, a.s_bytes);

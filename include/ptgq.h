@@ -293,7 +293,8 @@ PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int
  * one wave per row, 1 one block per row, 2 two-pass block, 3 persistent waves
  * walking the rows), 4 fused bf16 SiLU
  * path (0 direct evaluation, 1 LDS lookup table), 5 blocks per XCD chunk of
- * the flat kernel's block-to-task mapping (0 one contiguous range per XCD).
+ * the flat quantization and dequantization kernels' block-to-task mappings
+ * (0 one contiguous range per XCD).
  * Results never depend on these; only speed does.  Not synchronized
  * with calls running on other host threads.  Returns PTGQ_OK or PTGQ_EINVAL.
  */

@@ -143,3 +143,38 @@ def test_full_headline_shape():
     got = run(q, "e4m3", M, K, G, s, "ue8m0", "col", "bf16")
     want = oracle.dequant(q, "e4m3", M, K, G, s, "ue8m0", "col", "bf16")
     compare("dequant full [16384, 7168] e4m3->bf16 ue8m0/col", got, want, "bf16")
+
+
+@pytest.mark.parametrize("out", OUTS)
+def test_uncapped_grid_ragged(out):
+    """Enough tasks for the uncapped, XCD-chunked grid (more tasks than the
+    chip holds waves) with rows that end mid-task and a last, partial span of
+    blocks, every scale format and layout."""
+    M, K, G = 2401, 7040, 128
+    rng = np.random.default_rng(2401 + OSZ[out])
+    q = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    for fmt, layout in LAYOUTS:
+        s = random_scales(rng, M, K, G, fmt, layout)
+        got = run(q, "e4m3", M, K, G, s, fmt, layout, out)
+        want = oracle.dequant(q, "e4m3", M, K, G, s, fmt, layout, out)
+        compare(f"dequant uncapped M={M} K={K} ->{out} {fmt}/{layout}", got, want, out)
+
+
+def test_tuning_knobs_never_change_results():
+    """Grid caps, task sizes and XCD chunks (including chunks that leave a
+    ragged last span) change speed only."""
+    M, K, G = 2401, 7040, 128
+    rng = np.random.default_rng(77)
+    q = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    s = random_scales(rng, M, K, G, "ue8m0", "col")
+    want = oracle.dequant(q, "e4m3", M, K, G, s, "ue8m0", "col", "bf16")
+    try:
+        for knob, values in ((0, [1, 4]), (2, [1, 4, 100000]), (5, [0, 1, 3, 16, 1000])):
+            for v in values:
+                aq.ptgq_set_tuning(knob, v)
+                got = run(q, "e4m3", M, K, G, s, "ue8m0", "col", "bf16")
+                compare(f"dequant knob {knob}={v}", got, want, "bf16")
+                aq.ptgq_set_tuning(knob, -1)
+    finally:
+        for k in range(6):
+            aq.ptgq_set_tuning(k, -1)
