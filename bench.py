@@ -279,20 +279,22 @@ def rows_of_scales(s_dev, M, K, G, fmt, layout, rows):
     return out
 
 
-def error_over_bound(oracle, y, gq, code, sc):
-    """max over elements of |dequant(code) - y| / bound, where the bound is
-    half an e4m3 ulp of |y / scale| (half a unit for int8) times the scale,
-    with 2^-19 of slack for the reciprocal's rounding (fp32 scales).  `sc`:
-    each element's scale (float64, broadcast over its group)."""
+def error_over_bound(oracle, y, gq, code, sc, fp32_scale):
+    """max over elements of |dequant(code) - y| / bound.  The code is within
+    half an output ulp (e4m3 ulp of |v|, or 1 for int8) of v = y * multiplier;
+    with fp32 scales v = fl(y * fl(1/scale)) also drifts from y / scale by at
+    most |y / scale| * 2^-22 (two roundings), so bound = (ulp/2 + drift) *
+    scale.  `sc`: each element's scale (float64, broadcast over its group)."""
     vals = oracle.e4m3_decode(gq) if code == "e4m3" else gq.view(np.int8)
     dq = vals.astype(np.float64) * sc
-    a = np.abs(y.astype(np.float64) / np.where(sc > 0, sc, 1.0))
+    t = np.abs(y.astype(np.float64) / np.where(sc > 0, sc, 1.0))
+    drift = t * 2.0 ** -22 if fp32_scale else np.zeros_like(t)
     if code == "e4m3":
-        _, ex = np.frexp(a)
-        ulp = np.where(a >= 2.0 ** -6, np.ldexp(1.0, ex - 4), 2.0 ** -9)
+        _, ex = np.frexp(t + drift)
+        ulp = np.where(t + drift >= 2.0 ** -6, np.ldexp(1.0, ex - 4), 2.0 ** -9)
     else:
-        ulp = np.ones_like(a)
-    bound = 0.5 * ulp * sc * (1 + 2.0 ** -19)
+        ulp = np.ones_like(t)
+    bound = (0.5 * ulp + drift) * sc
     err = np.abs(dq - y.astype(np.float64))
     r = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
     return float(r.max()) if r.size else 0.0
@@ -322,8 +324,8 @@ def capture_flat(x_host, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, q_dev,
         sc = gs.astype(np.float64) if fmt == "f32" else np.ldexp(1.0, gs.astype(np.int64) - 127)
         return {"rows": int(n), "code_mismatches": int((gq != rq).sum()),
                 "scale_mismatches": int((gs.view(np.uint8) != rs.view(np.uint8)).sum()),
-                "max_error_over_bound": round(error_over_bound(oracle, y, gq, out_dtype,
-                                                               np.repeat(sc, G, axis=1)), 6)}
+                "max_error_over_bound": round(error_over_bound(
+                    oracle, y, gq, out_dtype, np.repeat(sc, G, axis=1), fmt == "f32"), 6)}
     return check
 
 
@@ -541,7 +543,7 @@ def main():
             return {"rows": int(len(rows5)), "code_mismatches": int((q50 != rq5).sum()),
                     "scale_mismatches": int((s50.view(np.uint32) != rs5.view(np.uint32)).sum()),
                     "max_error_over_bound": round(error_over_bound(
-                        oracle, oracle.decode(x5s, "fp16"), q50, "e4m3", sc), 6)}
+                        oracle, oracle.decode(x5s, "fp16"), q50, "e4m3", sc, True), 6)}
         checks["per_token_fp8_fp16_M8192_K3584"] = check5
         del c5b
         torch.cuda.empty_cache()
