@@ -55,10 +55,10 @@ int current_cus(int *dev_out)
 // ------------------------------------------------------------ tuning knobs
 // Process-wide overrides of the geometry chooser (diagnostics and sweeps
 // only; -1 = automatic), set through ptgq_set_tuning.
-constexpr int kKnobs = 6;
-std::atomic<int64_t> g_knob[kKnobs] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+constexpr int kKnobs = 7;
+std::atomic<int64_t> g_knob[kKnobs] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
 enum { KNOB_SLABS_PER_TASK = 0, KNOB_WAVES_PER_BLOCK = 1, KNOB_BLOCKS_PER_CU = 2,
-       KNOB_TOKEN_MODE = 3, KNOB_SILU_TABLE = 4, KNOB_XCD_CHUNK = 5 };
+       KNOB_TOKEN_MODE = 3, KNOB_SILU_TABLE = 4, KNOB_XCD_CHUNK = 5, KNOB_GRID_MODE = 6 };
 
 int64_t knob(int k) { return g_knob[k].load(std::memory_order_relaxed); }
 
@@ -232,7 +232,13 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         a.n_tasks = (int32_t)tasks;
         a.q_pad_bytes = (q_rows - rows) * K;
         // a large zero-filled tail also needs waves: one 1 KiB wave store each
-        const bool uncapped = !fuse && es == 2 && geo.U == 2;
+        // Uncapped: plain (unfused) two-slab tasks of 16-bit input, and of
+        // fp32 input with rows of >= 4 tasks, where the XCD chunks below apply
+        // (measured on MI355X, fp32 with 58.7 M elements: K = 7168, 4096 and
+        // 14336 51.5 -> 50.5 us; K = 2048 and 1024 51.5 -> 53.9 us, so those
+        // stay capped).
+        bool uncapped = !fuse && geo.U == 2 && (es == 2 || a.tpr >= 4);
+        if (knob(KNOB_GRID_MODE) >= 0) uncapped = knob(KNOB_GRID_MODE) > 0;
         choose_blocks(geo, std::max<int64_t>(tasks, (a.q_pad_bytes + 1023) / 1024), cus,
                       fuse != 0, es, uncapped);
         // Block -> task mapping of a grid far larger than the chip: chunks of
@@ -472,6 +478,7 @@ int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int grou
     a.inv_k = 1.0f / (float)K;
     a.E = (int32_t)E;
     a.log2g = __builtin_ctz((unsigned)group_size);
+    a.xcd_chunk = 0;
     // Tasks of 2048 contiguous codes unless there are too few of them to
     // spread over the CUs; the grid is sized for the expected live rows.  When
     // it is capped, the blocks per CU (2, 3, 4 or 6 four-wave blocks, every
@@ -500,9 +507,20 @@ int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int grou
         }
     }
     if (per_cu <= 0) per_cu = 2;
-    const int64_t cap = (int64_t)cus * per_cu;
+    // Uncapped (one wave per expected task, blocks dealt to the XCDs in
+    // chunks of 16) once the capped grid would loop: measured on MI355X at E
+    // = 8, K = 3584, 1024 live rows per expert: 12.85 -> 12.5 us (chunks of
+    // 64: 12.7; contiguous ranges: 13.3).  Only for E <= 64, where each wave
+    // sums masked_m in registers: the LDS prefix sum of more experts would be
+    // repeated by every short-lived block.
+    bool uncapped = E <= 64 && blocks > (int64_t)cus * per_cu;
+    if (knob(KNOB_GRID_MODE) >= 0) uncapped = knob(KNOB_GRID_MODE) > 0;
+    const int64_t cap = uncapped ? blocks : (int64_t)cus * per_cu;
     if (blocks > cap) blocks = cap;
     else if (blocks >= 64) blocks = (blocks + 7) / 8 * 8;
+    if (uncapped && blocks >= 4 * 8 * kDequantXcdChunk) a.xcd_chunk = (int32_t)kDequantXcdChunk;
+    if (knob(KNOB_XCD_CHUNK) >= 0)
+        a.xcd_chunk = (int32_t)std::min<int64_t>(knob(KNOB_XCD_CHUNK), 1 << 20);
     const hipError_t err = launch_requant(a, (unsigned)std::max<int64_t>(blocks, 1),
                                           (unsigned)(wpb * 64), static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;

@@ -80,6 +80,7 @@ struct RequantArgs {
     float inv_k;              // 1 / K, for the row estimate when K < a task
     int32_t E;
     int32_t log2g;            // log2(group size)
+    int32_t xcd_chunk;        // blocks per XCD chunk of the block -> task mapping (0: ranges)
 };
 
 // Arguments of the dequantization kernel.  Codes and outputs are contiguous

@@ -548,6 +548,13 @@ struct MaskedRows {
     {
     }
 
+    // E <= 64: the whole prefix sum is the register window `win_` (lane l
+    // holds the sum over experts 0..l); no LDS copy exists or is read.
+    __device__ __forceinline__ MaskedRows(int win_, int E_, int lane)
+        : scan(nullptr), E(E_), chunk(0), base(0), win(lane < E_ ? win_ : INT32_MAX)
+    {
+    }
+
     // live row R (< total live rows) -> expert e and row r within it
     __device__ __forceinline__ void locate(int R, int lane, int &e, int &r)
     {
@@ -590,10 +597,36 @@ __device__ __forceinline__ void masked_prefix_sum(const int32_t *masked_m, int E
     }
 }
 
+// Inclusive prefix sum of `v` over the lanes of a wave (lane l gets the sum
+// over lanes 0..l).
+__device__ __forceinline__ int wave_inclusive_sum(int v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(v, d);
+        if (lane >= d) v += y;
+    }
+    return v;
+}
+
+// clamp(masked_m[lane], 0, rows) for lane < E (every row when masked_m is
+// NULL), 0 for the other lanes.  E <= 64.
+__device__ __forceinline__ int live_rows_of_lane(const int32_t *masked_m, int E, int64_t rows,
+                                                 int lane)
+{
+    int v = 0;
+    if (lane < E) {
+        v = masked_m ? masked_m[lane] : (int)rows;
+        v = v < 0 ? 0 : (v > rows ? (int)rows : v);
+    }
+    return v;
+}
+
 struct MaskedMap {
     MaskedRows rows;
 
     __device__ __forceinline__ MaskedMap(const int *scan, int E, int lane) : rows(scan, E, lane) {}
+    __device__ __forceinline__ MaskedMap(int win, int E, int lane) : rows(win, E, lane) {}
 
     __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int lane)
     {
@@ -710,10 +743,11 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     }
 }
 
-// Masked layout, balanced over experts: every block reads masked_m (E values,
-// clamped to [0, tokens_pad]) into an LDS prefix sum, and the grid walks the
-// live rows of all experts as one task space.  Rows at or past masked_m are
-// never read or written.  Dynamic LDS: E ints.
+// Masked layout, balanced over experts: masked_m (E values, clamped to [0,
+// tokens_pad]) is summed into a prefix sum (in each wave's registers for E <=
+// 64, else by wave 0 into LDS), and the grid walks the live rows of all
+// experts as one task space.  Rows at or past masked_m are never read or
+// written.  Dynamic LDS: E ints.
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupArgs a)
 {
@@ -724,9 +758,21 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x);
     const int E = a.num_experts;
-    // The table copy (all waves; table kernels always run 1024-lane blocks, 2
-    // float4 per lane) and the prefix sum of masked_m (wave 0) run side by
-    // side, behind one barrier.
+    if (E <= 64) {
+        // Every wave reads masked_m and sums it in registers: no LDS and no
+        // barrier before the first task's loads, which are issued before the
+        // SiLU table is staged (every wave reaches that barrier, with or
+        // without a task).
+        const int win = wave_inclusive_sum(live_rows_of_lane(a.masked_m, E, a.rows, lane), lane);
+        const int n = __builtin_amdgcn_readlane(win, E - 1) * a.tpr;
+        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, true>(a, MaskedMap(win, E, lane),
+                                                           lb * wpb + wib, n, gridDim.x * wpb,
+                                                           lane, tab);
+        return;
+    }
+    // More experts: the table copy (all waves; table kernels always run
+    // 1024-lane blocks, 2 float4 per lane) and the prefix sum of masked_m
+    // into LDS (wave 0) run side by side, behind one barrier.
     float4 staged[TABLE ? kSiluTab / 4 / 1024 : 1];
     if constexpr (TABLE) {
         const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
@@ -1100,12 +1146,24 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
-    const int lb = logical_block(blockIdx.x, gridDim.x);
-    if (wib == 0) requant_task_scan(a, lane, scan, live);
-    __syncthreads();
-    const int n = scan[a.E - 1];
+    const int lb = logical_block(blockIdx.x, gridDim.x, a.xcd_chunk);
+    // E <= 64: every wave reads masked_m and sums its experts' task counts in
+    // registers (lane e: live rows of expert e, and the prefix sum), with no
+    // LDS and no barrier; more experts: wave 0 builds both in LDS.
+    const bool in_regs = a.E <= 64;
+    int live_lane = 0, win = 0;
+    if (in_regs) {
+        live_lane = live_rows_of_lane(a.masked_m, a.E, a.T, lane);
+        const int shift = __builtin_ctzll((unsigned long long)a.tcodes);   // a power of two
+        win = wave_inclusive_sum(
+            (int)(((int64_t)live_lane * a.K + a.tcodes - 1) >> shift), lane);
+    } else {
+        if (wib == 0) requant_task_scan(a, lane, scan, live);
+        __syncthreads();
+    }
+    const int n = in_regs ? __builtin_amdgcn_readlane(win, a.E - 1) : scan[a.E - 1];
     if (lb * wpb >= n) return;                              // block-uniform
-    MaskedRows tasks(scan, a.E, lane);
+    MaskedRows tasks = in_regs ? MaskedRows(win, a.E, lane) : MaskedRows(scan, a.E, lane);
     const float inv = 1.0f / a.output_scale[0];
     const uint32_t K = (uint32_t)a.K;
     constexpr uint32_t TS = NS * kRqSub;
@@ -1127,7 +1185,8 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
         tasks.locate(t, lane, e, r);
         Loc l;
         const uint32_t off0 = (uint32_t)r * TS;               // < T * K < 2^31
-        const uint32_t region = (uint32_t)live[e] * K;
+        const int live_e = in_regs ? __builtin_amdgcn_readlane(live_lane, e) : live[e];
+        const uint32_t region = (uint32_t)live_e * K;
         l.len = region - off0 < TS ? region - off0 : TS;
         l.row0 = off0 / K;
         l.c0 = off0 - l.row0 * K;

@@ -294,7 +294,9 @@ PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int
  * walking the rows), 4 fused bf16 SiLU
  * path (0 direct evaluation, 1 LDS lookup table), 5 blocks per XCD chunk of
  * the flat quantization and dequantization kernels' block-to-task mappings
- * (0 one contiguous range per XCD).
+ * (0 one contiguous range per XCD), 6 grid of the flat quantization and
+ * requantization kernels (0 capped: resident blocks loop over the tasks; 1
+ * uncapped: one wave per task).
  * Results never depend on these; only speed does.  Not synchronized
  * with calls running on other host threads.  Returns PTGQ_OK or PTGQ_EINVAL.
  */

@@ -176,5 +176,5 @@ def test_tuning_knobs_never_change_results():
                 compare(f"dequant knob {knob}={v}", got, want, "bf16")
                 aq.ptgq_set_tuning(knob, -1)
     finally:
-        for k in range(6):
+        for k in range(7):
             aq.ptgq_set_tuning(k, -1)

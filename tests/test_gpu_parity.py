@@ -121,12 +121,18 @@ def test_masked_sweep(fuse, fmt, layout):
 
 
 @pytest.mark.parametrize("dist", ["one_expert", "alternating", "many_experts", "single",
-                                  "all_empty", "all_full"])
+                                  "all_empty", "all_full", "e64", "e65"])
 def test_masked_balanced_schedule(dist):
     """The balanced masked schedule under skewed live-row distributions, more
-    than 64 experts (several search windows) and degenerate cases."""
-    rng = np.random.default_rng(abs(hash(dist)) % 1000)
-    if dist == "one_expert":
+    than 64 experts (several search windows), the 64 / 65 expert boundary
+    between the prefix sum held in registers and the one in LDS, and
+    degenerate cases."""
+    rng = np.random.default_rng(sum(map(ord, dist)))
+    if dist in ("e64", "e65"):
+        E, T, K = int(dist[1:]), 21, 1024
+        mm = rng.integers(-3, T + 4, E).astype(np.int32)
+        mm[E - 1] = T
+    elif dist == "one_expert":
         E, T, K, mm = 16, 200, 1024, np.zeros(16, np.int32)
         mm[11] = 200
     elif dist == "alternating":
@@ -228,7 +234,7 @@ def test_special_values(eps, fmt):
 
 
 def reset_knobs():
-    for k in range(6):
+    for k in range(7):
         aq.ptgq_set_tuning(k, -1)
 
 
@@ -241,7 +247,7 @@ def test_tuning_knobs_never_change_results(fuse):
     try:
         # knob 5 (XCD chunk): 1, 3 and 64 leave a ragged last span of blocks
         for knob, values in ((0, [1, 2, 4]), (1, [1, 2, 4]), (2, [1, 2, 64]), (4, [0, 1]),
-                             (5, [0, 1, 3, 64])):
+                             (5, [0, 1, 3, 64]), (6, [0, 1])):
             for v in values:
                 aq.ptgq_set_tuning(knob, v)
                 compare(f"fuse={fuse} knob {knob}={v}", *run_flat(*args), *ref)

@@ -94,3 +94,30 @@ def test_many_experts_and_all_rows():
                                   out_init=np.full((E, T, K), SENTINEL, np.uint8))
         compare(f"requant E=130 masked={masked is not None}", got, np.zeros(0, np.uint8), want,
                 np.zeros(0, np.uint8))
+
+
+@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("E", [64, 65])
+def test_grid_modes_at_the_expert_window(E, grid):
+    """Both grids (capped persistent, uncapped XCD-chunked) at 64 experts,
+    whose prefix sum each wave holds in registers, and 65, which the kernel
+    sums in LDS; the last expert is full, the first empty."""
+    rng = np.random.default_rng(6400 + E + 7 * grid)
+    T, K = 40, 1152
+    x = rng.integers(0, 256, (E, T, K)).astype(np.uint8)
+    x[(x & 0x7F) == 0x7F] = 0x30
+    s = rng.uniform(0.25, 4.0, E * T * (K // 128)).astype(np.float32)
+    strides = (T * (K // 128), 1, T)
+    mm = rng.integers(-2, T + 3, E).astype(np.int32)
+    mm[0], mm[E - 1] = 0, T
+    try:
+        aq.ptgq_set_tuning(6, grid)
+        aq.ptgq_set_tuning(5, 1)        # chunks of one block: a ragged last span
+        got = run(x, E, T, K, 128, s, strides, mm, 8, 1.5)
+    finally:
+        aq.ptgq_set_tuning(6, -1)
+        aq.ptgq_set_tuning(5, -1)
+    want = oracle.requant_fp8(x, E, T, K, 128, s, strides, mm, 1.5,
+                              out_init=np.full((E, T, K), SENTINEL, np.uint8))
+    compare(f"requant E={E} grid={grid}", got, np.zeros(0, np.uint8), want,
+            np.zeros(0, np.uint8))
