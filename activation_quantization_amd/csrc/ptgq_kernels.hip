@@ -126,16 +126,16 @@ __device__ __forceinline__ uint32_t absmax8_bits(uint32_t w0, uint32_t w1, uint3
         return __float_as_uint(fp16_to_f32(h));
 }
 
-// |x| maximum of fp32 values, as a bit pattern.
+// |x| maximum of fp32 values, as a bit pattern: gfx950's three-operand
+// IEEE maximum with |.| source modifiers, 4 instructions for 8 values.  For
+// non-NaN values this is the largest magnitude exactly (-0 counts as +0);
+// NaN propagates.
 __device__ __forceinline__ uint32_t absmax_bits(const float (&y)[8])
 {
-    uint32_t m = 0;
+    float m = __builtin_elementwise_maximum(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t b = __float_as_uint(y[k]) & 0x7FFFFFFFu;
-        m = m > b ? m : b;
-    }
-    return m;
+    for (int k = 2; k < 8; ++k) m = __builtin_elementwise_maximum(m, __builtin_fabsf(y[k]));
+    return __float_as_uint(m);
 }
 
 // --------------------------------------------------------------------------
@@ -222,15 +222,24 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d)
     return (uint32_t)p;
 }
 
-__device__ __forceinline__ uint32_t int8_1(float v)
+// int8 code of v in the low byte of the result: v is clamped to [-128, 127]
+// (the same as rounding first, the bounds being integers), then 1.5 * 2^23
+// is added.  The sum lies in [2^23, 2^24), where the fp32 ulp is 1, and the
+// offset is even, so round-to-nearest-even of the sum is the offset plus
+// rne(v): the sum's low byte is the two's-complement code.  (Checked against
+// rint + clamp + convert for every non-NaN fp32 value.)
+__device__ __forceinline__ uint32_t int8_bits(float v)
 {
-    const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(v), -128.0f, 127.0f);
-    return (uint32_t)((int)r) & 0xFFu;
+    return __float_as_uint(__builtin_amdgcn_fmed3f(v, -128.0f, 127.0f) + 12582912.0f);
 }
 
+// 4 floats -> 4 int8 codes (byte i = code of value i), round to nearest
+// even, saturated; two byte permutes (selector 0x0C: a zero byte).
 __device__ __forceinline__ uint32_t int8x4(float a, float b, float c, float d)
 {
-    return int8_1(a) | (int8_1(b) << 8) | (int8_1(c) << 16) | (int8_1(d) << 24);
+    const uint32_t ab = __builtin_amdgcn_perm(int8_bits(b), int8_bits(a), 0x0C0C0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(int8_bits(d), int8_bits(c), 0x04000C0Cu);
+    return ab | cd;
 }
 
 template <int OUT, bool CLAMP>
@@ -770,20 +779,13 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
                                                            lane, tab);
         return;
     }
-    // More experts: the table copy (all waves; table kernels always run
-    // 1024-lane blocks, 2 float4 per lane) and the prefix sum of masked_m
-    // into LDS (wave 0) run side by side, behind one barrier.
-    float4 staged[TABLE ? kSiluTab / 4 / 1024 : 1];
-    if constexpr (TABLE) {
-        const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
-#pragma unroll
-        for (int i = 0; i < kSiluTab / 4 / 1024; ++i) staged[i] = src[threadIdx.x + 1024 * i];
-    }
+    // More experts: wave 0 builds the prefix sum of masked_m in LDS, then
+    // the whole block copies the table (any block size), behind one barrier.
     if (wib == 0) masked_prefix_sum(a.masked_m, E, a.rows, lane, scan);
     if constexpr (TABLE) {
+        const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
         float4 *dst = reinterpret_cast<float4 *>(tab);
-#pragma unroll
-        for (int i = 0; i < kSiluTab / 4 / 1024; ++i) dst[threadIdx.x + 1024 * i] = staged[i];
+        for (int i = threadIdx.x; i < kSiluTab / 4; i += blockDim.x) dst[i] = src[i];
     }
     __syncthreads();
     const int n = scan[E - 1] * a.tpr;

@@ -163,6 +163,17 @@ def variant_entry(timer, calls, nbytes, steps=100):
             "us_per_call_eager": round(r["region_ms"] * 1e3 / steps, 2)}
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def rotation_sets(footprint, cap=64):
     return int(max(2, min(cap, math.ceil(GIB / max(footprint, 1)))))
 
@@ -522,6 +533,16 @@ def main():
             d5["x"], "fp16", 8192, 3584, 128, False, "int8", "f32", "row", s5s[0][1], s5s[0][2],
             spread(8192))
         del c5, s5s
+        # the rest of the group-size sweep of the same tensor
+        for G5 in (16, 32, 64):
+            f5g = alg_bytes_flat(8192, 3584, G5, 2, False, 4)
+            s5g, c5g = make_flat_sets(torch, aq, d5["x"], 8192, 3584, G5, False, "int8", "f32",
+                                      "row", "fp16", rotation_sets(f5g))
+            name = f"int8_fp16_M8192_K3584_G{G5}"
+            variants[name] = variant_entry(timer, c5g, f5g)
+            checks[name] = capture_flat(d5["x"], "fp16", 8192, 3584, G5, False, "int8", "f32",
+                                        "row", s5g[0][1], s5g[0][2], spread(8192, 8))
+            del c5g, s5g
         f5b = 8192 * 3584 * 2 + 8192 * 3584 + 8192 * 4
         x5 = torch.from_numpy(d5["x"].view(np.int16)).to("cuda")
         c5b = []
@@ -571,15 +592,25 @@ def main():
     parity = {}
     if not args.no_cpu_baseline:
         import oracle
-        # whole steps, repeated until about 10 s of CPU work (at most 4)
-        steps_cpu, t0 = 0, time.perf_counter()
-        while steps_cpu < 4 and (steps_cpu == 0 or time.perf_counter() - t0 < 10.0):
-            oracle.ptgq(x_host, "bf16", M, K, G, False, "e4m3", "ue8m0", "col", eps=1e-10)
-            steps_cpu += 1
-        dt = (time.perf_counter() - t0) / steps_cpu
+        # whole steps, repeated until about 10 s of CPU work (at most 4), the
+        # process pinned to one host core (the oracle is single-threaded C)
+        allowed = sorted(os.sched_getaffinity(0))
+        core = allowed[-1]
+        os.sched_setaffinity(0, {core})
+        try:
+            steps_cpu, t0 = 0, time.perf_counter()
+            while steps_cpu < 4 and (steps_cpu == 0 or time.perf_counter() - t0 < 10.0):
+                oracle.ptgq(x_host, "bf16", M, K, G, False, "e4m3", "ue8m0", "col", eps=1e-10)
+                steps_cpu += 1
+            dt = (time.perf_counter() - t0) / steps_cpu
+        finally:
+            os.sched_setaffinity(0, allowed)
         cpu = {"value": round(foot / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"{steps_cpu} full steps of all {M} rows of the bf16 [{M},{K}] input "
-                         f"({M * K} elements each), single-threaded, {dt:.1f} s per step"}
+                         f"({M * K} elements each), single-threaded, {dt:.1f} s per step",
+               "ns_per_element": round(dt / (M * K) * 1e9, 2),
+               "host": {"cpu_model": host_cpu_model(), "cores_visible": len(allowed),
+                        "pinned_core": core}}
         parity = {name: check(oracle) for name, check in checks.items()}
     for name in variants:
         variants[name]["parity"] = parity.get(name)
