@@ -21,7 +21,8 @@ dequantization error over its bound (null with --no-cpu-baseline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --profile-main   (only the headline loop, for rocprofv3)
-    python bench.py --profile-dequant / --profile-requant  (only that loop)
+    python bench.py --profile-dequant / --profile-requant / --profile-fused /
+                    --profile-masked  (only that loop)
     python bench.py --calib-copy     (a plain device copy of known size, for
                                       calibrating rocprofv3 byte counters)
 """
@@ -227,6 +228,39 @@ def dequant_calls(torch, aq):
     return cd, fd, capture
 
 
+def fused_calls(torch, aq, W):
+    """Fused silu(gate)*up quantization, bf16 [8192, 2*4096] -> e4m3 [8192, 4096],
+    G = 128, UE8M0 column-major scales, over rotated buffer sets."""
+    d3 = W.cfg3(8192)
+    f3 = alg_bytes_flat(8192, 4096, 128, 2, True, 1)
+    s3, c3 = make_flat_sets(torch, aq, d3["x"], 8192, 4096, 128, True, "e4m3", "ue8m0",
+                            "col", "bf16", rotation_sets(f3))
+    return d3, s3, c3, f3
+
+
+def masked_calls(torch, aq, W):
+    """Masked MoE layout, bf16 [32, 384, 2*2048] fused, the seeded masked_m of
+    the workload, UE8M0 column-major scales per expert, over rotated buffer
+    sets.  Returns the workload, the calls, the algorithmic bytes (live rows
+    only, plus masked_m) and the live row count."""
+    d4 = W.cfg4()
+    E, T, K4, mm = d4["E"], d4["T"], d4["K"], d4["masked_m"]
+    live = int(np.clip(mm, 0, T).sum())
+    f4 = live * (2 * K4 * 2 + K4 + K4 // 128) + 4 * E
+    x4 = torch.from_numpy(d4["x"].view(np.int16)).to("cuda")
+    mm_d = torch.from_numpy(mm).to("cuda")
+    sb4 = aq.ptgq_scale_bytes(T, K4, 128, "ue8m0", "col")
+    c4 = []
+    for i in range(rotation_sets(E * T * (4 * K4 + K4))):
+        xi = x4 if i == 0 else x4.clone()
+        q4 = torch.empty((E, T, K4), dtype=torch.uint8, device="cuda")
+        s4 = torch.empty((E * sb4,), dtype=torch.uint8, device="cuda")
+        c4.append((lambda xi=xi, q4=q4, s4=s4: aq.ptgq_quant_masked(
+            xi, "bf16", E, T, K4, 128, True, mm_d, int(live // E), "e4m3", "ue8m0", "col",
+            1e-10, q4, s4, check=False)))
+    return d4, c4, f4, live
+
+
 def requant_calls(torch, aq, live):
     """fp8 requantization at the sglang #35593 page's timed shape: K = 3584,
     8 experts, tokens_pad 1024, `live` rows per expert, DeepEP column-major
@@ -362,6 +396,8 @@ def main():
                     help="rows of the workload that --profile-main launches")
     ap.add_argument("--profile-dequant", action="store_true")
     ap.add_argument("--profile-requant", action="store_true")
+    ap.add_argument("--profile-fused", action="store_true")
+    ap.add_argument("--profile-masked", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
 
@@ -394,12 +430,17 @@ def main():
         print(json.dumps({"calib_copy_bytes_each_way": GIB, "copies": 5}))
         return
 
-    if args.profile_dequant or args.profile_requant:
-        calls, nbytes, _ = dequant_calls(torch, aq) if args.profile_dequant else \
-            requant_calls(torch, aq, 1024)
+    if args.profile_dequant or args.profile_requant or args.profile_fused or args.profile_masked:
+        if args.profile_dequant:
+            name, (calls, nbytes, _) = "dequant", dequant_calls(torch, aq)
+        elif args.profile_requant:
+            name, (calls, nbytes, _) = "requant", requant_calls(torch, aq, 1024)
+        elif args.profile_fused:
+            name, (_, _, calls, nbytes) = "fused", fused_calls(torch, aq, W)
+        else:
+            name, (_, calls, nbytes, _) = "masked", masked_calls(torch, aq, W)
         r = timer.run(calls, args.steps, args.warmup, per_launch=False)
-        print(json.dumps({"profile": "dequant" if args.profile_dequant else "requant",
-                          "steps": args.steps, "bytes": nbytes,
+        print(json.dumps({"profile": name, "steps": args.steps, "bytes": nbytes,
                           "us_per_launch": r["region_ms"] * 1e3 / args.steps}))
         return
 
@@ -488,31 +529,16 @@ def main():
         del c32, x32
         torch.cuda.empty_cache()
         # fused silu(gate)*up, bf16 [8192, 2*4096]
-        d3 = W.cfg3(8192)
-        f3 = alg_bytes_flat(8192, 4096, 128, 2, True, 1)
-        s3, c3 = make_flat_sets(torch, aq, d3["x"], 8192, 4096, 128, True, "e4m3", "ue8m0",
-                                "col", "bf16", rotation_sets(f3))
+        d3, s3, c3, f3 = fused_calls(torch, aq, W)
         variants["fused_silu_mul_M8192_K4096"] = variant_entry(timer, c3, f3)
         checks["fused_silu_mul_M8192_K4096"] = capture_flat(
             d3["x"], "bf16", 8192, 4096, 128, True, "e4m3", "ue8m0", "col", s3[0][1], s3[0][2],
             spread(8192))
         del c3, s3
         # masked MoE, E=32, tokens_pad=384, fused, K=2048
-        d4 = W.cfg4()
+        d4, c4, f4, live = masked_calls(torch, aq, W)
         E, T, K4, mm = d4["E"], d4["T"], d4["K"], d4["masked_m"]
-        live = int(np.clip(mm, 0, T).sum())
-        f4 = live * (2 * K4 * 2 + K4 + K4 // 128) + 4 * E
-        x4 = torch.from_numpy(d4["x"].view(np.int16)).to("cuda")
-        mm_d = torch.from_numpy(mm).to("cuda")
         sb4 = aq.ptgq_scale_bytes(T, K4, 128, "ue8m0", "col")
-        c4 = []
-        for i in range(rotation_sets(E * T * (4 * K4 + K4))):
-            xi = x4 if i == 0 else x4.clone()
-            q4 = torch.empty((E, T, K4), dtype=torch.uint8, device="cuda")
-            s4 = torch.empty((E * sb4,), dtype=torch.uint8, device="cuda")
-            c4.append((lambda xi=xi, q4=q4, s4=s4: aq.ptgq_quant_masked(
-                xi, "bf16", E, T, K4, 128, True, mm_d, int(live // E), "e4m3", "ue8m0", "col",
-                1e-10, q4, s4, check=False)))
         variants["masked_E32_T384_K2048_fused"] = dict(variant_entry(timer, c4, f4),
                                                        live_rows=live)
         # every live row of four experts of set 0 (its other rows hold
