@@ -26,7 +26,7 @@ SCALE_LAYOUTS = {"row": PTGQ_ROW_MAJOR, "col": PTGQ_COL_MAJOR}
 
 EXPORTS = ("ptgq_quant", "ptgq_quant_padded", "ptgq_quant_masked", "ptq_quant_fp8", "ptgq_requant_fp8",
            "ptgq_dequant", "ptgq_scale_bytes", "ptgq_status_string", "ptgq_init", "ptgq_probe_e4m3",
-           "ptgq_probe_silu_mul", "ptgq_set_tuning")
+           "ptgq_probe_silu_mul", "ptgq_set_tuning", "ptgq_plan_group")
 
 
 class PtgqError(RuntimeError):
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH):
     lib.ptgq_probe_silu_mul.restype = i32
     lib.ptgq_set_tuning.argtypes = [i32, i64]
     lib.ptgq_set_tuning.restype = i32
+    lib.ptgq_plan_group.argtypes = [i32, i64, i64, i64, i32, i32, i64, i64, i32, vp]
+    lib.ptgq_plan_group.restype = i32
     _lib = lib
     return lib
 
@@ -141,6 +143,23 @@ def ptgq_init(device: int = 0) -> int:
 
 def ptgq_set_tuning(knob: int, value: int) -> int:
     return _check("ptgq_set_tuning", load_library().ptgq_set_tuning(int(knob), int(value)))
+
+
+PLAN_FIELDS = ("grid", "block", "slabs_per_task", "tasks_per_row", "tasks", "xcd_chunk",
+               "silu_table", "uncapped")
+
+
+def ptgq_plan_group(in_dtype, E, rows, K, group_size, fuse_silu_mul, expected_m, q_rows, cus):
+    """The launch geometry the chooser picks for a flat (E = 0) or masked
+    (E >= 1) group call on a device of `cus` compute units, as a dict of
+    PLAN_FIELDS.  Host only: no device is touched."""
+    out = (ctypes.c_int64 * 8)()
+    rc = load_library().ptgq_plan_group(_enum(in_dtype, IN_DTYPES), int(E), int(rows), int(K),
+                                        int(group_size), int(bool(fuse_silu_mul)),
+                                        int(expected_m), int(q_rows), int(cus),
+                                        ctypes.cast(out, ctypes.c_void_p))
+    _check("ptgq_plan_group", rc)
+    return dict(zip(PLAN_FIELDS, (int(v) for v in out)))
 
 
 def ptgq_quant(x, in_dtype, M, K, group_size, fuse_silu_mul, out_dtype, scale_fmt, scale_layout,

@@ -98,6 +98,7 @@ struct GroupGeom {
     int U;          // slabs per task
     int wpb;        // waves per block
     bool table;     // fused bf16: LDS SiLU table (16-wave blocks)
+    bool uncapped;  // one wave per task (no grid-stride loop)
     int64_t per_cu; // resident blocks per CU the grid is capped at
     unsigned grid;  // blocks
 };
@@ -183,6 +184,7 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es, 
     }
     g.wpb = wpb;
     g.per_cu = per_cu;
+    g.uncapped = uncapped;
     int64_t blocks = (tasks + wpb - 1) / wpb;
     const int64_t cap = uncapped && knob(KNOB_BLOCKS_PER_CU) <= 0
                             ? blocks
@@ -194,37 +196,27 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es, 
     g.grid = (unsigned)std::max<int64_t>(blocks, 1);
 }
 
-// `q_rows` (flat only): rows of the q buffer, >= rows; the extra rows are
-// written as zero.
-int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, int G, int fuse,
-                        int out_dtype, int scale_fmt, int scale_layout, float eps, void *q,
-                        void *s, const int32_t *masked_m, int64_t E, int64_t expected_m,
-                        int64_t q_rows, void *stream)
+// The launch geometry and the geometry fields of `a` for a group call on a
+// device of `cus` compute units; no HIP call (pointers, eps and the stream
+// are the launcher's).  `masked`: the masked layout of E experts (rows =
+// tokens_pad).  `q_rows` (flat only): rows of the q buffer, >= rows; the
+// extra rows are written as zero.
+int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t K, int G,
+               int fuse, int scale_fmt, int scale_layout, bool masked, int64_t E,
+               int64_t expected_m, int64_t q_rows, int cus)
 {
-    int dev = 0;
-    const int cus = current_cus(&dev);
-    if (cus <= 0) return PTGQ_EDEVICE;
-
-    GroupArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.x = x;
-    a.q = static_cast<uint8_t *>(q);
-    a.s = s;
-    a.masked_m = masked_m;
     a.rows = rows;
     a.K = K;
     const int64_t es = in_dtype == PTGQ_FP32 ? 4 : 2;   // input element bytes
     a.in_stride = (fuse ? 2 * K : K) * es;
     a.ng = K / G;
     a.rows_pad = pad4(rows);
-    a.eps = eps;
     a.spr = (int32_t)((K + kSlab - 1) / kSlab);
     a.scale_fmt = scale_fmt;
     a.scale_layout = scale_layout;
-    const bool masked = masked_m != nullptr;
     const bool bf16 = in_dtype == PTGQ_BF16;
 
-    GroupGeom geo;
     if (!masked) {
         choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, !fuse && es == 2, cus);
         a.U = geo.U;
@@ -233,7 +225,6 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.n_tasks = (int32_t)tasks;
         a.q_pad_bytes = (q_rows - rows) * K;
-        // a large zero-filled tail also needs waves: one 1 KiB wave store each
         // Uncapped: plain (unfused) two-slab tasks of 16-bit input, and of
         // fp32 input with rows of >= 4 tasks, where the XCD chunks below apply
         // (measured on MI355X, fp32 with 58.7 M elements: K = 7168, 4096 and
@@ -241,6 +232,7 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         // stay capped).
         bool uncapped = !fuse && geo.U == 2 && (es == 2 || a.tpr >= 4);
         if (knob(KNOB_GRID_MODE) >= 0) uncapped = knob(KNOB_GRID_MODE) > 0;
+        // a large zero-filled tail also needs waves: one 1 KiB wave store each
         choose_blocks(geo, std::max<int64_t>(tasks, (a.q_pad_bytes + 1023) / 1024), cus,
                       fuse != 0, es, uncapped);
         // Block -> task mapping of a grid far larger than the chip: chunks of
@@ -268,11 +260,35 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
         a.tpr = (a.spr + a.U - 1) / a.U;
         if (E * rows * (int64_t)a.tpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         choose_blocks(geo, std::max<int64_t>(hint, 1) * a.tpr * E, cus, fuse != 0, es, false);
+        a.n_tasks = (int32_t)(std::max<int64_t>(hint, 1) * a.tpr * E);   // expected; set on the device
         a.num_experts = (int32_t)E;
         a.x_expert_stride = rows * a.in_stride;
         a.q_expert_stride = rows * K;
         a.s_expert_stride = (int64_t)ptgq_scale_bytes(rows, K, G, scale_fmt, scale_layout);
     }
+    return PTGQ_OK;
+}
+
+int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, int G, int fuse,
+                        int out_dtype, int scale_fmt, int scale_layout, float eps, void *q,
+                        void *s, const int32_t *masked_m, int64_t E, int64_t expected_m,
+                        int64_t q_rows, void *stream)
+{
+    int dev = 0;
+    const int cus = current_cus(&dev);
+    if (cus <= 0) return PTGQ_EDEVICE;
+
+    GroupArgs a;
+    GroupGeom geo;
+    const bool masked = masked_m != nullptr;
+    const int rc = plan_group(a, geo, in_dtype, rows, K, G, fuse, scale_fmt, scale_layout, masked,
+                              E, expected_m, q_rows, cus);
+    if (rc != PTGQ_OK) return rc;
+    a.x = x;
+    a.q = static_cast<uint8_t *>(q);
+    a.s = s;
+    a.masked_m = masked_m;
+    a.eps = eps;
     const hipError_t err = launch_group(a, in_dtype, G, fuse != 0, out_dtype, geo.table, masked,
                                         geo.grid, (unsigned)(geo.wpb * 64),
                                         static_cast<hipStream_t>(stream));
@@ -633,6 +649,37 @@ int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int path, fl
     const hipError_t err = launch_probe_silu(g, u, in_dtype, path, out, n,
                                              static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
+}
+
+int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, int group_size,
+                    int fuse_silu_mul, int64_t expected_m, int64_t q_rows, int cus, int64_t *out)
+{
+    if (!out || cus < 1) return PTGQ_EINVAL;
+    for (int i = 0; i < 8; ++i) out[i] = 0;
+    if (in_dtype != PTGQ_BF16 && in_dtype != PTGQ_FP16 && in_dtype != PTGQ_FP32)
+        return PTGQ_EINVAL;
+    if (!valid_group_size(group_size) || E < 0 || rows < 0 || K < 0 || K % group_size != 0)
+        return PTGQ_EINVAL;
+    const bool masked = E > 0;
+    if (!masked && q_rows < rows) return PTGQ_EINVAL;
+    if (fuse_silu_mul && in_dtype == PTGQ_FP32) return PTGQ_EUNSUPPORTED;
+    if (K >= (int64_t)1 << 29 || q_rows >= ((int64_t)1 << 31)) return PTGQ_EUNSUPPORTED;
+    if (K == 0 || (masked ? rows == 0 : q_rows == 0)) return PTGQ_OK;   // nothing is launched
+    GroupArgs a;
+    GroupGeom geo;
+    const int rc = plan_group(a, geo, in_dtype, rows, K, group_size, fuse_silu_mul,
+                              PTGQ_SCALE_UE8M0, PTGQ_COL_MAJOR, masked, E, expected_m,
+                              masked ? rows : q_rows, cus);
+    if (rc != PTGQ_OK) return rc;
+    out[0] = geo.grid;
+    out[1] = (int64_t)geo.wpb * 64;
+    out[2] = a.U;
+    out[3] = a.tpr;
+    out[4] = a.n_tasks;
+    out[5] = a.xcd_chunk;
+    out[6] = geo.table ? 1 : 0;
+    out[7] = geo.uncapped ? 1 : 0;
+    return PTGQ_OK;
 }
 
 int ptgq_set_tuning(int which, int64_t value)

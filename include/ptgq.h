@@ -285,6 +285,31 @@ PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int
                                  float *out, int64_t n, void *stream);
 
 /*
+ * ptgq_plan_group - diagnostics and tests of the launch-geometry chooser:
+ * the launch a ptgq_quant / ptgq_quant_padded call (E = 0; q_rows = rows of
+ * the code buffer, >= rows) or a ptgq_quant_masked call (E >= 1 experts of
+ * rows = tokens_pad rows, sized for expected_m) would make on a device of
+ * `cus` compute units.  Tiny calls spread one-slab tasks over the compute
+ * units; large ones use two-slab tasks and, for plain 16-bit input, a grid of
+ * one wave per task dealt to the XCDs in chunks (the pages size their launch
+ * by token count the same way: the sglang #34257 review page, key source
+ * snippets, dispatch; `expected_m` of the sglang #30924 review page,
+ * implementation breakdown).  Makes no HIP call and touches no device;
+ * honours the ptgq_set_tuning overrides.
+ *   out: host array of 8, written with: blocks in the grid, threads per
+ *        block, slabs (512 consecutive elements of a row) per task, tasks per
+ *        row, tasks in all (masked: the expected ones), blocks per XCD chunk
+ *        of the block -> task mapping (0: one contiguous range per XCD),
+ *        SiLU lookup table (0/1), uncapped grid (0/1); all zero when nothing
+ *        would be launched.
+ * Returns PTGQ_OK, PTGQ_EINVAL (invalid shape, cus < 1, out NULL) or
+ * PTGQ_EUNSUPPORTED, as the calls would for the same shape.
+ */
+PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, int group_size,
+                             int fuse_silu_mul, int64_t expected_m, int64_t q_rows, int cus,
+                             int64_t *out);
+
+/*
  * ptgq_set_tuning - diagnostics only: override one decision of the launch
  * geometry chooser for the whole process (value -1 restores the automatic
  * choice).  Knobs: 0 slabs per task (quantization: 1 or 2, one slab = 512

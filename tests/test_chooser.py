@@ -1,0 +1,147 @@
+"""The launch-geometry chooser on the host (no GPU): the plans it makes for the
+seeded workloads on a 256-CU MI355X, and the rules every plan keeps."""
+import numpy as np
+import pytest
+
+import activation_quantization_amd as aq
+
+CUS = 256            # MI355X
+SLAB = 512           # elements of a row per slab
+
+
+@pytest.fixture(autouse=True)
+def _reset_knobs():
+    for k in range(7):
+        aq.ptgq_set_tuning(k, -1)
+    yield
+    for k in range(7):
+        aq.ptgq_set_tuning(k, -1)
+
+
+def plan(in_dtype, rows, K, G=128, fuse=False, E=0, expected_m=0, q_rows=None, cus=CUS):
+    return aq.ptgq_plan_group(in_dtype, E, rows, K, G, fuse, expected_m,
+                              rows if q_rows is None else q_rows, cus)
+
+
+def test_headline_uncapped_xcd_chunked():
+    p = plan("bf16", 16384, 7168)
+    assert p["slabs_per_task"] == 2 and p["tasks_per_row"] == 7
+    assert p["tasks"] == 16384 * 7
+    assert p["uncapped"] == 1 and p["block"] == 256
+    assert p["grid"] == 16384 * 7 // 4             # one wave per task
+    assert p["xcd_chunk"] == 64 and p["silu_table"] == 0
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_sizes_spread_one_slab_tasks_over_one_wave_blocks(M):
+    p = plan("bf16", M, 7168)
+    assert p["slabs_per_task"] == 1 and p["block"] == 64
+    assert p["tasks"] == M * 14 and p["grid"] == M * 14
+    assert p["uncapped"] == 0 and p["xcd_chunk"] == 0
+
+
+def test_m256_one_slab_tasks_capped_grid_covers_every_task_once():
+    p = plan("bf16", 256, 7168)
+    assert p["slabs_per_task"] == 1 and p["tasks"] == 256 * 14
+    assert p["uncapped"] == 0 and p["xcd_chunk"] == 0
+    assert p["grid"] * p["block"] // 64 >= p["tasks"]
+
+
+def test_fused_large_call_takes_the_silu_table_one_block_per_cu():
+    p = plan("bf16", 8192, 4096, fuse=True)
+    assert p["silu_table"] == 1 and p["block"] == 1024 and p["grid"] == CUS
+    assert p["slabs_per_task"] == 1 and p["uncapped"] == 0
+    # small fused calls evaluate directly
+    assert plan("bf16", 64, 4096, fuse=True)["silu_table"] == 0
+    # fp16 gates never use the table
+    assert plan("fp16", 8192, 4096, fuse=True)["silu_table"] == 0
+
+
+def test_masked_workload_sized_by_expected_rows():
+    p = plan("bf16", 384, 2048, fuse=True, E=32, expected_m=189)
+    assert p["silu_table"] == 1 and p["grid"] == CUS and p["block"] == 1024
+    assert p["tasks"] == 32 * 189 * 4
+    # unknown expected_m: every row of every expert
+    assert plan("bf16", 384, 2048, fuse=True, E=32)["tasks"] == 32 * 384 * 4
+    # masked grids are never uncapped (the task count is only known on the device)
+    assert plan("bf16", 384, 7168, E=32)["uncapped"] == 0
+
+
+@pytest.mark.parametrize("K,uncapped", [(7168, 1), (4096, 1), (14336, 1), (2048, 0), (1024, 0)])
+def test_fp32_input_uncapped_only_with_rows_of_four_tasks(K, uncapped):
+    p = plan("fp32", 8192 * 7168 // K, K)
+    assert p["slabs_per_task"] == 2 and p["uncapped"] == uncapped
+    if not uncapped:
+        assert p["grid"] % CUS == 0 and p["xcd_chunk"] == 0
+
+
+def test_odd_slab_16bit_rows_still_take_two_slab_tasks():
+    p = plan("fp16", 8192, 3584)                   # 7 slabs per row
+    assert p["slabs_per_task"] == 2 and p["tasks_per_row"] == 4 and p["uncapped"] == 1
+
+
+def test_padded_rows_get_waves_for_the_zero_fill():
+    # nothing to quantize, 28 MiB of code rows to zero: a full capped grid
+    # whose waves loop over the fill (1 KiB per wave store)
+    p = plan("bf16", 0, 7168, q_rows=4096)
+    assert p["tasks"] == 0 and p["uncapped"] == 0
+    assert p["grid"] % CUS == 0 and p["grid"] * p["block"] // 64 >= CUS * 16
+    # a few rows and no padding: one-wave blocks, as many as the tasks
+    # rounded up to a multiple of the 8 XCDs
+    p = plan("bf16", 5, 7168)
+    assert p["block"] == 64 and p["grid"] == 72 and p["tasks"] == 70
+
+
+@pytest.mark.parametrize("cus", [80, 256, 304])
+def test_rules_hold_for_random_shapes(cus):
+    rng = np.random.default_rng(cus)
+    for _ in range(300):
+        G = int(rng.choice([16, 32, 64, 128]))
+        K = G * int(rng.integers(1, 30000 // G))
+        rows = int(rng.integers(1, 20000))
+        dt = str(rng.choice(["bf16", "fp16", "fp32"]))
+        fuse = dt != "fp32" and bool(rng.integers(0, 2))
+        p = plan(dt, rows, K, G, fuse, cus=cus)
+        spr = -(-K // SLAB)
+        U = p["slabs_per_task"]
+        assert U in (1, 2)
+        assert p["tasks_per_row"] == -(-spr // U)
+        assert p["tasks"] == rows * p["tasks_per_row"]
+        assert p["block"] in (64, 256, 1024) and p["grid"] >= 1
+        waves = p["grid"] * p["block"] // 64
+        if p["uncapped"]:
+            assert waves >= p["tasks"]                  # one wave per task
+            assert not fuse and U == 2
+        elif waves < p["tasks"]:
+            assert p["grid"] % cus == 0                 # looping grids: equal blocks per CU
+        if p["xcd_chunk"]:
+            assert p["uncapped"] and p["tasks_per_row"] >= 4 and p["grid"] >= 4 * 8 * 64
+        if p["silu_table"]:
+            assert fuse and dt == "bf16" and p["block"] == 1024
+
+
+def test_tuning_knobs_are_honoured():
+    aq.ptgq_set_tuning(6, 0)                      # capped grid
+    p = plan("bf16", 16384, 7168)
+    assert p["uncapped"] == 0 and p["grid"] % CUS == 0
+    aq.ptgq_set_tuning(6, -1)
+    aq.ptgq_set_tuning(5, 16)                     # XCD chunk
+    assert plan("bf16", 16384, 7168)["xcd_chunk"] == 16
+    aq.ptgq_set_tuning(5, -1)
+    aq.ptgq_set_tuning(0, 1)                      # one-slab tasks
+    assert plan("bf16", 16384, 7168)["tasks_per_row"] == 14
+
+
+def test_plan_validation():
+    lib = aq.load_library()
+    with pytest.raises(aq.PtgqError):
+        plan("bf16", 16, 7168, cus=0)
+    with pytest.raises(aq.PtgqError):
+        plan("bf16", 16, 7100)                    # K % G != 0
+    with pytest.raises(aq.PtgqError):
+        plan("fp32", 16, 7168, fuse=True)         # fused fp32 is unsupported
+    with pytest.raises(aq.PtgqError):
+        plan("bf16", 16, 7168, q_rows=8)          # q buffer shorter than the rows
+    assert lib.ptgq_plan_group(0, 0, 16, 7168, 128, 0, 0, 16, 256, None) == aq.PTGQ_EINVAL
+    assert all(v == 0 for v in plan("bf16", 0, 7168).values())     # nothing launched
+    assert all(v == 0 for v in plan("bf16", 0, 2048, E=4).values())
