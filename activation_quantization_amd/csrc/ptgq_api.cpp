@@ -156,9 +156,7 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es, 
     int wpb;
     int64_t per_cu;
     if (g.table) {
-        wpb = kTableWaves;
-        if (knob(KNOB_WAVES_PER_BLOCK) > 0)
-            wpb = (int)std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), kTableWaves);
+        wpb = kTableWaves;   // the kernels stage the table with exactly 1024 lanes
         per_cu = kTableBlocksPerCu;
     } else {
         wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;

@@ -631,6 +631,19 @@ __device__ __forceinline__ int live_rows_of_lane(const int32_t *masked_m, int E,
     return v;
 }
 
+// Row r of expert e, task j of the row.
+__device__ __forceinline__ TaskLoc masked_loc(const GroupArgs &a, int e, int r, int j)
+{
+    TaskLoc l;
+    l.xrow = static_cast<const char *>(a.x) + (int64_t)e * a.x_expert_stride +
+             (int64_t)r * a.in_stride;
+    l.qrow = a.q + (int64_t)e * a.q_expert_stride + (int64_t)r * a.K;
+    l.sbase = static_cast<uint8_t *>(a.s) + (int64_t)e * a.s_expert_stride;
+    l.m = r;
+    l.j = j;
+    return l;
+}
+
 struct MaskedMap {
     MaskedRows rows;
 
@@ -642,63 +655,89 @@ struct MaskedMap {
         const int R = t / a.tpr;
         int e, r;
         rows.locate(R, lane, e, r);
-        TaskLoc l;
-        l.xrow = static_cast<const char *>(a.x) + (int64_t)e * a.x_expert_stride +
-                 (int64_t)r * a.in_stride;
-        l.qrow = a.q + (int64_t)e * a.q_expert_stride + (int64_t)r * a.K;
-        l.sbase = static_cast<uint8_t *>(a.s) + (int64_t)e * a.s_expert_stride;
-        l.m = r;
-        l.j = t - R * a.tpr;
-        return l;
+        return masked_loc(a, e, r, t - R * a.tpr);
     }
 };
+// The SiLU table staged into LDS in two steps, so that its global loads can
+// be issued before a wave's first task loads and its LDS stores wait for the
+// table alone (vector memory loads complete in issue order): table kernels
+// always run 1024-lane blocks, 2 float4 of the table per lane.
+constexpr int kTableLanes = 1024;
+struct TableRegs {
+    float4 v[kSiluTab / 4 / kTableLanes];
+};
 
-// Copy the SiLU table into LDS (whole block; call before any early exit that
-// is not block-uniform).
 template <bool TABLE>
-__device__ __forceinline__ void stage_table(float *tab)
+__device__ __forceinline__ void table_fetch(TableRegs &r)
 {
     if constexpr (TABLE) {
         const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
+#pragma unroll
+        for (int i = 0; i < kSiluTab / 4 / kTableLanes; ++i)
+            r.v[i] = src[threadIdx.x + kTableLanes * i];
+    }
+}
+
+// Stores the fetched table and synchronizes the block (call before any early
+// exit that is not block-uniform).
+template <bool TABLE>
+__device__ __forceinline__ void table_store(const TableRegs &r, float *tab)
+{
+    if constexpr (TABLE) {
         float4 *dst = reinterpret_cast<float4 *>(tab);
-        for (int i = threadIdx.x; i < kSiluTab / 4; i += blockDim.x) dst[i] = src[i];
+#pragma unroll
+        for (int i = 0; i < kSiluTab / 4 / kTableLanes; ++i)
+            dst[threadIdx.x + kTableLanes * i] = r.v[i];
         __syncthreads();
     }
 }
 
-// Tasks first, first + stride, ... < n, two at a time in flight.  A task
-// index past n is clamped for address arithmetic and loaded over an empty
-// range.  Table kernels stage the SiLU table into LDS after the first task's
-// loads are issued (every wave of the block reaches that barrier, with or
-// without a task), so the table copy overlaps the first HBM reads.  n >= 1.
+// Continues the task sequence t, t + stride, ... < n from task t, whose loads
+// are already in flight in `cur` (location lcur); `spare` is free.  Two tasks
+// are in flight at a time.  A task index past n is clamped for address
+// arithmetic and loaded over an empty range.
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, class Map>
+__device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int t, TaskLoc lcur,
+                                               TaskBuf<UMAX> &cur, TaskBuf<UMAX> &spare, int n,
+                                               int stride, int lane, const float *tab)
+{
+    while (true) {
+        const int tB = t + stride;
+        const bool hasB = tB < n;
+        const TaskLoc lB = map(a, hasB ? tB : t, lane);
+        load_task<IN, FUSE, UMAX>(a, lB, lane, hasB, spare);
+        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lcur, lane, cur, tab);
+        if (!hasB) break;
+        t = tB;
+        const int tA = t + stride;
+        const bool hasA = tA < n;
+        lcur = map(a, hasA ? tA : t, lane);
+        load_task<IN, FUSE, UMAX>(a, lcur, lane, hasA, cur);
+        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lB, lane, spare, tab);
+        if (!hasA) break;
+        t = tA;
+    }
+}
+
+// Tasks first, first + stride, ... < n, two at a time in flight.  Table
+// kernels (STAGE) fetch the SiLU table, issue the first task's loads, then
+// store the table into LDS (every wave of the block reaches that barrier,
+// with or without a task), so the table copy overlaps the first HBM reads.
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, bool STAGE,
           class Map>
 __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
                                           int stride, int lane, float *tab)
 {
-    int t = first;
-    const bool hasA0 = t < n;
+    const bool hasA0 = first < n;
     TaskBuf<UMAX> A, B;
-    TaskLoc lA = map(a, hasA0 ? t : 0, lane);
+    TableRegs tr;
+    if constexpr (STAGE) table_fetch<TABLE>(tr);
+    const TaskLoc lA = map(a, hasA0 ? first : 0, lane);
     load_task<IN, FUSE, UMAX>(a, lA, lane, hasA0, A);
-    if constexpr (STAGE) stage_table<TABLE>(tab);
+    if constexpr (STAGE) table_store<TABLE>(tr, tab);
     if (!hasA0) return;
-    while (true) {
-        const int tB = t + stride;
-        const bool hasB = tB < n;
-        const TaskLoc lB = map(a, hasB ? tB : t, lane);
-        load_task<IN, FUSE, UMAX>(a, lB, lane, hasB, B);
-        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lA, lane, A, tab);
-        if (!hasB) break;
-        t = tB;
-        const int tA = t + stride;
-        const bool hasA = tA < n;
-        lA = map(a, hasA ? tA : t, lane);
-        load_task<IN, FUSE, UMAX>(a, lA, lane, hasA, A);
-        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lB, lane, B, tab);
-        if (!hasA) break;
-        t = tA;
-    }
+    continue_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, map, first, lA, A, B, n, stride, lane,
+                                                      tab);
 }
 
 // XCD-aware logical block id.  Blocks are dealt to the 8 XCDs round-robin
@@ -770,7 +809,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
     if (E <= 64) {
         // Every wave reads masked_m and sums it in registers: no LDS and no
         // barrier before the first task's loads, which are issued before the
-        // SiLU table is staged (every wave reaches that barrier, with or
+        // SiLU table is stored (every wave reaches that barrier, with or
         // without a task).
         const int win = wave_inclusive_sum(live_rows_of_lane(a.masked_m, E, a.rows, lane), lane);
         const int n = __builtin_amdgcn_readlane(win, E - 1) * a.tpr;
@@ -779,15 +818,13 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
                                                            lane, tab);
         return;
     }
-    // More experts: wave 0 builds the prefix sum of masked_m in LDS, then
-    // the whole block copies the table (any block size), behind one barrier.
+    // More experts: the table's loads, then the prefix sum of masked_m into
+    // LDS (wave 0), then the table's stores, behind one barrier.
+    TableRegs tr;
+    table_fetch<TABLE>(tr);
     if (wib == 0) masked_prefix_sum(a.masked_m, E, a.rows, lane, scan);
-    if constexpr (TABLE) {
-        const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
-        float4 *dst = reinterpret_cast<float4 *>(tab);
-        for (int i = threadIdx.x; i < kSiluTab / 4; i += blockDim.x) dst[i] = src[i];
-    }
-    __syncthreads();
+    if constexpr (TABLE) table_store<TABLE>(tr, tab);
+    else __syncthreads();
     const int n = scan[E - 1] * a.tpr;
     if (lb * wpb >= n) return;                    // block-uniform: nothing to do
     run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, false>(a, MaskedMap(scan, E, lane), lb * wpb + wib,
