@@ -22,7 +22,8 @@ dequantization error over its bound (null with --no-cpu-baseline).
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --profile-main   (only the headline loop, for rocprofv3)
     python bench.py --profile-dequant / --profile-requant / --profile-fused /
-                    --profile-masked  (only that loop)
+                    --profile-masked / --profile-fp32 / --profile-per-token /
+                    --profile-int8  (only that loop)
     python bench.py --calib-copy     (a plain device copy of known size, for
                                       calibrating rocprofv3 byte counters)
 """
@@ -261,6 +262,50 @@ def masked_calls(torch, aq, W):
     return d4, c4, f4, live
 
 
+def fp32_calls(torch, aq, W):
+    """fp32 input [8192, 7168] -> e4m3, G = 128, packed column-major UE8M0
+    scales, over rotated buffer sets.  Returns the host input, the calls and
+    the algorithmic bytes."""
+    M32, K, G = 8192, 7168, 128
+    x32h = W.normal_f32(32, (M32, K))
+    x32 = torch.from_numpy(x32h).to("cuda")
+    f32b = alg_bytes_flat(M32, K, G, 4, False, 1)
+    sb32 = aq.ptgq_scale_bytes(M32, K, G, "ue8m0", "col")
+    c32 = []
+    for i in range(rotation_sets(f32b)):
+        xi = x32 if i == 0 else x32.clone()
+        qi = torch.empty((M32, K), dtype=torch.uint8, device="cuda")
+        si = torch.empty((sb32,), dtype=torch.uint8, device="cuda")
+        c32.append((lambda xi=xi, qi=qi, si=si: aq.ptgq_quant(
+            xi, "fp32", M32, K, G, False, "e4m3", "ue8m0", "col", 1e-10, qi, si, check=False)))
+    return x32h, c32, f32b
+
+
+def per_token_calls(torch, aq, d5):
+    """Whole-row per-token e4m3 of the fp16 [8192, 3584] workload tensor, over
+    rotated buffer sets.  Returns the calls and the algorithmic bytes."""
+    f5b = 8192 * 3584 * 2 + 8192 * 3584 + 8192 * 4
+    x5 = torch.from_numpy(d5["x"].view(np.int16)).to("cuda")
+    c5b = []
+    for i in range(rotation_sets(f5b)):
+        xi = x5 if i == 0 else x5.clone()
+        q5 = torch.empty((8192, 3584), dtype=torch.uint8, device="cuda")
+        s5 = torch.empty((8192,), dtype=torch.float32, device="cuda")
+        c5b.append((lambda xi=xi, q5=q5, s5=s5: aq.ptq_quant_fp8(xi, "fp16", 8192, 3584, q5, s5,
+                                                                check=False)))
+    return c5b, f5b
+
+
+def int8_fp16_calls(torch, aq, W):
+    """fp16 [8192, 3584] -> int8, G = 128, fp32 row-major scales, over rotated
+    buffer sets.  Returns the calls and the algorithmic bytes."""
+    d5 = W.cfg5()
+    f5 = alg_bytes_flat(8192, 3584, 128, 2, False, 4)
+    _, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, 128, False, "int8", "f32", "row",
+                           "fp16", rotation_sets(f5))
+    return c5, f5
+
+
 def requant_calls(torch, aq, live):
     """fp8 requantization at the sglang #35593 page's timed shape: K = 3584,
     8 experts, tokens_pad 1024, `live` rows per expert, DeepEP column-major
@@ -398,6 +443,9 @@ def main():
     ap.add_argument("--profile-requant", action="store_true")
     ap.add_argument("--profile-fused", action="store_true")
     ap.add_argument("--profile-masked", action="store_true")
+    ap.add_argument("--profile-fp32", action="store_true")
+    ap.add_argument("--profile-per-token", action="store_true")
+    ap.add_argument("--profile-int8", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
 
@@ -430,15 +478,22 @@ def main():
         print(json.dumps({"calib_copy_bytes_each_way": GIB, "copies": 5}))
         return
 
-    if args.profile_dequant or args.profile_requant or args.profile_fused or args.profile_masked:
+    if (args.profile_dequant or args.profile_requant or args.profile_fused or args.profile_masked
+            or args.profile_fp32 or args.profile_per_token or args.profile_int8):
         if args.profile_dequant:
             name, (calls, nbytes, _) = "dequant", dequant_calls(torch, aq)
         elif args.profile_requant:
             name, (calls, nbytes, _) = "requant", requant_calls(torch, aq, 1024)
         elif args.profile_fused:
             name, (_, _, calls, nbytes) = "fused", fused_calls(torch, aq, W)
-        else:
+        elif args.profile_masked:
             name, (_, calls, nbytes, _) = "masked", masked_calls(torch, aq, W)
+        elif args.profile_fp32:
+            name, (_, calls, nbytes) = "fp32", fp32_calls(torch, aq, W)
+        elif args.profile_per_token:
+            name, (calls, nbytes) = "per_token", per_token_calls(torch, aq, W.cfg5())
+        else:
+            name, (calls, nbytes) = "int8", int8_fp16_calls(torch, aq, W)
         r = timer.run(calls, args.steps, args.warmup, per_launch=False)
         print(json.dumps({"profile": name, "steps": args.steps, "bytes": nbytes,
                           "us_per_launch": r["region_ms"] * 1e3 / args.steps}))
@@ -510,23 +565,12 @@ def main():
         del ci8, si8
         # fp32 input [8192, 7168] -> e4m3, packed column-major UE8M0 scales
         M32 = 8192
-        x32h = W.normal_f32(32, (M32, K))
-        x32 = torch.from_numpy(x32h).to("cuda")
-        f32b = alg_bytes_flat(M32, K, G, 4, False, 1)
-        sb32 = aq.ptgq_scale_bytes(M32, K, G, "ue8m0", "col")
-        c32 = []
-        for i in range(rotation_sets(f32b)):
-            xi = x32 if i == 0 else x32.clone()
-            qi = torch.empty((M32, K), dtype=torch.uint8, device="cuda")
-            si = torch.empty((sb32,), dtype=torch.uint8, device="cuda")
-            c32.append((lambda xi=xi, qi=qi, si=si: aq.ptgq_quant(
-                xi, "fp32", M32, K, G, False, "e4m3", "ue8m0", "col", 1e-10, qi, si,
-                check=False)))
+        x32h, c32, f32b = fp32_calls(torch, aq, W)
         variants["fp32_input_M8192_K7168"] = variant_entry(timer, c32, f32b)
         checks["fp32_input_M8192_K7168"] = capture_flat(
             x32h, "fp32", M32, K, G, False, "e4m3", "ue8m0", "col", c32[0].__defaults__[1],
             c32[0].__defaults__[2], spread(M32))
-        del c32, x32
+        del c32
         torch.cuda.empty_cache()
         # fused silu(gate)*up, bf16 [8192, 2*4096]
         d3, s3, c3, f3 = fused_calls(torch, aq, W)
@@ -569,15 +613,7 @@ def main():
             checks[name] = capture_flat(d5["x"], "fp16", 8192, 3584, G5, False, "int8", "f32",
                                         "row", s5g[0][1], s5g[0][2], spread(8192, 8))
             del c5g, s5g
-        f5b = 8192 * 3584 * 2 + 8192 * 3584 + 8192 * 4
-        x5 = torch.from_numpy(d5["x"].view(np.int16)).to("cuda")
-        c5b = []
-        for i in range(rotation_sets(f5b)):
-            xi = x5 if i == 0 else x5.clone()
-            q5 = torch.empty((8192, 3584), dtype=torch.uint8, device="cuda")
-            s5 = torch.empty((8192,), dtype=torch.float32, device="cuda")
-            c5b.append((lambda xi=xi, q5=q5, s5=s5: aq.ptq_quant_fp8(xi, "fp16", 8192, 3584, q5,
-                                                                    s5, check=False)))
+        c5b, f5b = per_token_calls(torch, aq, d5)
         variants["per_token_fp8_fp16_M8192_K3584"] = variant_entry(timer, c5b, f5b)
         rows5 = spread(8192)
         x5s = np.ascontiguousarray(d5["x"][rows5])
