@@ -354,6 +354,16 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // with the default policy.  Scale words keep the default policy so that the
 // partial lines of neighbouring rows merge in L2.
 constexpr int kStreamPolicy = 2;
+// Code stores of the flat SiLU-table kernel (persistent 16-wave blocks) keep
+// the default policy: measured on MI355X, fused [8192, 2*4096] 29.3 us with
+// non-temporal code stores, 28.6 us with the default (or sc0 / sc1) policy.
+// Every other kernel's code stores are non-temporal (the masked SiLU-table
+// kernel: 13.4 us non-temporal, 13.7 us default).
+constexpr int kTableStorePolicy = 0;
+// Dequantized output (two or four bytes written per byte read): system-scope
+// (sc1) non-temporal stores, measured 57.4 -> 56.9 us at [16384, 7168] -> bf16
+// (default policy: 59.7 us).
+constexpr int kDequantStorePolicy = 16 | 2;
 
 // Raw (unstructured) buffer resource over [base, base + bytes); the third
 // dword selects 32-bit data format, as gfx9 raw buffers expect.
@@ -414,7 +424,7 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
 
 __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL>
 __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &t, int lane,
                                              const TaskBuf<UMAX> &b, const float *tab)
 {
@@ -479,7 +489,7 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
         u32x2 c2;
         c2.x = codes.x;
         c2.y = codes.y;
-        __builtin_amdgcn_raw_buffer_store_b64(c2, rq, col, 0, kStreamPolicy);  // dropped past the row
+        __builtin_amdgcn_raw_buffer_store_b64(c2, rq, col, 0, SPOL);  // dropped past the row
 
         // scales of the slab's groups
         const int lg = lane / LPG;                                  // group within slab
@@ -696,7 +706,8 @@ __device__ __forceinline__ void table_store(const TableRegs &r, float *tab)
 // are already in flight in `cur` (location lcur); `spare` is free.  Two tasks
 // are in flight at a time.  A task index past n is clamped for address
 // arithmetic and loaded over an empty range.
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, class Map>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL,
+          class Map>
 __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int t, TaskLoc lcur,
                                                TaskBuf<UMAX> &cur, TaskBuf<UMAX> &spare, int n,
                                                int stride, int lane, const float *tab)
@@ -706,14 +717,14 @@ __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int
         const bool hasB = tB < n;
         const TaskLoc lB = map(a, hasB ? tB : t, lane);
         load_task<IN, FUSE, UMAX>(a, lB, lane, hasB, spare);
-        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lcur, lane, cur, tab);
+        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL>(a, lcur, lane, cur, tab);
         if (!hasB) break;
         t = tB;
         const int tA = t + stride;
         const bool hasA = tA < n;
         lcur = map(a, hasA ? tA : t, lane);
         load_task<IN, FUSE, UMAX>(a, lcur, lane, hasA, cur);
-        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, lB, lane, spare, tab);
+        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL>(a, lB, lane, spare, tab);
         if (!hasA) break;
         t = tA;
     }
@@ -723,7 +734,8 @@ __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int
 // kernels (STAGE) fetch the SiLU table, issue the first task's loads, then
 // store the table into LDS (every wave of the block reaches that barrier,
 // with or without a task), so the table copy overlaps the first HBM reads.
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, bool STAGE,
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL,
+          bool STAGE,
           class Map>
 __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
                                           int stride, int lane, float *tab)
@@ -736,7 +748,7 @@ __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first
     load_task<IN, FUSE, UMAX>(a, lA, lane, hasA0, A);
     if constexpr (STAGE) table_store<TABLE>(tr, tab);
     if (!hasA0) return;
-    continue_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE>(a, map, first, lA, A, B, n, stride, lane,
+    continue_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL>(a, map, first, lA, A, B, n, stride, lane,
                                                       tab);
 }
 
@@ -767,8 +779,10 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x, a.xcd_chunk);
-    run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, true>(a, FlatMap{}, lb * wpb + wib, a.n_tasks,
-                                             gridDim.x * wpb, lane, tab);
+    constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
+    run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true>(a, FlatMap{}, lb * wpb + wib,
+                                                             a.n_tasks, gridDim.x * wpb, lane,
+                                                             tab);
     // code rows past M (a padded q buffer) are zero: 16 bytes per lane,
     // grid-strided over all waves
     if (a.q_pad_bytes > 0) {
@@ -813,9 +827,8 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
         // without a task).
         const int win = wave_inclusive_sum(live_rows_of_lane(a.masked_m, E, a.rows, lane), lane);
         const int n = __builtin_amdgcn_readlane(win, E - 1) * a.tpr;
-        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, true>(a, MaskedMap(win, E, lane),
-                                                           lb * wpb + wib, n, gridDim.x * wpb,
-                                                           lane, tab);
+        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, true>(
+            a, MaskedMap(win, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab);
         return;
     }
     // More experts: the table's loads, then the prefix sum of masked_m into
@@ -827,8 +840,8 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
     else __syncthreads();
     const int n = scan[E - 1] * a.tpr;
     if (lb * wpb >= n) return;                    // block-uniform: nothing to do
-    run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, false>(a, MaskedMap(scan, E, lane), lb * wpb + wib,
-                                                    n, gridDim.x * wpb, lane, tab);
+    run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, false>(
+        a, MaskedMap(scan, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab);
 }
 
 // --------------------------------------------------------------------------
@@ -1520,7 +1533,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a)
                 o.w = pack2_out_fp16(f[6], f[7]);
             }
             __builtin_amdgcn_raw_buffer_store_b128(o, ry, (k * SUB + lane * W) * OSZ, 0,
-                                                   kStreamPolicy);
+                                                   kDequantStorePolicy);
         }
     };
 
