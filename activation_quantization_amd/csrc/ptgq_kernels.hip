@@ -360,6 +360,12 @@ constexpr int kStreamPolicy = 2;
 // Every other kernel's code stores are non-temporal (the masked SiLU-table
 // kernel: 13.4 us non-temporal, 13.7 us default).
 constexpr int kTableStorePolicy = 0;
+// fp32 input loads keep the default policy: each lane's two 16-byte loads
+// request every 128-byte line twice, and the second request then hits in
+// cache (measured on MI355X, fp32 [8192, 7168]: 50.5 us non-temporal, 49.05
+// us default; sc1 alone 50.4).  16-bit inputs and fused gates/ups stream
+// non-temporally (the SiLU-table kernels lose 10-12 % with the default).
+constexpr int kFp32LoadPolicy = 0;
 // Dequantized output (two or four bytes written per byte read): system-scope
 // (sc1) non-temporal stores, measured 57.4 -> 56.9 us at [16384, 7168] -> bf16
 // (default policy: 59.7 us).
@@ -401,24 +407,22 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
                                           bool live, TaskBuf<UMAX> &b)
 {
     constexpr int ES = IN == IN_FP32 ? 4 : 2;   // input element bytes
+    constexpr int pol = IN == IN_FP32 ? kFp32LoadPolicy : kStreamPolicy;
     const uint32_t row_bytes = live ? (uint32_t)(a.K * ES) : 0u;
     const rsrc_t rg = make_rsrc(t.xrow, row_bytes);
     const uint32_t off = (uint32_t)t.j * (UMAX * kSlab * ES) + (uint32_t)lane * (8 * ES);
 #pragma unroll
     for (int s = 0; s < UMAX; ++s) {
-        b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES, 0,
-                                                       kStreamPolicy);
+        b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES, 0, pol);
         if constexpr (IN == IN_FP32)
-            b.gh[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES + 16, 0,
-                                                            kStreamPolicy);
+            b.gh[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES + 16, 0, pol);
     }
     if constexpr (FUSE) {
         static_assert(IN != IN_FP32, "fused calls take 16-bit inputs");
         const rsrc_t ru = make_rsrc(t.xrow + a.K * ES, row_bytes);
 #pragma unroll
         for (int s = 0; s < UMAX; ++s)
-            b.u[s] = __builtin_amdgcn_raw_buffer_load_b128(ru, off + s * kSlab * 2, 0,
-                                                           kStreamPolicy);
+            b.u[s] = __builtin_amdgcn_raw_buffer_load_b128(ru, off + s * kSlab * 2, 0, pol);
     }
 }
 
