@@ -370,6 +370,9 @@ constexpr int kFp32LoadPolicy = 0;
 // (sc1) non-temporal stores, measured 57.4 -> 56.9 us at [16384, 7168] -> bf16
 // (default policy: 59.7 us).
 constexpr int kDequantStorePolicy = 16 | 2;
+// and its code loads keep the default policy (57.0 -> 56.4 us against
+// non-temporal code loads).
+constexpr int kDequantLoadPolicy = 0;
 
 // Raw (unstructured) buffer resource over [base, base + bytes); the third
 // dword selects 32-bit data format, as gfx9 raw buffers expect.
@@ -1462,9 +1465,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a)
         for (int k = 0; k < NS; ++k) {
             const uint32_t off = k * SUB + lane * W;
             if constexpr (W == 4) {
-                T.c[k][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, kStreamPolicy);
+                T.c[k][0] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, kDequantLoadPolicy);
             } else {
-                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, kStreamPolicy);
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, kDequantLoadPolicy);
                 T.c[k][0] = v.x;
                 T.c[k][1] = v.y;
             }
