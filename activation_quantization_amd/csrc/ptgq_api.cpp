@@ -223,12 +223,8 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.n_tasks = (int32_t)tasks;
         a.q_pad_bytes = (q_rows - rows) * K;
-        // Uncapped: plain (unfused) two-slab tasks of 16-bit input, and of
-        // fp32 input with rows of >= 4 tasks, where the XCD chunks below apply
-        // (measured on MI355X, fp32 with 58.7 M elements: K = 7168, 4096 and
-        // 14336 51.5 -> 50.5 us; K = 2048 and 1024 51.5 -> 53.9 us, so those
-        // stay capped).
-        bool uncapped = !fuse && geo.U == 2 && (es == 2 || a.tpr >= 4);
+        // Uncapped: plain (unfused) two-slab tasks, 16-bit or fp32 input.
+        bool uncapped = !fuse && geo.U == 2;
         if (knob(KNOB_GRID_MODE) >= 0) uncapped = knob(KNOB_GRID_MODE) > 0;
         // a large zero-filled tail also needs waves: one 1 KiB wave store each
         choose_blocks(geo, std::max<int64_t>(tasks, (a.q_pad_bytes + 1023) / 1024), cus,
@@ -240,7 +236,11 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // 3584]: 30.3 -> 28.6 us).  Rows of fewer than 4 tasks (fp16 K =
         // 1536, 2560: 3-7 % slower chunked) and grids of fewer than 4 spans
         // (M = 256 here: 3.1 us against 3.3-3.6) keep the contiguous ranges.
-        if (uncapped && a.tpr >= 4 && geo.grid >= 4 * 8 * kXcdChunk) a.xcd_chunk = kXcdChunk;
+        // fp32 input is chunked whatever its row length (58.7 M elements, K =
+        // 1024 and 2048: capped 51.5 us, uncapped with contiguous ranges 53.7,
+        // chunked 49.4; K = 7168: capped 51.4, chunked 49.1-49.4).
+        if (uncapped && (a.tpr >= 4 || es == 4) && geo.grid >= 4 * 8 * kXcdChunk)
+            a.xcd_chunk = kXcdChunk;
         if (knob(KNOB_XCD_CHUNK) >= 0) a.xcd_chunk = (int32_t)std::min<int64_t>(knob(KNOB_XCD_CHUNK), 1 << 20);
         if (scale_layout == PTGQ_COL_MAJOR && a.rows_pad > rows)
             a.pad_cols = (int32_t)(scale_fmt == PTGQ_SCALE_UE8M0 ? (a.ng + 3) / 4 : a.ng);

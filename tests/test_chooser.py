@@ -67,12 +67,16 @@ def test_masked_workload_sized_by_expected_rows():
     assert plan("bf16", 384, 7168, E=32)["uncapped"] == 0
 
 
-@pytest.mark.parametrize("K,uncapped", [(7168, 1), (4096, 1), (14336, 1), (2048, 0), (1024, 0)])
-def test_fp32_input_uncapped_only_with_rows_of_four_tasks(K, uncapped):
+@pytest.mark.parametrize("K", [7168, 4096, 14336, 2048, 1024])
+def test_fp32_input_uncapped_and_xcd_chunked_for_every_row_length(K):
     p = plan("fp32", 8192 * 7168 // K, K)
-    assert p["slabs_per_task"] == 2 and p["uncapped"] == uncapped
-    if not uncapped:
-        assert p["grid"] % CUS == 0 and p["xcd_chunk"] == 0
+    assert p["slabs_per_task"] == 2 and p["uncapped"] == 1 and p["xcd_chunk"] == 64
+
+
+@pytest.mark.parametrize("K", [1536, 2560])
+def test_short_16bit_rows_keep_contiguous_xcd_ranges(K):
+    p = plan("fp16", 16384, K)                     # 3 or 5 slabs: 2 or 3 tasks per row
+    assert p["uncapped"] == 1 and p["tasks_per_row"] < 4 and p["xcd_chunk"] == 0
 
 
 def test_odd_slab_16bit_rows_still_take_two_slab_tasks():
@@ -115,7 +119,8 @@ def test_rules_hold_for_random_shapes(cus):
         elif waves < p["tasks"]:
             assert p["grid"] % cus == 0                 # looping grids: equal blocks per CU
         if p["xcd_chunk"]:
-            assert p["uncapped"] and p["tasks_per_row"] >= 4 and p["grid"] >= 4 * 8 * 64
+            assert p["uncapped"] and p["grid"] >= 4 * 8 * 64
+            assert p["tasks_per_row"] >= 4 or dt == "fp32"
         if p["silu_table"]:
             assert fuse and dt == "bf16" and p["block"] == 1024
 
