@@ -53,3 +53,16 @@ def test_error_bound_is_tight_for_a_half_ulp_miss():
     bad = good.copy()
     bad[0, 1] += 1                                          # 3.0 -> 3.25
     assert bench.error_over_bound(oracle, y, bad, "e4m3", sc, False) > 1.0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The path needs no exchange between GPUs; bench.py measures one and says
+    so for any other count, before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and "--gpus 1" in res.stderr
