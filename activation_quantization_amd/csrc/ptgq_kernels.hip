@@ -89,6 +89,11 @@ __device__ __forceinline__ uint32_t cluster_max_bits(uint32_t v)
     if constexpr (LANES >= 4) v = dpp_umax<0x4E>(v);    // quad_perm [2,3,0,1]
     if constexpr (LANES >= 8) v = dpp_umax<0x141>(v);   // row_half_mirror
     if constexpr (LANES >= 16) v = dpp_umax<0x140>(v);  // row_mirror
+    if constexpr (LANES >= 32) {
+        // rows 0 <-> 1 and 2 <-> 3: ds_swizzle bit mode, lane ^ 16 within 32
+        const uint32_t o = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+        v = v > o ? v : o;
+    }
     return v;
 }
 
@@ -135,6 +140,14 @@ __device__ __forceinline__ uint32_t absmax_bits(const float (&y)[8])
     float m = __builtin_elementwise_maximum(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
 #pragma unroll
     for (int k = 2; k < 8; ++k) m = __builtin_elementwise_maximum(m, __builtin_fabsf(y[k]));
+    return __float_as_uint(m);
+}
+
+__device__ __forceinline__ uint32_t absmax4_bits(const float (&y)[4])
+{
+    float m = __builtin_elementwise_maximum(__builtin_fabsf(y[0]), __builtin_fabsf(y[1]));
+    m = __builtin_elementwise_maximum(m, __builtin_fabsf(y[2]));
+    m = __builtin_elementwise_maximum(m, __builtin_fabsf(y[3]));
     return __float_as_uint(m);
 }
 
@@ -240,6 +253,15 @@ __device__ __forceinline__ uint32_t int8x4(float a, float b, float c, float d)
     const uint32_t ab = __builtin_amdgcn_perm(int8_bits(b), int8_bits(a), 0x0C0C0400u);
     const uint32_t cd = __builtin_amdgcn_perm(int8_bits(d), int8_bits(c), 0x04000C0Cu);
     return ab | cd;
+}
+
+template <int OUT, bool CLAMP>
+__device__ __forceinline__ uint32_t narrow4(const float (&v)[4])
+{
+    if constexpr (OUT == OUT_E4M3)
+        return e4m3x4<CLAMP>(v[0], v[1], v[2], v[3]);
+    else
+        return int8x4(v[0], v[1], v[2], v[3]);
 }
 
 template <int OUT, bool CLAMP>
@@ -360,12 +382,6 @@ constexpr int kStreamPolicy = 2;
 // Every other kernel's code stores are non-temporal (the masked SiLU-table
 // kernel: 13.4 us non-temporal, 13.7 us default).
 constexpr int kTableStorePolicy = 0;
-// fp32 input loads keep the default policy: each lane's two 16-byte loads
-// request every 128-byte line twice, and the second request then hits in
-// cache (measured on MI355X, fp32 [8192, 7168]: 50.5 us non-temporal, 49.05
-// us default; sc1 alone 50.4).  16-bit inputs and fused gates/ups stream
-// non-temporally (the SiLU-table kernels lose 10-12 % with the default).
-constexpr int kFp32LoadPolicy = 0;
 // Dequantized output (two or four bytes written per byte read): system-scope
 // (sc1) non-temporal stores, measured 57.4 -> 56.9 us at [16384, 7168] -> bf16
 // (default policy: 59.7 us).
@@ -410,15 +426,18 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
                                           bool live, TaskBuf<UMAX> &b)
 {
     constexpr int ES = IN == IN_FP32 ? 4 : 2;   // input element bytes
-    constexpr int pol = IN == IN_FP32 ? kFp32LoadPolicy : kStreamPolicy;
+    constexpr int pol = kStreamPolicy;
     const uint32_t row_bytes = live ? (uint32_t)(a.K * ES) : 0u;
     const rsrc_t rg = make_rsrc(t.xrow, row_bytes);
-    const uint32_t off = (uint32_t)t.j * (UMAX * kSlab * ES) + (uint32_t)lane * (8 * ES);
+    // 16-bit: lane l holds elements 8l..8l+7 of a slab; fp32: 4l..4l+3 (g)
+    // and 256+4l..256+4l+3 (gh), so every load instruction reads one
+    // contiguous KiB
+    const uint32_t off = (uint32_t)t.j * (UMAX * kSlab * ES) + (uint32_t)lane * 16;
 #pragma unroll
     for (int s = 0; s < UMAX; ++s) {
         b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES, 0, pol);
         if constexpr (IN == IN_FP32)
-            b.gh[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES + 16, 0, pol);
+            b.gh[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES + 1024, 0, pol);
     }
     if constexpr (FUSE) {
         static_assert(IN != IN_FP32, "fused calls take 16-bit inputs");
@@ -430,6 +449,97 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
 }
 
 __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+
+// One slab of fp32 input: lane l holds elements 4l..4l+3 (half A, `ga`) and
+// 256+4l..256+4l+3 (half B, `gb`) of the slab, so a group of G elements is
+// held by G/4 adjacent lanes of one half and every lane derives two scales.
+// Codes are stored 4 bytes per lane and half (each store instruction writes
+// 256 contiguous bytes; stores past the row are dropped); scales go to the
+// layout's slots like those of the 16-bit path.
+template <int G, int OUT, int SF, int SPOL>
+__device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x4 &ga,
+                                                  const u32x4 &gb, int slab, rsrc_t rq,
+                                                  uint8_t *se, int64_t m, int lane)
+{
+    constexpr int LA = G / 4;           // lanes per group within a half (4..32)
+    constexpr int GPH = 256 / G;        // groups per half (2..16)
+    constexpr int GPS = kSlab / G;      // groups per slab
+    constexpr bool ue8m0 = SF == SCALE_UE8M0;
+    const uint32_t colA = (uint32_t)slab * kSlab + (uint32_t)lane * 4;
+    const uint32_t colB = colA + 256;
+    const bool validA = (int64_t)colA < a.K, validB = (int64_t)colB < a.K;
+    const float ya[4] = {__uint_as_float(ga.x), __uint_as_float(ga.y), __uint_as_float(ga.z),
+                         __uint_as_float(ga.w)};
+    const float yb[4] = {__uint_as_float(gb.x), __uint_as_float(gb.y), __uint_as_float(gb.z),
+                         __uint_as_float(gb.w)};
+    const uint32_t amA = cluster_max_bits<LA>(absmax4_bits(ya));
+    const uint32_t amB = cluster_max_bits<LA>(absmax4_bits(yb));
+    const Scale sA = group_scale<OUT>(amA, __float_as_uint(a.eps), ue8m0);
+    const Scale sB = group_scale<OUT>(amB, __float_as_uint(a.eps), ue8m0);
+    float va[4], vb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        va[k] = ya[k] * sA.inv;
+        vb[k] = yb[k] * sB.inv;
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(narrow4<OUT, !ue8m0>(va), rq, colA, 0, SPOL);
+    __builtin_amdgcn_raw_buffer_store_b32(narrow4<OUT, !ue8m0>(vb), rq, colB, 0, SPOL);
+
+    const int lg = lane / LA;                          // group within the half
+    const bool leader = (lane % LA) == 0;
+    const int64_t g0 = (int64_t)slab * GPS;            // first group of the slab
+    const int64_t gA = g0 + lg, gB = g0 + GPH + lg;
+    if constexpr (ue8m0) {
+        if (a.scale_layout == LAYOUT_COL) {
+            const uint32_t byteA = validA ? sA.e : 0u, byteB = validB ? sB.e : 0u;
+            uint32_t *words = reinterpret_cast<uint32_t *>(se);
+            if constexpr (GPH <= 4) {
+                // G >= 64: the slab's 4 or 8 groups, read from their leaders
+#pragma unroll
+                for (int w = 0; w < GPS / 4; ++w) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int gi = 4 * w + i;      // group within the slab
+                        const uint32_t bi =
+                            gi < GPH ? (uint32_t)__builtin_amdgcn_readlane((int)byteA, gi * LA)
+                                     : (uint32_t)__builtin_amdgcn_readlane((int)byteB,
+                                                                           (gi - GPH) * LA);
+                        word |= bi << (8 * i);
+                    }
+                    const int64_t gw = g0 + 4 * w;
+                    if (lane == 0 && gw < a.ng) words[(gw >> 2) * a.rows_pad + m] = word;
+                }
+            } else {
+                // G <= 32: each word's 4 groups lie in one half
+                const uint32_t a1 = (uint32_t)__shfl((int)byteA, lane + LA);
+                const uint32_t a2 = (uint32_t)__shfl((int)byteA, lane + 2 * LA);
+                const uint32_t a3 = (uint32_t)__shfl((int)byteA, lane + 3 * LA);
+                const uint32_t b1 = (uint32_t)__shfl((int)byteB, lane + LA);
+                const uint32_t b2 = (uint32_t)__shfl((int)byteB, lane + 2 * LA);
+                const uint32_t b3 = (uint32_t)__shfl((int)byteB, lane + 3 * LA);
+                if (leader && (lg & 3) == 0) {
+                    if (validA)
+                        words[(gA >> 2) * a.rows_pad + m] = byteA | (a1 << 8) | (a2 << 16) | (a3 << 24);
+                    if (validB)
+                        words[(gB >> 2) * a.rows_pad + m] = byteB | (b1 << 8) | (b2 << 16) | (b3 << 24);
+                }
+            }
+        } else if (leader) {
+            if (validA) se[m * a.ng + gA] = (uint8_t)sA.e;
+            if (validB) se[m * a.ng + gB] = (uint8_t)sB.e;
+        }
+    } else if (leader) {
+        float *sf = reinterpret_cast<float *>(se);
+        if (a.scale_layout == LAYOUT_ROW) {
+            if (validA) sf[m * a.ng + gA] = sA.r;
+            if (validB) sf[m * a.ng + gB] = sB.r;
+        } else {
+            if (validA) sf[gA * a.rows_pad + m] = sA.r;
+            if (validB) sf[gB * a.rows_pad + m] = sB.r;
+        }
+    }
+}
 
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL>
 __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &t, int lane,
@@ -444,6 +554,10 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
 #pragma unroll
     for (int s = 0; s < UMAX; ++s) {
         const int slab = t.j * UMAX + s;                            // slab within row
+        if constexpr (IN == IN_FP32) {
+            process_slab_fp32<G, OUT, SF, SPOL>(a, b.g[s], b.gh[s], slab, rq, se, m, lane);
+            continue;
+        }
         const uint32_t col = (uint32_t)slab * kSlab + (uint32_t)lane * 8;
         const bool valid = (int64_t)col < a.K;
         float y[8];
