@@ -660,16 +660,17 @@ def main():
         core = allowed[-1]
         os.sched_setaffinity(0, {core})
         try:
-            steps_cpu, t0 = 0, time.perf_counter()
-            while steps_cpu < 4 and (steps_cpu == 0 or time.perf_counter() - t0 < 10.0):
+            times, t0 = [], time.perf_counter()
+            while len(times) < 4 and (not times or time.perf_counter() - t0 < 10.0):
+                t1 = time.perf_counter()
                 oracle.ptgq(x_host, "bf16", M, K, G, False, "e4m3", "ue8m0", "col", eps=1e-10)
-                steps_cpu += 1
-            dt = (time.perf_counter() - t0) / steps_cpu
+                times.append(time.perf_counter() - t1)
+            steps_cpu, dt = len(times), float(np.median(times))
         finally:
             os.sched_setaffinity(0, allowed)
         cpu = {"value": round(foot / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"{steps_cpu} full steps of all {M} rows of the bf16 [{M},{K}] input "
-                         f"({M * K} elements each), single-threaded, {dt:.1f} s per step",
+                         f"({M * K} elements each), single-threaded, median {dt:.1f} s per step",
                "ns_per_element": round(dt / (M * K) * 1e9, 2),
                "host": {"cpu_model": host_cpu_model(), "cores_visible": len(allowed),
                         "pinned_core": core}}
