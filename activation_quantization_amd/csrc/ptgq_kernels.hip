@@ -856,15 +856,14 @@ __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int
 // store the table into LDS (every wave of the block reaches that barrier,
 // with or without a task), so the table copy overlaps the first HBM reads.
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL,
-          bool STAGE,
-          class Map>
+          bool STAGE, bool FETCHED = false, class Map>
 __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
-                                          int stride, int lane, float *tab)
+                                          int stride, int lane, float *tab,
+                                          TableRegs tr = TableRegs{})
 {
     const bool hasA0 = first < n;
     TaskBuf<UMAX> A, B;
-    TableRegs tr;
-    if constexpr (STAGE) table_fetch<TABLE>(tr);
+    if constexpr (STAGE && !FETCHED) table_fetch<TABLE>(tr);
     const TaskLoc lA = map(a, hasA0 ? first : 0, lane);
     load_task<IN, FUSE, UMAX>(a, lA, lane, hasA0, A);
     if constexpr (STAGE) table_store<TABLE>(tr, tab);
@@ -946,10 +945,17 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
         // barrier before the first task's loads, which are issued before the
         // SiLU table is stored (every wave reaches that barrier, with or
         // without a task).
-        const int win = wave_inclusive_sum(live_rows_of_lane(a.masked_m, E, a.rows, lane), lane);
+        // masked_m (never NULL here) read by every lane without a branch, so
+        // that the table's loads are in flight while it arrives
+        const int raw = a.masked_m[lane < E ? lane : E - 1];
+        TableRegs tr;
+        table_fetch<TABLE>(tr);
+        __builtin_amdgcn_sched_barrier(0);   // keep both loads ahead of the wait
+        const int live = lane < E ? (raw < 0 ? 0 : (raw > a.rows ? (int)a.rows : raw)) : 0;
+        const int win = wave_inclusive_sum(live, lane);
         const int n = __builtin_amdgcn_readlane(win, E - 1) * a.tpr;
-        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, true>(
-            a, MaskedMap(win, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab);
+        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, true, true>(
+            a, MaskedMap(win, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab, tr);
         return;
     }
     // More experts: the table's loads, then the prefix sum of masked_m into
