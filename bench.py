@@ -579,6 +579,32 @@ def main():
             d3["x"], "bf16", 8192, 4096, 128, True, "e4m3", "ue8m0", "col", s3[0][1], s3[0][2],
             spread(8192))
         del c3, s3
+        # the rest of the fused workload's sizes, M = 1, 64 and 2048 (graph
+        # figures; M <= 64 is latency-bound), each with every output row or
+        # 24 sampled rows checked
+        for M3 in W.CFG3_M:
+            if M3 == 8192:
+                continue
+            d3m = W.cfg3(M3)
+            f3m = alg_bytes_flat(M3, 4096, 128, 2, True, 1)
+            s3m, c3m = make_flat_sets(torch, aq, d3m["x"], M3, 4096, 128, True, "e4m3", "ue8m0",
+                                      "col", "bf16", rotation_sets(f3m))
+            name = f"fused_silu_mul_M{M3}_K4096"
+            variants[name] = variant_entry(timer, c3m, f3m)
+            checks[name] = capture_flat(d3m["x"], "bf16", M3, 4096, 128, True, "e4m3", "ue8m0",
+                                        "col", s3m[0][1], s3m[0][2], spread(M3))
+            del c3m, s3m
+        # the plain workload: bf16 [64, 2048] -> e4m3, fp32 row-major scales
+        # (latency-bound), every row checked
+        d1 = W.cfg1()
+        f1 = alg_bytes_flat(64, 2048, 128, 2, False, 4)
+        s1, c1 = make_flat_sets(torch, aq, d1["x"], 64, 2048, 128, False, "e4m3", "f32", "row",
+                                "bf16", rotation_sets(f1))
+        variants["plain_fp32_rowmajor_M64_K2048"] = variant_entry(timer, c1, f1)
+        checks["plain_fp32_rowmajor_M64_K2048"] = capture_flat(
+            d1["x"], "bf16", 64, 2048, 128, False, "e4m3", "f32", "row", s1[0][1], s1[0][2],
+            np.arange(64))
+        del c1, s1
         # masked MoE, E=32, tokens_pad=384, fused, K=2048
         d4, c4, f4, live = masked_calls(torch, aq, W)
         E, T, K4, mm = d4["E"], d4["T"], d4["K"], d4["masked_m"]
