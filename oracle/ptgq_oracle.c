@@ -29,6 +29,9 @@
  *     the per-token kernel in [sglang #34257] key source snippets.
  *   - SiLU uses a correctly rounded binary32 exp; every other step of
  *     silu(g)*u is one IEEE fp32 operation.
+ *   - a zero value times an infinite multiplier (fl(1/r) overflowed: r below
+ *     about 2^-128) is a zero of the value's sign, not NaN; a non-zero value
+ *     times it saturates.
  *   - e4m3 narrowing is round-to-nearest-even with saturation to +-448
  *     ([sglang #35593] key source snippets, satfinite conversion); a negative
  *     value that rounds to zero keeps its sign (code 0x80).
@@ -194,9 +197,23 @@ static group_scale make_scale(float amax, float eps, float qmax, int ue8m0)
     return gs;
 }
 
+/* The value narrowed for y: v = y * inv, one fp32 rounding, except that a
+ * zero y gives v = y.  The two differ only when inv is infinite, which
+ * happens when fl(1/r) overflows (r below about 2^-128: an fp32 scale with a
+ * floor eps below about 1.3e-36, or a per-token row whose largest magnitude is
+ * below that): the product 0 * inf would be NaN, while the quotient y / r the
+ * codes stand for is exactly zero.  So a zero keeps its sign (e4m3 0x00 or
+ * 0x80) and a non-zero y times an infinite multiplier saturates.  (The pages
+ * leave this corner open; [sglang #34257] key source snippets guard only the
+ * all-zero row, by a zero multiplier.) */
+static float scaled(float y, float inv)
+{
+    return (y == 0.0f) ? y : y * inv;
+}
+
 static uint8_t quantize(float y, float inv, int out_dtype)
 {
-    float v = y * inv;
+    float v = scaled(y, inv);
     if (out_dtype == OR_E4M3) return e4m3_rne_sat(v);
     return (uint8_t)int8_rne_sat(v);
 }
@@ -350,7 +367,9 @@ int oracle_ptgq_masked(const void *x, int in_dtype, int64_t E, int64_t T, int64_
 }
 
 /* Whole-row per-token e4m3: scale = rowmax / 448 with no floor, multiplier
- * zero when the scale is zero, codes narrowed with saturation.
+ * zero when the scale is zero, codes narrowed with saturation (a zero element
+ * gives a zero code of its sign even when the multiplier overflowed, as in
+ * scaled() above).
  * ([sglang #34257] key source snippets, the warp kernel.) */
 int oracle_ptq_fp8(const void *x, int in_dtype, int64_t M, int64_t K, uint8_t *q, float *s)
 {
@@ -366,7 +385,7 @@ int oracle_ptq_fp8(const void *x, int in_dtype, int64_t M, int64_t K, uint8_t *q
         float inv = (r == 0.0f) ? 0.0f : 1.0f / r;
         s[m] = r;
         for (int64_t k = 0; k < K; ++k)
-            q[m * K + k] = e4m3_rne_sat(decode_elem(x, in_dtype, m * K + k) * inv);
+            q[m * K + k] = e4m3_rne_sat(scaled(decode_elem(x, in_dtype, m * K + k), inv));
     }
     return 0;
 }
@@ -387,7 +406,8 @@ static float e4m3_decode(uint8_t c)
 /* For expert e and rows t < min(max(masked_m[e], 0), T) (every row when
  * masked_m is NULL): out[e][t][k] = e4m3_sat((dec(x[e][t][k]) * s) * inv) with
  * s = x_scale[e*se + t*st + (k/G)*sg] and inv = 1 / output_scale, each product
- * one fp32 rounding; rows past masked_m keep out's contents.
+ * one fp32 rounding (a zero product keeps its sign whatever inv, as in
+ * scaled() above); rows past masked_m keep out's contents.
  * ([sglang #35593] key source snippets: dequantize by the group scale, then
  * multiply by the reciprocal of the per-tensor output scale, saturating RN
  * narrowing; implementation breakdown: 128-wide scale groups, column-major
@@ -407,7 +427,7 @@ int oracle_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int G,
                 const int64_t i = (e * T + t) * K + k;
                 const float s = x_scale[e * se + t * st + (k / G) * sg];
                 const float h = e4m3_decode(x[i]) * s;
-                out[i] = e4m3_rne_sat(h * inv);
+                out[i] = e4m3_rne_sat(scaled(h, inv));
             }
         }
     }

@@ -16,7 +16,7 @@ with open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json"))
 
 
 def bf16_exact(values):
-    f = np.array([float(v) for v in values], dtype=np.float64)
+    f = np.array([float.fromhex(v) if "p" in v else float(v) for v in values], dtype=np.float64)
     b = to_bf16_bits(f)
     back = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.array_equal(back, f) and np.array_equal(np.signbit(back), np.signbit(f))

@@ -244,3 +244,88 @@ def test_masked_expert_equals_flat_call_on_its_rows(in_dtype):
             assert np.array_equal(s[e * sb:e * sb + fs.size], fs)
         assert np.all(q[e, live:] == 0x7F)
         assert np.all(s[e * sb + live * (K // G) * 4:(e + 1) * sb] == 0xFF)
+
+
+def tiny_rows(seed, M, K, in_dtype):
+    """Rows whose largest magnitude lies in [1e-38, 4e-36] (normal fp32 and
+    bf16 values included), a quarter of each row zeros of both signs, one row
+    all zero and one row of ordinary size (its multiplier stays finite)."""
+    rng = np.random.default_rng(seed)
+    amax = np.exp(rng.uniform(np.log(1e-38), np.log(4e-36), M))
+    y = rng.uniform(-1.0, 1.0, (M, K)) * amax[:, None]
+    y[rng.random((M, K)) < 0.25] = 0.0
+    y[rng.random((M, K)) < 0.1] = -0.0
+    y[1] = 0.0
+    y[2] = rng.normal(size=K)
+    if in_dtype == "fp32":
+        return y.astype(np.float32)
+    return W.to_bf16_bits(y)
+
+
+def codes_from_multiplier(y, inv, out_dtype):
+    """Codes of y (float32) times a per-row or per-group multiplier: where the
+    multiplier is infinite, zeros keep their sign and the rest saturate;
+    elsewhere torch's saturating e4m3 cast / numpy rint of the fp32 product."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        v = (y * inv).astype(np.float32)
+    v = np.where(y == 0, y, v)
+    if out_dtype == "e4m3":
+        c = torch.from_numpy(np.clip(v, -448.0, 448.0)).to(F8).view(torch.uint8).numpy()
+    else:
+        c = np.clip(np.rint(v.astype(np.float64)), -128, 127).astype(np.int8).view(np.uint8)
+    return c
+
+
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp32"])
+def test_overflowed_multiplier_per_token(in_dtype):
+    """Per-token rows with a maximum below ~1.3e-36: 1 / (max / 448) overflows
+    to +inf (numpy's IEEE quotients decide where); zeros keep their sign, the
+    other elements saturate to +-448."""
+    M, K = 16, 256
+    x = tiny_rows(71, M, K, in_dtype)
+    y = x if in_dtype == "fp32" else oracle.decode(x, "bf16").reshape(M, K)
+    q, s = oracle.ptq_fp8(x, in_dtype, M, K)
+    r = (np.abs(y).max(axis=1) / np.float32(448.0)).astype(np.float32)
+    assert np.array_equal(s.view(np.uint32), r.view(np.uint32))
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = np.where(r == 0, np.float32(0), np.float32(1.0) / r).astype(np.float32)
+    assert np.isinf(inv).sum() >= M // 2          # the corner is reached
+    assert np.array_equal(q, codes_from_multiplier(y, inv[:, None], "e4m3"))
+    neg_zero = (y == 0) & np.signbit(y)
+    assert np.all(q[neg_zero] == 0x80) and np.all(q[(y == 0) & ~np.signbit(y)] == 0x00)
+
+
+@pytest.mark.parametrize("out_dtype", ["e4m3", "int8"])
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp32"])
+def test_overflowed_multiplier_group_fp32_scale_eps0(in_dtype, out_dtype):
+    M, K, G = 12, 512, 64
+    x = tiny_rows(72, M, K, in_dtype)
+    y = x if in_dtype == "fp32" else oracle.decode(x, "bf16").reshape(M, K)
+    q, s = oracle.ptgq(x, in_dtype, M, K, G, False, out_dtype, "f32", "row", eps=0.0)
+    qmax = np.float32(448.0 if out_dtype == "e4m3" else 127.0)
+    r = (np.abs(y).reshape(M, K // G, G).max(axis=2) / qmax).astype(np.float32)
+    assert np.array_equal(s.view(np.float32).reshape(M, K // G).view(np.uint32), r.view(np.uint32))
+    with np.errstate(divide="ignore", over="ignore"):
+        inv = np.where(r == 0, np.float32(0), np.float32(1.0) / r).astype(np.float32)
+    assert np.isinf(inv).any()
+    want = codes_from_multiplier(y.reshape(M, K // G, G), inv[:, :, None], out_dtype)
+    assert np.array_equal(q, want.reshape(M, K))
+
+
+def test_overflowed_multiplier_requant():
+    """An output scale whose reciprocal overflows (1e-39): zero products keep
+    their sign, the others saturate."""
+    E, T, K = 2, 5, 256
+    rng = np.random.default_rng(73)
+    x = rng.integers(0, 256, (E, T, K)).astype(np.uint8)
+    x[(x & 0x7F) == 0x7F] = 0x00
+    x[:, :, :16] = 0x80                                          # -0
+    s = rng.uniform(0.5, 2.0, (E, T, K // 128)).astype(np.float32)
+    os_ = np.float32(1e-39)
+    with np.errstate(divide="ignore", over="ignore"):
+        assert np.isinf(np.float32(1.0) / os_)
+    out = oracle.requant_fp8(x, E, T, K, 128, s, (T * (K // 128), K // 128, 1), None, os_)
+    dec = torch.from_numpy(x).view(F8).to(torch.float32).numpy()
+    h = (dec * np.repeat(s, 128, axis=2)).astype(np.float32)
+    assert np.array_equal(out, codes_from_multiplier(h, np.float32(np.inf), "e4m3"))
+    assert np.all(out[:, :, :16] == 0x80)
