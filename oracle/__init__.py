@@ -56,6 +56,8 @@ def _load():
         for name in ("oracle_bf16_rne_vec", "oracle_fp16_rne_vec"):
             getattr(lib, name).argtypes = [vp, vp, i64]
             getattr(lib, name).restype = None
+        lib.oracle_scale_vec.argtypes = [vp, i64, f32, i32, i32, vp, vp, vp]
+        lib.oracle_scale_vec.restype = None
         _lib = lib
     return _lib
 
@@ -185,6 +187,19 @@ def e4m3(v) -> np.ndarray:
     out = np.empty(v.shape, dtype=np.uint8)
     _load().oracle_e4m3_vec(_ptr(v), _ptr(out), v.size)
     return out
+
+
+def scale(amax, eps, out_dtype, scale_fmt):
+    """The scale of groups with the given absmax values (float32 array):
+    (r float32, UE8M0 byte uint8, multiplier float32), as the quantizer makes
+    them (the byte is 0 for the fp32 format)."""
+    a = np.ascontiguousarray(amax, dtype=np.float32)
+    r = np.empty(a.shape, dtype=np.float32)
+    e = np.empty(a.shape, dtype=np.uint8)
+    inv = np.empty(a.shape, dtype=np.float32)
+    _load().oracle_scale_vec(_ptr(a), a.size, float(eps), _OUT[out_dtype],
+                             int(scale_fmt == "ue8m0"), _ptr(r), _ptr(e), _ptr(inv))
+    return r, e, inv
 
 
 def int8(v) -> np.ndarray:

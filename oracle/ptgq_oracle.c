@@ -569,3 +569,17 @@ void oracle_decode_vec(const uint16_t *h, int dtype, float *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_decode(h[i], dtype);
 }
+
+/* The scale step alone over many absmax values (for exhaustive device
+ * probes): r, the UE8M0 byte and the multiplier of make_scale. */
+void oracle_scale_vec(const float *amax, int64_t n, float eps, int out_dtype, int ue8m0,
+                      float *r, uint8_t *e, float *inv)
+{
+    const float qmax = (out_dtype == OR_E4M3) ? 448.0f : 127.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        group_scale gs = make_scale(amax[i], eps, qmax, ue8m0);
+        if (r) r[i] = gs.r;
+        if (e) e[i] = gs.ue8m0;
+        if (inv) inv[i] = gs.inv;
+    }
+}

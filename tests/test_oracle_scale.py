@@ -97,3 +97,32 @@ def test_fp32_codes_use_reciprocal_multiply_and_stay_in_range():
     qi, _ = oracle.ptgq(x, "bf16", 512, 128, 128, False, "int8", "f32", "row")
     topi = qi.view(np.int8)[np.arange(512), amax_col]
     assert np.all(np.abs(topi.astype(np.int32)) == 127)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-10])
+@pytest.mark.parametrize("out_dtype,qmax", [("e4m3", 448.0), ("int8", 127.0)])
+def test_vector_scale_export_equals_the_pins(out_dtype, qmax, eps):
+    """oracle.scale (the vector form the device probes are compared with):
+    every bf16 absmax plus fp32 values around the subnormal quotients, against
+    numpy's IEEE quotients and the exact power-of-two ceiling."""
+    bits = all_bf16_magnitudes()
+    a16 = (bits.astype(np.uint32) << 16).view(np.float32)
+    tiny = np.arange(0, 1 << 24, 4099, dtype=np.uint32).view(np.float32)   # up to 2^-126 * 2
+    a = np.concatenate([a16, tiny])
+    e32 = np.float32(eps)
+    r, e, inv = oracle.scale(a, eps, out_dtype, "f32")
+    r_expect = (np.maximum(a, e32) / np.float32(qmax)).astype(np.float32)
+    assert np.array_equal(r.view(np.uint32), r_expect.view(np.uint32))
+    with np.errstate(divide="ignore", over="ignore"):
+        inv_expect = np.where(r_expect == 0, np.float32(0), np.float32(1) / r_expect)
+    assert np.array_equal(inv.view(np.uint32), inv_expect.astype(np.float32).view(np.uint32))
+    assert np.all(e == 0)
+    r8, e8, inv8 = oracle.scale(a, eps, out_dtype, "ue8m0")
+    assert np.array_equal(r8.view(np.uint32), r_expect.view(np.uint32))
+    # a subnormal quotient has exponent field 0 and a non-zero fraction: the
+    # exponent-plus-carry rule gives byte 1 (2^-126), the power-of-two ceiling
+    # clamped to the normal range
+    want = np.array([max(pow2_ceil_byte(x), 1) if x > 0 else 0 for x in r_expect],
+                    dtype=np.uint8)
+    assert np.array_equal(e8, want)
+    assert np.array_equal(inv8.astype(np.float64), np.ldexp(1.0, 127 - want.astype(np.int64)))
