@@ -24,9 +24,12 @@ OUT_DTYPES = {"e4m3": PTGQ_E4M3, "int8": PTGQ_INT8}
 SCALE_FMTS = {"f32": PTGQ_SCALE_F32, "ue8m0": PTGQ_SCALE_UE8M0}
 SCALE_LAYOUTS = {"row": PTGQ_ROW_MAJOR, "col": PTGQ_COL_MAJOR}
 
+# include/ptgq.h: the quantization interface
 EXPORTS = ("ptgq_quant", "ptgq_quant_padded", "ptgq_quant_masked", "ptq_quant_fp8", "ptgq_requant_fp8",
-           "ptgq_dequant", "ptgq_scale_bytes", "ptgq_status_string", "ptgq_init", "ptgq_probe_e4m3",
-           "ptgq_probe_silu_mul", "ptgq_set_tuning", "ptgq_plan_group")
+           "ptgq_dequant", "ptgq_scale_bytes", "ptgq_status_string", "ptgq_init")
+# include/ptgq_diag.h: probes, the stream reference, the chooser's report and overrides
+DIAG_EXPORTS = ("ptgq_probe_e4m3", "ptgq_probe_silu_mul", "ptgq_probe_scale", "ptgq_probe_int8",
+                "ptgq_probe_stream", "ptgq_diag_fastdiv", "ptgq_plan_group", "ptgq_set_tuning")
 
 
 class PtgqError(RuntimeError):
@@ -76,6 +79,15 @@ def load_library(path: str = LIB_PATH):
     lib.ptgq_set_tuning.restype = i32
     lib.ptgq_plan_group.argtypes = [i32, i64, i64, i64, i32, i32, i64, i64, i32, vp]
     lib.ptgq_plan_group.restype = i32
+    u32 = ctypes.c_uint32
+    lib.ptgq_probe_scale.argtypes = [u32, i64, f32, i32, i32, vp, vp, vp]
+    lib.ptgq_probe_scale.restype = i32
+    lib.ptgq_probe_int8.argtypes = [u32, i64, vp, vp]
+    lib.ptgq_probe_int8.restype = i32
+    lib.ptgq_probe_stream.argtypes = [vp, i64, vp, vp]
+    lib.ptgq_probe_stream.restype = i32
+    lib.ptgq_diag_fastdiv.argtypes = [u32, vp, vp, i64]
+    lib.ptgq_diag_fastdiv.restype = i32
     _lib = lib
     return lib
 
@@ -146,14 +158,14 @@ def ptgq_set_tuning(knob: int, value: int) -> int:
 
 
 PLAN_FIELDS = ("grid", "block", "slabs_per_task", "tasks_per_row", "tasks", "xcd_chunk",
-               "silu_table", "uncapped")
+               "silu_table", "uncapped", "flat_slabs")
 
 
 def ptgq_plan_group(in_dtype, E, rows, K, group_size, fuse_silu_mul, expected_m, q_rows, cus):
     """The launch geometry the chooser picks for a flat (E = 0) or masked
     (E >= 1) group call on a device of `cus` compute units, as a dict of
     PLAN_FIELDS.  Host only: no device is touched."""
-    out = (ctypes.c_int64 * 8)()
+    out = (ctypes.c_int64 * len(PLAN_FIELDS))()
     rc = load_library().ptgq_plan_group(_enum(in_dtype, IN_DTYPES), int(E), int(rows), int(K),
                                         int(group_size), int(bool(fuse_silu_mul)),
                                         int(expected_m), int(q_rows), int(cus),
@@ -269,3 +281,43 @@ def ptgq_probe_silu_mul(g, u, in_dtype, path, out, n, stream=None, check=True):
     rc = load_library().ptgq_probe_silu_mul(_ptr(g), _ptr(u), _enum(in_dtype, IN_DTYPES),
                                             int(path), _ptr(out), n, _stream(stream))
     return _check("ptgq_probe_silu_mul", rc) if check else rc
+
+
+def ptgq_probe_scale(first_bits, n, eps, out_dtype, scale_fmt, scale_out, inv_out=None,
+                     stream=None, check=True):
+    fmt = _enum(scale_fmt, SCALE_FMTS)
+    if n > 0:
+        _need(scale_out, n * (4 if fmt == PTGQ_SCALE_F32 else 1), "ptgq_probe_scale", "scale_out")
+        if inv_out is not None:
+            _need(inv_out, 4 * n, "ptgq_probe_scale", "inv_out")
+    rc = load_library().ptgq_probe_scale(int(first_bits), int(n), float(eps),
+                                         _enum(out_dtype, OUT_DTYPES), fmt, _ptr(scale_out),
+                                         _ptr(inv_out), _stream(stream))
+    return _check("ptgq_probe_scale", rc) if check else rc
+
+
+def ptgq_probe_int8(first_bits, n, out, stream=None, check=True):
+    if n > 0:
+        _need(out, n, "ptgq_probe_int8", "out")
+    rc = load_library().ptgq_probe_int8(int(first_bits), int(n), _ptr(out), _stream(stream))
+    return _check("ptgq_probe_int8", rc) if check else rc
+
+
+def ptgq_probe_stream(x, n, q, stream=None, check=True):
+    if n > 0:
+        _need(x, 2 * n, "ptgq_probe_stream", "x")
+        _need(q, n, "ptgq_probe_stream", "q")
+    rc = load_library().ptgq_probe_stream(_ptr(x), int(n), _ptr(q), _stream(stream))
+    return _check("ptgq_probe_stream", rc) if check else rc
+
+
+def ptgq_diag_fastdiv(d, n):
+    """floor(n / d) for a host numpy array n (uint32, each < 2^31) by the
+    kernels' multiply-high division.  Host only."""
+    import numpy as np
+    n = np.ascontiguousarray(n, dtype=np.uint32)
+    q = np.empty_like(n)
+    rc = load_library().ptgq_diag_fastdiv(int(d), ctypes.c_void_p(n.ctypes.data),
+                                          ctypes.c_void_p(q.ctypes.data), n.size)
+    _check("ptgq_diag_fastdiv", rc)
+    return q

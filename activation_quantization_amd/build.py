@@ -6,15 +6,18 @@ correctly rounded and fp32 denormals by default); packed fp32 instructions
 disabled.
 """
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libptgq.so")
 SOURCES = [os.path.join(CSRC, "ptgq_kernels.hip"), os.path.join(CSRC, "ptgq_api.cpp")]
-HEADERS = [os.path.join(ROOT, "include", "ptgq.h"), os.path.join(CSRC, "ptgq_internal.h")]
+HEADERS = [os.path.join(ROOT, "include", "ptgq.h"), os.path.join(ROOT, "include", "ptgq_diag.h"),
+           os.path.join(CSRC, "ptgq_internal.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -26,19 +29,38 @@ FLAGS = [
 ]
 
 
+# The packed-fp32 feature can only be switched off for both compilation passes
+# at once (clang forwards no -Xclang pair to the device pass alone), so the
+# host pass warns that an x86 target has no such feature.  That one warning is
+# dropped; in its place the build checks the device assembly it produced (kept
+# from the same compilation) for packed fp32 arithmetic.
+HOST_PASS_NOTE = "'-packed-fp32-ops' is not a recognized feature for this target"
+PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
+
+
 def build(verbose: bool = False) -> str:
     """Compile the library unconditionally; return its path."""
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, "-x", "hip", SOURCES[0], "-x", "hip", SOURCES[1]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
+    with tempfile.TemporaryDirectory(prefix="ptgq_build_") as work:
+        cmd = [HIPCC, *FLAGS, "-save-temps=cwd", "-o", tmp, "-x", "hip", SOURCES[0], "-x", "hip",
+               SOURCES[1]]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True, cwd=work)
+        lines = res.stderr.splitlines()
+        err = "\n".join(l for l in lines if HOST_PASS_NOTE not in l)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+        if verbose and err.strip():
+            print(err)
+        device_asm = [f for f in os.listdir(work) if "amdgcn" in f and f.endswith(".s")]
+        if not device_asm:
+            raise RuntimeError("hipcc left no device assembly to check")
+        for name in device_asm:
+            with open(os.path.join(work, name)) as fh:
+                bad = sorted({m.group(0) for m in PACKED_FP32.finditer(fh.read())})
+            if bad:
+                raise RuntimeError(f"packed fp32 instructions in {name}: {bad}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -14,6 +14,7 @@
 #include <mutex>
 
 #include "ptgq.h"
+#include "ptgq_diag.h"
 #include "ptgq_internal.h"
 
 using namespace ptgq;
@@ -21,27 +22,45 @@ using namespace ptgq;
 namespace {
 
 // ----------------------------------------------------------------- devices
+//
+// Per-device state: the compute-unit count (queried once it succeeds; a
+// failed query is not remembered) and the SiLU lookup table of the fused bf16
+// kernels, a file-scope device array filled by one small kernel.  The table
+// is built stream-ordered on the stream of the first call that needs it and
+// an event is recorded after the build; later calls on other streams wait for
+// that event on the device (hipStreamWaitEvent), and once the event has
+// completed the table is ready for every stream.  No call synchronizes the
+// host.  A call made while its stream is being captured into a graph never
+// builds the table and never waits for a build recorded outside the capture:
+// until the table is ready it takes the direct SiLU evaluation instead (same
+// results, slower).
 
 constexpr int kMaxDevices = 64;
-std::once_flag g_dev_once[kMaxDevices];
-int g_dev_cus[kMaxDevices];            // compute units; 0 = query failed
+constexpr int kPlanFields = 9;   // ptgq_plan_group's report
 
-// Once per device: query the CU count and build the device's SiLU lookup table
-// (one small kernel and one host synchronization, never repeated).
+enum TableState : int { TABLE_NONE = 0, TABLE_PENDING = 1, TABLE_READY = 2 };
+
+struct DeviceState {
+    std::mutex mu;
+    int cus = 0;                 // 0: not known yet
+    int table = TABLE_NONE;
+    hipEvent_t built = nullptr;  // recorded after the table kernel (PENDING, READY)
+};
+
+DeviceState g_dev[kMaxDevices];
+
 int device_cus(int dev)
 {
     if (dev < 0 || dev >= kMaxDevices) return 0;
-    std::call_once(g_dev_once[dev], [dev] {
+    DeviceState &d = g_dev[dev];
+    std::lock_guard<std::mutex> lock(d.mu);
+    if (d.cus <= 0) {
         int cus = 0;
-        int prev = -1;
-        if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            launch_silu_table_init(nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
-            cus = 0;
-        if (prev >= 0) (void)hipSetDevice(prev);
-        g_dev_cus[dev] = cus;
-    });
-    return g_dev_cus[dev];
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0)
+            d.cus = cus;
+    }
+    return d.cus;
 }
 
 int current_cus(int *dev_out)
@@ -52,13 +71,47 @@ int current_cus(int *dev_out)
     return device_cus(dev);
 }
 
+// True when work enqueued on `stream` (of device `dev`, the current device)
+// after this call may read the SiLU table; builds it on `stream` when no
+// build exists yet and the stream is not capturing.  Never waits on the host.
+bool table_usable(int dev, hipStream_t stream)
+{
+    if (dev < 0 || dev >= kMaxDevices) return false;
+    DeviceState &d = g_dev[dev];
+    std::lock_guard<std::mutex> lock(d.mu);
+    if (d.table == TABLE_READY) return true;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return false;
+    if (d.table == TABLE_PENDING) {
+        const hipError_t q = hipEventQuery(d.built);
+        if (q == hipSuccess) {
+            d.table = TABLE_READY;
+            return true;
+        }
+        return q == hipErrorNotReady && hipStreamWaitEvent(stream, d.built, 0) == hipSuccess;
+    }
+    if (!d.built && hipEventCreateWithFlags(&d.built, hipEventDisableTiming) != hipSuccess) {
+        d.built = nullptr;
+        return false;
+    }
+    if (launch_silu_table_init(stream) != hipSuccess) return false;
+    // the build is only known to precede this stream's later work; without the
+    // event no other stream could order itself after it, so the table stays
+    // unused (a later call builds it again: the same values)
+    if (hipEventRecord(d.built, stream) != hipSuccess) return false;
+    d.table = TABLE_PENDING;
+    return true;
+}
+
 // ------------------------------------------------------------ tuning knobs
 // Process-wide overrides of the geometry chooser (diagnostics and sweeps
 // only; -1 = automatic), set through ptgq_set_tuning.
-constexpr int kKnobs = 7;
-std::atomic<int64_t> g_knob[kKnobs] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+constexpr int kKnobs = 8;
+std::atomic<int64_t> g_knob[kKnobs] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
 enum { KNOB_SLABS_PER_TASK = 0, KNOB_WAVES_PER_BLOCK = 1, KNOB_BLOCKS_PER_CU = 2,
-       KNOB_TOKEN_MODE = 3, KNOB_SILU_TABLE = 4, KNOB_XCD_CHUNK = 5, KNOB_GRID_MODE = 6 };
+       KNOB_TOKEN_MODE = 3, KNOB_SILU_TABLE = 4, KNOB_XCD_CHUNK = 5, KNOB_GRID_MODE = 6,
+       KNOB_FLAT_SLABS = 7 };
 
 int64_t knob(int k) { return g_knob[k].load(std::memory_order_relaxed); }
 
@@ -120,21 +173,28 @@ constexpr int64_t kDequantXcdChunk = 16;
 // work spreads over as many waves and CUs as possible.  Many: two slabs per
 // task for the plain and direct-SiLU kernels when a row has an even number of
 // slabs (no task runs past a row), else one (measured best on MI355X).
-// `flat16`: an unfused flat call on 16-bit input, which runs the uncapped
-// grid with two-slab tasks also when a row has an odd number (>= 3) of slabs:
-// its last task per row holds one slab (measured on MI355X, fp16 rows of 3, 5
-// and 7 slabs: 2-10 % faster than capped one-slab tasks; one-slab rows stay
-// one-slab).
+// `flat_slabs`: an unfused flat call whose K is a multiple of the slab, so
+// that input and codes are one contiguous sequence of whole-row slabs; its
+// two-slab tasks then run over that sequence and cross row ends (no half
+// task at the end of a row with an odd number of slabs).  `flat16`: other
+// unfused flat calls on 16-bit input, which run two-slab row tasks also when
+// a row has an odd number (>= 3) of slabs: the last task of a row holds one
+// slab (measured on MI355X, fp16 rows of 3, 5 and 7 slabs: 2-10 % faster than
+// capped one-slab tasks; one-slab rows stay one-slab).  `table_ok`: the SiLU
+// lookup table may be read (it is built and ordered before the call).
 void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16, bool flat16,
-                 int cus)
+                 bool flat_slabs, bool table_ok, int cus)
 {
     const int64_t wave_slots = (int64_t)cus * 4 * 8;   // 8 waves per SIMD
     g.table = fuse && bf16 && slabs >= (int64_t)cus * 4 * kTableWaves;
     if (fuse && bf16 && knob(KNOB_SILU_TABLE) >= 0) g.table = knob(KNOB_SILU_TABLE) > 0;
+    if (!table_ok) g.table = false;
     // Table kernels (16 waves per CU) run one-slab tasks: measured 6-8 % faster
     // than two-slab tasks for the fused flat and masked workloads.
     int U = 1;
-    if (!g.table && slabs >= 2 * wave_slots && (spr % 2 == 0 || (flat16 && spr >= 3))) U = 2;
+    if (!g.table && slabs >= 2 * wave_slots &&
+        (flat_slabs || spr % 2 == 0 || (flat16 && spr >= 3)))
+        U = 2;
     if (knob(KNOB_SLABS_PER_TASK) > 0) U = knob(KNOB_SLABS_PER_TASK) >= 2 ? 2 : 1;
     g.U = std::min(U, kMaxSlabsPerTask);
 }
@@ -201,7 +261,7 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es, 
 // extra rows are written as zero.
 int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t K, int G,
                int fuse, int scale_fmt, int scale_layout, bool masked, int64_t E,
-               int64_t expected_m, int64_t q_rows, int cus)
+               int64_t expected_m, int64_t q_rows, bool table_ok, int cus)
 {
     std::memset(&a, 0, sizeof(a));
     a.rows = rows;
@@ -216,10 +276,18 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
     const bool bf16 = in_dtype == PTGQ_BF16;
 
     if (!masked) {
-        choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, !fuse && es == 2, cus);
+        const bool fs_ok = !fuse && K % kSlab == 0 && knob(KNOB_FLAT_SLABS) != 0;
+        choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, !fuse && es == 2, fs_ok, table_ok,
+                    cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
-        const int64_t tasks = rows * (int64_t)a.tpr;
+        // Flat-slab tasks for two-slab tasks over whole-slab rows (measured on
+        // MI355X, fp16 [8192, 3584], 7 slabs per row: see the design notes).
+        a.flat_slabs = fs_ok && a.U == 2 ? 1 : 0;
+        a.n_slabs = rows * (int64_t)a.spr;
+        if (a.n_slabs >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+        a.spr_div = make_fastdiv((uint32_t)a.spr);
+        const int64_t tasks = a.flat_slabs ? (a.n_slabs + a.U - 1) / a.U : rows * (int64_t)a.tpr;
         if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.n_tasks = (int32_t)tasks;
         a.q_pad_bytes = (q_rows - rows) * K;
@@ -253,7 +321,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         if (E > kMaxExperts) return PTGQ_EUNSUPPORTED;
         const int64_t hint = (expected_m > 0 && expected_m < rows) ? expected_m : rows;
         choose_task(geo, std::max<int64_t>(hint, 1) * a.spr * E, a.spr, fuse != 0, bf16, false,
-                    cus);
+                    false, table_ok, cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
         if (E * rows * (int64_t)a.tpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
@@ -279,9 +347,15 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
     GroupArgs a;
     GroupGeom geo;
     const bool masked = masked_m != nullptr;
-    const int rc = plan_group(a, geo, in_dtype, rows, K, G, fuse, scale_fmt, scale_layout, masked,
-                              E, expected_m, q_rows, cus);
+    int rc = plan_group(a, geo, in_dtype, rows, K, G, fuse, scale_fmt, scale_layout, masked, E,
+                        expected_m, q_rows, true, cus);
     if (rc != PTGQ_OK) return rc;
+    if (geo.table && !table_usable(dev, static_cast<hipStream_t>(stream))) {
+        // the table is not ready for this stream: the direct evaluation
+        rc = plan_group(a, geo, in_dtype, rows, K, G, fuse, scale_fmt, scale_layout, masked, E,
+                        expected_m, q_rows, false, cus);
+        if (rc != PTGQ_OK) return rc;
+    }
     a.x = x;
     a.q = static_cast<uint8_t *>(q);
     a.s = s;
@@ -331,7 +405,23 @@ const char *ptgq_status_string(int status)
 
 int ptgq_init(int device)
 {
-    return device_cus(device) > 0 ? PTGQ_OK : PTGQ_EDEVICE;
+    if (device < 0 || device >= kMaxDevices || device_cus(device) <= 0) return PTGQ_EDEVICE;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device) != hipSuccess)
+        return PTGQ_EDEVICE;
+    int rc = PTGQ_OK;
+    if (!table_usable(device, nullptr)) {
+        rc = PTGQ_EDEVICE;
+    } else {
+        DeviceState &d = g_dev[device];
+        std::lock_guard<std::mutex> lock(d.mu);
+        if (d.table == TABLE_PENDING) {
+            if (hipEventSynchronize(d.built) == hipSuccess) d.table = TABLE_READY;
+            else rc = PTGQ_EDEVICE;
+        }
+    }
+    if (prev >= 0) (void)hipSetDevice(prev);
+    return rc;
 }
 
 int ptgq_quant(const void *x, int in_dtype, int64_t M, int64_t K, int group_size,
@@ -643,17 +733,79 @@ int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int path, fl
     if (n == 0) return PTGQ_OK;
     if (!g || !u || !out) return PTGQ_EINVAL;
     if (n >= (int64_t)UINT32_MAX * 256) return PTGQ_EUNSUPPORTED;
-    if (current_cus(nullptr) <= 0) return PTGQ_EDEVICE;   // builds the lookup table
+    int dev = 0;
+    if (current_cus(&dev) <= 0) return PTGQ_EDEVICE;
+    // path 1 reads the lookup table: built (or ordered) on this stream first
+    if (path == 1 && !table_usable(dev, static_cast<hipStream_t>(stream))) return PTGQ_EDEVICE;
     const hipError_t err = launch_probe_silu(g, u, in_dtype, path, out, n,
                                              static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
+}
+
+int ptgq_probe_scale(uint32_t first_bits, int64_t n, float eps, int out_dtype, int scale_fmt,
+                     void *scale_out, float *inv_out, void *stream)
+{
+    if (out_dtype != PTGQ_E4M3 && out_dtype != PTGQ_INT8) return PTGQ_EINVAL;
+    if (scale_fmt != PTGQ_SCALE_F32 && scale_fmt != PTGQ_SCALE_UE8M0) return PTGQ_EINVAL;
+    if (!(std::isfinite(eps) && eps >= 0.0f) || std::signbit(eps)) return PTGQ_EINVAL;
+    if (n < 0) return PTGQ_EINVAL;
+    if (n == 0) return PTGQ_OK;
+    // every amax must be a non-negative finite fp32: bit patterns below +inf
+    if ((int64_t)first_bits + n > (int64_t)0x7F800000) return PTGQ_EINVAL;
+    if (!scale_out) return PTGQ_EINVAL;
+    if (scale_fmt == PTGQ_SCALE_F32 && !aligned(scale_out, 4)) return PTGQ_EALIGN;
+    if (inv_out && !aligned(inv_out, 4)) return PTGQ_EALIGN;
+    if (current_cus(nullptr) <= 0) return PTGQ_EDEVICE;
+    const hipError_t err = launch_probe_scale(first_bits, n, eps, out_dtype, scale_fmt, scale_out,
+                                              inv_out, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
+}
+
+int ptgq_probe_int8(uint32_t first_bits, int64_t n, int8_t *out, void *stream)
+{
+    if (n < 0 || n > ((int64_t)1 << 32)) return PTGQ_EINVAL;
+    if (n == 0) return PTGQ_OK;
+    if (!out) return PTGQ_EINVAL;
+    if (current_cus(nullptr) <= 0) return PTGQ_EDEVICE;
+    const hipError_t err = launch_probe_int8(first_bits, n, out, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
+}
+
+int ptgq_probe_stream(const void *x, int64_t n, uint8_t *q, void *stream)
+{
+    constexpr int64_t kTask = 2 * kSlab;   // elements per wave
+    if (n < 0 || n % kTask != 0) return PTGQ_EINVAL;
+    if (n == 0) return PTGQ_OK;
+    if (!x || !q) return PTGQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(q, 16)) return PTGQ_EALIGN;
+    const int64_t tasks = n / kTask;
+    if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+    if (current_cus(nullptr) <= 0) return PTGQ_EDEVICE;
+    // the plain quantization kernel's uncapped geometry: four-wave blocks,
+    // one wave per task, XCD chunks of 64 blocks for large grids
+    const int64_t blocks = (tasks + 3) / 4;
+    const int32_t chunk = blocks >= 4 * 8 * kXcdChunk ? (int32_t)kXcdChunk : 0;
+    const hipError_t err = launch_probe_stream(x, n, q, (unsigned)blocks, chunk,
+                                               static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
+}
+
+int ptgq_diag_fastdiv(uint32_t d, const uint32_t *n, uint32_t *q, int64_t count)
+{
+    if (d == 0 || count < 0 || (count > 0 && (!n || !q))) return PTGQ_EINVAL;
+    const FastDiv f = make_fastdiv(d);
+    for (int64_t i = 0; i < count; ++i) {
+        if (n[i] >= (1u << 31)) return PTGQ_EINVAL;
+        q[i] = fastdiv(n[i], f);
+    }
+    return PTGQ_OK;
 }
 
 int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, int group_size,
                     int fuse_silu_mul, int64_t expected_m, int64_t q_rows, int cus, int64_t *out)
 {
     if (!out || cus < 1) return PTGQ_EINVAL;
-    for (int i = 0; i < 8; ++i) out[i] = 0;
+    for (int i = 0; i < kPlanFields; ++i) out[i] = 0;
     if (in_dtype != PTGQ_BF16 && in_dtype != PTGQ_FP16 && in_dtype != PTGQ_FP32)
         return PTGQ_EINVAL;
     if (!valid_group_size(group_size) || E < 0 || rows < 0 || K < 0 || K % group_size != 0)
@@ -667,7 +819,7 @@ int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, int group_
     GroupGeom geo;
     const int rc = plan_group(a, geo, in_dtype, rows, K, group_size, fuse_silu_mul,
                               PTGQ_SCALE_UE8M0, PTGQ_COL_MAJOR, masked, E, expected_m,
-                              masked ? rows : q_rows, cus);
+                              masked ? rows : q_rows, true, cus);
     if (rc != PTGQ_OK) return rc;
     out[0] = geo.grid;
     out[1] = (int64_t)geo.wpb * 64;
@@ -677,6 +829,7 @@ int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, int group_
     out[5] = a.xcd_chunk;
     out[6] = geo.table ? 1 : 0;
     out[7] = geo.uncapped ? 1 : 0;
+    out[8] = a.flat_slabs;
     return PTGQ_OK;
 }
 

@@ -21,6 +21,33 @@ constexpr int kMaxSlabsPerTask = 2;
 // Masked calls keep a prefix sum of E ints in LDS.
 constexpr int kMaxExperts = 4096;
 
+// Exact unsigned division by a divisor fixed on the host (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// with l = ceil(log2 d) and mul = floor(2^32 (2^l - d) / d) + 1,
+// floor(n / d) = (mulhi(mul, n) + n) >> l for every n < 2^31 (the sum then
+// fits in 32 bits).  Used for wave-uniform task indices, so the device does it
+// with three scalar instructions.
+struct FastDiv {
+    uint32_t mul;
+    uint32_t shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while (l < 32 && ((uint64_t)1 << l) < d) ++l;
+    FastDiv f;
+    f.mul = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+    f.shift = l;
+    return f;
+}
+
+__host__ __device__ inline uint32_t fastdiv(uint32_t n, FastDiv f)
+{
+    const uint32_t hi = (uint32_t)(((uint64_t)n * f.mul) >> 32);
+    return (hi + n) >> f.shift;
+}
+
 // Arguments of the group-quantization kernels (flat and masked).  All shape
 // scalars are computed on the host; the device only indexes.
 struct GroupArgs {
@@ -49,6 +76,11 @@ struct GroupArgs {
     int64_t q_pad_bytes;      // flat: bytes of q past row M written as zero
     int32_t xcd_chunk;        // flat: blocks per XCD chunk of the block -> task
                               // mapping; 0 = one contiguous range per XCD
+    int32_t flat_slabs;       // flat, unfused, K % kSlab == 0: task t is slabs
+                              // U*t .. U*t+U-1 of the whole [M, K] tensor taken
+                              // as one sequence of slabs (tasks cross row ends)
+    int64_t n_slabs;          // flat_slabs: rows * spr
+    FastDiv spr_div;          // flat_slabs: division by spr
 };
 
 // Arguments of the whole-row per-token kernels.
@@ -128,5 +160,10 @@ hipError_t launch_dequant(const DequantArgs &a, int code_dtype, int scale_fmt, i
 hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_t stream);
 hipError_t launch_probe_silu(const void *g, const void *u, int in_dtype, int path, float *out,
                              int64_t n, hipStream_t stream);
+hipError_t launch_probe_scale(uint32_t first, int64_t n, float eps, int out_dtype, int scale_fmt,
+                              void *scale_out, float *inv_out, hipStream_t stream);
+hipError_t launch_probe_int8(uint32_t first, int64_t n, int8_t *out, hipStream_t stream);
+hipError_t launch_probe_stream(const void *x, int64_t n, uint8_t *q, unsigned grid,
+                               int32_t xcd_chunk, hipStream_t stream);
 
 }  // namespace ptgq

@@ -213,6 +213,27 @@ __device__ __forceinline__ Scale group_scale(uint32_t amax_bits, uint32_t eps_bi
     return sc;
 }
 
+// v = y * inv, one fp32 rounding per element, except that a zero y keeps its
+// value (and sign) when inv is infinite.  fl(1/r) overflows for a scale r
+// below about 2^-128 (an fp32 scale with no floor, or one under ~1.3e-36):
+// the quotient y / r of a zero is then still zero, where the product 0 * inf
+// would be NaN; every other y times inf saturates when narrowed.  A finite
+// multiplier already gives y * inv == y for a zero y, so the fix-up runs only
+// when some lane of the wave holds an infinite multiplier (a scalar branch).
+// MAYBE_INF false: the caller knows inv is finite (UE8M0 multipliers).
+template <bool MAYBE_INF, int N>
+__device__ __forceinline__ void scale_by(const float (&y)[N], float inv, float (&v)[N])
+{
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = y[k] * inv;
+    if constexpr (MAYBE_INF) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(inv == __builtin_inff()) != 0, 0)) {
+#pragma unroll
+            for (int k = 0; k < N; ++k) v[k] = (y[k] == 0.0f) ? y[k] : v[k];
+        }
+    }
+}
+
 // --------------------------------------------------------------------------
 // Narrowing.
 // --------------------------------------------------------------------------
@@ -407,13 +428,20 @@ struct TaskBuf {
     u32x4 u[UMAX];
 };
 
-// Where a task lives: its row of input and codes, the scale tensor its row
-// belongs to (flat: the whole tensor; masked: the expert's), the row index in
-// that scale tensor, and the task index within the row.
+// Where a task lives.  Its slabs are consecutive in memory: `x` and `q` point
+// at the input (gate half when fused) and codes of its first slab, and
+// `codes` is the number of code bytes (elements) from q on that belong to
+// the task (fewer than UMAX slabs at the end of a row, or of the tensor for
+// flat-slab tasks); loads and stores past it are dropped by the buffer range
+// check.  `sbase` is the scale tensor of the rows (flat: the whole tensor;
+// masked: the expert's); `m` and `j` are the row and the slab index within
+// that row of the first slab.  Row tasks keep all their slabs in row m;
+// flat-slab tasks move on to row m + 1 when a slab index reaches spr.
 struct TaskLoc {
-    const char *xrow;
-    uint8_t *qrow;
+    const char *x;
+    uint8_t *q;
     uint8_t *sbase;
+    uint32_t codes;
     int64_t m;
     int j;
 };
@@ -427,12 +455,12 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
 {
     constexpr int ES = IN == IN_FP32 ? 4 : 2;   // input element bytes
     constexpr int pol = kStreamPolicy;
-    const uint32_t row_bytes = live ? (uint32_t)(a.K * ES) : 0u;
-    const rsrc_t rg = make_rsrc(t.xrow, row_bytes);
+    const uint32_t bytes = live ? t.codes * ES : 0u;
+    const rsrc_t rg = make_rsrc(t.x, bytes);
     // 16-bit: lane l holds elements 8l..8l+7 of a slab; fp32: 4l..4l+3 (g)
     // and 256+4l..256+4l+3 (gh), so every load instruction reads one
     // contiguous KiB
-    const uint32_t off = (uint32_t)t.j * (UMAX * kSlab * ES) + (uint32_t)lane * 16;
+    const uint32_t off = (uint32_t)lane * 16;
 #pragma unroll
     for (int s = 0; s < UMAX; ++s) {
         b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES, 0, pol);
@@ -441,7 +469,7 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
     }
     if constexpr (FUSE) {
         static_assert(IN != IN_FP32, "fused calls take 16-bit inputs");
-        const rsrc_t ru = make_rsrc(t.xrow + a.K * ES, row_bytes);
+        const rsrc_t ru = make_rsrc(t.x + a.K * ES, bytes);
 #pragma unroll
         for (int s = 0; s < UMAX; ++s)
             b.u[s] = __builtin_amdgcn_raw_buffer_load_b128(ru, off + s * kSlab * 2, 0, pol);
@@ -456,18 +484,21 @@ __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y,
 // Codes are stored 4 bytes per lane and half (each store instruction writes
 // 256 contiguous bytes; stores past the row are dropped); scales go to the
 // layout's slots like those of the 16-bit path.
+// `slab`: index of the slab within row m; `at`: offset of the slab's first
+// code from the task's codes, `codes`: the task's code count.
 template <int G, int OUT, int SF, int SPOL>
 __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x4 &ga,
-                                                  const u32x4 &gb, int slab, rsrc_t rq,
-                                                  uint8_t *se, int64_t m, int lane)
+                                                  const u32x4 &gb, int slab, uint32_t at,
+                                                  uint32_t codes, rsrc_t rq, uint8_t *se,
+                                                  int64_t m, int lane)
 {
     constexpr int LA = G / 4;           // lanes per group within a half (4..32)
     constexpr int GPH = 256 / G;        // groups per half (2..16)
     constexpr int GPS = kSlab / G;      // groups per slab
     constexpr bool ue8m0 = SF == SCALE_UE8M0;
-    const uint32_t colA = (uint32_t)slab * kSlab + (uint32_t)lane * 4;
+    const uint32_t colA = at + (uint32_t)lane * 4;     // offsets within the task
     const uint32_t colB = colA + 256;
-    const bool validA = (int64_t)colA < a.K, validB = (int64_t)colB < a.K;
+    const bool validA = colA < codes, validB = colB < codes;
     const float ya[4] = {__uint_as_float(ga.x), __uint_as_float(ga.y), __uint_as_float(ga.z),
                          __uint_as_float(ga.w)};
     const float yb[4] = {__uint_as_float(gb.x), __uint_as_float(gb.y), __uint_as_float(gb.z),
@@ -477,11 +508,8 @@ __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x
     const Scale sA = group_scale<OUT>(amA, __float_as_uint(a.eps), ue8m0);
     const Scale sB = group_scale<OUT>(amB, __float_as_uint(a.eps), ue8m0);
     float va[4], vb[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        va[k] = ya[k] * sA.inv;
-        vb[k] = yb[k] * sB.inv;
-    }
+    scale_by<!ue8m0>(ya, sA.inv, va);
+    scale_by<!ue8m0>(yb, sB.inv, vb);
     __builtin_amdgcn_raw_buffer_store_b32(narrow4<OUT, !ue8m0>(va), rq, colA, 0, SPOL);
     __builtin_amdgcn_raw_buffer_store_b32(narrow4<OUT, !ue8m0>(vb), rq, colB, 0, SPOL);
 
@@ -508,7 +536,8 @@ __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x
                         word |= bi << (8 * i);
                     }
                     const int64_t gw = g0 + 4 * w;
-                    if (lane == 0 && gw < a.ng) words[(gw >> 2) * a.rows_pad + m] = word;
+                    if (lane == 0 && at < codes && gw < a.ng)
+                        words[(gw >> 2) * a.rows_pad + m] = word;
                 }
             } else {
                 // G <= 32: each word's 4 groups lie in one half
@@ -541,25 +570,36 @@ __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x
     }
 }
 
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL,
+          bool FS = false>
 __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &t, int lane,
                                              const TaskBuf<UMAX> &b, const float *tab)
 {
     constexpr int LPG = G / 8;          // lanes per group
     constexpr int GPS = kSlab / G;      // groups per slab (>= 4)
-    const rsrc_t rq = make_rsrc(t.qrow, (uint32_t)a.K);
+    const rsrc_t rq = make_rsrc(t.q, t.codes);
     uint8_t *se = t.sbase;
-    const int64_t m = t.m;
     constexpr bool ue8m0 = SF == SCALE_UE8M0;
 #pragma unroll
     for (int s = 0; s < UMAX; ++s) {
-        const int slab = t.j * UMAX + s;                            // slab within row
+        // row and slab-within-row of slab s; flat-slab tasks cross into the
+        // next row (whole slabs only: K is a multiple of the slab)
+        int slab = t.j + s;
+        int64_t m = t.m;
+        if constexpr (FS) {
+            if (slab >= a.spr) {
+                slab -= a.spr;
+                m += 1;
+            }
+        }
+        const uint32_t at = (uint32_t)s * kSlab;                    // offset in the task
         if constexpr (IN == IN_FP32) {
-            process_slab_fp32<G, OUT, SF, SPOL>(a, b.g[s], b.gh[s], slab, rq, se, m, lane);
+            process_slab_fp32<G, OUT, SF, SPOL>(a, b.g[s], b.gh[s], slab, at, t.codes, rq, se,
+                                                m, lane);
             continue;
         }
-        const uint32_t col = (uint32_t)slab * kSlab + (uint32_t)lane * 8;
-        const bool valid = (int64_t)col < a.K;
+        const uint32_t col = at + (uint32_t)lane * 8;
+        const bool valid = col < t.codes;
         float y[8];
         if constexpr (FUSE && TABLE) {
             const u32x4 w = b.g[s];
@@ -604,13 +644,12 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
 
         const Scale sc = group_scale<OUT>(amax, __float_as_uint(a.eps), ue8m0);
         float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = y[k] * sc.inv;
+        scale_by<!ue8m0>(y, sc.inv, v);
         const uint2 codes = narrow8<OUT, !ue8m0>(v);
         u32x2 c2;
         c2.x = codes.x;
         c2.y = codes.y;
-        __builtin_amdgcn_raw_buffer_store_b64(c2, rq, col, 0, SPOL);  // dropped past the row
+        __builtin_amdgcn_raw_buffer_store_b64(c2, rq, col, 0, SPOL);  // dropped past the task
 
         // scales of the slab's groups
         const int lg = lane / LPG;                                  // group within slab
@@ -629,7 +668,7 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
                         ((uint32_t)__builtin_amdgcn_readlane((int)byte, (4 * w + 2) * LPG) << 16) |
                         ((uint32_t)__builtin_amdgcn_readlane((int)byte, (4 * w + 3) * LPG) << 24);
                     const int64_t gw = g0 + 4 * w;
-                    if (lane == 0 && gw < a.ng)
+                    if (lane == 0 && at < t.codes && gw < a.ng)
                         reinterpret_cast<uint32_t *>(se)[(gw >> 2) * a.rows_pad + m] = word;
                 }
             } else {
@@ -654,17 +693,56 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
     }
 }
 
-// Flat schedule: task t is task t % tpr of row t / tpr.
+// A row task: task j of row m (slabs j*U .. j*U+U-1 of the row) whose row
+// starts at xrow (input) and qrow (codes) and whose scales live in sbase.
+template <int IN, int UMAX>
+__device__ __forceinline__ TaskLoc row_task(const GroupArgs &a, const char *xrow, uint8_t *qrow,
+                                            uint8_t *sbase, int64_t m, int j)
+{
+    constexpr int ES = IN == IN_FP32 ? 4 : 2;
+    const int64_t c0 = (int64_t)j * (UMAX * kSlab);     // first column of the task
+    TaskLoc l;
+    l.x = xrow + c0 * ES;
+    l.q = qrow + c0;
+    l.sbase = sbase;
+    l.codes = (uint32_t)(a.K - c0 < UMAX * kSlab ? a.K - c0 : UMAX * kSlab);
+    l.m = m;
+    l.j = j * UMAX;
+    return l;
+}
+
+// Flat schedule, row tasks: task t is task t % tpr of row t / tpr.
+template <int IN, int UMAX>
 struct FlatMap {
     __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int /*lane*/)
     {
         const int m = t / a.tpr;
+        return row_task<IN, UMAX>(a, static_cast<const char *>(a.x) + (int64_t)m * a.in_stride,
+                                  a.q + (int64_t)m * a.K, static_cast<uint8_t *>(a.s), m,
+                                  t - m * a.tpr);
+    }
+};
+
+// Flat schedule, flat-slab tasks (unfused, K a multiple of the slab, so input
+// and codes are one contiguous sequence of whole-row slabs): task t is slabs
+// U*t .. U*t+U-1 of that sequence, crossing row ends; no task is short
+// except the tensor's last one.  The row of slab S is S / spr (a wave-uniform
+// multiply-high division).
+template <int IN, int UMAX>
+struct FlatSlabMap {
+    __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int /*lane*/)
+    {
+        constexpr int ES = IN == IN_FP32 ? 4 : 2;
+        const uint32_t S = (uint32_t)t * UMAX;                      // first slab (< 2^31)
+        const uint32_t m = fastdiv(S, a.spr_div);
+        const int64_t left = a.n_slabs - S;                          // >= 1 for live tasks
         TaskLoc l;
-        l.xrow = static_cast<const char *>(a.x) + (int64_t)m * a.in_stride;
-        l.qrow = a.q + (int64_t)m * a.K;
+        l.x = static_cast<const char *>(a.x) + (int64_t)S * (kSlab * ES);
+        l.q = a.q + (int64_t)S * kSlab;
         l.sbase = static_cast<uint8_t *>(a.s);
+        l.codes = (uint32_t)(left < UMAX ? left : UMAX) * kSlab;
         l.m = m;
-        l.j = t - m * a.tpr;
+        l.j = (int)(S - m * (uint32_t)a.spr);
         return l;
     }
 };
@@ -763,18 +841,16 @@ __device__ __forceinline__ int live_rows_of_lane(const int32_t *masked_m, int E,
 }
 
 // Row r of expert e, task j of the row.
+template <int IN, int UMAX>
 __device__ __forceinline__ TaskLoc masked_loc(const GroupArgs &a, int e, int r, int j)
 {
-    TaskLoc l;
-    l.xrow = static_cast<const char *>(a.x) + (int64_t)e * a.x_expert_stride +
-             (int64_t)r * a.in_stride;
-    l.qrow = a.q + (int64_t)e * a.q_expert_stride + (int64_t)r * a.K;
-    l.sbase = static_cast<uint8_t *>(a.s) + (int64_t)e * a.s_expert_stride;
-    l.m = r;
-    l.j = j;
-    return l;
+    return row_task<IN, UMAX>(
+        a, static_cast<const char *>(a.x) + (int64_t)e * a.x_expert_stride + (int64_t)r * a.in_stride,
+        a.q + (int64_t)e * a.q_expert_stride + (int64_t)r * a.K,
+        static_cast<uint8_t *>(a.s) + (int64_t)e * a.s_expert_stride, r, j);
 }
 
+template <int IN, int UMAX>
 struct MaskedMap {
     MaskedRows rows;
 
@@ -786,7 +862,7 @@ struct MaskedMap {
         const int R = t / a.tpr;
         int e, r;
         rows.locate(R, lane, e, r);
-        return masked_loc(a, e, r, t - R * a.tpr);
+        return masked_loc<IN, UMAX>(a, e, r, t - R * a.tpr);
     }
 };
 // The SiLU table staged into LDS in two steps, so that its global loads can
@@ -827,7 +903,7 @@ __device__ __forceinline__ void table_store(const TableRegs &r, float *tab)
 // are already in flight in `cur` (location lcur); `spare` is free.  Two tasks
 // are in flight at a time.  A task index past n is clamped for address
 // arithmetic and loaded over an empty range.
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL,
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL, bool FS,
           class Map>
 __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int t, TaskLoc lcur,
                                                TaskBuf<UMAX> &cur, TaskBuf<UMAX> &spare, int n,
@@ -838,14 +914,14 @@ __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int
         const bool hasB = tB < n;
         const TaskLoc lB = map(a, hasB ? tB : t, lane);
         load_task<IN, FUSE, UMAX>(a, lB, lane, hasB, spare);
-        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL>(a, lcur, lane, cur, tab);
+        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL, FS>(a, lcur, lane, cur, tab);
         if (!hasB) break;
         t = tB;
         const int tA = t + stride;
         const bool hasA = tA < n;
         lcur = map(a, hasA ? tA : t, lane);
         load_task<IN, FUSE, UMAX>(a, lcur, lane, hasA, cur);
-        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL>(a, lB, lane, spare, tab);
+        process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL, FS>(a, lB, lane, spare, tab);
         if (!hasA) break;
         t = tA;
     }
@@ -856,7 +932,7 @@ __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int
 // store the table into LDS (every wave of the block reaches that barrier,
 // with or without a task), so the table copy overlaps the first HBM reads.
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL,
-          bool STAGE, bool FETCHED = false, class Map>
+          bool STAGE, bool FETCHED = false, bool FS = false, class Map>
 __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
                                           int stride, int lane, float *tab,
                                           TableRegs tr = TableRegs{})
@@ -868,8 +944,8 @@ __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first
     load_task<IN, FUSE, UMAX>(a, lA, lane, hasA0, A);
     if constexpr (STAGE) table_store<TABLE>(tr, tab);
     if (!hasA0) return;
-    continue_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL>(a, map, first, lA, A, B, n, stride, lane,
-                                                      tab);
+    continue_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL, FS>(a, map, first, lA, A, B, n, stride,
+                                                            lane, tab);
 }
 
 // XCD-aware logical block id.  Blocks are dealt to the 8 XCDs round-robin
@@ -891,7 +967,8 @@ __device__ __forceinline__ int logical_block(int b, int nb, int chunk = 0)
     return (b - r) + (r & 7) * chunk + (r >> 3);
 }
 
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
+// FS: flat-slab tasks (FlatSlabMap) instead of row tasks (FlatMap).
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, bool FS>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs a)
 {
     __shared__ float tab[TABLE ? kSiluTab : 1];
@@ -900,9 +977,14 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     const int wpb = blockDim.x >> 6;
     const int lb = logical_block(blockIdx.x, gridDim.x, a.xcd_chunk);
     constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
-    run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true>(a, FlatMap{}, lb * wpb + wib,
-                                                             a.n_tasks, gridDim.x * wpb, lane,
-                                                             tab);
+    if constexpr (FS) {
+        static_assert(!FUSE && !TABLE, "flat-slab tasks: unfused inputs");
+        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true, false, true>(
+            a, FlatSlabMap<IN, UMAX>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
+    } else {
+        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true>(
+            a, FlatMap<IN, UMAX>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
+    }
     // code rows past M (a padded q buffer) are zero: 16 bytes per lane,
     // grid-strided over all waves
     if (a.q_pad_bytes > 0) {
@@ -955,7 +1037,8 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
         const int win = wave_inclusive_sum(live, lane);
         const int n = __builtin_amdgcn_readlane(win, E - 1) * a.tpr;
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, true, true>(
-            a, MaskedMap(win, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab, tr);
+            a, MaskedMap<IN, UMAX>(win, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab,
+            tr);
         return;
     }
     // More experts: the table's loads, then the prefix sum of masked_m into
@@ -968,7 +1051,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
     const int n = scan[E - 1] * a.tpr;
     if (lb * wpb >= n) return;                    // block-uniform: nothing to do
     run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, false>(
-        a, MaskedMap(scan, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab);
+        a, MaskedMap<IN, UMAX>(scan, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab);
 }
 
 // --------------------------------------------------------------------------
@@ -1093,11 +1176,10 @@ __global__ __launch_bounds__(256) void ptq_wave_kernel(TokenArgs a)
     for (int k = 0; k < NV; ++k) {
         const int i = lane + 64 * k;
         if (i < a.nv) {
-            float f[EV];
+            float f[EV], v[EV];
             TV::widen(raw[k], f);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) f[e] = f[e] * inv;
-            TV::store_codes(qr + (int64_t)i * EV, f);
+            scale_by<true>(f, inv, v);
+            TV::store_codes(qr + (int64_t)i * EV, v);
         }
     }
 }
@@ -1151,10 +1233,9 @@ __global__ __launch_bounds__(256) void ptq_wave_loop_kernel(TokenArgs a)
         const rsrc_t rq = make_rsrc(a.q + row * a.K, (uint32_t)a.K);
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
-            float f[EV];
-            TV::widen(r[k], f);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) f[e] = f[e] * inv;
+            float y[EV], f[EV];
+            TV::widen(r[k], y);
+            scale_by<true>(y, inv, f);
             const uint32_t off = (uint32_t)(lane + 64 * k) * EV;
             if constexpr (EV == 8) {
                 u32x2 o;
@@ -1227,11 +1308,10 @@ __global__ __launch_bounds__(256) void ptq_block_kernel(TokenArgs a)
     for (int k = 0; k < NV; ++k) {
         const int i = tid + nt * k;
         if (i < a.nv) {
-            float f[EV];
+            float f[EV], v[EV];
             TV::widen(raw[k], f);
-#pragma unroll
-            for (int e = 0; e < EV; ++e) f[e] = f[e] * inv;
-            TV::store_codes(qr + (int64_t)i * EV, f);
+            scale_by<true>(f, inv, v);
+            TV::store_codes(qr + (int64_t)i * EV, v);
         }
     }
 }
@@ -1255,11 +1335,10 @@ __global__ __launch_bounds__(256) void ptq_block_loop_kernel(TokenArgs a)
     const float inv = token_inv(__uint_as_float(block_max_bits(amax, red)), r);
     if (tid == 0) a.s[m] = r;
     for (int i = tid; i < a.nv; i += 256) {
-        float f[EV];
+        float f[EV], v[EV];
         TV::widen(TV::load(xr + (int64_t)i * VB), f);
-#pragma unroll
-        for (int e = 0; e < EV; ++e) f[e] = f[e] * inv;
-        TV::store_codes(qr + (int64_t)i * EV, f);
+        scale_by<true>(f, inv, v);
+        TV::store_codes(qr + (int64_t)i * EV, v);
     }
 }
 
@@ -1417,10 +1496,11 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
             uint32_t oo[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float f[4];
+                float f[4], h[4];
                 decode4_e4m3(ww[i], f);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) f[j] = (f[j] * b.s[k]) * inv;
+                for (int j = 0; j < 4; ++j) h[j] = f[j] * b.s[k];
+                scale_by<true>(h, inv, f);
                 oo[i] = e4m3x4<true>(f[0], f[1], f[2], f[3]);
             }
             o.x = oo[0];
@@ -1692,6 +1772,66 @@ __global__ __launch_bounds__(256) void probe_e4m3_kernel(const float *__restrict
     if (i < n) out[i] = (uint8_t)(e4m3x4<true>(v[i], 0.0f, 0.0f, 0.0f) & 0xFFu);
 }
 
+// The scale step alone: amax = the fp32 with bit pattern first + i (a
+// non-negative finite value), the group_scale of the quantization kernels.
+template <int OUT, bool UE>
+__global__ __launch_bounds__(256) void probe_scale_kernel(uint32_t first, int64_t n,
+                                                          uint32_t eps_bits, void *scale_out,
+                                                          float *inv_out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const Scale sc = group_scale<OUT>(first + (uint32_t)i, eps_bits, UE);
+        if constexpr (UE)
+            static_cast<uint8_t *>(scale_out)[i] = (uint8_t)sc.e;
+        else
+            static_cast<float *>(scale_out)[i] = sc.r;
+        if (inv_out) inv_out[i] = sc.inv;
+    }
+}
+
+// The int8 narrowing alone, over the fp32 values with bit patterns first + i
+// (mod 2^32): the int8x4 of the quantization kernels.
+__global__ __launch_bounds__(256) void probe_int8_kernel(uint32_t first, int64_t n,
+                                                         int8_t *__restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const float v = __uint_as_float(first + (uint32_t)i);
+        out[i] = (int8_t)(uint8_t)(int8x4(v, 0.0f, 0.0f, 0.0f) & 0xFFu);
+    }
+}
+
+// A stream with the plain quantization kernel's traffic and geometry and no
+// arithmetic: each wave reads two 512-element slabs of 16-bit elements (two
+// contiguous KiB per load instruction pair) and writes one byte per element
+// (its low byte), 8 bytes per lane per slab; one wave per task, blocks dealt
+// to the XCDs in chunks.  What it reaches is what the memory system gives
+// this 2:1 read/write mix.
+__global__ __launch_bounds__(256) void probe_stream_kernel(const uint16_t *x, int64_t n,
+                                                           uint8_t *q, int32_t xcd_chunk)
+{
+    const int lane = threadIdx.x & 63;
+    const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wpb = blockDim.x >> 6;
+    const int64_t t = (int64_t)logical_block(blockIdx.x, gridDim.x, xcd_chunk) * wpb + wib;
+    if (t * (2 * kSlab) >= n) return;                        // wave-uniform
+    const rsrc_t rx = make_rsrc(x + t * (2 * kSlab), 2 * kSlab * 2);
+    const rsrc_t rq = make_rsrc(q + t * (2 * kSlab), 2 * kSlab);
+    u32x4 v[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        v[s] = __builtin_amdgcn_raw_buffer_load_b128(rx, s * kSlab * 2 + lane * 16, 0,
+                                                     kStreamPolicy);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        u32x2 o;
+        o.x = __builtin_amdgcn_perm(v[s].y, v[s].x, 0x06040200u);
+        o.y = __builtin_amdgcn_perm(v[s].w, v[s].z, 0x06040200u);
+        __builtin_amdgcn_raw_buffer_store_b64(o, rq, s * kSlab + lane * 8, 0, kStreamPolicy);
+    }
+}
+
 // path 0: direct evaluation; path 1: the bf16 lookup (global-memory copy of
 // the table the fused kernels stage in LDS).
 template <int IN>
@@ -1752,8 +1892,15 @@ static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid,
     if (masked)
         ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE>
             <<<grid, block, (size_t)a.num_experts * sizeof(int), st>>>(a);
-    else
-        ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE><<<grid, block, 0, st>>>(a);
+    else if constexpr (!FUSE && !TABLE && UMAX == 2) {
+        if (a.flat_slabs)
+            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, true><<<grid, block, 0, st>>>(a);
+        else
+            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, false><<<grid, block, 0, st>>>(a);
+    } else {
+        if (a.flat_slabs) return hipErrorInvalidValue;
+        ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, false><<<grid, block, 0, st>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -1937,6 +2084,36 @@ hipError_t launch_probe_e4m3(const float *v, uint8_t *out, int64_t n, hipStream_
 {
     const unsigned grid = (unsigned)((n + 255) / 256);
     probe_e4m3_kernel<<<grid, 256, 0, stream>>>(v, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_scale(uint32_t first, int64_t n, float eps, int out_dtype, int scale_fmt,
+                              void *scale_out, float *inv_out, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    const uint32_t eb = __builtin_bit_cast(uint32_t, eps);
+    const bool ue = scale_fmt == SCALE_UE8M0;
+    if (out_dtype == OUT_E4M3) {
+        if (ue) probe_scale_kernel<OUT_E4M3, true><<<grid, 256, 0, stream>>>(first, n, eb, scale_out, inv_out);
+        else probe_scale_kernel<OUT_E4M3, false><<<grid, 256, 0, stream>>>(first, n, eb, scale_out, inv_out);
+    } else {
+        if (ue) probe_scale_kernel<OUT_INT8, true><<<grid, 256, 0, stream>>>(first, n, eb, scale_out, inv_out);
+        else probe_scale_kernel<OUT_INT8, false><<<grid, 256, 0, stream>>>(first, n, eb, scale_out, inv_out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_int8(uint32_t first, int64_t n, int8_t *out, hipStream_t stream)
+{
+    probe_int8_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(first, n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_stream(const void *x, int64_t n, uint8_t *q, unsigned grid,
+                               int32_t xcd_chunk, hipStream_t stream)
+{
+    probe_stream_kernel<<<grid, 256, 0, stream>>>(static_cast<const uint16_t *>(x), n, q,
+                                                  xcd_chunk);
     return hipGetLastError();
 }
 

@@ -30,10 +30,14 @@
  *     place.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous on that stream and never synchronize the host, so they may
- *     be captured into a HIP graph.  The first call on a device (or ptgq_init)
- *     queries the device's compute-unit count and builds the device's SiLU
- *     lookup table (one small kernel and one host synchronization, never
- *     repeated); no other host work happens.
+ *     be captured into a HIP graph, the first call on a device included.  The
+ *     fused bf16 calls large enough to read the SiLU lookup table build it
+ *     on their own stream the first time (one small kernel, stream-ordered;
+ *     other streams then wait for it on the device); a call captured before
+ *     the table exists evaluates SiLU directly instead (same results, slower).
+ *     ptgq_init does that set-up ahead of time.
+ *   - The library's only device memory of its own is that table; no entry
+ *     point allocates or frees memory.
  *   - Arguments are validated on the host before anything is launched.  A
  *     negative return value means nothing was launched and nothing written.
  *   - Sizes are int64.  A call with zero rows (M == 0, E == 0, or K == 0)
@@ -41,6 +45,12 @@
  *   - Inputs must not alias outputs.  Concurrent calls writing the same
  *     outputs race, as any two kernels would.
  *   - NaN or infinite inputs give unspecified (but in-bounds) outputs.
+ *   - When the fp32 multiplier 1 / r overflows to +inf (a scale r below about
+ *     2^-128: per-token rows, or fp32 group scales with a floor eps, whose
+ *     largest magnitude is below ~1.3e-36), a zero element gives the zero code
+ *     of its sign and every other element saturates; the same holds for a
+ *     zero product in ptgq_requant_fp8.  (The pages leave this corner open;
+ *     the quotient y / r of a zero is zero.)
  *
  * Scale tensor layouts (ng = K / G groups per row, rows_pad = ceil(rows/4)*4):
  *   PTGQ_ROW_MAJOR + PTGQ_SCALE_F32    float   [rows][ng]
@@ -171,6 +181,9 @@ PTGQ_API int ptgq_quant_masked(const void *x, int in_dtype, int64_t E, int64_t t
  *       row-major contiguous; 16-byte aligned.  K % 4 == 0.
  *   q   device uint8 [M, K] e4m3 codes; 16-byte aligned.
  *   s   device float [M]; 4-byte aligned.
+ *   q and s may be the first M rows of longer buffers (serving code pads its
+ *   outputs): only rows 0 .. M-1 are written (sglang #34257 review page, key
+ *   source snippets, the host contract on output rows).
  * Sources: sglang #34257 review page, key source snippets (warp kernel and
  * its dispatch by token count), implementation breakdown (hidden % 4 == 0).
  * Errors: PTGQ_EINVAL (M < 0, K < 0, K % 4, bad dtype, NULL pointer),
@@ -255,78 +268,15 @@ PTGQ_API size_t ptgq_scale_bytes(int64_t rows, int64_t K, int group_size, int sc
 PTGQ_API const char *ptgq_status_string(int status);
 
 /*
- * ptgq_init - optional: make `device` (a HIP ordinal) ready now rather than
- * at the first call on it: query its compute-unit count and build its SiLU
- * lookup table (this synchronizes the device once).  Calls that are captured
- * into a HIP graph must follow one ptgq_init (or one ordinary call) on their
- * device.  Returns PTGQ_OK or PTGQ_EDEVICE.
+ * ptgq_init - optional: make `device` (a HIP ordinal) ready now: query its
+ * compute-unit count and build its SiLU lookup table on the default stream,
+ * then wait on the host until the build has finished (the one call of the
+ * library that blocks the host; not to be called while a stream captures).
+ * Calls captured into a HIP graph after it use the table.  A failed
+ * initialization is not remembered: a later call tries again.  Returns
+ * PTGQ_OK or PTGQ_EDEVICE.
  */
 PTGQ_API int ptgq_init(int device);
-
-/*
- * Single-step device probes, for checking the device arithmetic against
- * a reference over whole input spaces.  They run exactly the device code the
- * quantization kernels use for that step.
- *
- * ptgq_probe_e4m3: out[i] = e4m3 code of v[i] (round-to-nearest-even,
- *   saturated to +-448, signed zero kept).  v device float [n], out device
- *   uint8 [n]; both 4-byte aligned.
- * ptgq_probe_silu_mul: out[i] = silu(g[i]) * u[i] in fp32, where g, u are
- *   device arrays of in_dtype (PTGQ_BF16 or PTGQ_FP16) bit patterns [n]
- *   and out is device float [n].  path 0: the direct evaluation (e^-g in
- *   double precision rounded to fp32, then fp32 add, divide, multiply);
- *   path 1 (bf16 only): the lookup of g / (1 + e^-g) that large fused calls
- *   use, followed by the multiply.
- * Errors: PTGQ_EINVAL (n < 0, NULL pointer, bad dtype or path), PTGQ_ELAUNCH,
- * PTGQ_EDEVICE.
- */
-PTGQ_API int ptgq_probe_e4m3(const float *v, uint8_t *out, int64_t n, void *stream);
-PTGQ_API int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int path,
-                                 float *out, int64_t n, void *stream);
-
-/*
- * ptgq_plan_group - diagnostics and tests of the launch-geometry chooser:
- * the launch a ptgq_quant / ptgq_quant_padded call (E = 0; q_rows = rows of
- * the code buffer, >= rows) or a ptgq_quant_masked call (E >= 1 experts of
- * rows = tokens_pad rows, sized for expected_m) would make on a device of
- * `cus` compute units.  Tiny calls spread one-slab tasks over the compute
- * units; large ones use two-slab tasks and, for plain 16-bit input, a grid of
- * one wave per task dealt to the XCDs in chunks (the pages size their launch
- * by token count the same way: the sglang #34257 review page, key source
- * snippets, dispatch; `expected_m` of the sglang #30924 review page,
- * implementation breakdown).  Makes no HIP call and touches no device;
- * honours the ptgq_set_tuning overrides.
- *   out: host array of 8, written with: blocks in the grid, threads per
- *        block, slabs (512 consecutive elements of a row) per task, tasks per
- *        row, tasks in all (masked: the expected ones), blocks per XCD chunk
- *        of the block -> task mapping (0: one contiguous range per XCD),
- *        SiLU lookup table (0/1), uncapped grid (0/1); all zero when nothing
- *        would be launched.
- * Returns PTGQ_OK, PTGQ_EINVAL (invalid shape, cus < 1, out NULL) or
- * PTGQ_EUNSUPPORTED, as the calls would for the same shape.
- */
-PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, int group_size,
-                             int fuse_silu_mul, int64_t expected_m, int64_t q_rows, int cus,
-                             int64_t *out);
-
-/*
- * ptgq_set_tuning - diagnostics only: override one decision of the launch
- * geometry chooser for the whole process (value -1 restores the automatic
- * choice).  Knobs: 0 slabs per task (quantization: 1 or 2, one slab = 512
- * elements of a row; dequantization: 1 or 4 sub-slabs), 1 waves per block
- * (1..4; not the fused SiLU-table kernels, which always run 16), 2 resident
- * blocks per compute unit (grid cap), 3 per-token mode (0 one wave per row,
- * 1 one block per row, 2 two-pass block, 3 persistent waves walking the
- * rows), 4 fused bf16 SiLU path (0 direct evaluation, 1 LDS lookup table), 5
- * blocks per XCD chunk of the flat quantization and dequantization kernels'
- * block-to-task mappings (0 one contiguous range per XCD), 6 grid of the flat
- * quantization and
- * requantization kernels (0 capped: resident blocks loop over the tasks; 1
- * uncapped: one wave per task).
- * Results never depend on these; only speed does.  Not synchronized
- * with calls running on other host threads.  Returns PTGQ_OK or PTGQ_EINVAL.
- */
-PTGQ_API int ptgq_set_tuning(int knob, int64_t value);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,7 @@
-"""CPU checks of the C ABI: the library loads, exports every function that
-include/ptgq.h declares, and rejects invalid arguments on the host (no device
-is touched, nothing is launched)."""
+"""CPU checks of the C ABI: the library loads, exports exactly the functions
+that include/ptgq.h (the quantization interface) and include/ptgq_diag.h
+(diagnostics) declare, and rejects invalid arguments on the host (no device is
+touched, nothing is launched)."""
 import ctypes
 import os
 import re
@@ -22,23 +23,48 @@ def lib():
     return aq.load_library()
 
 
-def declared_functions():
-    with open(os.path.join(ROOT, "include", "ptgq.h")) as fh:
+def declared_functions(header="ptgq.h"):
+    with open(os.path.join(ROOT, "include", header)) as fh:
         text = fh.read()
     return sorted(set(re.findall(r"PTGQ_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
 
 
-def test_header_declares_the_binding_names():
-    assert declared_functions() == sorted(aq.EXPORTS)
+def test_headers_declare_the_binding_names():
+    assert declared_functions("ptgq.h") == sorted(aq.EXPORTS)
+    assert declared_functions("ptgq_diag.h") == sorted(aq.DIAG_EXPORTS)
+    assert not set(aq.EXPORTS) & set(aq.DIAG_EXPORTS)
 
 
 def test_every_declared_symbol_is_exported(lib):
-    for name in declared_functions():
+    both = sorted(declared_functions("ptgq.h") + declared_functions("ptgq_diag.h"))
+    for name in both:
         assert hasattr(lib, name), name
-    # nothing but the C ABI is visible
+    # nothing but the two headers' C ABI is visible
     out = os.popen(f"nm -D --defined-only {aq.LIB_PATH}").read()
     exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
-    assert exported == declared_functions()
+    assert exported == both
+
+
+def test_quantization_header_has_no_diagnostics():
+    """The production header declares the quantization calls only: probes,
+    tuning overrides and the geometry report live in ptgq_diag.h."""
+    names = declared_functions("ptgq.h")
+    assert not [n for n in names if "probe" in n or "tuning" in n or "plan" in n or "diag" in n]
+
+
+def test_fastdiv_matches_integer_division(lib):
+    """The multiply-high division the kernels use for task indices, for every
+    divisor 1..4096 and selected large ones, on numerators spread over
+    [0, 2^31) including every multiple boundary near the top."""
+    rng = np.random.default_rng(1994)
+    for d in list(range(1, 4097)) + [5000, 7 * 512, 65535, 65537, 1 << 20, (1 << 20) + 1,
+                                      (1 << 30) - 1, 1 << 30, (1 << 31) - 1]:
+        n = np.concatenate([rng.integers(0, 1 << 31, 256, dtype=np.int64),
+                            np.arange(0, 64),
+                            (1 << 31) - 1 - np.arange(0, 64),
+                            ((((1 << 31) - 1) // d) * d + np.arange(-2, 1)).clip(0)]).astype(np.uint32)
+        q = aq.ptgq_diag_fastdiv(d, n)
+        assert np.array_equal(q, (n.astype(np.int64) // d).astype(np.uint32)), d
 
 
 def test_status_strings(lib):
@@ -195,6 +221,18 @@ def test_probe_validation(lib):
     assert aq.ptgq_probe_silu_mul(A16, A16, "bf16", 2, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
     with pytest.raises(aq.PtgqError):
         aq.ptgq_set_tuning(9, 1)
+    assert aq.ptgq_probe_scale(0x7F800000, 1, 0.0, "e4m3", "ue8m0", A16, stream=0,
+                               check=False) == aq.PTGQ_EINVAL          # +inf is no amax
+    assert aq.ptgq_probe_scale(0, 4, -1.0, "e4m3", "f32", A16, stream=0,
+                               check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_scale(0, 4, 0.0, "e4m3", "f32", A16 + 2, stream=0,
+                               check=False) == aq.PTGQ_EALIGN
+    assert aq.ptgq_probe_scale(0, 0, 0.0, "e4m3", "f32", 0, stream=0, check=False) == aq.PTGQ_OK
+    assert aq.ptgq_probe_int8(0, (1 << 32) + 1, A16, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_int8(0, 4, 0, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_stream(A16, 1000, A16 * 2, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_stream(A16 + 8, 1024, A16 * 2, stream=0, check=False) == aq.PTGQ_EALIGN
+    assert aq.ptgq_probe_stream(0, 0, 0, stream=0, check=False) == aq.PTGQ_OK
 
 
 def test_binding_raises_on_error(lib):

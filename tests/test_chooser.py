@@ -11,10 +11,10 @@ SLAB = 512           # elements of a row per slab
 
 @pytest.fixture(autouse=True)
 def _reset_knobs():
-    for k in range(7):
+    for k in range(8):
         aq.ptgq_set_tuning(k, -1)
     yield
-    for k in range(7):
+    for k in range(8):
         aq.ptgq_set_tuning(k, -1)
 
 
@@ -79,9 +79,21 @@ def test_short_16bit_rows_keep_contiguous_xcd_ranges(K):
     assert p["uncapped"] == 1 and p["tasks_per_row"] < 4 and p["xcd_chunk"] == 0
 
 
-def test_odd_slab_16bit_rows_still_take_two_slab_tasks():
+def test_odd_slab_rows_take_flat_slab_tasks_across_row_ends():
     p = plan("fp16", 8192, 3584)                   # 7 slabs per row
-    assert p["slabs_per_task"] == 2 and p["tasks_per_row"] == 4 and p["uncapped"] == 1
+    assert p["slabs_per_task"] == 2 and p["uncapped"] == 1 and p["flat_slabs"] == 1
+    assert p["tasks"] == 8192 * 7 // 2             # no half task per row
+    assert p["grid"] == p["tasks"] // 4 and p["xcd_chunk"] == 64
+    # fp32 rows of an odd slab count too
+    p = plan("fp32", 4096, 3584)
+    assert p["slabs_per_task"] == 2 and p["flat_slabs"] == 1 and p["tasks"] == 4096 * 7 // 2
+    # rows that are not whole slabs keep row tasks (a slab would span two rows)
+    p = plan("fp16", 8192, 3584 + 128)
+    assert p["flat_slabs"] == 0 and p["tasks"] == 8192 * p["tasks_per_row"]
+    # the override restores row tasks, whose last task per row holds one slab
+    aq.ptgq_set_tuning(7, 0)
+    p = plan("fp16", 8192, 3584)
+    assert p["flat_slabs"] == 0 and p["tasks_per_row"] == 4 and p["tasks"] == 8192 * 4
 
 
 def test_padded_rows_get_waves_for_the_zero_fill():
@@ -110,7 +122,12 @@ def test_rules_hold_for_random_shapes(cus):
         U = p["slabs_per_task"]
         assert U in (1, 2)
         assert p["tasks_per_row"] == -(-spr // U)
-        assert p["tasks"] == rows * p["tasks_per_row"]
+        if p["flat_slabs"]:
+            assert U == 2 and not fuse and K % SLAB == 0
+            assert p["tasks"] == -(-(rows * spr) // 2)
+        else:
+            assert p["tasks"] == rows * p["tasks_per_row"]
+            assert U == 1 or fuse or K % SLAB != 0
         assert p["block"] in (64, 256, 1024) and p["grid"] >= 1
         waves = p["grid"] * p["block"] // 64
         if p["uncapped"]:

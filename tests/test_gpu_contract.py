@@ -1,0 +1,243 @@
+"""GPU parity for the contract points beside the workloads: the overflowed
+multiplier corner (zeros keep their sign, other values saturate), the
+per-token host contract on padded output rows, flat-slab tasks across row
+ends, the first call of a process made inside a graph capture, and the
+no-arithmetic stream reference.  Every output sits between guard bands."""
+import os
+import subprocess
+import sys
+import textwrap
+
+import numpy as np
+import pytest
+import torch
+
+import activation_quantization_amd as aq
+import oracle
+import workloads as W
+from gpu_util import DEV, Guarded, compare, run_flat, run_per_token, to_dev
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def tiny_rows(seed, M, K, in_dtype):
+    """Rows whose largest magnitude lies in [1e-38, 4e-36] (so 1 / (max / qmax)
+    overflows for most of them), about a third zeros of both signs, one zero
+    row and one ordinary row."""
+    rng = np.random.default_rng(seed)
+    amax = np.exp(rng.uniform(np.log(1e-38), np.log(4e-36), M))
+    y = rng.uniform(-1.0, 1.0, (M, K)) * amax[:, None]
+    y[rng.random((M, K)) < 0.25] = 0.0
+    y[rng.random((M, K)) < 0.1] = -0.0
+    y[1] = 0.0
+    y[2] = rng.normal(size=K)
+    return y.astype(np.float32) if in_dtype == "fp32" else W.to_bf16_bits(y)
+
+
+@pytest.mark.parametrize("mode", [-1, 0, 1, 2, 3])
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp32"])
+def test_overflowed_multiplier_per_token(in_dtype, mode):
+    try:
+        aq.ptgq_set_tuning(3, mode)
+        for M, K in ((40, 1076), (9, 3584), (5, 8192 * 3)):
+            x = tiny_rows(M + K, M, K, in_dtype)
+            compare(f"tiny per-token {in_dtype} mode={mode} M={M} K={K}",
+                    *run_per_token(x, in_dtype, M, K), *oracle.ptq_fp8(x, in_dtype, M, K))
+    finally:
+        aq.ptgq_set_tuning(3, -1)
+
+
+@pytest.mark.parametrize("layout", ["row", "col"])
+@pytest.mark.parametrize("out_dtype", ["e4m3", "int8"])
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp32"])
+def test_overflowed_multiplier_group_fp32_scales(in_dtype, out_dtype, layout):
+    for M, K, G in ((12, 512, 64), (33, 7168, 128), (7, 640, 16)):
+        x = tiny_rows(M * K + G, M, K, in_dtype)
+        args = (x, in_dtype, M, K, G, False, out_dtype, "f32", layout)
+        compare(f"tiny group {in_dtype} {out_dtype} {layout} M={M} K={K} G={G}",
+                *run_flat(*args, eps=0.0), *oracle.ptgq(*args, eps=0.0))
+
+
+def test_overflowed_multiplier_fused_and_masked():
+    """Fused silu(g)*u products that are zero or tiny, eps = 0, fp32 scales:
+    gates of 0 give silu 0; tiny ups give tiny products."""
+    M, K = 6, 1024
+    rng = np.random.default_rng(88)
+    g = rng.normal(size=(M, K))
+    u = rng.normal(size=(M, K)) * 1e-37
+    g[:, ::3] = 0.0
+    x = W.to_bf16_bits(np.concatenate([g, u], axis=1))
+    for fmt in ("f32", "ue8m0"):
+        args = (x, "bf16", M, K, 128, True, "e4m3", fmt, "row")
+        compare(f"tiny fused {fmt}", *run_flat(*args, eps=0.0), *oracle.ptgq(*args, eps=0.0))
+
+
+def test_overflowed_multiplier_requant():
+    E, T, K = 3, 20, 1152
+    rng = np.random.default_rng(89)
+    x = rng.integers(0, 256, (E, T, K)).astype(np.uint8)
+    x[(x & 0x7F) == 0x7F] = 0x00
+    x[:, :, :40] = 0x80
+    s = rng.uniform(0.5, 2.0, E * T * (K // 128)).astype(np.float32)
+    strides = (T * (K // 128), 1, T)
+    mm = np.array([20, 0, 7], np.int32)
+    out = Guarded((E, T, K), torch.uint8, 0x2C)
+    aq.ptgq_requant_fp8(to_dev(x), E, T, K, 128, to_dev(s), strides, to_dev(mm), 0,
+                        torch.tensor([1e-39], dtype=torch.float32, device=DEV), out.t)
+    torch.cuda.synchronize()
+    out.check("requant out")
+    want = oracle.requant_fp8(x, E, T, K, 128, s, strides, mm, np.float32(1e-39),
+                              out_init=np.full((E, T, K), 0x2C, np.uint8))
+    compare("requant, overflowed 1/output_scale", out.host(), np.zeros(0, np.uint8), want,
+            np.zeros(0, np.uint8))
+
+
+@pytest.mark.parametrize("mode", [-1, 0, 1, 2, 3])
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp16", "fp32"])
+def test_per_token_writes_only_the_first_M_rows(in_dtype, mode):
+    """The host contract of the sglang #34257 page: output buffers may hold
+    more rows than M; rows past M keep their contents."""
+    try:
+        aq.ptgq_set_tuning(3, mode)
+        for M, K, extra in ((39, 1076, 5), (64, 3584, 1), (3, 8192 * 3, 4)):
+            seed = 3 * M + K
+            x = {"bf16": W.normal_bf16, "fp16": W.normal_fp16, "fp32": W.normal_f32}[in_dtype](
+                seed, (M, K))
+            compare(f"per-token padded outputs {in_dtype} mode={mode} M={M}+{extra} K={K}",
+                    *run_per_token(x, in_dtype, M, K, extra_rows=extra),
+                    *oracle.ptq_fp8(x, in_dtype, M, K))
+    finally:
+        aq.ptgq_set_tuning(3, -1)
+
+
+# ------------------------------------------------------------ flat-slab tasks
+
+@pytest.mark.parametrize("flat", [-1, 0])
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp16", "fp32"])
+def test_flat_slab_tasks_across_row_ends(in_dtype, flat):
+    """Rows of 1, 3, 7 and 14 slabs with row counts that leave a last task of
+    one slab, every scale format and layout, with flat-slab tasks on (default)
+    and off (row tasks); large enough that two-slab tasks are chosen."""
+    try:
+        aq.ptgq_set_tuning(7, flat)
+        for M, K in ((16385, 512), (5463, 1536), (2341, 3584), (1171, 7168)):
+            seed = M + K
+            x = {"bf16": W.normal_bf16, "fp16": W.normal_fp16, "fp32": W.normal_f32}[in_dtype](
+                seed, (M, K))
+            p = aq.ptgq_plan_group(in_dtype, 0, M, K, 128, False, 0, M,
+                                   torch.cuda.get_device_properties(0).multi_processor_count)
+            assert p["slabs_per_task"] == 2 and p["flat_slabs"] == (1 if flat < 0 else 0)
+            for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row"),
+                                           ("e4m3", "f32", "col"), ("int8", "ue8m0", "row")):
+                G = 128 if fmt == "ue8m0" else 32
+                args = (x, in_dtype, M, K, G, False, out_dtype, fmt, layout)
+                compare(f"flat-slab={flat} {in_dtype} M={M} K={K} G={G} {out_dtype} {fmt} {layout}",
+                        *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
+    finally:
+        aq.ptgq_set_tuning(7, -1)
+
+
+def test_flat_slab_padded_codes():
+    """ptgq_quant_padded with flat-slab tasks: rows past M are zero."""
+    M, K, q_rows = 3001, 3584, 3008
+    x = W.normal_fp16(3001, (M, K))
+    q = Guarded((q_rows, K), torch.uint8, 0xA7)
+    sb = aq.ptgq_scale_bytes(M, K, 64, "f32", "row")
+    s = Guarded((sb,), torch.uint8, 0xA7)
+    aq.ptgq_quant_padded(to_dev(x), "fp16", M, K, 64, False, "int8", "f32", "row", 1e-10, q.t,
+                         q_rows, s.t)
+    torch.cuda.synchronize()
+    q.check("padded q")
+    s.check("padded s")
+    qh = q.host()
+    rq, rs = oracle.ptgq(x, "fp16", M, K, 64, False, "int8", "f32", "row", eps=1e-10)
+    compare("flat-slab padded", qh[:M], s.host(), rq, rs)
+    assert np.all(qh[M:] == 0)
+
+
+# ------------------------------------------- first call inside a graph capture
+
+CAPTURE_CHILD = textwrap.dedent("""
+    import sys
+    sys.path.insert(0, {root!r})
+    import numpy as np
+    import torch
+    import activation_quantization_amd as aq
+    import oracle
+    import workloads as W
+
+    dev = "cuda"
+    M, K = 2048, 4096                    # fused bf16, large enough for the SiLU table
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert aq.ptgq_plan_group("bf16", 0, M, K, 128, True, 0, M, cus)["silu_table"] == 1
+    xh = W.normal_bf16(2048, (M, 2 * K))
+    x = torch.from_numpy(xh.view(np.int16)).to(dev)
+    ph = W.normal_bf16(2049, (64, 7168))
+    p = torch.from_numpy(ph.view(np.int16)).to(dev)
+    sb = aq.ptgq_scale_bytes(M, K, 128, "ue8m0", "col")
+    spb = aq.ptgq_scale_bytes(64, 7168, 128, "ue8m0", "col")
+    q = torch.full((M, K), 0xCD, dtype=torch.uint8, device=dev)
+    s = torch.full((sb,), 0xCD, dtype=torch.uint8, device=dev)
+    qp = torch.full((64, 7168), 0xCD, dtype=torch.uint8, device=dev)
+    sp = torch.full((spb,), 0xCD, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rc1 = aq.ptgq_quant(x, "bf16", M, K, 128, True, "e4m3", "ue8m0", "col", 1e-10, q, s,
+                            check=False)
+        rc2 = aq.ptgq_quant(p, "bf16", 64, 7168, 128, False, "e4m3", "ue8m0", "col", 1e-10, qp,
+                            sp, check=False)
+    print("captured first calls: status", rc1, rc2, flush=True)
+    rq, rs = oracle.ptgq(xh, "bf16", M, K, 128, True, "e4m3", "ue8m0", "col", eps=1e-10)
+    rpq, rps = oracle.ptgq(ph, "bf16", 64, 7168, 128, False, "e4m3", "ue8m0", "col", eps=1e-10)
+    for replay in range(3):
+        q.fill_(0xCD); s.fill_(0xCD); qp.fill_(0xCD); sp.fill_(0xCD)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if rc1 == 0:
+            assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy(), rs)
+        if rc2 == 0:
+            assert np.array_equal(qp.cpu().numpy(), rpq) and np.array_equal(sp.cpu().numpy(), rps)
+        print("replay", replay, "bit-exact", flush=True)
+    assert rc1 in (0, aq.PTGQ_EDEVICE) and rc2 in (0, aq.PTGQ_EDEVICE)
+    # eager calls afterwards, on the default stream and on a side stream
+    for st in (None, torch.cuda.Stream()):
+        q.fill_(0xCD); s.fill_(0xCD)
+        torch.cuda.synchronize()
+        if st is None:
+            aq.ptgq_quant(x, "bf16", M, K, 128, True, "e4m3", "ue8m0", "col", 1e-10, q, s)
+        else:
+            with torch.cuda.stream(st):
+                aq.ptgq_quant(x, "bf16", M, K, 128, True, "e4m3", "ue8m0", "col", 1e-10, q, s)
+        torch.cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy(), rs)
+        print("eager call after the capture bit-exact", flush=True)
+    print("CHILD OK", flush=True)
+""")
+
+
+def test_first_call_inside_a_graph_capture():
+    """A fresh process whose first library call is made while torch captures a
+    graph: the call builds nothing and never synchronizes; replays are
+    bit-exact (or the call reports a clean error status), and eager calls
+    afterwards are bit-exact on the default and on a side stream."""
+    res = subprocess.run([sys.executable, "-c", CAPTURE_CHILD.format(root=ROOT)],
+                         capture_output=True, text=True, timeout=150)
+    print(res.stdout[-3000:], flush=True)
+    if res.returncode != 0:
+        print(res.stderr[-3000:], flush=True)
+    assert res.returncode == 0 and "CHILD OK" in res.stdout
+
+
+# ----------------------------------------------------- the stream reference
+
+def test_stream_probe_moves_the_low_bytes():
+    n = 1024 * 3001
+    xh = np.random.default_rng(9).integers(0, 1 << 16, n).astype(np.uint16)
+    q = Guarded((n,), torch.uint8, 0x11)
+    aq.ptgq_probe_stream(to_dev(xh), n, q.t)
+    torch.cuda.synchronize()
+    q.check("stream probe")
+    assert np.array_equal(q.host(), (xh & 0xFF).astype(np.uint8))

@@ -10,14 +10,13 @@ import torch
 import activation_quantization_amd as aq
 import oracle
 import workloads as W
-from gpu_util import DEV
+from gpu_util import DEV, Guarded
 
 pytestmark = pytest.mark.gpu
 OUTS = ("bf16", "fp16", "fp32")
 CODES = ("e4m3", "int8")
 LAYOUTS = (("f32", "row"), ("f32", "col"), ("ue8m0", "row"), ("ue8m0", "col"))
 OSZ = {"bf16": 2, "fp16": 2, "fp32": 4}
-GUARD = 4096
 
 
 def random_scales(rng, M, K, G, fmt, layout):
@@ -38,12 +37,11 @@ def run(q, code, M, K, G, s, fmt, layout, out, fill=0x5A):
     qd = torch.from_numpy(np.ascontiguousarray(q)).to(DEV)
     sd = torch.from_numpy(np.ascontiguousarray(s).view(np.uint8)).to(DEV)
     n = M * K * OSZ[out]
-    y = torch.full((n + GUARD,), fill, dtype=torch.uint8, device=DEV)
-    aq.ptgq_dequant(qd, code, M, K, G, sd, fmt, layout, out, y)
+    y = Guarded((n,), torch.uint8, fill)
+    aq.ptgq_dequant(qd, code, M, K, G, sd, fmt, layout, out, y.t)
     torch.cuda.synchronize()
-    yh = y.cpu().numpy()
-    assert np.all(yh[n:] == fill), "write past the output"
-    return yh[:n].view(np.float32 if out == "fp32" else np.uint16).reshape(M, K)
+    y.check("ptgq_dequant y")
+    return y.host().view(np.float32 if out == "fp32" else np.uint16).reshape(M, K)
 
 
 def as_f32(y, out):
@@ -176,5 +174,5 @@ def test_tuning_knobs_never_change_results():
                 compare(f"dequant knob {knob}={v}", got, want, "bf16")
                 aq.ptgq_set_tuning(knob, -1)
     finally:
-        for k in range(7):
+        for k in range(8):
             aq.ptgq_set_tuning(k, -1)

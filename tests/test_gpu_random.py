@@ -8,7 +8,7 @@ import torch
 import activation_quantization_amd as aq
 import oracle
 import workloads as W
-from gpu_util import DEV, compare, run_flat, run_masked, run_per_token
+from gpu_util import DEV, Guarded, compare, run_flat, run_masked, run_per_token
 
 pytestmark = pytest.mark.gpu
 GS = (16, 32, 64, 128)
@@ -95,13 +95,14 @@ def test_random_requant(case):
     sd = torch.from_numpy(s).to(DEV)
     md = None if mm is None else torch.from_numpy(mm).to(DEV)
     od = torch.tensor([os_], dtype=torch.float32, device=DEV)
-    outd = torch.full((E, T, K), 0x2C, dtype=torch.uint8, device=DEV)
-    aq.ptgq_requant_fp8(xd, E, T, K, G, sd, strides, md, int(rng.integers(0, T + 1)), od, outd)
+    outd = Guarded((E, T, K), torch.uint8, 0x2C)
+    aq.ptgq_requant_fp8(xd, E, T, K, G, sd, strides, md, int(rng.integers(0, T + 1)), od, outd.t)
     torch.cuda.synchronize()
+    outd.check("random requant out")
     want = oracle.requant_fp8(x, E, T, K, G, s, strides, mm, os_,
                               out_init=np.full((E, T, K), 0x2C, np.uint8))
     compare(f"random requant #{case} E={E} T={T} K={K} G={G} strides={strides}",
-            outd.cpu().numpy(), np.zeros(0, np.uint8), want, np.zeros(0, np.uint8))
+            outd.host(), np.zeros(0, np.uint8), want, np.zeros(0, np.uint8))
 
 
 @pytest.mark.parametrize("case", range(10))
@@ -124,10 +125,11 @@ def test_random_dequant(case):
     qd = torch.from_numpy(q).to(DEV)
     sd = torch.from_numpy(s).to(DEV)
     osz = 4 if outd == "fp32" else 2
-    y = torch.empty(M * K * osz, dtype=torch.uint8, device=DEV)
-    aq.ptgq_dequant(qd, code, M, K, G, sd, fmt, lay, outd, y)
+    y = Guarded((M * K * osz,), torch.uint8, 0x5A)
+    aq.ptgq_dequant(qd, code, M, K, G, sd, fmt, lay, outd, y.t)
     torch.cuda.synchronize()
-    got = y.cpu().numpy().view(np.float32 if outd == "fp32" else np.uint16).reshape(M, K)
+    y.check("random dequant y")
+    got = y.host().view(np.float32 if outd == "fp32" else np.uint16).reshape(M, K)
     want = oracle.dequant(q, code, M, K, G, s, fmt, lay, outd)
     gf = got.astype(np.float32) if outd == "fp32" else None
     nan_g = np.isnan(gf) if outd == "fp32" else np.zeros(got.shape, bool)

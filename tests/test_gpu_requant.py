@@ -6,7 +6,7 @@ import torch
 
 import activation_quantization_amd as aq
 import oracle
-from gpu_util import DEV, compare
+from gpu_util import DEV, Guarded, compare
 from workloads import splitmix64, substream
 
 pytestmark = pytest.mark.gpu
@@ -23,10 +23,11 @@ def run(x, E, T, K, G, s, strides, mm, exp_m, os_, fill=SENTINEL):
     sd = torch.from_numpy(np.ascontiguousarray(s, dtype=np.float32)).to(DEV)
     md = None if mm is None else torch.from_numpy(np.ascontiguousarray(mm, dtype=np.int32)).to(DEV)
     od = torch.tensor([os_], dtype=torch.float32, device=DEV)
-    out = torch.full((E, T, K), fill, dtype=torch.uint8, device=DEV)
-    aq.ptgq_requant_fp8(xd, E, T, K, G, sd, strides, md, exp_m, od, out)
+    out = Guarded((E, T, K), torch.uint8, fill)
+    aq.ptgq_requant_fp8(xd, E, T, K, G, sd, strides, md, exp_m, od, out.t)
     torch.cuda.synchronize()
-    return out.cpu().numpy()
+    out.check("ptgq_requant_fp8 out")
+    return out.host()
 
 
 @pytest.mark.parametrize("k", [7168, 3584, 1152])

@@ -8,7 +8,7 @@ import torch
 import activation_quantization_amd as aq
 import oracle
 import workloads as W
-from gpu_util import DEV, compare, run_flat, run_masked, to_dev
+from gpu_util import DEV, Guarded, compare, run_flat, run_masked, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -84,16 +84,15 @@ SENT = 0xA7
 
 def run_padded(x, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, q_rows):
     xd = to_dev(x) if M > 0 else None
-    guard = 4096
-    qbuf = torch.full((q_rows * K + guard,), SENT, dtype=torch.uint8, device=DEV)
+    q = Guarded((q_rows, K), torch.uint8, SENT)
     sb = aq.ptgq_scale_bytes(M, K, G, fmt, layout)
-    s = torch.full((max(sb, 1),), SENT, dtype=torch.uint8, device=DEV)
-    aq.ptgq_quant_padded(xd, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, 1e-10, qbuf, q_rows,
-                         s if M > 0 else None)
+    s = Guarded((sb,), torch.uint8, SENT)
+    aq.ptgq_quant_padded(xd, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, 1e-10, q.t, q_rows,
+                         s.t if M > 0 else None)
     torch.cuda.synchronize()
-    qh = qbuf.cpu().numpy()
-    assert np.all(qh[q_rows * K:] == SENT), "write past the padded buffer"
-    return qh[:q_rows * K].reshape(q_rows, K), s.cpu().numpy()[:sb]
+    q.check("ptgq_quant_padded q")
+    s.check("ptgq_quant_padded s")
+    return q.host(), s.host()
 
 
 @pytest.mark.parametrize("M,K,q_rows,fuse", [(1, 7168, 4, False), (5, 7168, 8, False),
