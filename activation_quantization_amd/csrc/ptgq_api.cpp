@@ -276,13 +276,17 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
     const bool bf16 = in_dtype == PTGQ_BF16;
 
     if (!masked) {
-        const bool fs_ok = !fuse && K % kSlab == 0 && knob(KNOB_FLAT_SLABS) != 0;
+        // Flat-slab tasks for rows of an odd number of whole slabs (measured
+        // on MI355X, fp16 [8192, 3584] -> int8, fp32 row scales: G = 128
+        // 16.13 -> 15.92 us, G = 32 16.88 -> 16.63 us); rows of an even
+        // number keep row tasks, which measured faster there (bf16 [4096,
+        // 7168]: 15.35 against 15.96 us with the same tasks).
+        const bool fs_ok = !fuse && K % kSlab == 0 && (a.spr % 2 == 1 || knob(KNOB_FLAT_SLABS) > 0) &&
+                           knob(KNOB_FLAT_SLABS) != 0;
         choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, !fuse && es == 2, fs_ok, table_ok,
                     cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
-        // Flat-slab tasks for two-slab tasks over whole-slab rows (measured on
-        // MI355X, fp16 [8192, 3584], 7 slabs per row: see the design notes).
         a.flat_slabs = fs_ok && a.U == 2 ? 1 : 0;
         a.n_slabs = rows * (int64_t)a.spr;
         if (a.n_slabs >= INT32_MAX) return PTGQ_EUNSUPPORTED;
@@ -361,17 +365,22 @@ int launch_group_common(const void *x, int in_dtype, int64_t rows, int64_t K, in
     a.s = s;
     a.masked_m = masked_m;
     a.eps = eps;
+    a.wpb = geo.wpb;
     const hipError_t err = launch_group(a, in_dtype, G, fuse != 0, out_dtype, geo.table, masked,
                                         geo.grid, (unsigned)(geo.wpb * 64),
                                         static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PTGQ_OK : PTGQ_ELAUNCH;
 }
 
-int next_pow2(int64_t n)
+// Vectors per lane of the per-token kernels that keep a row in registers:
+// instantiated for 1, 2, 4, 7, 8 and 16 (7: a 7 KiB row of 16-bit elements
+// over one wave, or 14 KiB over two, with no idle lane); other counts round
+// up to the next instantiated one.
+int vectors_per_lane(int64_t n)
 {
-    int p = 1;
-    while (p < n && p < 32) p <<= 1;
-    return p;
+    for (const int p : {1, 2, 4, 7, 8, 16})
+        if (p >= n) return p;
+    return 32;
 }
 
 }  // namespace
@@ -523,7 +532,7 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
     unsigned grid, block;
     int nvl = 0;
     if (mode == TOKEN_WAVE) {
-        nvl = next_pow2(per_wave);
+        nvl = vectors_per_lane(per_wave);
         block = 256;
         grid = (unsigned)((M + 3) / 4);
     } else if (mode == TOKEN_WAVE_LOOP) {
@@ -531,12 +540,12 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
         // CU measured best (fp16 [8192, 3584]: 16.1 us against 16.7 for one
         // wave per row and 17.4 with four blocks per CU); the grid never
         // exceeds one wave per row
-        nvl = next_pow2(per_wave);
+        nvl = vectors_per_lane(per_wave);
         block = 256;
         const int64_t per_cu = knob(KNOB_BLOCKS_PER_CU) > 0 ? knob(KNOB_BLOCKS_PER_CU) : 1;
         grid = (unsigned)std::min<int64_t>((M + 3) / 4, (int64_t)cus * per_cu);
     } else {
-        nvl = mode == TOKEN_BLOCK ? next_pow2(per_block) : 0;
+        nvl = mode == TOKEN_BLOCK ? vectors_per_lane(per_block) : 0;
         block = mode == TOKEN_BLOCK ? (unsigned)(64 * tw) : 256;
         grid = (unsigned)M;
     }

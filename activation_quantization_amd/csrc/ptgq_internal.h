@@ -81,6 +81,7 @@ struct GroupArgs {
                               // as one sequence of slabs (tasks cross row ends)
     int64_t n_slabs;          // flat_slabs: rows * spr
     FastDiv spr_div;          // flat_slabs: division by spr
+    int32_t wpb;              // waves per block of the launch
 };
 
 // Arguments of the whole-row per-token kernels.

@@ -218,20 +218,39 @@ __device__ __forceinline__ Scale group_scale(uint32_t amax_bits, uint32_t eps_bi
 // below about 2^-128 (an fp32 scale with no floor, or one under ~1.3e-36):
 // the quotient y / r of a zero is then still zero, where the product 0 * inf
 // would be NaN; every other y times inf saturates when narrowed.  A finite
-// multiplier already gives y * inv == y for a zero y, so the fix-up runs only
-// when some lane of the wave holds an infinite multiplier (a scalar branch).
-// MAYBE_INF false: the caller knows inv is finite (UE8M0 multipliers).
-template <bool MAYBE_INF, int N>
+// multiplier already gives y * inv == y for a zero y, so:
+//   MUL_PLAIN  the caller knows inv is finite (UE8M0 multipliers, or a
+//              uniform multiplier tested beforehand);
+//   MUL_CHECK  per-lane multipliers: the fix-up runs only when some lane of
+//              the wave holds an infinite one (a scalar branch);
+//   MUL_FIX    the caller knows inv is infinite.
+enum { MUL_PLAIN = 0, MUL_CHECK = 1, MUL_FIX = 2 };
+
+template <int MODE, int N>
 __device__ __forceinline__ void scale_by(const float (&y)[N], float inv, float (&v)[N])
 {
 #pragma unroll
     for (int k = 0; k < N; ++k) v[k] = y[k] * inv;
-    if constexpr (MAYBE_INF) {
+    if constexpr (MODE == MUL_FIX) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] = (y[k] == 0.0f) ? y[k] : v[k];
+    } else if constexpr (MODE == MUL_CHECK) {
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(inv == __builtin_inff()) != 0, 0)) {
 #pragma unroll
             for (int k = 0; k < N; ++k) v[k] = (y[k] == 0.0f) ? y[k] : v[k];
         }
     }
+}
+
+// Runs body(std::integral_constant<int, MUL_FIX or MUL_PLAIN>) for a
+// wave-uniform multiplier: one scalar branch instead of a test per vector.
+template <class Body>
+__device__ __forceinline__ void with_uniform_multiplier(float inv, Body &&body)
+{
+    if (__builtin_expect(inv == __builtin_inff(), 0))
+        body(std::integral_constant<int, MUL_FIX>{});
+    else
+        body(std::integral_constant<int, MUL_PLAIN>{});
 }
 
 // --------------------------------------------------------------------------
@@ -428,19 +447,29 @@ struct TaskBuf {
     u32x4 u[UMAX];
 };
 
-// Where a task lives.  Its slabs are consecutive in memory: `x` and `q` point
-// at the input (gate half when fused) and codes of its first slab, and
-// `codes` is the number of code bytes (elements) from q on that belong to
-// the task (fewer than UMAX slabs at the end of a row, or of the tensor for
-// flat-slab tasks); loads and stores past it are dropped by the buffer range
-// check.  `sbase` is the scale tensor of the rows (flat: the whole tensor;
-// masked: the expert's); `m` and `j` are the row and the slab index within
-// that row of the first slab.  Row tasks keep all their slabs in row m;
-// flat-slab tasks move on to row m + 1 when a slab index reaches spr.
+// Where a task lives.  `xb` / `qb` are the base of the region the task's
+// input (gate half when fused) and codes are addressed from, `xrange` /
+// `qrange` that region's bytes (loads past it read zeros, stores past it are
+// dropped by the buffer range check), and `c0` the offset, in elements, of
+// the task's first slab from the bases.  The region is the task's row (its
+// last task may run past the row end), extended for a flat-slab task by the
+// slab that crosses into the next row.  `codes` is the number of elements of
+// the task (fewer than UMAX slabs at the end of a row, or of the tensor).
+// `sbase` is the scale tensor of the rows (flat: the whole tensor; masked:
+// the expert's); `m` and `j` are the row and the slab index within that row
+// of the first slab.  Row tasks keep all their slabs in row m; flat-slab
+// tasks move on to row m + 1 when a slab index reaches spr.  (Measured on
+// MI355X, same addresses, bf16 -> e4m3: buffer descriptors based at the row
+// are faster than descriptors based at each task, [256, 7168] 3.0 against
+// 3.19 us, or one descriptor over the whole tensor, [4096, 7168] 15.4
+// against 15.9 us.)
 struct TaskLoc {
-    const char *x;
-    uint8_t *q;
+    const char *xb;
+    uint8_t *qb;
     uint8_t *sbase;
+    uint32_t xrange;
+    uint32_t qrange;
+    uint32_t c0;
     uint32_t codes;
     int64_t m;
     int j;
@@ -455,12 +484,12 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
 {
     constexpr int ES = IN == IN_FP32 ? 4 : 2;   // input element bytes
     constexpr int pol = kStreamPolicy;
-    const uint32_t bytes = live ? t.codes * ES : 0u;
-    const rsrc_t rg = make_rsrc(t.x, bytes);
+    const uint32_t bytes = live ? t.xrange : 0u;
+    const rsrc_t rg = make_rsrc(t.xb, bytes);
     // 16-bit: lane l holds elements 8l..8l+7 of a slab; fp32: 4l..4l+3 (g)
     // and 256+4l..256+4l+3 (gh), so every load instruction reads one
     // contiguous KiB
-    const uint32_t off = (uint32_t)lane * 16;
+    const uint32_t off = t.c0 * ES + (uint32_t)lane * 16;
 #pragma unroll
     for (int s = 0; s < UMAX; ++s) {
         b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + s * kSlab * ES, 0, pol);
@@ -469,7 +498,7 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
     }
     if constexpr (FUSE) {
         static_assert(IN != IN_FP32, "fused calls take 16-bit inputs");
-        const rsrc_t ru = make_rsrc(t.x + a.K * ES, bytes);
+        const rsrc_t ru = make_rsrc(t.xb + a.K * ES, bytes);
 #pragma unroll
         for (int s = 0; s < UMAX; ++s)
             b.u[s] = __builtin_amdgcn_raw_buffer_load_b128(ru, off + s * kSlab * 2, 0, pol);
@@ -485,12 +514,13 @@ __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y,
 // 256 contiguous bytes; stores past the row are dropped); scales go to the
 // layout's slots like those of the 16-bit path.
 // `slab`: index of the slab within row m; `at`: offset of the slab's first
-// code from the task's codes, `codes`: the task's code count.
+// code from the task's first code, `c0`: offset of that from the code
+// region's base, `codes`: the task's code count.
 template <int G, int OUT, int SF, int SPOL>
 __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x4 &ga,
                                                   const u32x4 &gb, int slab, uint32_t at,
-                                                  uint32_t codes, rsrc_t rq, uint8_t *se,
-                                                  int64_t m, int lane)
+                                                  uint32_t c0, uint32_t codes, rsrc_t rq,
+                                                  uint8_t *se, int64_t m, int lane)
 {
     constexpr int LA = G / 4;           // lanes per group within a half (4..32)
     constexpr int GPH = 256 / G;        // groups per half (2..16)
@@ -508,10 +538,10 @@ __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x
     const Scale sA = group_scale<OUT>(amA, __float_as_uint(a.eps), ue8m0);
     const Scale sB = group_scale<OUT>(amB, __float_as_uint(a.eps), ue8m0);
     float va[4], vb[4];
-    scale_by<!ue8m0>(ya, sA.inv, va);
-    scale_by<!ue8m0>(yb, sB.inv, vb);
-    __builtin_amdgcn_raw_buffer_store_b32(narrow4<OUT, !ue8m0>(va), rq, colA, 0, SPOL);
-    __builtin_amdgcn_raw_buffer_store_b32(narrow4<OUT, !ue8m0>(vb), rq, colB, 0, SPOL);
+    scale_by<ue8m0 ? MUL_PLAIN : MUL_CHECK>(ya, sA.inv, va);
+    scale_by<ue8m0 ? MUL_PLAIN : MUL_CHECK>(yb, sB.inv, vb);
+    __builtin_amdgcn_raw_buffer_store_b32(narrow4<OUT, !ue8m0>(va), rq, c0 + colA, 0, SPOL);
+    __builtin_amdgcn_raw_buffer_store_b32(narrow4<OUT, !ue8m0>(vb), rq, c0 + colB, 0, SPOL);
 
     const int lg = lane / LA;                          // group within the half
     const bool leader = (lane % LA) == 0;
@@ -577,7 +607,7 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
 {
     constexpr int LPG = G / 8;          // lanes per group
     constexpr int GPS = kSlab / G;      // groups per slab (>= 4)
-    const rsrc_t rq = make_rsrc(t.q, t.codes);
+    const rsrc_t rq = make_rsrc(t.qb, t.qrange);
     uint8_t *se = t.sbase;
     constexpr bool ue8m0 = SF == SCALE_UE8M0;
 #pragma unroll
@@ -594,11 +624,11 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
         }
         const uint32_t at = (uint32_t)s * kSlab;                    // offset in the task
         if constexpr (IN == IN_FP32) {
-            process_slab_fp32<G, OUT, SF, SPOL>(a, b.g[s], b.gh[s], slab, at, t.codes, rq, se,
-                                                m, lane);
+            process_slab_fp32<G, OUT, SF, SPOL>(a, b.g[s], b.gh[s], slab, at, t.c0, t.codes, rq,
+                                                se, m, lane);
             continue;
         }
-        const uint32_t col = at + (uint32_t)lane * 8;
+        const uint32_t col = at + (uint32_t)lane * 8;              // in the task
         const bool valid = col < t.codes;
         float y[8];
         if constexpr (FUSE && TABLE) {
@@ -644,12 +674,12 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
 
         const Scale sc = group_scale<OUT>(amax, __float_as_uint(a.eps), ue8m0);
         float v[8];
-        scale_by<!ue8m0>(y, sc.inv, v);
+        scale_by<ue8m0 ? MUL_PLAIN : MUL_CHECK>(y, sc.inv, v);
         const uint2 codes = narrow8<OUT, !ue8m0>(v);
         u32x2 c2;
         c2.x = codes.x;
         c2.y = codes.y;
-        __builtin_amdgcn_raw_buffer_store_b64(c2, rq, col, 0, SPOL);  // dropped past the task
+        __builtin_amdgcn_raw_buffer_store_b64(c2, rq, t.c0 + col, 0, SPOL);  // dropped past the region
 
         // scales of the slab's groups
         const int lg = lane / LPG;                                  // group within slab
@@ -700,12 +730,18 @@ __device__ __forceinline__ TaskLoc row_task(const GroupArgs &a, const char *xrow
                                             uint8_t *sbase, int64_t m, int j)
 {
     constexpr int ES = IN == IN_FP32 ? 4 : 2;
-    const int64_t c0 = (int64_t)j * (UMAX * kSlab);     // first column of the task
+    // 32-bit column arithmetic: K < 2^29
+    const uint32_t K = (uint32_t)a.K;
+    const uint32_t c0 = (uint32_t)j * (UMAX * kSlab);   // first column of the task
+    const uint32_t left = K - c0;
     TaskLoc l;
-    l.x = xrow + c0 * ES;
-    l.q = qrow + c0;
+    l.xb = xrow;
+    l.qb = qrow;
     l.sbase = sbase;
-    l.codes = (uint32_t)(a.K - c0 < UMAX * kSlab ? a.K - c0 : UMAX * kSlab);
+    l.xrange = K * ES;
+    l.qrange = K;
+    l.c0 = c0;
+    l.codes = left < UMAX * kSlab ? left : UMAX * kSlab;
     l.m = m;
     l.j = j * UMAX;
     return l;
@@ -727,7 +763,8 @@ struct FlatMap {
 // and codes are one contiguous sequence of whole-row slabs): task t is slabs
 // U*t .. U*t+U-1 of that sequence, crossing row ends; no task is short
 // except the tensor's last one.  The row of slab S is S / spr (a wave-uniform
-// multiply-high division).
+// multiply-high division).  The task is addressed from its first row, whose
+// range is extended by the slab that crosses into the next row.
 template <int IN, int UMAX>
 struct FlatSlabMap {
     __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int /*lane*/)
@@ -735,14 +772,23 @@ struct FlatSlabMap {
         constexpr int ES = IN == IN_FP32 ? 4 : 2;
         const uint32_t S = (uint32_t)t * UMAX;                      // first slab (< 2^31)
         const uint32_t m = fastdiv(S, a.spr_div);
-        const int64_t left = a.n_slabs - S;                          // >= 1 for live tasks
+        const uint32_t j = S - m * (uint32_t)a.spr;
+        const uint32_t left = (uint32_t)a.n_slabs - S;               // >= 1 for live tasks
+        const uint32_t K = (uint32_t)a.K;
+        // the region is row m and the slabs after it up to the task's end
+        // (the next row's first slab when the task crosses the row end)
+        const uint32_t span = j * kSlab + (left < UMAX ? left : UMAX) * kSlab;
+        const uint32_t reach = span > K ? span : K;
         TaskLoc l;
-        l.x = static_cast<const char *>(a.x) + (int64_t)S * (kSlab * ES);
-        l.q = a.q + (int64_t)S * kSlab;
+        l.xb = static_cast<const char *>(a.x) + (uint64_t)m * K * ES;
+        l.qb = a.q + (uint64_t)m * K;
         l.sbase = static_cast<uint8_t *>(a.s);
-        l.codes = (uint32_t)(left < UMAX ? left : UMAX) * kSlab;
+        l.xrange = reach * ES;
+        l.qrange = reach;
+        l.c0 = j * kSlab;
+        l.codes = (left < UMAX ? left : UMAX) * kSlab;
         l.m = m;
-        l.j = (int)(S - m * (uint32_t)a.spr);
+        l.j = (int)j;
         return l;
     }
 };
@@ -948,6 +994,19 @@ __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first
                                                             lane, tab);
 }
 
+// Kernel arguments live in memory and are read by scalar loads, which the
+// compiler places at each argument's first use; a prologue with branches then
+// waits for several rounds of them before its first input load.  Naming the
+// arguments the prologue needs in one empty asm statement at entry makes all
+// those loads one batch behind one wait (no instruction is emitted).
+__device__ __forceinline__ void args_in_sgprs(const GroupArgs &a)
+{
+    asm volatile("" ::"s"(a.x), "s"(a.q), "s"(a.s), "s"(a.K), "s"(a.in_stride),
+                 "s"(a.n_tasks), "s"(a.tpr), "s"(a.xcd_chunk), "s"(a.n_slabs), "s"(a.spr_div.mul),
+                 "s"(a.spr_div.shift), "s"(a.spr), "s"(a.wpb), "s"(a.q_pad_bytes),
+                 "s"(gridDim.x));
+}
+
 // XCD-aware logical block id.  Blocks are dealt to the 8 XCDs round-robin
 // (block b runs on XCD b % 8).  With chunk == 0 and a grid that is a multiple
 // of 8, XCD x gets the logical ids [x * nb/8, (x+1) * nb/8): one contiguous
@@ -972,9 +1031,10 @@ template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, bool 
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs a)
 {
     __shared__ float tab[TABLE ? kSiluTab : 1];
+    args_in_sgprs(a);
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wpb = blockDim.x >> 6;
+    const int wpb = TABLE ? kTableLanes / 64 : a.wpb;
     const int lb = logical_block(blockIdx.x, gridDim.x, a.xcd_chunk);
     constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
     if constexpr (FS) {
@@ -1017,9 +1077,10 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
 {
     __shared__ float tab[TABLE ? kSiluTab : 1];
     extern __shared__ int scan[];
+    args_in_sgprs(a);
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wpb = blockDim.x >> 6;
+    const int wpb = TABLE ? kTableLanes / 64 : a.wpb;
     const int lb = logical_block(blockIdx.x, gridDim.x);
     const int E = a.num_experts;
     if (E <= 64) {
@@ -1172,16 +1233,18 @@ __global__ __launch_bounds__(256) void ptq_wave_kernel(TokenArgs a)
     float r;
     const float inv = token_inv(__uint_as_float(wave_max_bits(amax)), r);
     if (lane == 0) a.s[m] = r;
+    with_uniform_multiplier(inv, [&](auto mode) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int i = lane + 64 * k;
-        if (i < a.nv) {
-            float f[EV], v[EV];
-            TV::widen(raw[k], f);
-            scale_by<true>(f, inv, v);
-            TV::store_codes(qr + (int64_t)i * EV, v);
+        for (int k = 0; k < NV; ++k) {
+            const int i = lane + 64 * k;
+            if (i < a.nv) {
+                float f[EV], v[EV];
+                TV::widen(raw[k], f);
+                scale_by<decltype(mode)::value>(f, inv, v);
+                TV::store_codes(qr + (int64_t)i * EV, v);
+            }
         }
-    }
+    });
 }
 
 // Persistent form of the wave-per-row kernel: a grid of a few blocks per CU
@@ -1231,22 +1294,24 @@ __global__ __launch_bounds__(256) void ptq_wave_loop_kernel(TokenArgs a)
         const float inv = token_inv(__uint_as_float(wave_max_bits(amax)), rs);
         if (lane == 0) a.s[row] = rs;
         const rsrc_t rq = make_rsrc(a.q + row * a.K, (uint32_t)a.K);
+        with_uniform_multiplier(inv, [&](auto mode) {
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            float y[EV], f[EV];
-            TV::widen(r[k], y);
-            scale_by<true>(y, inv, f);
-            const uint32_t off = (uint32_t)(lane + 64 * k) * EV;
-            if constexpr (EV == 8) {
-                u32x2 o;
-                o.x = e4m3x4<true>(f[0], f[1], f[2], f[3]);
-                o.y = e4m3x4<true>(f[4], f[5], f[6], f[7]);
-                __builtin_amdgcn_raw_buffer_store_b64(o, rq, off, 0, kStreamPolicy);
-            } else {
-                __builtin_amdgcn_raw_buffer_store_b32(e4m3x4<true>(f[0], f[1], f[2], f[3]), rq,
-                                                      off, 0, kStreamPolicy);
+            for (int k = 0; k < NV; ++k) {
+                float y[EV], f[EV];
+                TV::widen(r[k], y);
+                scale_by<decltype(mode)::value>(y, inv, f);
+                const uint32_t off = (uint32_t)(lane + 64 * k) * EV;
+                if constexpr (EV == 8) {
+                    u32x2 o;
+                    o.x = e4m3x4<true>(f[0], f[1], f[2], f[3]);
+                    o.y = e4m3x4<true>(f[4], f[5], f[6], f[7]);
+                    __builtin_amdgcn_raw_buffer_store_b64(o, rq, off, 0, kStreamPolicy);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b32(e4m3x4<true>(f[0], f[1], f[2], f[3]),
+                                                          rq, off, 0, kStreamPolicy);
+                }
             }
-        }
+        });
     };
 
     raw_t A[NV], B[NV];
@@ -1304,16 +1369,18 @@ __global__ __launch_bounds__(256) void ptq_block_kernel(TokenArgs a)
     float r;
     const float inv = token_inv(__uint_as_float(block_max_bits(amax, red)), r);
     if (tid == 0) a.s[m] = r;
+    with_uniform_multiplier(inv, [&](auto mode) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int i = tid + nt * k;
-        if (i < a.nv) {
-            float f[EV], v[EV];
-            TV::widen(raw[k], f);
-            scale_by<true>(f, inv, v);
-            TV::store_codes(qr + (int64_t)i * EV, v);
+        for (int k = 0; k < NV; ++k) {
+            const int i = tid + nt * k;
+            if (i < a.nv) {
+                float f[EV], v[EV];
+                TV::widen(raw[k], f);
+                scale_by<decltype(mode)::value>(f, inv, v);
+                TV::store_codes(qr + (int64_t)i * EV, v);
+            }
         }
-    }
+    });
 }
 
 template <int IN, int VB>
@@ -1334,12 +1401,14 @@ __global__ __launch_bounds__(256) void ptq_block_loop_kernel(TokenArgs a)
     float r;
     const float inv = token_inv(__uint_as_float(block_max_bits(amax, red)), r);
     if (tid == 0) a.s[m] = r;
-    for (int i = tid; i < a.nv; i += 256) {
-        float f[EV], v[EV];
-        TV::widen(TV::load(xr + (int64_t)i * VB), f);
-        scale_by<true>(f, inv, v);
-        TV::store_codes(qr + (int64_t)i * EV, v);
-    }
+    with_uniform_multiplier(inv, [&](auto mode) {
+        for (int i = tid; i < a.nv; i += 256) {
+            float f[EV], v[EV];
+            TV::widen(TV::load(xr + (int64_t)i * VB), f);
+            scale_by<decltype(mode)::value>(f, inv, v);
+            TV::store_codes(qr + (int64_t)i * EV, v);
+        }
+    });
 }
 
 // --------------------------------------------------------------------------
@@ -1489,27 +1558,29 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
     };
     auto process = [&](const Loc &l, const Buf &b) {
         const rsrc_t ro = make_rsrc(a.out + l.base, l.len);
+        with_uniform_multiplier(inv, [&](auto mode) {
 #pragma unroll
-        for (int k = 0; k < NS; ++k) {
-            const uint32_t ww[4] = {b.w[k].x, b.w[k].y, b.w[k].z, b.w[k].w};
-            u32x4 o;
-            uint32_t oo[4];
+            for (int k = 0; k < NS; ++k) {
+                const uint32_t ww[4] = {b.w[k].x, b.w[k].y, b.w[k].z, b.w[k].w};
+                u32x4 o;
+                uint32_t oo[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float f[4], h[4];
-                decode4_e4m3(ww[i], f);
+                for (int i = 0; i < 4; ++i) {
+                    float f[4], h[4];
+                    decode4_e4m3(ww[i], f);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) h[j] = f[j] * b.s[k];
-                scale_by<true>(h, inv, f);
-                oo[i] = e4m3x4<true>(f[0], f[1], f[2], f[3]);
+                    for (int j = 0; j < 4; ++j) h[j] = f[j] * b.s[k];
+                    scale_by<decltype(mode)::value>(h, inv, f);
+                    oo[i] = e4m3x4<true>(f[0], f[1], f[2], f[3]);
+                }
+                o.x = oo[0];
+                o.y = oo[1];
+                o.z = oo[2];
+                o.w = oo[3];
+                __builtin_amdgcn_raw_buffer_store_b128(o, ro, k * kRqSub + lane * 16, 0,
+                                                       kStreamPolicy);
             }
-            o.x = oo[0];
-            o.y = oo[1];
-            o.z = oo[2];
-            o.w = oo[3];
-            __builtin_amdgcn_raw_buffer_store_b128(o, ro, k * kRqSub + lane * 16, 0,
-                                                   kStreamPolicy);
-        }
+        });
     };
 
     const int stride = gridDim.x * wpb;
@@ -1996,6 +2067,7 @@ static hipError_t launch_token_v(const TokenArgs &a, TokenMode mode, int nvl, un
         PTGQ_TOKEN_CASE(1)
         PTGQ_TOKEN_CASE(2)
         PTGQ_TOKEN_CASE(4)
+        PTGQ_TOKEN_CASE(7)
         PTGQ_TOKEN_CASE(8)
         PTGQ_TOKEN_CASE(16)
     default: return hipErrorInvalidValue;

@@ -125,9 +125,11 @@ PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, i
  * rows), 4 fused bf16 SiLU path (0 direct evaluation, 1 LDS lookup table), 5
  * blocks per XCD chunk of the flat quantization and dequantization kernels'
  * block-to-task mappings (0 one contiguous range per XCD), 6 grid of the flat
- * quantization and
- * requantization kernels (0 capped: resident blocks loop over the tasks; 1
- * uncapped: one wave per task).
+ * quantization and requantization kernels (0 capped: resident blocks loop
+ * over the tasks; 1 uncapped: one wave per task), 7 two-slab tasks of unfused
+ * flat calls whose K is a multiple of 512 (0 row tasks; 1 flat-slab tasks,
+ * which cross row ends; automatic: flat-slab tasks for an odd number of
+ * slabs per row).
  * Results never depend on these; only speed does.  Not synchronized
  * with calls running on other host threads.  Returns PTGQ_OK or PTGQ_EINVAL.
  */

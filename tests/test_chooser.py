@@ -90,10 +90,16 @@ def test_odd_slab_rows_take_flat_slab_tasks_across_row_ends():
     # rows that are not whole slabs keep row tasks (a slab would span two rows)
     p = plan("fp16", 8192, 3584 + 128)
     assert p["flat_slabs"] == 0 and p["tasks"] == 8192 * p["tasks_per_row"]
-    # the override restores row tasks, whose last task per row holds one slab
+    # rows of an even slab count keep row tasks (the same tasks)
+    p = plan("bf16", 4096, 7168)
+    assert p["flat_slabs"] == 0 and p["tasks"] == 4096 * 7
+    # the override: 0 restores row tasks, whose last task per row holds one
+    # slab; 1 takes flat-slab tasks for even slab counts too
     aq.ptgq_set_tuning(7, 0)
     p = plan("fp16", 8192, 3584)
     assert p["flat_slabs"] == 0 and p["tasks_per_row"] == 4 and p["tasks"] == 8192 * 4
+    aq.ptgq_set_tuning(7, 1)
+    assert plan("bf16", 4096, 7168)["flat_slabs"] == 1
 
 
 def test_padded_rows_get_waves_for_the_zero_fill():
@@ -123,11 +129,11 @@ def test_rules_hold_for_random_shapes(cus):
         assert U in (1, 2)
         assert p["tasks_per_row"] == -(-spr // U)
         if p["flat_slabs"]:
-            assert U == 2 and not fuse and K % SLAB == 0
+            assert U == 2 and not fuse and K % SLAB == 0 and spr % 2 == 1
             assert p["tasks"] == -(-(rows * spr) // 2)
         else:
             assert p["tasks"] == rows * p["tasks_per_row"]
-            assert U == 1 or fuse or K % SLAB != 0
+            assert U == 1 or fuse or K % SLAB != 0 or spr % 2 == 0
         assert p["block"] in (64, 256, 1024) and p["grid"] >= 1
         waves = p["grid"] * p["block"] // 64
         if p["uncapped"]:
