@@ -152,6 +152,8 @@ struct GroupGeom {
     int wpb;        // waves per block
     bool table;     // fused bf16: LDS SiLU table (16-wave blocks)
     bool uncapped;  // one wave per task (no grid-stride loop)
+    bool flat_slabs = false;  // flat-slab tasks (set before choose_blocks)
+    bool fp32 = false;        // fp32 input
     int64_t per_cu; // resident blocks per CU the grid is capped at
     unsigned grid;  // blocks
 };
@@ -220,6 +222,14 @@ void choose_blocks(GroupGeom &g, int64_t tasks, int cus, bool fuse, int64_t es, 
         per_cu = kTableBlocksPerCu;
     } else {
         wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
+        // Uncapped grids of flat-slab tasks run one-wave blocks, of fp32 input
+        // two-wave blocks: measured on MI355X (A/B in one process) fp16 [8192,
+        // 3584] -> int8 with fp32 row scales G = 128 15.93 -> 15.63 us, G = 16
+        // 17.13 -> 16.38 us, -> e4m3 with UE8M0 16.0 -> 15.35 us; fp32 [8192,
+        // 7168] 46.6 -> 45.7 us.  (Rows of an even number of 16-bit slabs
+        // measured the same or slower with smaller blocks.)
+        if (uncapped && g.flat_slabs && !g.fp32) wpb = 1;
+        else if (uncapped && g.fp32) wpb = 2;
         if (knob(KNOB_WAVES_PER_BLOCK) > 0)
             wpb = (int)std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), 4);
         const int64_t wave_bytes = 2 * (int64_t)g.U * kSlab * es * (fuse ? 2 : 1);
@@ -288,6 +298,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
         a.flat_slabs = fs_ok && a.U == 2 ? 1 : 0;
+        geo.flat_slabs = a.flat_slabs != 0;
         a.n_slabs = rows * (int64_t)a.spr;
         if (a.n_slabs >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.spr_div = make_fastdiv((uint32_t)a.spr);
@@ -299,6 +310,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         bool uncapped = !fuse && geo.U == 2;
         if (knob(KNOB_GRID_MODE) >= 0) uncapped = knob(KNOB_GRID_MODE) > 0;
         // a large zero-filled tail also needs waves: one 1 KiB wave store each
+        geo.fp32 = es == 4;
         choose_blocks(geo, std::max<int64_t>(tasks, (a.q_pad_bytes + 1023) / 1024), cus,
                       fuse != 0, es, uncapped);
         // Block -> task mapping of a grid far larger than the chip: chunks of
@@ -311,8 +323,13 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // fp32 input is chunked whatever its row length (58.7 M elements, K =
         // 1024 and 2048: capped 51.5 us, uncapped with contiguous ranges 53.7,
         // chunked 49.4; K = 7168: capped 51.4, chunked 49.1-49.4).
-        if (uncapped && (a.tpr >= 4 || es == 4) && geo.grid >= 4 * 8 * kXcdChunk)
-            a.xcd_chunk = kXcdChunk;
+        // chunks of 512 one-wave blocks for flat-slab tasks, 256 two-wave
+        // blocks for fp32 input (measured with the block sizes above: fp16
+        // [8192, 3584] G = 16 16.66 us with chunks of 64, 16.38 with 512; fp32
+        // 45.65 us with 256)
+        const int64_t chunk = geo.wpb == 1 && geo.flat_slabs ? 512 : geo.wpb == 2 ? 256 : kXcdChunk;
+        if (uncapped && (a.tpr >= 4 || es == 4) && geo.grid >= 4 * 8 * chunk)
+            a.xcd_chunk = (int32_t)chunk;
         if (knob(KNOB_XCD_CHUNK) >= 0) a.xcd_chunk = (int32_t)std::min<int64_t>(knob(KNOB_XCD_CHUNK), 1 << 20);
         if (scale_layout == PTGQ_COL_MAJOR && a.rows_pad > rows)
             a.pad_cols = (int32_t)(scale_fmt == PTGQ_SCALE_UE8M0 ? (a.ng + 3) / 4 : a.ng);
@@ -532,9 +549,11 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
     unsigned grid, block;
     int nvl = 0;
     if (mode == TOKEN_WAVE) {
+        // one wave per row, rows_per_block rows (waves) per block
+        const int64_t rpb = knob(KNOB_WAVES_PER_BLOCK) > 0 ? std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), 4) : 4;
         nvl = vectors_per_lane(per_wave);
-        block = 256;
-        grid = (unsigned)((M + 3) / 4);
+        block = (unsigned)(64 * rpb);
+        grid = (unsigned)((M + rpb - 1) / rpb);
     } else if (mode == TOKEN_WAVE_LOOP) {
         // persistent waves, two rows in flight each: one four-wave block per
         // CU measured best (fp16 [8192, 3584]: 16.1 us against 16.7 for one

@@ -473,6 +473,7 @@ struct TaskLoc {
     uint32_t codes;
     int64_t m;
     int j;
+    int next_row;   // flat-slab tasks: first slab (0..UMAX) that lies in row m + 1
 };
 
 // `live` false: the loads are issued over an empty range (zeros, no memory
@@ -617,10 +618,12 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
         int slab = t.j + s;
         int64_t m = t.m;
         if constexpr (FS) {
-            if (slab >= a.spr) {
-                slab -= a.spr;
-                m += 1;
-            }
+            // 1 when slab s lies in the next row: the sign bit of
+            // next_row - s - 1, plain integer arithmetic (a comparison would
+            // be materialized through a vector register)
+            const int nx = (int)((uint32_t)(t.next_row - s - 1) >> 31);
+            slab -= nx * a.spr;
+            m += nx;
         }
         const uint32_t at = (uint32_t)s * kSlab;                    // offset in the task
         if constexpr (IN == IN_FP32) {
@@ -744,6 +747,7 @@ __device__ __forceinline__ TaskLoc row_task(const GroupArgs &a, const char *xrow
     l.codes = left < UMAX * kSlab ? left : UMAX * kSlab;
     l.m = m;
     l.j = j * UMAX;
+    l.next_row = UMAX;
     return l;
 }
 
@@ -789,6 +793,7 @@ struct FlatSlabMap {
         l.codes = (left < UMAX ? left : UMAX) * kSlab;
         l.m = m;
         l.j = (int)j;
+        l.next_row = (int)((uint32_t)a.spr - j);     // >= UMAX: no crossing
         return l;
     }
 };

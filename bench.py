@@ -23,7 +23,12 @@ dequantization error over its bound (null with --no-cpu-baseline).
     python bench.py --profile-main   (only the headline loop, for rocprofv3)
     python bench.py --profile-dequant / --profile-requant / --profile-fused /
                     --profile-masked / --profile-fp32 / --profile-per-token /
-                    --profile-int8  (only that loop)
+                    --profile-int8 / --profile-stream  (only that loop)
+
+`roofline.achievable_GBps` is the rate of a no-arithmetic stream with the
+headline kernel's traffic and geometry (ptgq_probe_stream, 2 bytes read per
+byte written) timed the same way; `stream_reference` gives the same stream at
+the element counts of the smaller workloads (graph figures).
     python bench.py --calib-copy     (a plain device copy of known size, for
                                       calibrating rocprofv3 byte counters)
 """
@@ -195,6 +200,21 @@ def make_flat_sets(torch, aq, x_host, M, K, G, fuse, out_dtype, fmt, layout, in_
         return lambda: aq.ptgq_quant(xi, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, 1e-10,
                                      q, s, check=False)
     return sets, [mk(*st) for st in sets]
+
+
+def stream_calls(torch, aq, M, K, nsets):
+    """The no-arithmetic stream with the plain quantization kernel's traffic and
+    geometry (2 bytes read per byte written, two 512-element slabs per wave,
+    uncapped grid, XCD chunks) over M x K 16-bit elements, rotated buffer
+    sets.  Its rate is what the memory system gives the headline's access
+    pattern."""
+    n = M * K
+    calls = []
+    for _ in range(nsets):
+        xi = torch.empty(n, dtype=torch.int16, device="cuda").fill_(0x3F80)
+        qi = torch.empty(n, dtype=torch.uint8, device="cuda")
+        calls.append(lambda xi=xi, qi=qi: aq.ptgq_probe_stream(xi, n, qi, check=False))
+    return calls, 3 * n
 
 
 def dequant_calls(torch, aq):
@@ -369,25 +389,40 @@ def rows_of_scales(s_dev, M, K, G, fmt, layout, rows):
     return out
 
 
-def error_over_bound(oracle, y, gq, code, sc, fp32_scale):
-    """max over elements of |dequant(code) - y| / bound.  The code is within
-    half an output ulp (e4m3 ulp of |v|, or 1 for int8) of v = y * multiplier;
-    with fp32 scales v = fl(y * fl(1/scale)) also drifts from y / scale by at
-    most |y / scale| * 2^-22 (two roundings), so bound = (ulp/2 + drift) *
-    scale.  `sc`: each element's scale (float64, broadcast over its group)."""
+def error_stats(oracle, y, gq, code, sc, fp32_scale):
+    """Dequantization error of every element against two bounds.
+
+    strict: |dequant(code) - y| <= ulp/2 * scale, half an output ulp of
+    |y / scale| (e4m3 ulp, or 1 for int8) -- the bound the codes meet when the
+    multiplier is exact (UE8M0 scales: v = y * 2^k exactly).
+    drift-aware: with fp32 scales v = fl(y * fl(1/scale)) also drifts from
+    y / scale by at most |y / scale| * 2^-22 (two roundings), so the bound is
+    (ulp/2 + drift) * scale, with the ulp taken at |y / scale| + drift.
+    Returns the worst error over the drift-aware bound and the number of
+    elements past the strict bound.  `sc`: each element's scale (float64,
+    broadcast over its group)."""
     vals = oracle.e4m3_decode(gq) if code == "e4m3" else gq.view(np.int8)
     dq = vals.astype(np.float64) * sc
     t = np.abs(y.astype(np.float64) / np.where(sc > 0, sc, 1.0))
     drift = t * 2.0 ** -22 if fp32_scale else np.zeros_like(t)
-    if code == "e4m3":
-        _, ex = np.frexp(t + drift)
-        ulp = np.where(t + drift >= 2.0 ** -6, np.ldexp(1.0, ex - 4), 2.0 ** -9)
-    else:
-        ulp = np.ones_like(t)
-    bound = (0.5 * ulp + drift) * sc
+
+    def half_ulp(a):
+        if code != "e4m3":
+            return np.full_like(a, 0.5)
+        _, ex = np.frexp(a)
+        return 0.5 * np.where(a >= 2.0 ** -6, np.ldexp(1.0, ex - 4), 2.0 ** -9)
+
     err = np.abs(dq - y.astype(np.float64))
+    bound = (half_ulp(t + drift) + drift) * sc
     r = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
-    return float(r.max()) if r.size else 0.0
+    strict = err > half_ulp(t) * sc
+    return (float(r.max()) if r.size else 0.0), int(strict.sum())
+
+
+def error_fields(oracle, y, gq, code, sc, fp32_scale):
+    worst, strict = error_stats(oracle, y, gq, code, sc, fp32_scale)
+    return {"max_error_over_bound": round(worst, 6), "elements": int(gq.size),
+            "past_strict_bound": strict}
 
 
 def capture_flat(x_host, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, q_dev, s_dev, rows):
@@ -412,10 +447,10 @@ def capture_flat(x_host, in_dtype, M, K, G, fuse, out_dtype, fmt, layout, q_dev,
         else:
             y = oracle.decode(xs, in_dtype)
         sc = gs.astype(np.float64) if fmt == "f32" else np.ldexp(1.0, gs.astype(np.int64) - 127)
-        return {"rows": int(n), "code_mismatches": int((gq != rq).sum()),
-                "scale_mismatches": int((gs.view(np.uint8) != rs.view(np.uint8)).sum()),
-                "max_error_over_bound": round(error_over_bound(
-                    oracle, y, gq, out_dtype, np.repeat(sc, G, axis=1), fmt == "f32"), 6)}
+        return dict({"rows": int(n), "code_mismatches": int((gq != rq).sum()),
+                     "scale_mismatches": int((gs.view(np.uint8) != rs.view(np.uint8)).sum())},
+                    **error_fields(oracle, y, gq, out_dtype, np.repeat(sc, G, axis=1),
+                                   fmt == "f32"))
     return check
 
 
@@ -446,6 +481,8 @@ def main():
     ap.add_argument("--profile-fp32", action="store_true")
     ap.add_argument("--profile-per-token", action="store_true")
     ap.add_argument("--profile-int8", action="store_true")
+    ap.add_argument("--profile-stream", action="store_true",
+                    help="only the no-arithmetic stream over the headline's element count")
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
 
@@ -500,6 +537,12 @@ def main():
         return
 
     M, K, G = 16384, 7168, 128
+    if args.profile_stream:
+        calls, nbytes = stream_calls(torch, aq, M, K, rotation_sets(alg_bytes_flat(M, K, G, 2, False, 1)))
+        r = timer.run(calls, args.steps, args.warmup, per_launch=False)
+        print(json.dumps({"profile": "stream", "steps": args.steps, "bytes": nbytes,
+                          "us_per_launch": r["region_ms"] * 1e3 / args.steps}))
+        return
     if args.profile_main:
         M = args.profile_m
     d = W.cfg2(M)
@@ -517,6 +560,13 @@ def main():
 
     main_res = timer.run(calls, args.steps, args.warmup)
     ms_per_step = main_res["region_ms"] / args.steps
+    # the stream reference over the same element count, timed the same way
+    # right after the headline (the same number of launches)
+    s_calls, s_bytes = stream_calls(torch, aq, M, K, nsets)
+    stream_res = timer.run(s_calls, args.steps, args.warmup, per_launch=False)
+    stream_us = stream_res["region_ms"] * 1e3 / args.steps
+    del s_calls
+    torch.cuda.empty_cache()
     value = foot / (ms_per_step * 1e-3) / 1e9
     # the kernel's average launch duration: the event pair around the K
     # back-to-back launches on the stream they run on (gaps included, so a
@@ -548,6 +598,20 @@ def main():
             ent["us_per_call_warm"] = round(t_warm * 1e3, 3)
         per_m.append(ent)
         del ci
+        torch.cuda.empty_cache()
+
+    # the stream reference at the smaller workloads' element counts (M x 7168
+    # for M = 4096 equals fp16 [8192, 3584]; M = 2048 is the fused
+    # workload's output count at M = 2048 x 2)
+    stream_ref = []
+    for Mi in (2048, 4096):
+        sc_i, sb_i = stream_calls(torch, aq, Mi, K, rotation_sets(3 * Mi * K))
+        per_graph = max(len(sc_i), min(200, max(8, math.ceil(1.2e10 / sb_i))))
+        us = timer.graph(sc_i, per_graph, 5) * 1e3
+        stream_ref.append({"elements": Mi * K, "bytes": sb_i, "us_per_call": round(us, 3),
+                           "GBps": round(sb_i / us / 1e3, 1),
+                           "frac_of_peak": round(sb_i / us / 1e3 / PEAK_GBS, 4)})
+        del sc_i
         torch.cuda.empty_cache()
 
     variants = {}
@@ -649,10 +713,9 @@ def main():
         def check5(oracle):
             rq5, rs5 = oracle.ptq_fp8(x5s, "fp16", len(rows5), 3584)
             sc = np.repeat(s50.astype(np.float64)[:, None], 3584, axis=1)
-            return {"rows": int(len(rows5)), "code_mismatches": int((q50 != rq5).sum()),
-                    "scale_mismatches": int((s50.view(np.uint32) != rs5.view(np.uint32)).sum()),
-                    "max_error_over_bound": round(error_over_bound(
-                        oracle, oracle.decode(x5s, "fp16"), q50, "e4m3", sc, True), 6)}
+            return dict({"rows": int(len(rows5)), "code_mismatches": int((q50 != rq5).sum()),
+                         "scale_mismatches": int((s50.view(np.uint32) != rs5.view(np.uint32)).sum())},
+                        **error_fields(oracle, oracle.decode(x5s, "fp16"), q50, "e4m3", sc, True))
         checks["per_token_fp8_fp16_M8192_K3584"] = check5
         del c5b
         torch.cuda.empty_cache()
@@ -729,9 +792,16 @@ def main():
                      "kernel": "ptgq_flat_kernel<bf16, G=128, no fuse, e4m3>",
                      "avg_launch_us": round(ms_per_step * 1e3, 3),
                      "avg_launch_us_isolated": round(main_res["launch_ms_mean"] * 1e3, 3),
-                     "kernel_source_digest": kernel_source_digest()},
+                     "kernel_source_digest": kernel_source_digest(),
+                     # what a no-arithmetic stream with this kernel's traffic
+                     # and geometry reaches here (ptgq_probe_stream, the same
+                     # launch count): the memory system's share of the gap
+                     "achievable_GBps": round(s_bytes / stream_us / 1e3, 1),
+                     "achievable_us_per_launch": round(stream_us, 3),
+                     "frac_of_achievable": round(achieved / (s_bytes / stream_us / 1e3), 4)},
         "parity_sample": parity.get("headline"),
         "per_m": per_m,
+        "stream_reference": stream_ref,
         "variants": variants,
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(main_res["wall_s"], 4),

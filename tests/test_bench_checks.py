@@ -45,14 +45,51 @@ def test_fused_and_fp32_checks():
 
 
 def test_error_bound_is_tight_for_a_half_ulp_miss():
-    """A code one step away from the nearest exceeds the bound."""
+    """A code one step away from the nearest exceeds both bounds and is
+    counted past the strict one."""
     y = np.array([[1.0625, 3.0]], dtype=np.float32)          # e4m3 1.0625 is a tie: 0x38
     sc = np.ones((1, 2))
     good = oracle.e4m3(y)
-    assert bench.error_over_bound(oracle, y, good, "e4m3", sc, False) <= 1.0
+    assert bench.error_stats(oracle, y, good, "e4m3", sc, False) == (1.0, 0)
     bad = good.copy()
     bad[0, 1] += 1                                          # 3.0 -> 3.25
-    assert bench.error_over_bound(oracle, y, bad, "e4m3", sc, False) > 1.0
+    worst, strict = bench.error_stats(oracle, y, bad, "e4m3", sc, False)
+    assert worst > 1.0 and strict == 1
+
+
+def test_strict_bound_counts_the_fp32_multiplier_drift():
+    """With an fp32 scale the reciprocal-multiply drift can move a value across
+    an e4m3 midpoint: y / s a hair below the midpoint 1.0625 while
+    fl(y * fl(1/s)) lands on it (ties to the even code 1.0): within the
+    drift-aware bound, past the strict one.  Independent of the oracle's
+    quantizer: the code is the nearest-even e4m3 of the fp32 product."""
+    s = np.float32(3.0)
+    inv = np.float32(1.0) / s
+    # search y near 1.0625 * 3 whose product rounds onto the midpoint
+    base = np.float32(1.0625) * s
+    found = None
+    for k in range(-64, 64):
+        y = np.nextafter(base, np.float32(np.inf if k > 0 else -np.inf))
+        for _ in range(abs(k)):
+            y = np.nextafter(y, np.float32(np.inf if k > 0 else -np.inf))
+        v = np.float32(y * inv)
+        if v == np.float32(1.0625) and float(y) / float(s) != 1.0625:
+            found = y
+            break
+    if found is None:
+        import pytest
+        pytest.skip("no drift case near this midpoint")
+    y = np.array([[found]], dtype=np.float32)
+    code = torch.from_numpy(np.array([[1.0625]], np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+    worst, strict = bench.error_stats(oracle, y, code, "e4m3", np.full((1, 1), float(s)), True)
+    exact = float(y[0, 0]) / float(s)
+    nearest = 1.125 if exact > 1.0625 else 1.0
+    if torch.from_numpy(np.array([[nearest]], np.float32)).to(torch.float8_e4m3fn) \
+            .view(torch.uint8).numpy()[0, 0] != code[0, 0]:
+        assert worst <= 1.0 and strict == 1
+    else:
+        assert worst <= 1.0 and strict == 0
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -70,7 +70,8 @@ def test_masked_workload_sized_by_expected_rows():
 @pytest.mark.parametrize("K", [7168, 4096, 14336, 2048, 1024])
 def test_fp32_input_uncapped_and_xcd_chunked_for_every_row_length(K):
     p = plan("fp32", 8192 * 7168 // K, K)
-    assert p["slabs_per_task"] == 2 and p["uncapped"] == 1 and p["xcd_chunk"] == 64
+    assert p["slabs_per_task"] == 2 and p["uncapped"] == 1
+    assert p["block"] == 128 and p["xcd_chunk"] == 256     # two-wave blocks
 
 
 @pytest.mark.parametrize("K", [1536, 2560])
@@ -83,7 +84,8 @@ def test_odd_slab_rows_take_flat_slab_tasks_across_row_ends():
     p = plan("fp16", 8192, 3584)                   # 7 slabs per row
     assert p["slabs_per_task"] == 2 and p["uncapped"] == 1 and p["flat_slabs"] == 1
     assert p["tasks"] == 8192 * 7 // 2             # no half task per row
-    assert p["grid"] == p["tasks"] // 4 and p["xcd_chunk"] == 64
+    # one-wave blocks, dealt to the XCDs in chunks of 512
+    assert p["block"] == 64 and p["grid"] == p["tasks"] and p["xcd_chunk"] == 512
     # fp32 rows of an odd slab count too
     p = plan("fp32", 4096, 3584)
     assert p["slabs_per_task"] == 2 and p["flat_slabs"] == 1 and p["tasks"] == 4096 * 7 // 2
@@ -134,7 +136,9 @@ def test_rules_hold_for_random_shapes(cus):
         else:
             assert p["tasks"] == rows * p["tasks_per_row"]
             assert U == 1 or fuse or K % SLAB != 0 or spr % 2 == 0
-        assert p["block"] in (64, 256, 1024) and p["grid"] >= 1
+        assert p["block"] in (64, 128, 256, 1024) and p["grid"] >= 1
+        if p["block"] == 128:
+            assert dt == "fp32" and p["uncapped"]
         waves = p["grid"] * p["block"] // 64
         if p["uncapped"]:
             assert waves >= p["tasks"]                  # one wave per task
