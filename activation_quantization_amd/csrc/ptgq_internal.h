@@ -92,6 +92,8 @@ struct TokenArgs {
     int64_t M;
     int64_t K;
     int32_t nv;               // vectors per row (row bytes / vector bytes)
+    int32_t xcd_chunk;        // one-block-per-row kernels: blocks per XCD chunk of
+                              // the block -> row mapping (0: block b takes row b)
 };
 
 enum TokenMode : int { TOKEN_WAVE = 0, TOKEN_BLOCK = 1, TOKEN_BLOCK_LOOP = 2, TOKEN_WAVE_LOOP = 3 };

@@ -1147,6 +1147,19 @@ struct TokVec {
         }
         return r;
     }
+    // through a buffer descriptor: past its range the load reads zeros
+    __device__ static __forceinline__ raw_t load_buf(rsrc_t rs, uint32_t off)
+    {
+        raw_t r;
+        if constexpr (VB == 16) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kStreamPolicy);
+            r = make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kStreamPolicy);
+            r = make_uint2(v.x, v.y);
+        }
+        return r;
+    }
     __device__ static __forceinline__ raw_t zero()
     {
         raw_t r;
@@ -1192,6 +1205,20 @@ struct TokVec {
         }
     }
 
+    // codes of one vector through a buffer descriptor (dropped past its range)
+    __device__ static __forceinline__ void store_codes_buf(rsrc_t rs, uint32_t off,
+                                                           const float (&v)[EV])
+    {
+        if constexpr (EV == 8) {
+            u32x2 o;
+            o.x = e4m3x4<true>(v[0], v[1], v[2], v[3]);
+            o.y = e4m3x4<true>(v[4], v[5], v[6], v[7]);
+            __builtin_amdgcn_raw_buffer_store_b64(o, rs, off, 0, kStreamPolicy);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b32(e4m3x4<true>(v[0], v[1], v[2], v[3]), rs, off,
+                                                  0, kStreamPolicy);
+        }
+    }
     __device__ static __forceinline__ void store_codes(uint8_t *p, const float (&v)[EV])
     {
         if constexpr (EV == 8) {
@@ -1337,6 +1364,7 @@ __global__ __launch_bounds__(256) void ptq_wave_loop_kernel(TokenArgs a)
     }
 }
 
+// Block maximum (up to 8 waves), uniform over the block.
 __device__ __forceinline__ uint32_t block_max_bits(uint32_t v, uint32_t *red)
 {
     v = wave_max_bits(v);
@@ -1348,23 +1376,27 @@ __device__ __forceinline__ uint32_t block_max_bits(uint32_t v, uint32_t *red)
     return m;
 }
 
+// One block per row (1 to 8 waves), the row held in registers: NV vectors
+// per lane, lane t of the block holding vectors t, t + threads, ...  Loads
+// and code stores go through buffer descriptors over the row, so vectors past
+// the row read zeros and their stores are dropped (no branch per vector).
 template <int IN, int VB, int NV>
-__global__ __launch_bounds__(256) void ptq_block_kernel(TokenArgs a)
+__global__ __launch_bounds__(512) void ptq_block_kernel(TokenArgs a)
 {
     using TV = TokVec<IN, VB>;
     constexpr int EV = TV::EV;
-    __shared__ uint32_t red[4];
+    __shared__ uint32_t red[8];
+    asm volatile("" ::"s"(a.x), "s"(a.q), "s"(a.s), "s"(a.K), "s"(a.xcd_chunk), "s"(gridDim.x));
     const int tid = threadIdx.x;
-    const int64_t m = blockIdx.x;
-    const uint8_t *xr = static_cast<const uint8_t *>(a.x) + m * a.K * TV::insz;
-    uint8_t *qr = a.q + m * a.K;
+    const int64_t m = a.xcd_chunk > 0 ? logical_block(blockIdx.x, gridDim.x, a.xcd_chunk)
+                                      : (int)blockIdx.x;
+    const uint32_t row_bytes = (uint32_t)(a.K * TV::insz);
+    const rsrc_t rx = make_rsrc(static_cast<const uint8_t *>(a.x) + m * row_bytes, row_bytes);
+    const rsrc_t rq = make_rsrc(a.q + m * a.K, (uint32_t)a.K);
     typename TV::raw_t raw[NV];
     const int nt = blockDim.x;
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int i = tid + nt * k;
-        raw[k] = (i < a.nv) ? TV::load(xr + (int64_t)i * VB) : TV::zero();
-    }
+    for (int k = 0; k < NV; ++k) raw[k] = TV::load_buf(rx, (uint32_t)(tid + nt * k) * VB);
     uint32_t amax = 0;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -1377,13 +1409,10 @@ __global__ __launch_bounds__(256) void ptq_block_kernel(TokenArgs a)
     with_uniform_multiplier(inv, [&](auto mode) {
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
-            const int i = tid + nt * k;
-            if (i < a.nv) {
-                float f[EV], v[EV];
-                TV::widen(raw[k], f);
-                scale_by<decltype(mode)::value>(f, inv, v);
-                TV::store_codes(qr + (int64_t)i * EV, v);
-            }
+            float f[EV], v[EV];
+            TV::widen(raw[k], f);
+            scale_by<decltype(mode)::value>(f, inv, v);
+            TV::store_codes_buf(rq, (uint32_t)(tid + nt * k) * EV, v);
         }
     });
 }
