@@ -529,14 +529,22 @@ int ptq_quant_fp8(const void *x, int in_dtype, int64_t M, int64_t K, void *q, fl
     a.xcd_chunk = 0;
 
     // Dispatch (the analogue of the warp/CTA threshold of the sglang #34257
-    // page, by row length here): one block per row, of one wave per ~4 KiB of
-    // row, for rows that fit in registers (16 vectors per lane); longer rows
-    // take the two-pass loop.  Measured on MI355X against one wave per row and
-    // persistent waves: equal or faster for 2, 7, 8 and 14 KiB rows (bf16
-    // [16384, 7168]: 6.4 TB/s).  The other modes stay selectable for tests.
+    // page, by row length here): one block per row for rows that fit in
+    // registers (16 vectors per lane); longer rows take the two-pass loop.
+    // Measured on MI355X against one wave per row and persistent waves: equal
+    // or faster for 2, 7, 8 and 14 KiB rows.  The other modes stay selectable
+    // for tests.
     const int64_t per_wave = (nv + 63) / 64;
-    // block mode: one block per row with one wave per ~4 KiB of row (1..4)
-    int64_t tw = std::min<int64_t>(4, std::max<int64_t>(1, (row_bytes + 4095) / 4096));
+    // Waves per row: the largest power of two up to 8 that leaves each wave
+    // at least 1.75 KiB of the row.  Measured on MI355X (A/B in one process,
+    // waves per row 1..8): best or within 0.3 % of best for 16-bit rows of
+    // 2.7, 4, 7, 8, 10, 12, 14 and 16 KiB and fp32 rows of 14 and 28 KiB
+    // (fp16 [8192, 3584] 15.53 us with 4 waves, 15.65 with 2, 18.6-20.5 with
+    // 5-8; bf16 [16384, 7168] 53.6 with 8, 54.7 with 4); fp32 [8192, 2048]
+    // 15.1 us, against 14.5 with 3 waves.  Fewer than ~1.75 KiB per wave is
+    // slower everywhere.
+    int64_t tw = 1;
+    while (tw < 8 && row_bytes >= tw * 2 * 1792) tw *= 2;
     if (knob(KNOB_WAVES_PER_BLOCK) > 0) tw = std::min<int64_t>(knob(KNOB_WAVES_PER_BLOCK), 8);
     const int64_t per_block = (nv + 64 * tw - 1) / (64 * tw);
     TokenMode mode;

@@ -183,6 +183,27 @@ def test_per_token_modes(in_dtype, mode):
         aq.ptgq_set_tuning(3, -1)
 
 
+@pytest.mark.parametrize("waves", [1, 2, 3, 5, 7, 8])
+def test_per_token_block_waves_per_row(waves):
+    """One block per row with every block size the override allows (rows
+    whose vector count does not divide the block, idle lanes and waves, the
+    XCD-chunked row order at M >= 1024)."""
+    try:
+        aq.ptgq_set_tuning(3, 1)
+        aq.ptgq_set_tuning(1, waves)
+        for in_dtype, M, K in [("fp16", 1100, 3584), ("bf16", 37, 7168), ("fp32", 64, 1076),
+                               ("bf16", 1030, 2048), ("fp32", 9, 7168)]:
+            gen = {"bf16": W.normal_bf16, "fp16": W.normal_fp16, "fp32": W.normal_f32}[in_dtype]
+            x = gen(M * 13 + K + waves, (M, K))
+            x[M // 3] = 0
+            gq, gs = run_per_token(x, in_dtype, M, K)
+            compare(f"per-token block waves={waves} {in_dtype} M={M} K={K}", gq, gs,
+                    *oracle.ptq_fp8(x, in_dtype, M, K))
+    finally:
+        aq.ptgq_set_tuning(1, -1)
+        aq.ptgq_set_tuning(3, -1)
+
+
 @pytest.mark.parametrize("K", [1368, 3584, 1076, 4096])
 def test_per_token_many_rows_wave_dispatch(K):
     """Enough rows for the persistent wave loop (several rows per wave, an odd
