@@ -23,14 +23,16 @@ dequantization error over its bound (null with --no-cpu-baseline).
     python bench.py --profile-main   (only the headline loop, for rocprofv3)
     python bench.py --profile-dequant / --profile-requant / --profile-fused /
                     --profile-masked / --profile-fp32 / --profile-per-token /
-                    --profile-int8 / --profile-stream  (only that loop)
+                    --profile-int8 [--int8-group G] / --profile-stream
+                    (only that loop; --graph: the variant loops in HIP graphs)
+    ... --tuning KNOB=VALUE  (profile loops only, repeatable: a launch-geometry
+                              override of ptgq_set_tuning, for comparing
+                              geometries under the profiler)
 
 `roofline.achievable_GBps` is the rate of a no-arithmetic stream with the
 headline kernel's traffic and geometry (ptgq_probe_stream, 2 bytes read per
 byte written) timed the same way; `stream_reference` gives the same stream at
 the element counts of the smaller workloads (graph figures).
-    python bench.py --calib-copy     (a plain device copy of known size, for
-                                      calibrating rocprofv3 byte counters)
 """
 import argparse
 import hashlib
@@ -316,12 +318,12 @@ def per_token_calls(torch, aq, d5):
     return c5b, f5b
 
 
-def int8_fp16_calls(torch, aq, W):
-    """fp16 [8192, 3584] -> int8, G = 128, fp32 row-major scales, over rotated
-    buffer sets.  Returns the calls and the algorithmic bytes."""
+def int8_fp16_calls(torch, aq, W, G=128):
+    """fp16 [8192, 3584] -> int8, group size G, fp32 row-major scales, over
+    rotated buffer sets.  Returns the calls and the algorithmic bytes."""
     d5 = W.cfg5()
-    f5 = alg_bytes_flat(8192, 3584, 128, 2, False, 4)
-    _, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, 128, False, "int8", "f32", "row",
+    f5 = alg_bytes_flat(8192, 3584, G, 2, False, 4)
+    _, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, G, False, "int8", "f32", "row",
                            "fp16", rotation_sets(f5))
     return c5, f5
 
@@ -483,8 +485,17 @@ def main():
     ap.add_argument("--profile-int8", action="store_true")
     ap.add_argument("--profile-stream", action="store_true",
                     help="only the no-arithmetic stream over the headline's element count")
-    ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--int8-group", type=int, default=128, choices=[16, 32, 64, 128],
+                    help="group size of the --profile-int8 loop")
+    ap.add_argument("--graph", action="store_true",
+                    help="variant profile loops: launch in HIP graphs of 200 launches")
+    ap.add_argument("--tuning", action="append", default=[], metavar="KNOB=VALUE",
+                    help="launch-geometry override for the profile loops (ptgq_set_tuning)")
     args = ap.parse_args()
+    tuning = []
+    for t in args.tuning:
+        k, _, v = t.partition("=")
+        tuning.append((int(k), int(v)))
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this quantization path needs no exchange between "
@@ -503,17 +514,14 @@ def main():
     aq.ptgq_init(0)
     timer = Timer(torch)
 
-    if args.calib_copy:
-        # plain device-to-device copy of exactly 1 GiB, 5 times
-        a = torch.empty(GIB, dtype=torch.uint8, device="cuda")
-        b = torch.empty(GIB, dtype=torch.uint8, device="cuda")
-        a.fill_(1)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"calib_copy_bytes_each_way": GIB, "copies": 5}))
-        return
+    profiling = (args.profile_main or args.profile_dequant or args.profile_requant or
+                 args.profile_fused or args.profile_masked or args.profile_fp32 or
+                 args.profile_per_token or args.profile_int8 or args.profile_stream)
+    if tuning and not profiling:
+        print("--tuning applies to the profile loops only", file=sys.stderr)
+        sys.exit(2)
+    for k, v in tuning:
+        aq.ptgq_set_tuning(k, v)
 
     if (args.profile_dequant or args.profile_requant or args.profile_fused or args.profile_masked
             or args.profile_fp32 or args.profile_per_token or args.profile_int8):
@@ -530,10 +538,17 @@ def main():
         elif args.profile_per_token:
             name, (calls, nbytes) = "per_token", per_token_calls(torch, aq, W.cfg5())
         else:
-            name, (calls, nbytes) = "int8", int8_fp16_calls(torch, aq, W)
-        r = timer.run(calls, args.steps, args.warmup, per_launch=False)
+            name, (calls, nbytes) = "int8", int8_fp16_calls(torch, aq, W, args.int8_group)
+        if args.graph:
+            # back-to-back launches in HIP graphs of 200, as the variant
+            # figures are taken (launched one by one from Python, a kernel
+            # shorter than the launch interval starts from an idle GPU)
+            us = timer.graph(calls, 200, max(1, args.steps // 200), min_ms=0.0) * 1e3
+        else:
+            r = timer.run(calls, args.steps, args.warmup, per_launch=False)
+            us = r["region_ms"] * 1e3 / args.steps
         print(json.dumps({"profile": name, "steps": args.steps, "bytes": nbytes,
-                          "us_per_launch": r["region_ms"] * 1e3 / args.steps}))
+                          "tuning": dict(tuning), "graph": args.graph, "us_per_launch": us}))
         return
 
     M, K, G = 16384, 7168, 128
@@ -767,7 +782,7 @@ def main():
     for name in variants:
         variants[name]["parity"] = parity.get(name)
 
-    traffic = read_traffic("traffic_ptgq_flat_cfg2_M16384.md")
+    traffic = read_traffic("traffic_ptgq_flat_bf16_M16384_K7168.md")
     out = {
         "metric": METRIC,
         "value": round(value, 1),
