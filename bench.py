@@ -637,7 +637,8 @@ def main():
         fi8 = alg_bytes_flat(M, K, G, 2, False, 1)
         si8, ci8 = make_flat_sets(torch, aq, x_host, M, K, G, False, "int8", "ue8m0", "col",
                                   "bf16", rotation_sets(fi8))
-        variants["int8_ue8m0_bf16_M16384_K7168"] = variant_entry(timer, ci8, fi8)
+        variants["int8_ue8m0_bf16_M16384_K7168"] = dict(variant_entry(timer, ci8, fi8),
+                                                        input_fnv1a=W.fnv1a(x_host))
         checks["int8_ue8m0_bf16_M16384_K7168"] = capture_flat(
             x_host, "bf16", M, K, G, False, "int8", "ue8m0", "col", si8[0][1], si8[0][2],
             spread(M))
@@ -645,7 +646,8 @@ def main():
         # fp32 input [8192, 7168] -> e4m3, packed column-major UE8M0 scales
         M32 = 8192
         x32h, c32, f32b = fp32_calls(torch, aq, W)
-        variants["fp32_input_M8192_K7168"] = variant_entry(timer, c32, f32b)
+        variants["fp32_input_M8192_K7168"] = dict(variant_entry(timer, c32, f32b),
+                                                  input_fnv1a=W.fnv1a(x32h))
         checks["fp32_input_M8192_K7168"] = capture_flat(
             x32h, "fp32", M32, K, G, False, "e4m3", "ue8m0", "col", c32[0].__defaults__[1],
             c32[0].__defaults__[2], spread(M32))
@@ -653,7 +655,8 @@ def main():
         torch.cuda.empty_cache()
         # fused silu(gate)*up, bf16 [8192, 2*4096]
         d3, s3, c3, f3 = fused_calls(torch, aq, W)
-        variants["fused_silu_mul_M8192_K4096"] = variant_entry(timer, c3, f3)
+        variants["fused_silu_mul_M8192_K4096"] = dict(variant_entry(timer, c3, f3),
+                                                      input_fnv1a=W.fnv1a(d3["x"]))
         checks["fused_silu_mul_M8192_K4096"] = capture_flat(
             d3["x"], "bf16", 8192, 4096, 128, True, "e4m3", "ue8m0", "col", s3[0][1], s3[0][2],
             spread(8192))
@@ -669,7 +672,7 @@ def main():
             s3m, c3m = make_flat_sets(torch, aq, d3m["x"], M3, 4096, 128, True, "e4m3", "ue8m0",
                                       "col", "bf16", rotation_sets(f3m))
             name = f"fused_silu_mul_M{M3}_K4096"
-            variants[name] = variant_entry(timer, c3m, f3m)
+            variants[name] = dict(variant_entry(timer, c3m, f3m), input_fnv1a=W.fnv1a(d3m["x"]))
             checks[name] = capture_flat(d3m["x"], "bf16", M3, 4096, 128, True, "e4m3", "ue8m0",
                                         "col", s3m[0][1], s3m[0][2], spread(M3))
             del c3m, s3m
@@ -679,7 +682,8 @@ def main():
         f1 = alg_bytes_flat(64, 2048, 128, 2, False, 4)
         s1, c1 = make_flat_sets(torch, aq, d1["x"], 64, 2048, 128, False, "e4m3", "f32", "row",
                                 "bf16", rotation_sets(f1))
-        variants["plain_fp32_rowmajor_M64_K2048"] = variant_entry(timer, c1, f1)
+        variants["plain_fp32_rowmajor_M64_K2048"] = dict(variant_entry(timer, c1, f1),
+                                                         input_fnv1a=W.fnv1a(d1["x"]))
         checks["plain_fp32_rowmajor_M64_K2048"] = capture_flat(
             d1["x"], "bf16", 64, 2048, 128, False, "e4m3", "f32", "row", s1[0][1], s1[0][2],
             np.arange(64))
@@ -689,7 +693,8 @@ def main():
         E, T, K4, mm = d4["E"], d4["T"], d4["K"], d4["masked_m"]
         sb4 = aq.ptgq_scale_bytes(T, K4, 128, "ue8m0", "col")
         variants["masked_E32_T384_K2048_fused"] = dict(variant_entry(timer, c4, f4),
-                                                       live_rows=live)
+                                                       live_rows=live,
+                                                       input_fnv1a=W.fnv1a(d4["x"]))
         # every live row of four experts of set 0 (its other rows hold
         # whatever the buffer held: only live rows are checked)
         q40, s40 = c4[0].__defaults__[1], c4[0].__defaults__[2]
@@ -703,7 +708,8 @@ def main():
         f5 = alg_bytes_flat(8192, 3584, 128, 2, False, 4)
         s5s, c5 = make_flat_sets(torch, aq, d5["x"], 8192, 3584, 128, False, "int8", "f32", "row",
                                  "fp16", rotation_sets(f5))
-        variants["int8_fp16_M8192_K3584_G128"] = variant_entry(timer, c5, f5)
+        variants["int8_fp16_M8192_K3584_G128"] = dict(variant_entry(timer, c5, f5),
+                                                      input_fnv1a=W.fnv1a(d5["x"]))
         checks["int8_fp16_M8192_K3584_G128"] = capture_flat(
             d5["x"], "fp16", 8192, 3584, 128, False, "int8", "f32", "row", s5s[0][1], s5s[0][2],
             spread(8192))
@@ -714,12 +720,13 @@ def main():
             s5g, c5g = make_flat_sets(torch, aq, d5["x"], 8192, 3584, G5, False, "int8", "f32",
                                       "row", "fp16", rotation_sets(f5g))
             name = f"int8_fp16_M8192_K3584_G{G5}"
-            variants[name] = variant_entry(timer, c5g, f5g)
+            variants[name] = dict(variant_entry(timer, c5g, f5g), input_fnv1a=W.fnv1a(d5["x"]))
             checks[name] = capture_flat(d5["x"], "fp16", 8192, 3584, G5, False, "int8", "f32",
                                         "row", s5g[0][1], s5g[0][2], spread(8192, 8))
             del c5g, s5g
         c5b, f5b = per_token_calls(torch, aq, d5)
-        variants["per_token_fp8_fp16_M8192_K3584"] = variant_entry(timer, c5b, f5b)
+        variants["per_token_fp8_fp16_M8192_K3584"] = dict(variant_entry(timer, c5b, f5b),
+                                                          input_fnv1a=W.fnv1a(d5["x"]))
         rows5 = spread(8192)
         x5s = np.ascontiguousarray(d5["x"][rows5])
         q50 = c5b[0].__defaults__[1][rows5].cpu().numpy()
@@ -799,7 +806,7 @@ def main():
         "config": {"workload": "bf16 [16384, 7168] -> e4m3, G=128, UE8M0 scales column-major "
                                "(M padded to 4), N(0,1) with 1% outlier channels x30",
                    "M": M, "K": K, "group_size": G, "eps": 1e-10, "buffer_sets": nsets,
-                   "algorithmic_bytes_per_step": foot},
+                   "algorithmic_bytes_per_step": foot, "input_fnv1a": W.fnv1a(x_host)},
         "frac_of_peak": round(value / PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
