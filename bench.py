@@ -785,6 +785,20 @@ def main():
                "ns_per_element": round(dt / (M * K) * 1e9, 2),
                "host": {"cpu_model": host_cpu_model(), "cores_visible": len(allowed),
                         "pinned_core": core}}
+        # context: the same oracle run rows-parallel, one contiguous row range
+        # per thread on every visible core (at most 16), one whole step
+        from concurrent.futures import ThreadPoolExecutor
+        nth = min(16, len(allowed))
+        bounds = np.linspace(0, M, nth + 1).astype(np.int64)
+        with ThreadPoolExecutor(nth) as ex:
+            t1 = time.perf_counter()
+            list(ex.map(lambda i: oracle.ptgq(x_host[bounds[i]:bounds[i + 1]], "bf16",
+                                              int(bounds[i + 1] - bounds[i]), K, G, False,
+                                              "e4m3", "ue8m0", "col", eps=1e-10), range(nth)))
+            dtp = time.perf_counter() - t1
+        cpu["rows_parallel"] = {"value": round(foot / dtp / 1e9, 4), "unit": "GB/s", "cores": nth,
+                                "sample": f"one full step, {nth} threads over contiguous row "
+                                          f"ranges, {dtp:.2f} s"}
         parity = {name: check(oracle) for name, check in checks.items()}
     for name in variants:
         variants[name]["parity"] = parity.get(name)
