@@ -246,7 +246,12 @@ def dequant_calls(torch, aq):
 
         def check(oracle):
             ref = oracle.dequant(qs, "e4m3", len(rows), Kd, 128, srow, "ue8m0", "row", "bf16")
-            return {"rows": int(len(rows)), "mismatches": int((got != ref).sum())}
+            # the exact product code * 2^(e - 127) against the bf16 output
+            exact = oracle.e4m3_decode(qs).astype(np.float64) * np.repeat(
+                np.ldexp(1.0, srow.astype(np.int64) - 127), 128, axis=1)
+            return {"rows": int(len(rows)), "mismatches": int((got != ref).sum()),
+                    "elements": int(got.size),
+                    "past_strict_bound": bf16_past_half_ulp(exact, got)}
         return check
     return cd, fd, capture
 
@@ -363,12 +368,20 @@ def requant_calls(torch, aq, live):
                           outs[0][e, rows].cpu().numpy()))
 
         def check(oracle):
-            bad = 0
+            bad, worst, strict, n = 0, 0.0, 0, 0
             for xr, srow, got in cases:
                 ref = oracle.requant_fp8(xr, 1, len(rows), K8, 128, srow,
                                          (len(rows) * ng, ng, 1), None, 2.0)
                 bad += int((got != ref[0]).sum())
-            return {"rows": len(cases) * len(rows), "mismatches": bad}
+                # the exact dequantized input, against the output code times
+                # the output scale (two fp32 roundings: the drift-aware bound)
+                y = oracle.e4m3_decode(xr[0]).astype(np.float64) * np.repeat(
+                    srow.astype(np.float64), 128, axis=1)
+                w, st = error_stats(oracle, y, got, "e4m3", np.full(y.shape, 2.0), True)
+                worst, strict, n = max(worst, w), strict + st, n + got.size
+            return {"rows": len(cases) * len(rows), "mismatches": bad,
+                    "max_error_over_bound": round(worst, 6), "elements": n,
+                    "past_strict_bound": strict}
         return check
     return cq, fq, capture
 
@@ -419,6 +432,18 @@ def error_stats(oracle, y, gq, code, sc, fp32_scale):
     r = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
     strict = err > half_ulp(t) * sc
     return (float(r.max()) if r.size else 0.0), int(strict.sum())
+
+
+def bf16_past_half_ulp(exact, got_bits):
+    """Number of bf16 outputs (bit patterns `got_bits`) farther than half a
+    bf16 ulp from the exact float64 values `exact` (finite, below the bf16
+    maximum): the strict bound of a dequantization to bf16."""
+    out = (np.asarray(got_bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    a = np.abs(exact)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    # |exact| in [2^(ex-1), 2^ex): ulp 2^(ex-1-7), subnormals 2^-133
+    half = np.ldexp(1.0, np.maximum(ex - 1, -126) - 8)
+    return int((np.abs(out - exact) > half).sum())
 
 
 def error_fields(oracle, y, gq, code, sc, fp32_scale):

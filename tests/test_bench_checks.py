@@ -92,6 +92,22 @@ def test_strict_bound_counts_the_fp32_multiplier_drift():
         assert worst <= 1.0 and strict == 0
 
 
+def test_bf16_strict_bound_count():
+    """Half a bf16 ulp around exact values: the nearest bf16 passes, one ulp
+    off fails, ties pass either way, subnormals and zero included."""
+    exact = np.array([1.0, 1.0 + 2.0 ** -8, 3.0 * 2.0 ** -130, 0.0, -448.0, 1.0 + 2.0 ** -9])
+    near = torch.tensor(exact, dtype=torch.float64).to(torch.bfloat16).view(torch.int16)
+    bits = near.numpy().view(np.uint16)
+    assert bench.bf16_past_half_ulp(exact, bits) == 0
+    off = bits.copy()
+    off[0] += 1                      # 1 + 2^-7: one ulp above 1.0
+    off[2] += 1                      # subnormal, one ulp (2^-133) off
+    assert bench.bf16_past_half_ulp(exact, off) == 2
+    tie = bits.copy()
+    tie[1] = np.uint16(0x3F81)       # 1 + 2^-8 is a tie: 1 + 2^-7 is half an ulp away too
+    assert bench.bf16_past_half_ulp(exact, tie) == 0
+
+
 def test_bench_refuses_more_than_one_gpu():
     """The path needs no exchange between GPUs; bench.py measures one and says
     so for any other count, before touching a device."""
