@@ -318,19 +318,19 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // 64 blocks per XCD (measured on MI355X, bf16 [M, 7168]: M = 4096
         // 16.4 -> 15.4 us, M = 16384 55.9 -> 53.4 us against one contiguous
         // range per XCD; chunks of 32..256 blocks within 1 %; fp16 [16384,
-        // 3584]: 30.3 -> 28.6 us).  Rows of fewer than 4 tasks (fp16 K =
-        // 1536, 2560: 3-7 % slower chunked) and grids of fewer than 4 spans
-        // (M = 256 here: 3.1 us against 3.3-3.6) keep the contiguous ranges.
-        // fp32 input is chunked whatever its row length (58.7 M elements, K =
-        // 1024 and 2048: capped 51.5 us, uncapped with contiguous ranges 53.7,
-        // chunked 49.4; K = 7168: capped 51.4, chunked 49.1-49.4).
-        // chunks of 512 one-wave blocks for flat-slab tasks, 256 two-wave
+        // 3584]: 30.3 -> 28.6 us; short rows too: bf16 [16384, 2048] 17.63
+        // -> 17.07 us, [32768, 1024] 17.57 -> 17.09, [16384, 3072] 24.84 ->
+        // 24.25).  Grids of fewer than 4 spans (M = 256 here: 3.1 us against
+        // 3.3-3.6) keep the contiguous ranges.  fp32 input: 58.7 M elements,
+        // K = 1024 and 2048: capped 51.5 us, uncapped with contiguous ranges
+        // 53.7, chunked 49.4; K = 7168: capped 51.4, chunked 49.1-49.4.
+        // Chunks of 512 one-wave blocks for flat-slab tasks, 256 two-wave
         // blocks for fp32 input (measured with the block sizes above: fp16
         // [8192, 3584] G = 16 16.66 us with chunks of 64, 16.38 with 512; fp32
-        // 45.65 us with 256)
+        // 45.65 us with 256; fp16 [16384, 1536] 13.95 -> 13.69-13.78 us
+        // against contiguous ranges, bf16 [8192, 2560] 11.91 -> 11.70).
         const int64_t chunk = geo.wpb == 1 && geo.flat_slabs ? 512 : geo.wpb == 2 ? 256 : kXcdChunk;
-        if (uncapped && (a.tpr >= 4 || es == 4) && geo.grid >= 4 * 8 * chunk)
-            a.xcd_chunk = (int32_t)chunk;
+        if (uncapped && geo.grid >= 4 * 8 * chunk) a.xcd_chunk = (int32_t)chunk;
         if (knob(KNOB_XCD_CHUNK) >= 0) a.xcd_chunk = (int32_t)std::min<int64_t>(knob(KNOB_XCD_CHUNK), 1 << 20);
         if (scale_layout == PTGQ_COL_MAJOR && a.rows_pad > rows)
             a.pad_cols = (int32_t)(scale_fmt == PTGQ_SCALE_UE8M0 ? (a.ng + 3) / 4 : a.ng);

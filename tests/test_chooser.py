@@ -74,10 +74,18 @@ def test_fp32_input_uncapped_and_xcd_chunked_for_every_row_length(K):
     assert p["block"] == 128 and p["xcd_chunk"] == 256     # two-wave blocks
 
 
-@pytest.mark.parametrize("K", [1536, 2560])
-def test_short_16bit_rows_keep_contiguous_xcd_ranges(K):
-    p = plan("fp16", 16384, K)                     # 3 or 5 slabs: 2 or 3 tasks per row
-    assert p["uncapped"] == 1 and p["tasks_per_row"] < 4 and p["xcd_chunk"] == 0
+@pytest.mark.parametrize("K,chunk", [(1536, 512), (2560, 512), (1024, 64), (2048, 64), (3072, 64)])
+def test_short_16bit_rows_are_xcd_chunked_too(K, chunk):
+    # odd slab counts: flat-slab tasks in one-wave blocks; even: row tasks
+    p = plan("fp16", 16384, K)
+    assert p["uncapped"] == 1 and p["tasks_per_row"] < 4 and p["xcd_chunk"] == chunk
+
+
+def test_small_uncapped_grids_keep_contiguous_xcd_ranges():
+    # 12288 one-wave blocks: under 4 spans of 8 x 512
+    p = plan("fp16", 8192, 1536)
+    assert p["uncapped"] == 1 and p["flat_slabs"] == 1 and p["block"] == 64
+    assert p["grid"] == 12288 and p["xcd_chunk"] == 0
 
 
 def test_odd_slab_rows_take_flat_slab_tasks_across_row_ends():
@@ -146,8 +154,7 @@ def test_rules_hold_for_random_shapes(cus):
         elif waves < p["tasks"]:
             assert p["grid"] % cus == 0                 # looping grids: equal blocks per CU
         if p["xcd_chunk"]:
-            assert p["uncapped"] and p["grid"] >= 4 * 8 * 64
-            assert p["tasks_per_row"] >= 4 or dt == "fp32"
+            assert p["uncapped"] and p["grid"] >= 4 * 8 * p["xcd_chunk"]
         if p["silu_table"]:
             assert fuse and dt == "bf16" and p["block"] == 1024
 
