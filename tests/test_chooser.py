@@ -47,6 +47,15 @@ def test_m256_one_slab_tasks_capped_grid_covers_every_task_once():
     assert p["grid"] * p["block"] // 64 >= p["tasks"]
 
 
+@pytest.mark.parametrize("M", [512, 1024])
+def test_mid_sizes_take_two_slab_tasks_on_the_uncapped_grid(M):
+    p = plan("bf16", M, 7168)                     # from 4096 slabs on (half a wave per slot)
+    assert p["slabs_per_task"] == 2 and p["uncapped"] == 1 and p["grid"] == M * 7 // 4
+    # fused calls of the same size keep one-slab tasks on a capped grid
+    p = plan("bf16", M, 3584, fuse=True)
+    assert p["slabs_per_task"] == 1 and p["uncapped"] == 0
+
+
 def test_fused_large_call_takes_the_silu_table_one_block_per_cu():
     p = plan("bf16", 8192, 4096, fuse=True)
     assert p["silu_table"] == 1 and p["block"] == 1024 and p["grid"] == CUS
