@@ -93,9 +93,10 @@ PTGQ_API int ptgq_diag_fastdiv(uint32_t d, const uint32_t *n, uint32_t *q, int64
  * the code buffer, >= rows) or a ptgq_quant_masked call (E >= 1 experts of
  * rows = tokens_pad rows, sized for expected_m) would make on a device of
  * `cus` compute units.  Tiny calls spread one-slab tasks over the compute
- * units; large ones use two-slab tasks and, for plain 16-bit input, a grid of
- * one wave per task dealt to the XCDs in chunks (the pages size their launch
- * by token count the same way: the sglang #34257 review page, key source
+ * units; larger unfused flat ones use two-slab tasks on a grid of one wave
+ * per task dealt to the XCDs in chunks; fused and masked calls a capped grid
+ * whose persistent blocks loop over the tasks (the pages size their launch by
+ * token count the same way: the sglang #34257 review page, key source
  * snippets, dispatch; `expected_m` of the sglang #30924 review page,
  * implementation breakdown).  Makes no HIP call and touches no device;
  * honours the ptgq_set_tuning overrides.
