@@ -709,27 +709,31 @@ int ptgq_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int gro
     // for fp32), contiguous so that a wave's loads in flight stay within a few
     // pages, grid-strided over the waves for as many full rounds as fit; the
     // remainder is one last round in which every wave takes an equal share
-    // (whole sub-slabs).  Problems too small to give every wave a few tasks
-    // use one sub-slab per task.  With at least as many tasks as the chip
+    // (whole sub-slabs).  Problems of fewer than 16 sub-slabs per CU use one
+    // sub-slab per task (measured on MI355X, e4m3 [M, 7168] -> bf16, capped
+    // grid: four sub-slabs per task from M = 512 on, 4.01 -> 3.59 us; M =
+    // 1024 7.68 -> 5.61, M = 2048 12.56 -> 9.44; -> fp32 M = 1024 11.77 ->
+    // 6.95; M = 256 3.08 either way).  With at least as many tasks as the chip
     // holds waves, the grid is uncapped (one task per wave) and its blocks are
     // dealt to the XCDs in chunks of 16 (measured on MI355X, e4m3 [M, 7168] ->
     // bf16: M = 16384 63.7 -> 57.0 us, M = 4096 17.4 -> 16.6 us; fp32 out
     // [8192, 7168] 52.5 -> 48.3 us; chunks of 2..32 blocks within 1 %, one
     // contiguous range per XCD 62.6 us).  Fewer tasks: four four-wave blocks
     // per CU (two for fp32 outputs, whose stores are twice as wide), which
-    // measured best there (M = 1024: 6.9 us against 7.7 uncapped).
+    // measured best there (M = 1024: 5.61 us against 6.28 uncapped).
     const int64_t total = M * K;
     const int64_t sub = out_dtype == PTGQ_FP32 ? 256 : 512;
     const int64_t subs = (total + sub - 1) / sub;
     if (subs >= INT32_MAX) return PTGQ_EUNSUPPORTED;
-    int ns = subs >= (int64_t)cus * 16 * 8 ? 4 : 1;
+    int ns = subs >= (int64_t)cus * 16 ? 4 : 1;
     if (knob(KNOB_SLABS_PER_TASK) > 0) ns = knob(KNOB_SLABS_PER_TASK) >= 4 ? 4 : 1;
     const int64_t ts = ns * sub;
     const int64_t tasks = (subs + ns - 1) / ns;
     const int wpb = tasks >= (int64_t)cus * 4 ? 4 : 1;
     int64_t blocks = (tasks + wpb - 1) / wpb;
     int64_t per_cu = out_dtype == PTGQ_FP32 ? 2 : 4;
-    const bool uncapped = tasks >= (int64_t)cus * 32 && knob(KNOB_BLOCKS_PER_CU) <= 0;
+    bool uncapped = tasks >= (int64_t)cus * 32 && knob(KNOB_BLOCKS_PER_CU) <= 0;
+    if (knob(KNOB_GRID_MODE) >= 0) uncapped = knob(KNOB_GRID_MODE) > 0;
     if (knob(KNOB_BLOCKS_PER_CU) > 0) per_cu = knob(KNOB_BLOCKS_PER_CU);
     if (!uncapped && blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
     else if (blocks >= 64) blocks = (blocks + 7) / 8 * 8;

@@ -118,25 +118,24 @@ PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, i
 /*
  * ptgq_set_tuning - diagnostics only: override one decision of the launch
  * geometry chooser for the whole process (value -1 restores the automatic
- * choice).  Knobs: 0 slabs per task (quantization: 1 or 2, one slab = 512
+ * choice). Knobs: 0 slabs per task (quantization: 1 or 2, one slab = 512
  * elements of a row; dequantization: 1 or 4 sub-slabs), 1 waves per block
- * (group kernels 1..4, not the fused SiLU-table kernels, which always run
- * 16; per-token one-block-per-row mode: waves per row, 1..8; per-token
- * one-wave-per-row mode: rows per block, 1..4), 2 resident blocks per
- * compute unit (grid cap), 3 per-token mode (0 one wave per row, 1 one
- * block per row, 2 two-pass block, 3 persistent waves walking the rows), 4
- * fused bf16 SiLU path (0 direct evaluation, 1 LDS lookup table), 5 blocks
- * per XCD chunk of the block-to-task mappings of the flat quantization,
- * dequantization and requantization kernels and of the per-token
- * one-block-per-row mode (0 one contiguous range per XCD, or for the
- * per-token mode block b takes row b), 6 grid of the flat
- * quantization and requantization kernels (0 capped: resident blocks loop
- * over the tasks; 1 uncapped: one wave per task), 7 two-slab tasks of unfused
- * flat calls whose K is a multiple of 512 (0 row tasks; 1 flat-slab tasks,
- * which cross row ends; automatic: flat-slab tasks for an odd number of
- * slabs per row).
- * Results never depend on these; only speed does.  Not synchronized
- * with calls running on other host threads.  Returns PTGQ_OK or PTGQ_EINVAL.
+ * (group kernels 1..4, not the fused SiLU-table kernels, which always run 16;
+ * per-token one-block-per-row mode: waves per row, 1..8; per-token one-wave-
+ * per-row mode: rows per block, 1..4), 2 resident blocks per compute unit
+ * (grid cap), 3 per-token mode (0 one wave per row, 1 one block per row, 2
+ * two-pass block, 3 persistent waves walking the rows), 4 fused bf16 SiLU
+ * path (0 direct evaluation, 1 LDS lookup table), 5 blocks per XCD chunk of
+ * the block-to-task mappings of the flat quantization, dequantization and
+ * requantization kernels and of the per-token one-block-per-row mode (0 one
+ * contiguous range per XCD, or for the per-token mode block b takes row b), 6
+ * grid of the flat quantization, requantization and dequantization kernels (0
+ * capped: resident blocks loop over the tasks; 1 uncapped: one wave per
+ * task), 7 two-slab tasks of unfused flat calls whose K is a multiple of 512
+ * (0 row tasks; 1 flat-slab tasks, which cross row ends; automatic: flat-slab
+ * tasks for an odd number of slabs per row).
+ * Results never depend on these; only speed does. Not synchronized with calls
+ * running on other host threads. Returns PTGQ_OK or PTGQ_EINVAL.
  */
 PTGQ_API int ptgq_set_tuning(int knob, int64_t value);
 
