@@ -185,21 +185,27 @@ constexpr int64_t kTokenXcdChunk = 32;      // per-token block mode, blocks per 
 // slab (measured on MI355X, fp16 rows of 3, 5 and 7 slabs: 2-10 % faster than
 // capped one-slab tasks; one-slab rows stay one-slab).  `table_ok`: the SiLU
 // lookup table may be read (it is built and ordered before the call).
-void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool masked, bool bf16,
-                 bool flat16, bool flat_slabs, bool table_ok, int cus)
+void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16, bool flat16,
+                 bool flat_slabs, bool table_ok, int cus)
 {
     const int64_t wave_slots = (int64_t)cus * 4 * 8;   // 8 waves per SIMD
-    g.table = fuse && bf16 && slabs >= (int64_t)cus * 4 * kTableWaves;
+    // The table from one slab per wave of the table grid on (16 per CU):
+    // measured on MI355X, fused bf16 [M, 2 * 4096], the table against the
+    // direct evaluation: M = 512 4.71 against 4.89 us, M = 1024 6.29 against
+    // 7.66, M = 1536 7.98 against 11.02; M = 256 (8 slabs per CU) 4.30
+    // against 3.68.
+    g.table = fuse && bf16 && slabs >= (int64_t)cus * kTableWaves;
     if (fuse && bf16 && knob(KNOB_SILU_TABLE) >= 0) g.table = knob(KNOB_SILU_TABLE) > 0;
     if (!table_ok) g.table = false;
     // Table kernels (16 waves per CU) run one-slab tasks: measured 6-8 % faster
     // than two-slab tasks for the fused flat and masked workloads.
-    // Two-slab tasks from half a wave per resident slot on for unfused flat
-    // calls (they then take the uncapped grid; measured on MI355X, bf16
+    // Two-slab tasks from half a wave per resident slot on for unfused calls
+    // (flat calls then take the uncapped grid; measured on MI355X, bf16
     // [M, 7168]: M = 512 4.15 -> 3.83 us, M = 1024 6.11 -> 5.76; at M = 256,
-    // 3584 slabs, one-slab tasks stay faster, 3.00 against 3.08), from two
-    // waves per slot for fused and masked ones (capped grids).
-    const int64_t u2_min = fuse || masked ? 2 * wave_slots : wave_slots / 2;
+    // 3584 slabs, one-slab tasks stay faster, 3.00 against 3.08; masked,
+    // 8 experts x 128 live rows of 7168: 8.30 -> 6.89), from two waves per
+    // slot for fused ones.
+    const int64_t u2_min = fuse ? 2 * wave_slots : wave_slots / 2;
     int U = 1;
     if (!g.table && slabs >= u2_min && (flat_slabs || spr % 2 == 0 || (flat16 && spr >= 3)))
         U = 2;
@@ -299,8 +305,8 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // 7168]: 15.35 against 15.96 us with the same tasks).
         const bool fs_ok = !fuse && K % kSlab == 0 && (a.spr % 2 == 1 || knob(KNOB_FLAT_SLABS) > 0) &&
                            knob(KNOB_FLAT_SLABS) != 0;
-        choose_task(geo, rows * a.spr, a.spr, fuse != 0, false, bf16, !fuse && es == 2, fs_ok,
-                    table_ok, cus);
+        choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, !fuse && es == 2, fs_ok, table_ok,
+                    cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
         a.flat_slabs = fs_ok && a.U == 2 ? 1 : 0;
@@ -347,7 +353,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // expected only make each wave loop longer.
         if (E > kMaxExperts) return PTGQ_EUNSUPPORTED;
         const int64_t hint = (expected_m > 0 && expected_m < rows) ? expected_m : rows;
-        choose_task(geo, std::max<int64_t>(hint, 1) * a.spr * E, a.spr, fuse != 0, true, bf16, false,
+        choose_task(geo, std::max<int64_t>(hint, 1) * a.spr * E, a.spr, fuse != 0, bf16, false,
                     false, table_ok, cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;

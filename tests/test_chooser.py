@@ -62,6 +62,9 @@ def test_fused_large_call_takes_the_silu_table_one_block_per_cu():
     assert p["slabs_per_task"] == 1 and p["uncapped"] == 0
     # small fused calls evaluate directly
     assert plan("bf16", 64, 4096, fuse=True)["silu_table"] == 0
+    # from 16 slabs per CU (one per wave of the table grid) on
+    assert plan("bf16", 256, 4096, fuse=True)["silu_table"] == 0
+    assert plan("bf16", 512, 4096, fuse=True)["silu_table"] == 1
     # fp16 gates never use the table
     assert plan("fp16", 8192, 4096, fuse=True)["silu_table"] == 0
 
