@@ -175,7 +175,9 @@ constexpr int64_t kTokenXcdChunk = 32;      // per-token block mode, blocks per 
 // LDS reads the table.  Few slabs (decode-sized M): one slab per task so the
 // work spreads over as many waves and CUs as possible.  Many: two slabs per
 // task for the plain and direct-SiLU kernels when a row has an even number of
-// slabs (no task runs past a row), else one (measured best on MI355X).
+// slabs (no task runs past a row), when the call takes flat-slab tasks, or
+// for unfused 16-bit rows of at least 3 slabs; else one (measured best on
+// MI355X).
 // `flat_slabs`: an unfused flat call whose K is a multiple of the slab, so
 // that input and codes are one contiguous sequence of whole-row slabs; its
 // two-slab tasks then run over that sequence and cross row ends (no half

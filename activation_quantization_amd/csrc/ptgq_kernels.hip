@@ -1124,8 +1124,9 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
 // Whole-row per-token e4m3 (sglang #34257 review page, key source snippets):
 // scale = rowmax / 448 with no floor, multiplier 0 for a zero row.
 // A row is read once: it stays in registers between the max and the
-// quantization pass (TOKEN_WAVE: one wave per row; TOKEN_BLOCK: one 256-lane
-// block per row); very long rows take the two-pass TOKEN_BLOCK_LOOP form.
+// quantization pass (TOKEN_WAVE: one wave per row; TOKEN_BLOCK: one block of
+// 1 to 8 waves per row); very long rows take the two-pass TOKEN_BLOCK_LOOP
+// form.
 // --------------------------------------------------------------------------
 
 template <int IN, int VB>
