@@ -233,6 +233,53 @@ def test_first_call_inside_a_graph_capture():
     assert res.returncode == 0 and "CHILD OK" in res.stdout
 
 
+STREAMS_CHILD = textwrap.dedent("""
+    import sys
+    sys.path.insert(0, {root!r})
+    import numpy as np
+    import torch
+    import activation_quantization_amd as aq
+    import oracle
+    import workloads as W
+
+    dev = "cuda"
+    M, K = 2048, 4096                    # fused bf16, large enough for the SiLU table
+    xh = W.normal_bf16(2050, (M, 2 * K))
+    x = torch.from_numpy(xh.view(np.int16)).to(dev)
+    sb = aq.ptgq_scale_bytes(M, K, 128, "ue8m0", "col")
+    outs = [(torch.full((M, K), 0xCD, dtype=torch.uint8, device=dev),
+             torch.full((sb,), 0xCD, dtype=torch.uint8, device=dev)) for _ in range(3)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    # the first call builds the table on s1; the next two, on s2 and on the
+    # default stream, are enqueued at once, with no host synchronization
+    with torch.cuda.stream(s1):
+        aq.ptgq_quant(x, "bf16", M, K, 128, True, "e4m3", "ue8m0", "col", 1e-10, *outs[0])
+    with torch.cuda.stream(s2):
+        aq.ptgq_quant(x, "bf16", M, K, 128, True, "e4m3", "ue8m0", "col", 1e-10, *outs[1])
+    aq.ptgq_quant(x, "bf16", M, K, 128, True, "e4m3", "ue8m0", "col", 1e-10, *outs[2])
+    torch.cuda.synchronize()
+    rq, rs = oracle.ptgq(xh, "bf16", M, K, 128, True, "e4m3", "ue8m0", "col", eps=1e-10)
+    for i, (q, s) in enumerate(outs):
+        assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy(), rs), i
+        print("stream call", i, "bit-exact", flush=True)
+    print("CHILD OK", flush=True)
+""")
+
+
+def test_first_calls_on_several_streams():
+    """A fresh process whose first fused call runs on a side stream (building
+    the SiLU table there) and whose next calls are enqueued at once on another
+    side stream and on the default stream: each orders itself after the build
+    on the device and is bit-exact."""
+    res = subprocess.run([sys.executable, "-c", STREAMS_CHILD.format(root=ROOT)],
+                         capture_output=True, text=True, timeout=150)
+    print(res.stdout[-3000:], flush=True)
+    if res.returncode != 0:
+        print(res.stderr[-3000:], flush=True)
+    assert res.returncode == 0 and "CHILD OK" in res.stdout
+
+
 # ----------------------------------------------------- the stream reference
 
 def test_stream_probe_moves_the_low_bytes():
