@@ -46,8 +46,9 @@
  *     outputs race, as any two kernels would.
  *   - NaN or infinite inputs give unspecified (but in-bounds) outputs.
  *   - When the fp32 multiplier 1 / r overflows to +inf (a scale r below about
- *     2^-128: per-token rows, or fp32 group scales with a floor eps, whose
- *     largest magnitude is below ~1.3e-36), a zero element gives the zero code
+ *     2^-128: a per-token row, or a group with fp32 scales and eps below
+ *     ~1.3e-36, whose largest magnitude is below ~1.3e-36, normal values
+ *     included), a zero element gives the zero code
  *     of its sign and every other element saturates; the same holds for a
  *     zero product in ptgq_requant_fp8.  (The pages leave this corner open;
  *     the quotient y / r of a zero is zero.)
