@@ -48,10 +48,10 @@
  *   - When the fp32 multiplier 1 / r overflows to +inf (a scale r below about
  *     2^-128: a per-token row, or a group with fp32 scales and eps below
  *     ~1.3e-36, whose largest magnitude is below ~1.3e-36, normal values
- *     included), a zero element gives the zero code
- *     of its sign and every other element saturates; the same holds for a
- *     zero product in ptgq_requant_fp8.  (The pages leave this corner open;
- *     the quotient y / r of a zero is zero.)
+ *     included), a zero element gives the zero code of its sign and every
+ *     other element saturates; the same holds for a zero product in
+ *     ptgq_requant_fp8.  (The pages leave this corner open; the quotient
+ *     y / r of a zero is zero.)
  *
  * Scale tensor layouts (ng = K / G groups per row, rows_pad = ceil(rows/4)*4):
  *   PTGQ_ROW_MAJOR + PTGQ_SCALE_F32    float   [rows][ng]
