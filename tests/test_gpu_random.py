@@ -1,6 +1,9 @@
 """Seeded random parity sweep: shapes, traits and masks drawn at random (fixed
 seeds, so every run checks the same cases) across every entry point, each
-compared byte for byte with the oracle."""
+compared byte for byte with the oracle.  PTGQ_RANDOM_<FAMILY>=n widens a
+family to its first n seeds (the defaults keep the suite short)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,6 +17,10 @@ pytestmark = pytest.mark.gpu
 GS = (16, 32, 64, 128)
 
 
+def cases(family, default):
+    return range(int(os.environ.get(f"PTGQ_RANDOM_{family}", default)))
+
+
 def draw_x(rng, shape, in_dtype, seed):
     if in_dtype == "fp32":
         x = W.normal_f32(seed, shape) * np.float32(rng.choice([1e-3, 1.0, 50.0]))
@@ -24,13 +31,12 @@ def draw_x(rng, shape, in_dtype, seed):
                          factor=float(rng.choice([1.0, 30.0, 300.0])))
 
 
-@pytest.mark.parametrize("case", range(24))
-def test_random_flat(case):
-    rng = np.random.default_rng(1000 + case)
+def random_flat(case, seed, m_lo, m_hi):
+    rng = np.random.default_rng(seed)
     G = int(rng.choice(GS))
     fuse = bool(rng.integers(0, 2))
     in_dtype = str(rng.choice(["bf16", "fp16"] if fuse else ["bf16", "fp16", "fp32"]))
-    M = int(rng.integers(1, 700))
+    M = int(rng.integers(m_lo, m_hi))
     K = G * int(rng.integers(1, 9000 // G))
     out = str(rng.choice(["e4m3", "int8"]))
     fmt = str(rng.choice(["f32", "ue8m0"]))
@@ -42,7 +48,19 @@ def test_random_flat(case):
             *oracle.ptgq(*args, eps=eps))
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", cases("FLAT", 24))
+def test_random_flat(case):
+    random_flat(case, 1000 + case, 1, 700)
+
+
+@pytest.mark.parametrize("case", cases("FLAT_LARGE", 6))
+def test_random_flat_large(case):
+    """Sizes where two-slab tasks, flat-slab tasks, the uncapped grid, its XCD
+    chunks and the SiLU table take over."""
+    random_flat(case, 1500 + case, 700, 5000)
+
+
+@pytest.mark.parametrize("case", cases("MASKED", 12))
 def test_random_masked(case):
     rng = np.random.default_rng(2000 + case)
     G = int(rng.choice(GS))
@@ -66,7 +84,7 @@ def test_random_masked(case):
             f"{fmt} {lay}", gq, gs, rq, rs)
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", cases("PER_TOKEN", 10))
 def test_random_per_token(case):
     rng = np.random.default_rng(3000 + case)
     in_dtype = str(rng.choice(["bf16", "fp16", "fp32"]))
@@ -77,7 +95,7 @@ def test_random_per_token(case):
             *run_per_token(x, in_dtype, M, K), *oracle.ptq_fp8(x, in_dtype, M, K))
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", cases("REQUANT", 10))
 def test_random_requant(case):
     rng = np.random.default_rng(4000 + case)
     G = int(rng.choice(GS))
@@ -105,7 +123,7 @@ def test_random_requant(case):
             outd.host(), np.zeros(0, np.uint8), want, np.zeros(0, np.uint8))
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", cases("DEQUANT", 10))
 def test_random_dequant(case):
     rng = np.random.default_rng(5000 + case)
     G = int(rng.choice(GS))
