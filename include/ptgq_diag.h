@@ -120,7 +120,8 @@ PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, i
  * geometry chooser for the whole process (value -1 restores the automatic
  * choice). Knobs: 0 slabs per task (quantization: 1 or 2, one slab = 512
  * elements of a row; dequantization: 1 or 4 sub-slabs), 1 waves per block
- * (group kernels 1..4, not the fused SiLU-table kernels, which always run 16;
+ * (group, requantization and dequantization kernels 1..4, not the fused
+ * SiLU-table kernels, which always run 16;
  * per-token one-block-per-row mode: waves per row, 1..8; per-token one-wave-
  * per-row mode: rows per block, 1..4), 2 resident blocks per compute unit
  * (grid cap), 3 per-token mode (0 one wave per row, 1 one block per row, 2
