@@ -305,17 +305,30 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // 16.13 -> 15.92 us, G = 32 16.88 -> 16.63 us); rows of an even
         // number keep row tasks, which measured faster there (bf16 [4096,
         // 7168]: 15.35 against 15.96 us with the same tasks).
-        const bool fs_ok = !fuse && K % kSlab == 0 && (a.spr % 2 == 1 || knob(KNOB_FLAT_SLABS) > 0) &&
+        // Rows shorter than a slab whose length divides it (16-bit input,
+        // K = 16 .. 256): slabs of kSlab / K whole rows, so that no lane idles
+        // past a row end (measured on MI355X, bf16 [M, K] -> e4m3, UE8M0
+        // column-major, 33.5 M elements, one row per slab: K = 128 50.7 us,
+        // K = 256 27.7, K = 512 17.0).
+        const bool mr_ok = !fuse && es == 2 && K < kSlab && kSlab % K == 0 &&
                            knob(KNOB_FLAT_SLABS) != 0;
-        choose_task(geo, rows * a.spr, a.spr, fuse != 0, bf16, !fuse && es == 2, fs_ok, table_ok,
+        const bool fs_ok = mr_ok ||
+                           (!fuse && K % kSlab == 0 &&
+                            (a.spr % 2 == 1 || knob(KNOB_FLAT_SLABS) > 0) &&
+                            knob(KNOB_FLAT_SLABS) != 0);
+        const int64_t seq_slabs = mr_ok ? (rows * K + kSlab - 1) / kSlab : rows * (int64_t)a.spr;
+        choose_task(geo, seq_slabs, a.spr, fuse != 0, bf16, !fuse && es == 2, fs_ok, table_ok,
                     cus);
         a.U = geo.U;
         a.tpr = (a.spr + a.U - 1) / a.U;
-        a.flat_slabs = fs_ok && a.U == 2 ? 1 : 0;
+        a.flat_slabs = fs_ok && a.U == 2 ? (mr_ok ? 2 : 1) : 0;
         geo.flat_slabs = a.flat_slabs != 0;
-        a.n_slabs = rows * (int64_t)a.spr;
+        a.n_slabs = a.flat_slabs == 2 ? seq_slabs : rows * (int64_t)a.spr;
         if (a.n_slabs >= INT32_MAX) return PTGQ_EUNSUPPORTED;
-        a.spr_div = make_fastdiv((uint32_t)a.spr);
+        a.spr_div = make_fastdiv(a.flat_slabs == 2 ? 1u : (uint32_t)a.spr);
+        a.fs_row = (int32_t)(a.flat_slabs == 2 ? kSlab : K);
+        a.fs_total = rows * K;
+        a.mr_shift = a.flat_slabs == 2 ? __builtin_ctzll((unsigned long long)a.ng) : -1;
         const int64_t tasks = a.flat_slabs ? (a.n_slabs + a.U - 1) / a.U : rows * (int64_t)a.tpr;
         if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.n_tasks = (int32_t)tasks;

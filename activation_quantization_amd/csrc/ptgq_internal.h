@@ -76,11 +76,17 @@ struct GroupArgs {
     int64_t q_pad_bytes;      // flat: bytes of q past row M written as zero
     int32_t xcd_chunk;        // flat: blocks per XCD chunk of the block -> task
                               // mapping; 0 = one contiguous range per XCD
-    int32_t flat_slabs;       // flat, unfused, K % kSlab == 0: task t is slabs
-                              // U*t .. U*t+U-1 of the whole [M, K] tensor taken
-                              // as one sequence of slabs (tasks cross row ends)
-    int64_t n_slabs;          // flat_slabs: rows * spr
+    int32_t flat_slabs;       // flat, unfused: task t is slabs U*t .. U*t+U-1 of
+                              // the whole [M, K] tensor taken as one sequence of
+                              // slabs (tasks cross row ends).  1: K % kSlab == 0,
+                              // whole-row slabs; 2: 16-bit input, K < kSlab and
+                              // kSlab % K == 0, each slab kSlab / K whole rows
+    int64_t n_slabs;          // flat_slabs: slabs of the sequence
     FastDiv spr_div;          // flat_slabs: division by spr
+    int32_t fs_row;           // flat_slabs: elements per row of the slab sequence
+                              // (K; kSlab for multi-row slabs)
+    int32_t mr_shift;         // flat_slabs == 2: log2(ng)
+    int64_t fs_total;         // flat_slabs: elements of the tensor, M * K
     int32_t wpb;              // waves per block of the launch
 };
 

@@ -602,7 +602,7 @@ __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x
 }
 
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL,
-          bool FS = false>
+          int FS = 0>
 __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &t, int lane,
                                              const TaskBuf<UMAX> &b, const float *tab)
 {
@@ -688,6 +688,38 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
         const int lg = lane / LPG;                                  // group within slab
         const int64_t g0 = (int64_t)slab * GPS;                     // first group of slab
         const bool leader = (lane % LPG) == 0;
+        if constexpr (FS == 2) {
+            // multi-row slabs: slab m of the sequence holds groups m * GPS ..
+            // m * GPS + GPS - 1 of the tensor taken as one sequence of groups;
+            // group f is group f % ng of row f / ng (ng a power of two).  A
+            // packed word's groups (four, or the row's ng < 4) are consecutive
+            // groups of one slab.
+            const int64_t f = m * GPS + lg;
+            const int64_t mr = f >> a.mr_shift;
+            const int64_t gr = f & (a.ng - 1);
+            if constexpr (ue8m0) {
+                if (a.scale_layout == LAYOUT_COL) {
+                    const uint32_t byte = sc.e;
+                    const uint32_t b1 = (uint32_t)__shfl((int)byte, lane + LPG);
+                    const uint32_t b2 = (uint32_t)__shfl((int)byte, lane + 2 * LPG);
+                    const uint32_t b3 = (uint32_t)__shfl((int)byte, lane + 3 * LPG);
+                    if (leader && valid && (gr & 3) == 0) {
+                        uint32_t word = byte;
+                        if (a.ng > 1) word |= b1 << 8;
+                        if (a.ng > 2) word |= (b2 << 16) | (b3 << 24);
+                        reinterpret_cast<uint32_t *>(se)[(gr >> 2) * a.rows_pad + mr] = word;
+                    }
+                } else if (leader && valid) {
+                    se[f] = (uint8_t)sc.e;
+                }
+            } else if (leader && valid) {
+                if (a.scale_layout == LAYOUT_ROW)
+                    reinterpret_cast<float *>(se)[f] = sc.r;
+                else
+                    reinterpret_cast<float *>(se)[gr * a.rows_pad + mr] = sc.r;
+            }
+            continue;
+        }
         if constexpr (ue8m0) {
           if (a.scale_layout == LAYOUT_COL) {
             const uint32_t byte = valid ? sc.e : 0u;
@@ -778,11 +810,15 @@ struct FlatSlabMap {
         const uint32_t m = fastdiv(S, a.spr_div);
         const uint32_t j = S - m * (uint32_t)a.spr;
         const uint32_t left = (uint32_t)a.n_slabs - S;               // >= 1 for live tasks
-        const uint32_t K = (uint32_t)a.K;
+        const uint32_t K = (uint32_t)a.fs_row;
         // the region is row m and the slabs after it up to the task's end
-        // (the next row's first slab when the task crosses the row end)
+        // (the next row's first slab when the task crosses the row end),
+        // clipped to the tensor (a multi-row slab sequence may end inside
+        // its last slab)
         const uint32_t span = j * kSlab + (left < UMAX ? left : UMAX) * kSlab;
-        const uint32_t reach = span > K ? span : K;
+        const int64_t rest = a.fs_total - (int64_t)m * K;          // >= 1 for live tasks
+        const uint32_t reach0 = span > K ? span : K;
+        const uint32_t reach = rest < (int64_t)reach0 ? (uint32_t)rest : reach0;
         TaskLoc l;
         l.xb = static_cast<const char *>(a.x) + (uint64_t)m * K * ES;
         l.qb = a.q + (uint64_t)m * K;
@@ -790,7 +826,8 @@ struct FlatSlabMap {
         l.xrange = reach * ES;
         l.qrange = reach;
         l.c0 = j * kSlab;
-        l.codes = (left < UMAX ? left : UMAX) * kSlab;
+        const uint32_t codes = (left < UMAX ? left : UMAX) * kSlab;
+        l.codes = reach - l.c0 < codes ? reach - l.c0 : codes;
         l.m = m;
         l.j = (int)j;
         l.next_row = (int)((uint32_t)a.spr - j);     // >= UMAX: no crossing
@@ -954,7 +991,7 @@ __device__ __forceinline__ void table_store(const TableRegs &r, float *tab)
 // are already in flight in `cur` (location lcur); `spare` is free.  Two tasks
 // are in flight at a time.  A task index past n is clamped for address
 // arithmetic and loaded over an empty range.
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL, bool FS,
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL, int FS,
           class Map>
 __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int t, TaskLoc lcur,
                                                TaskBuf<UMAX> &cur, TaskBuf<UMAX> &spare, int n,
@@ -983,7 +1020,7 @@ __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int
 // store the table into LDS (every wave of the block reaches that barrier,
 // with or without a task), so the table copy overlaps the first HBM reads.
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int SPOL,
-          bool STAGE, bool FETCHED = false, bool FS = false, class Map>
+          bool STAGE, bool FETCHED = false, int FS = 0, class Map>
 __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
                                           int stride, int lane, float *tab,
                                           TableRegs tr = TableRegs{})
@@ -1032,7 +1069,7 @@ __device__ __forceinline__ int logical_block(int b, int nb, int chunk = 0)
 }
 
 // FS: flat-slab tasks (FlatSlabMap) instead of row tasks (FlatMap).
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, bool FS>
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int FS>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs a)
 {
     __shared__ float tab[TABLE ? kSiluTab : 1];
@@ -1044,7 +1081,8 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
     if constexpr (FS) {
         static_assert(!FUSE && !TABLE, "flat-slab tasks: unfused inputs");
-        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true, false, true>(
+        static_assert(FS != 2 || IN != IN_FP32, "multi-row slabs: 16-bit inputs");
+        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true, false, FS>(
             a, FlatSlabMap<IN, UMAX>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
     } else {
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true>(
@@ -1999,13 +2037,18 @@ static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid,
         ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE>
             <<<grid, block, (size_t)a.num_experts * sizeof(int), st>>>(a);
     else if constexpr (!FUSE && !TABLE && UMAX == 2) {
-        if (a.flat_slabs)
-            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, true><<<grid, block, 0, st>>>(a);
+        if (a.flat_slabs == 1)
+            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 1><<<grid, block, 0, st>>>(a);
+        else if (a.flat_slabs == 2) {
+            if constexpr (IN == IN_FP32) return hipErrorInvalidValue;
+            else ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 2><<<grid, block, 0, st>>>(a);
+        } else if (a.flat_slabs == 0)
+            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0><<<grid, block, 0, st>>>(a);
         else
-            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, false><<<grid, block, 0, st>>>(a);
+            return hipErrorInvalidValue;
     } else {
         if (a.flat_slabs) return hipErrorInvalidValue;
-        ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, false><<<grid, block, 0, st>>>(a);
+        ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0><<<grid, block, 0, st>>>(a);
     }
     return hipGetLastError();
 }

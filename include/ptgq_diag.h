@@ -105,8 +105,9 @@ PTGQ_API int ptgq_diag_fastdiv(uint32_t d, const uint32_t *n, uint32_t *q, int64
  *        row (row tasks; ceil(slabs per row / slabs per task)), tasks in all
  *        (masked: the expected ones), blocks per XCD chunk of the block ->
  *        task mapping (0: one contiguous range per XCD), SiLU lookup table
- *        (0/1), uncapped grid (0/1), flat-slab tasks (0/1: the tensor's slabs
- *        taken as one sequence, tasks crossing row ends); all zero when
+ *        (0/1), uncapped grid (0/1), flat-slab tasks (0 none; 1 the tensor's
+ *        whole-row slabs taken as one sequence, tasks crossing row ends; 2
+ *        slabs of several rows shorter than a slab); all zero when
  *        nothing would be launched.
  * Returns PTGQ_OK, PTGQ_EINVAL (invalid shape, cus < 1, out NULL) or
  * PTGQ_EUNSUPPORTED, as the calls would for the same shape.
@@ -134,7 +135,8 @@ PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, i
  * capped: resident blocks loop over the tasks; 1 uncapped: one wave per
  * task), 7 two-slab tasks of unfused flat calls whose K is a multiple of 512
  * (0 row tasks; 1 flat-slab tasks, which cross row ends; automatic: flat-slab
- * tasks for an odd number of slabs per row).
+ * tasks for an odd number of slabs per row) and multi-row slabs of 16-bit
+ * rows shorter than a slab (0 one row per slab; otherwise automatic).
  * Results never depend on these; only speed does. Not synchronized with calls
  * running on other host threads. Returns PTGQ_OK or PTGQ_EINVAL.
  */

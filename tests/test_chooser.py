@@ -124,6 +124,22 @@ def test_odd_slab_rows_take_flat_slab_tasks_across_row_ends():
     assert plan("bf16", 4096, 7168)["flat_slabs"] == 1
 
 
+@pytest.mark.parametrize("K", [16, 64, 128, 256])
+def test_short_rows_take_multi_row_slabs(K):
+    rows = 8192 * SLAB // K + 3                    # 8193 slabs of 512 // K rows, the last partial
+    p = plan("bf16", rows, K, G=16)
+    assert p["flat_slabs"] == 2 and p["slabs_per_task"] == 2 and p["uncapped"] == 1
+    assert p["tasks"] == (8193 + 1) // 2 and p["block"] == 64
+    # fp32 input and fused calls keep one row per slab
+    assert plan("fp32", rows, K, G=16)["flat_slabs"] == 0
+    assert plan("bf16", rows, K, G=16, fuse=True)["flat_slabs"] == 0
+    # K not dividing the slab: one row per slab
+    assert plan("bf16", 65536, 384)["flat_slabs"] == 0
+    # the override's 0 restores one row per slab
+    aq.ptgq_set_tuning(7, 0)
+    assert plan("bf16", rows, K, G=16)["flat_slabs"] == 0
+
+
 def test_padded_rows_get_waves_for_the_zero_fill():
     # nothing to quantize, 28 MiB of code rows to zero: a full capped grid
     # whose waves loop over the fill (1 KiB per wave store)
@@ -142,7 +158,9 @@ def test_rules_hold_for_random_shapes(cus):
     for _ in range(300):
         G = int(rng.choice([16, 32, 64, 128]))
         K = G * int(rng.integers(1, 30000 // G))
-        rows = int(rng.integers(1, 20000))
+        if rng.integers(0, 4) == 0:                       # rows shorter than a slab
+            K = int(rng.choice([k for k in (16, 32, 64, 128, 256) if k >= G] or [G]))
+        rows = int(rng.integers(1, 200000 if K < SLAB else 20000))
         dt = str(rng.choice(["bf16", "fp16", "fp32"]))
         fuse = dt != "fp32" and bool(rng.integers(0, 2))
         p = plan(dt, rows, K, G, fuse, cus=cus)
@@ -150,7 +168,10 @@ def test_rules_hold_for_random_shapes(cus):
         U = p["slabs_per_task"]
         assert U in (1, 2)
         assert p["tasks_per_row"] == -(-spr // U)
-        if p["flat_slabs"]:
+        if p["flat_slabs"] == 2:
+            assert U == 2 and not fuse and dt != "fp32" and K < SLAB and SLAB % K == 0
+            assert p["tasks"] == -(-(-(-(rows * K) // SLAB)) // 2)
+        elif p["flat_slabs"]:
             assert U == 2 and not fuse and K % SLAB == 0 and spr % 2 == 1
             assert p["tasks"] == -(-(rows * spr) // 2)
         else:

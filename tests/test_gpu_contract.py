@@ -1,7 +1,7 @@
 """GPU parity for the contract points beside the workloads: the overflowed
 multiplier corner (zeros keep their sign, other values saturate), the
 per-token host contract on padded output rows, flat-slab tasks across row
-ends, the first call of a process made inside a graph capture, and the
+ends, multi-row slabs for rows shorter than a slab, the first call of a process made inside a graph capture, and the
 no-arithmetic stream reference.  Every output sits between guard bands."""
 import os
 import subprocess
@@ -138,6 +138,51 @@ def test_flat_slab_tasks_across_row_ends(in_dtype, flat):
                         *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
     finally:
         aq.ptgq_set_tuning(7, -1)
+
+
+@pytest.mark.parametrize("K", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("in_dtype", ["bf16", "fp16"])
+def test_multi_row_slabs(in_dtype, K):
+    """Rows shorter than a slab (K divides 512): each slab holds 512 / K rows,
+    the last slab of the tensor is partial; every group size up to K, scale
+    format and layout (column-major packed words of fewer than four groups
+    included); large enough that two-slab tasks are chosen."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    M = cus * 16 * 512 // K + 3                         # >= 16 slabs per CU, ragged
+    x = (W.normal_bf16(M + K, (M, K), factor_cols=[K - 1], factor=40.0) if in_dtype == "bf16"
+         else W.normal_fp16(M + K, (M, K)))
+    x[M // 2] = 0                                       # a zero row: scale from eps
+    for G in [g for g in (16, 32, 64, 128) if g <= K]:
+        p = aq.ptgq_plan_group(in_dtype, 0, M, K, G, False, 0, M, cus)
+        assert p["flat_slabs"] == 2 and p["slabs_per_task"] == 2
+        for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row"),
+                                       ("e4m3", "f32", "col"), ("int8", "ue8m0", "row")):
+            args = (x, in_dtype, M, K, G, False, out_dtype, fmt, layout)
+            compare(f"multi-row slabs {in_dtype} M={M} K={K} G={G} {out_dtype} {fmt} {layout}",
+                    *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
+
+
+def test_multi_row_slabs_padded_codes():
+    """ptgq_quant_padded with multi-row slabs: rows past M are zero, the
+    column-major pad slots too."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    K, G = 128, 32
+    M = cus * 16 * 4 + 1
+    q_rows = M + 7
+    x = W.normal_bf16(77, (M, K))
+    assert aq.ptgq_plan_group("bf16", 0, M, K, G, False, 0, q_rows, cus)["flat_slabs"] == 2
+    q = Guarded((q_rows, K), torch.uint8, 0xCD)
+    sb = aq.ptgq_scale_bytes(M, K, G, "ue8m0", "col")
+    s = Guarded((sb,), torch.uint8, 0xCD)
+    aq.ptgq_quant_padded(to_dev(x), "bf16", M, K, G, False, "e4m3", "ue8m0", "col", 1e-10, q.t,
+                         q_rows, s.t)
+    torch.cuda.synchronize()
+    q.check("padded q")
+    s.check("padded s")
+    qh = q.host()
+    rq, rs = oracle.ptgq(x, "bf16", M, K, G, False, "e4m3", "ue8m0", "col", eps=1e-10)
+    compare("multi-row slabs padded", qh[:M], s.host(), rq, rs)
+    assert np.all(qh[M:] == 0)
 
 
 def test_flat_slab_padded_codes():
