@@ -312,23 +312,32 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // K = 256 27.7, K = 512 17.0).
         const bool mr_ok = !fuse && es == 2 && K < kSlab && kSlab % K == 0 &&
                            knob(KNOB_FLAT_SLABS) != 0;
-        const bool fs_ok = mr_ok ||
+        // Any other 16-bit K that is not a multiple of the slab: slabs of
+        // the flattened tensor, crossing row ends anywhere (groups never
+        // cross them, G dividing K), so that no lane idles on a row's ragged
+        // last slab (group indices stay 32-bit).
+        const bool fg_ok = !fuse && es == 2 && K % kSlab != 0 && !mr_ok &&
+                           rows * a.ng < ((int64_t)1 << 31) && knob(KNOB_FLAT_SLABS) != 0;
+        const bool fs_ok = mr_ok || fg_ok ||
                            (!fuse && K % kSlab == 0 &&
                             (a.spr % 2 == 1 || knob(KNOB_FLAT_SLABS) > 0) &&
                             knob(KNOB_FLAT_SLABS) != 0);
-        const int64_t seq_slabs = mr_ok ? (rows * K + kSlab - 1) / kSlab : rows * (int64_t)a.spr;
+        const int64_t seq_slabs =
+            mr_ok || fg_ok ? (rows * K + kSlab - 1) / kSlab : rows * (int64_t)a.spr;
         choose_task(geo, seq_slabs, a.spr, fuse != 0, bf16, !fuse && es == 2, fs_ok, table_ok,
                     cus);
         a.U = geo.U;
+        a.flat_slabs = fs_ok && a.U == 2 ? (mr_ok ? 2 : fg_ok ? 3 : 1) : 0;
+        if (a.flat_slabs >= 2) a.spr = 1;     // the sequence's rows are its slabs
         a.tpr = (a.spr + a.U - 1) / a.U;
-        a.flat_slabs = fs_ok && a.U == 2 ? (mr_ok ? 2 : 1) : 0;
         geo.flat_slabs = a.flat_slabs != 0;
-        a.n_slabs = a.flat_slabs == 2 ? seq_slabs : rows * (int64_t)a.spr;
+        a.n_slabs = a.flat_slabs >= 2 ? seq_slabs : rows * (int64_t)a.spr;
         if (a.n_slabs >= INT32_MAX) return PTGQ_EUNSUPPORTED;
-        a.spr_div = make_fastdiv(a.flat_slabs == 2 ? 1u : (uint32_t)a.spr);
-        a.fs_row = (int32_t)(a.flat_slabs == 2 ? kSlab : K);
+        a.spr_div = make_fastdiv((uint32_t)a.spr);
+        a.fs_row = (int32_t)(a.flat_slabs >= 2 ? kSlab : K);
         a.fs_total = rows * K;
         a.mr_shift = a.flat_slabs == 2 ? __builtin_ctzll((unsigned long long)a.ng) : -1;
+        a.ng_div = make_fastdiv((uint32_t)a.ng);
         const int64_t tasks = a.flat_slabs ? (a.n_slabs + a.U - 1) / a.U : rows * (int64_t)a.tpr;
         if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.n_tasks = (int32_t)tasks;

@@ -80,12 +80,15 @@ struct GroupArgs {
                               // the whole [M, K] tensor taken as one sequence of
                               // slabs (tasks cross row ends).  1: K % kSlab == 0,
                               // whole-row slabs; 2: 16-bit input, K < kSlab and
-                              // kSlab % K == 0, each slab kSlab / K whole rows
+                              // kSlab % K == 0, each slab kSlab / K whole rows;
+                              // 3: 16-bit input, any other K: slabs of kSlab
+                              // consecutive elements of the flattened tensor
     int64_t n_slabs;          // flat_slabs: slabs of the sequence
     FastDiv spr_div;          // flat_slabs: division by spr
     int32_t fs_row;           // flat_slabs: elements per row of the slab sequence
                               // (K; kSlab for multi-row slabs)
     int32_t mr_shift;         // flat_slabs == 2: log2(ng)
+    FastDiv ng_div;           // flat_slabs == 3: division by ng
     int64_t fs_total;         // flat_slabs: elements of the tensor, M * K
     int32_t wpb;              // waves per block of the launch
 };

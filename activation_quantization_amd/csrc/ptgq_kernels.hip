@@ -688,6 +688,35 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
         const int lg = lane / LPG;                                  // group within slab
         const int64_t g0 = (int64_t)slab * GPS;                     // first group of slab
         const bool leader = (lane % LPG) == 0;
+        if constexpr (FS == 3) {
+            // slabs of the flattened tensor: slab m holds groups m * GPS ..
+            // m * GPS + GPS - 1 of the tensor's group sequence (G divides K,
+            // so no group crosses a row); group f is group f % ng of row
+            // f / ng (a multiply-high division).  A packed column-major word
+            // may take its groups from two slabs (two waves), so its bytes
+            // are stored one by one; the bytes past a row's last group in its
+            // last word are written as zero by that group's lane.
+            const uint32_t f = (uint32_t)(m * GPS + lg);              // < 2^31
+            const uint32_t mr = fastdiv(f, a.ng_div);
+            const uint32_t gr = f - mr * (uint32_t)a.ng;
+            if (leader && valid) {
+                if constexpr (ue8m0) {
+                    if (a.scale_layout == LAYOUT_COL) {
+                        uint8_t *wb = se + ((int64_t)(gr >> 2) * a.rows_pad + mr) * 4;
+                        wb[gr & 3] = (uint8_t)sc.e;
+                        if (gr + 1 == (uint32_t)a.ng)
+                            for (uint32_t b = (gr & 3) + 1; b < 4; ++b) wb[b] = 0;
+                    } else {
+                        se[f] = (uint8_t)sc.e;
+                    }
+                } else if (a.scale_layout == LAYOUT_ROW) {
+                    reinterpret_cast<float *>(se)[f] = sc.r;
+                } else {
+                    reinterpret_cast<float *>(se)[(int64_t)gr * a.rows_pad + mr] = sc.r;
+                }
+            }
+            continue;
+        }
         if constexpr (FS == 2) {
             // multi-row slabs: slab m of the sequence holds groups m * GPS ..
             // m * GPS + GPS - 1 of the tensor taken as one sequence of groups;
@@ -1081,7 +1110,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
     if constexpr (FS) {
         static_assert(!FUSE && !TABLE, "flat-slab tasks: unfused inputs");
-        static_assert(FS != 2 || IN != IN_FP32, "multi-row slabs: 16-bit inputs");
+        static_assert(FS < 2 || IN != IN_FP32, "multi-row and flattened slabs: 16-bit inputs");
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true, false, FS>(
             a, FlatSlabMap<IN, UMAX>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
     } else {
@@ -2042,6 +2071,9 @@ static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid,
         else if (a.flat_slabs == 2) {
             if constexpr (IN == IN_FP32) return hipErrorInvalidValue;
             else ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 2><<<grid, block, 0, st>>>(a);
+        } else if (a.flat_slabs == 3) {
+            if constexpr (IN == IN_FP32) return hipErrorInvalidValue;
+            else ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 3><<<grid, block, 0, st>>>(a);
         } else if (a.flat_slabs == 0)
             ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0><<<grid, block, 0, st>>>(a);
         else

@@ -107,7 +107,8 @@ PTGQ_API int ptgq_diag_fastdiv(uint32_t d, const uint32_t *n, uint32_t *q, int64
  *        task mapping (0: one contiguous range per XCD), SiLU lookup table
  *        (0/1), uncapped grid (0/1), flat-slab tasks (0 none; 1 the tensor's
  *        whole-row slabs taken as one sequence, tasks crossing row ends; 2
- *        slabs of several rows shorter than a slab); all zero when
+ *        slabs of several rows shorter than a slab; 3 slabs of the flattened
+ *        tensor, for 16-bit rows that are not whole slabs); all zero when
  *        nothing would be launched.
  * Returns PTGQ_OK, PTGQ_EINVAL (invalid shape, cus < 1, out NULL) or
  * PTGQ_EUNSUPPORTED, as the calls would for the same shape.
@@ -135,8 +136,9 @@ PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, i
  * capped: resident blocks loop over the tasks; 1 uncapped: one wave per
  * task), 7 two-slab tasks of unfused flat calls whose K is a multiple of 512
  * (0 row tasks; 1 flat-slab tasks, which cross row ends; automatic: flat-slab
- * tasks for an odd number of slabs per row) and multi-row slabs of 16-bit
- * rows shorter than a slab (0 one row per slab; otherwise automatic).
+ * tasks for an odd number of slabs per row) and the slabs of 16-bit rows that
+ * are not whole slabs (0 row tasks; otherwise automatic: multi-row or
+ * flattened slabs).
  * Results never depend on these; only speed does. Not synchronized with calls
  * running on other host threads. Returns PTGQ_OK or PTGQ_EINVAL.
  */

@@ -109,9 +109,13 @@ def test_odd_slab_rows_take_flat_slab_tasks_across_row_ends():
     # fp32 rows of an odd slab count too
     p = plan("fp32", 4096, 3584)
     assert p["slabs_per_task"] == 2 and p["flat_slabs"] == 1 and p["tasks"] == 4096 * 7 // 2
-    # rows that are not whole slabs keep row tasks (a slab would span two rows)
+    # rows that are not whole slabs: slabs of the flattened tensor, crossing
+    # row ends anywhere
     p = plan("fp16", 8192, 3584 + 128)
-    assert p["flat_slabs"] == 0 and p["tasks"] == 8192 * p["tasks_per_row"]
+    assert p["flat_slabs"] == 3 and p["slabs_per_task"] == 2
+    assert p["tasks"] == -(-(-(-(8192 * 3712) // 512)) // 2)
+    # fp32 input keeps row tasks there
+    assert plan("fp32", 8192, 3584 + 128)["flat_slabs"] == 0
     # rows of an even slab count keep row tasks (the same tasks)
     p = plan("bf16", 4096, 7168)
     assert p["flat_slabs"] == 0 and p["tasks"] == 4096 * 7
@@ -133,8 +137,8 @@ def test_short_rows_take_multi_row_slabs(K):
     # fp32 input and fused calls keep one row per slab
     assert plan("fp32", rows, K, G=16)["flat_slabs"] == 0
     assert plan("bf16", rows, K, G=16, fuse=True)["flat_slabs"] == 0
-    # K not dividing the slab: one row per slab
-    assert plan("bf16", 65536, 384)["flat_slabs"] == 0
+    # K not dividing the slab: slabs of the flattened tensor
+    assert plan("bf16", 65536, 384)["flat_slabs"] == 3
     # the override's 0 restores one row per slab
     aq.ptgq_set_tuning(7, 0)
     assert plan("bf16", rows, K, G=16)["flat_slabs"] == 0
@@ -167,8 +171,15 @@ def test_rules_hold_for_random_shapes(cus):
         spr = -(-K // SLAB)
         U = p["slabs_per_task"]
         assert U in (1, 2)
-        assert p["tasks_per_row"] == -(-spr // U)
-        if p["flat_slabs"] == 2:
+        if p["flat_slabs"] >= 2:
+            assert p["tasks_per_row"] == 1
+        else:
+            assert p["tasks_per_row"] == -(-spr // U)
+        if p["flat_slabs"] == 3:
+            assert U == 2 and not fuse and dt != "fp32" and K % SLAB != 0
+            assert not (K < SLAB and SLAB % K == 0)
+            assert p["tasks"] == -(-(-(-(rows * K) // SLAB)) // 2)
+        elif p["flat_slabs"] == 2:
             assert U == 2 and not fuse and dt != "fp32" and K < SLAB and SLAB % K == 0
             assert p["tasks"] == -(-(-(-(rows * K) // SLAB)) // 2)
         elif p["flat_slabs"]:
@@ -176,7 +187,7 @@ def test_rules_hold_for_random_shapes(cus):
             assert p["tasks"] == -(-(rows * spr) // 2)
         else:
             assert p["tasks"] == rows * p["tasks_per_row"]
-            assert U == 1 or fuse or K % SLAB != 0 or spr % 2 == 0
+            assert U == 1 or fuse or dt == "fp32" or spr % 2 == 0
         assert p["block"] in (64, 128, 256, 1024) and p["grid"] >= 1
         if p["block"] == 128:
             assert dt == "fp32" and p["uncapped"]

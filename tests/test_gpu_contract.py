@@ -1,7 +1,8 @@
 """GPU parity for the contract points beside the workloads: the overflowed
 multiplier corner (zeros keep their sign, other values saturate), the
 per-token host contract on padded output rows, flat-slab tasks across row
-ends, multi-row slabs for rows shorter than a slab, the first call of a process made inside a graph capture, and the
+ends, multi-row slabs for rows shorter than a slab, slabs of the flattened
+tensor for other row lengths, the first call of a process made inside a graph capture, and the
 no-arithmetic stream reference.  Every output sits between guard bands."""
 import os
 import subprocess
@@ -160,6 +161,53 @@ def test_multi_row_slabs(in_dtype, K):
             args = (x, in_dtype, M, K, G, False, out_dtype, fmt, layout)
             compare(f"multi-row slabs {in_dtype} M={M} K={K} G={G} {out_dtype} {fmt} {layout}",
                     *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
+
+
+@pytest.mark.parametrize("K,Gs", [(48, (16,)), (96, (16, 32)), (384, (32, 128)),
+                                  (640, (64, 128)), (1152, (16, 128)), (2880, (32, 64)),
+                                  (3712, (128,)), (11008, (128,))])
+def test_flattened_slabs(K, Gs):
+    """16-bit rows that are not whole slabs and do not divide one: slabs of
+    the flattened tensor cross row ends at any column; packed column-major
+    words whose groups come from two slabs, partial last words (ng % 4 != 0),
+    a last slab ending inside the tensor; every scale format and layout."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    M = -(-(cus * 16 * 512) // K) + 5
+    for in_dtype in ("bf16", "fp16"):
+        x = (W.normal_bf16(M + K, (M, K), factor_cols=[K - 1], factor=40.0) if in_dtype == "bf16"
+             else W.normal_fp16(M + K, (M, K)))
+        x[M // 3] = 0
+        for G in Gs:
+            p = aq.ptgq_plan_group(in_dtype, 0, M, K, G, False, 0, M, cus)
+            assert p["flat_slabs"] == 3 and p["slabs_per_task"] == 2
+            for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row"),
+                                           ("e4m3", "f32", "col"), ("int8", "ue8m0", "row")):
+                args = (x, in_dtype, M, K, G, False, out_dtype, fmt, layout)
+                compare(f"flattened slabs {in_dtype} M={M} K={K} G={G} {out_dtype} {fmt} "
+                        f"{layout}", *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
+
+
+def test_flattened_slabs_padded_codes():
+    """ptgq_quant_padded with slabs of the flattened tensor: rows past M are
+    zero, the column-major pad slots and partial-word bytes too."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    K, G = 640, 128                                     # 5 groups: partial words
+    M = -(-(cus * 16 * 512) // K) + 2
+    q_rows = M + 9
+    x = W.normal_bf16(78, (M, K))
+    assert aq.ptgq_plan_group("bf16", 0, M, K, G, False, 0, q_rows, cus)["flat_slabs"] == 3
+    q = Guarded((q_rows, K), torch.uint8, 0xCD)
+    sb = aq.ptgq_scale_bytes(M, K, G, "ue8m0", "col")
+    s = Guarded((sb,), torch.uint8, 0xCD)
+    aq.ptgq_quant_padded(to_dev(x), "bf16", M, K, G, False, "e4m3", "ue8m0", "col", 1e-10, q.t,
+                         q_rows, s.t)
+    torch.cuda.synchronize()
+    q.check("padded q")
+    s.check("padded s")
+    qh = q.host()
+    rq, rs = oracle.ptgq(x, "bf16", M, K, G, False, "e4m3", "ue8m0", "col", eps=1e-10)
+    compare("flattened slabs padded", qh[:M], s.host(), rq, rs)
+    assert np.all(qh[M:] == 0)
 
 
 def test_multi_row_slabs_padded_codes():
