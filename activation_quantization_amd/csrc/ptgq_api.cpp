@@ -312,11 +312,11 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // K = 256 27.7, K = 512 17.0).
         const bool mr_ok = !fuse && es == 2 && K < kSlab && kSlab % K == 0 &&
                            knob(KNOB_FLAT_SLABS) != 0;
-        // Any other 16-bit K that is not a multiple of the slab: slabs of
-        // the flattened tensor, crossing row ends anywhere (groups never
-        // cross them, G dividing K), so that no lane idles on a row's ragged
-        // last slab (group indices stay 32-bit).
-        const bool fg_ok = !fuse && es == 2 && K % kSlab != 0 && !mr_ok &&
+        // Any other K that is not a multiple of the slab (fp32 input: any
+        // such K): slabs of the flattened tensor, crossing row ends anywhere
+        // (groups never cross them, G dividing K), so that no lane idles on
+        // a row's ragged last slab (group indices stay 32-bit).
+        const bool fg_ok = !fuse && K % kSlab != 0 && !mr_ok &&
                            rows * a.ng < ((int64_t)1 << 31) && knob(KNOB_FLAT_SLABS) != 0;
         const bool fs_ok = mr_ok || fg_ok ||
                            (!fuse && K % kSlab == 0 &&

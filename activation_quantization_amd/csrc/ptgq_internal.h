@@ -81,7 +81,7 @@ struct GroupArgs {
                               // slabs (tasks cross row ends).  1: K % kSlab == 0,
                               // whole-row slabs; 2: 16-bit input, K < kSlab and
                               // kSlab % K == 0, each slab kSlab / K whole rows;
-                              // 3: 16-bit input, any other K: slabs of kSlab
+                              // 3: any other K % kSlab != 0: slabs of kSlab
                               // consecutive elements of the flattened tensor
     int64_t n_slabs;          // flat_slabs: slabs of the sequence
     FastDiv spr_div;          // flat_slabs: division by spr

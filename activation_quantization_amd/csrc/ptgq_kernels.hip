@@ -508,6 +508,33 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
 
 __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
+// The scale of group f of the tensor's group sequence (slabs of the
+// flattened tensor): group f % ng of row f / ng, a multiply-high division
+// (f < 2^31).  A packed column-major word may take its groups from two slabs
+// (two waves), so its bytes are stored one by one; the lane of a row's last
+// group also zeroes the unused bytes of the row's last, partial word.
+template <bool UE8M0>
+__device__ __forceinline__ void flat_group_scale(const GroupArgs &a, uint8_t *se, uint32_t f,
+                                                 const Scale &sc)
+{
+    const uint32_t mr = fastdiv(f, a.ng_div);
+    const uint32_t gr = f - mr * (uint32_t)a.ng;
+    if constexpr (UE8M0) {
+        if (a.scale_layout == LAYOUT_COL) {
+            uint8_t *wb = se + ((int64_t)(gr >> 2) * a.rows_pad + mr) * 4;
+            wb[gr & 3] = (uint8_t)sc.e;
+            if (gr + 1 == (uint32_t)a.ng)
+                for (uint32_t b = (gr & 3) + 1; b < 4; ++b) wb[b] = 0;
+        } else {
+            se[f] = (uint8_t)sc.e;
+        }
+    } else if (a.scale_layout == LAYOUT_ROW) {
+        reinterpret_cast<float *>(se)[f] = sc.r;
+    } else {
+        reinterpret_cast<float *>(se)[(int64_t)gr * a.rows_pad + mr] = sc.r;
+    }
+}
+
 // One slab of fp32 input: lane l holds elements 4l..4l+3 (half A, `ga`) and
 // 256+4l..256+4l+3 (half B, `gb`) of the slab, so a group of G elements is
 // held by G/4 adjacent lanes of one half and every lane derives two scales.
@@ -517,7 +544,7 @@ __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v.x, v.y,
 // `slab`: index of the slab within row m; `at`: offset of the slab's first
 // code from the task's first code, `c0`: offset of that from the code
 // region's base, `codes`: the task's code count.
-template <int G, int OUT, int SF, int SPOL>
+template <int G, int OUT, int SF, int SPOL, int FS = 0>
 __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x4 &ga,
                                                   const u32x4 &gb, int slab, uint32_t at,
                                                   uint32_t c0, uint32_t codes, rsrc_t rq,
@@ -546,6 +573,13 @@ __device__ __forceinline__ void process_slab_fp32(const GroupArgs &a, const u32x
 
     const int lg = lane / LA;                          // group within the half
     const bool leader = (lane % LA) == 0;
+    if constexpr (FS == 3) {
+        // slabs of the flattened tensor: m is the slab's index in it
+        const uint32_t fA = (uint32_t)(m * GPS + lg);
+        if (leader && validA) flat_group_scale<SF == SCALE_UE8M0>(a, se, fA, sA);
+        if (leader && validB) flat_group_scale<SF == SCALE_UE8M0>(a, se, fA + GPH, sB);
+        return;
+    }
     const int64_t g0 = (int64_t)slab * GPS;            // first group of the slab
     const int64_t gA = g0 + lg, gB = g0 + GPH + lg;
     if constexpr (ue8m0) {
@@ -627,8 +661,8 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
         }
         const uint32_t at = (uint32_t)s * kSlab;                    // offset in the task
         if constexpr (IN == IN_FP32) {
-            process_slab_fp32<G, OUT, SF, SPOL>(a, b.g[s], b.gh[s], slab, at, t.c0, t.codes, rq,
-                                                se, m, lane);
+            process_slab_fp32<G, OUT, SF, SPOL, FS>(a, b.g[s], b.gh[s], slab, at, t.c0, t.codes,
+                                                    rq, se, m, lane);
             continue;
         }
         const uint32_t col = at + (uint32_t)lane * 8;              // in the task
@@ -691,30 +725,9 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
         if constexpr (FS == 3) {
             // slabs of the flattened tensor: slab m holds groups m * GPS ..
             // m * GPS + GPS - 1 of the tensor's group sequence (G divides K,
-            // so no group crosses a row); group f is group f % ng of row
-            // f / ng (a multiply-high division).  A packed column-major word
-            // may take its groups from two slabs (two waves), so its bytes
-            // are stored one by one; the bytes past a row's last group in its
-            // last word are written as zero by that group's lane.
-            const uint32_t f = (uint32_t)(m * GPS + lg);              // < 2^31
-            const uint32_t mr = fastdiv(f, a.ng_div);
-            const uint32_t gr = f - mr * (uint32_t)a.ng;
-            if (leader && valid) {
-                if constexpr (ue8m0) {
-                    if (a.scale_layout == LAYOUT_COL) {
-                        uint8_t *wb = se + ((int64_t)(gr >> 2) * a.rows_pad + mr) * 4;
-                        wb[gr & 3] = (uint8_t)sc.e;
-                        if (gr + 1 == (uint32_t)a.ng)
-                            for (uint32_t b = (gr & 3) + 1; b < 4; ++b) wb[b] = 0;
-                    } else {
-                        se[f] = (uint8_t)sc.e;
-                    }
-                } else if (a.scale_layout == LAYOUT_ROW) {
-                    reinterpret_cast<float *>(se)[f] = sc.r;
-                } else {
-                    reinterpret_cast<float *>(se)[(int64_t)gr * a.rows_pad + mr] = sc.r;
-                }
-            }
+            // so no group crosses a row)
+            if (leader && valid)
+                flat_group_scale<ue8m0>(a, se, (uint32_t)(m * GPS + lg), sc);
             continue;
         }
         if constexpr (FS == 2) {
@@ -1110,7 +1123,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
     if constexpr (FS) {
         static_assert(!FUSE && !TABLE, "flat-slab tasks: unfused inputs");
-        static_assert(FS < 2 || IN != IN_FP32, "multi-row and flattened slabs: 16-bit inputs");
+        static_assert(FS != 2 || IN != IN_FP32, "multi-row slabs: 16-bit inputs");
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true, false, FS>(
             a, FlatSlabMap<IN, UMAX>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
     } else {
@@ -2072,8 +2085,7 @@ static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid,
             if constexpr (IN == IN_FP32) return hipErrorInvalidValue;
             else ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 2><<<grid, block, 0, st>>>(a);
         } else if (a.flat_slabs == 3) {
-            if constexpr (IN == IN_FP32) return hipErrorInvalidValue;
-            else ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 3><<<grid, block, 0, st>>>(a);
+            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 3><<<grid, block, 0, st>>>(a);
         } else if (a.flat_slabs == 0)
             ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0><<<grid, block, 0, st>>>(a);
         else

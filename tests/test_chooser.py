@@ -114,8 +114,8 @@ def test_odd_slab_rows_take_flat_slab_tasks_across_row_ends():
     p = plan("fp16", 8192, 3584 + 128)
     assert p["flat_slabs"] == 3 and p["slabs_per_task"] == 2
     assert p["tasks"] == -(-(-(-(8192 * 3712) // 512)) // 2)
-    # fp32 input keeps row tasks there
-    assert plan("fp32", 8192, 3584 + 128)["flat_slabs"] == 0
+    # fp32 input too
+    assert plan("fp32", 8192, 3584 + 128)["flat_slabs"] == 3
     # rows of an even slab count keep row tasks (the same tasks)
     p = plan("bf16", 4096, 7168)
     assert p["flat_slabs"] == 0 and p["tasks"] == 4096 * 7
@@ -134,8 +134,9 @@ def test_short_rows_take_multi_row_slabs(K):
     p = plan("bf16", rows, K, G=16)
     assert p["flat_slabs"] == 2 and p["slabs_per_task"] == 2 and p["uncapped"] == 1
     assert p["tasks"] == (8193 + 1) // 2 and p["block"] == 64
-    # fp32 input and fused calls keep one row per slab
-    assert plan("fp32", rows, K, G=16)["flat_slabs"] == 0
+    # fp32 input takes slabs of the flattened tensor; fused calls keep one
+    # row per slab
+    assert plan("fp32", rows, K, G=16)["flat_slabs"] == 3
     assert plan("bf16", rows, K, G=16, fuse=True)["flat_slabs"] == 0
     # K not dividing the slab: slabs of the flattened tensor
     assert plan("bf16", 65536, 384)["flat_slabs"] == 3
@@ -176,8 +177,8 @@ def test_rules_hold_for_random_shapes(cus):
         else:
             assert p["tasks_per_row"] == -(-spr // U)
         if p["flat_slabs"] == 3:
-            assert U == 2 and not fuse and dt != "fp32" and K % SLAB != 0
-            assert not (K < SLAB and SLAB % K == 0)
+            assert U == 2 and not fuse and K % SLAB != 0
+            assert dt == "fp32" or not (K < SLAB and SLAB % K == 0)
             assert p["tasks"] == -(-(-(-(rows * K) // SLAB)) // 2)
         elif p["flat_slabs"] == 2:
             assert U == 2 and not fuse and dt != "fp32" and K < SLAB and SLAB % K == 0
@@ -187,7 +188,7 @@ def test_rules_hold_for_random_shapes(cus):
             assert p["tasks"] == -(-(rows * spr) // 2)
         else:
             assert p["tasks"] == rows * p["tasks_per_row"]
-            assert U == 1 or fuse or dt == "fp32" or spr % 2 == 0
+            assert U == 1 or fuse or spr % 2 == 0
         assert p["block"] in (64, 128, 256, 1024) and p["grid"] >= 1
         if p["block"] == 128:
             assert dt == "fp32" and p["uncapped"]

@@ -173,9 +173,10 @@ def test_flattened_slabs(K, Gs):
     a last slab ending inside the tensor; every scale format and layout."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     M = -(-(cus * 16 * 512) // K) + 5
-    for in_dtype in ("bf16", "fp16"):
-        x = (W.normal_bf16(M + K, (M, K), factor_cols=[K - 1], factor=40.0) if in_dtype == "bf16"
-             else W.normal_fp16(M + K, (M, K)))
+    for in_dtype in ("bf16", "fp16", "fp32"):
+        x = {"bf16": lambda: W.normal_bf16(M + K, (M, K), factor_cols=[K - 1], factor=40.0),
+             "fp16": lambda: W.normal_fp16(M + K, (M, K)),
+             "fp32": lambda: W.normal_f32(M + K, (M, K))}[in_dtype]()
         x[M // 3] = 0
         for G in Gs:
             p = aq.ptgq_plan_group(in_dtype, 0, M, K, G, False, 0, M, cus)
@@ -185,6 +186,22 @@ def test_flattened_slabs(K, Gs):
                 args = (x, in_dtype, M, K, G, False, out_dtype, fmt, layout)
                 compare(f"flattened slabs {in_dtype} M={M} K={K} G={G} {out_dtype} {fmt} "
                         f"{layout}", *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
+
+
+@pytest.mark.parametrize("K", [16, 64, 256])
+def test_flattened_slabs_fp32_short_rows(K):
+    """fp32 rows shorter than a slab take slabs of the flattened tensor."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    M = cus * 16 * 512 // K + 3
+    x = W.normal_f32(M + 3 * K, (M, K))
+    x[M // 2] = 0
+    for G in [g for g in (16, 32, 64, 128) if g <= K]:
+        assert aq.ptgq_plan_group("fp32", 0, M, K, G, False, 0, M, cus)["flat_slabs"] == 3
+        for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row"),
+                                       ("e4m3", "f32", "col"), ("int8", "ue8m0", "row")):
+            args = (x, "fp32", M, K, G, False, out_dtype, fmt, layout)
+            compare(f"flattened slabs fp32 M={M} K={K} G={G} {out_dtype} {fmt} {layout}",
+                    *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
 
 
 def test_flattened_slabs_padded_codes():
