@@ -318,16 +318,22 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // a row's ragged last slab (group indices stay 32-bit).
         const bool fg_ok = !fuse && K % kSlab != 0 && !mr_ok &&
                            rows * a.ng < ((int64_t)1 << 31) && knob(KNOB_FLAT_SLABS) != 0;
-        const bool fs_ok = mr_ok || fg_ok ||
+        // Fused calls likewise, their lanes reading the gate and up halves
+        // of their own rows (output elements < 2^31): measured on MI355X,
+        // 16.8 M output elements, K = 1024 / 1536 / 2048 16.0 us, K = 1152
+        // 19.9, K = 1408 18.4, K = 640 28.1 with one row per task.
+        const bool fgf_ok = fuse && K % kSlab != 0 && rows * K < ((int64_t)1 << 31) &&
+                            knob(KNOB_FLAT_SLABS) != 0;
+        const bool fs_ok = mr_ok || fg_ok || fgf_ok ||
                            (!fuse && K % kSlab == 0 &&
                             (a.spr % 2 == 1 || knob(KNOB_FLAT_SLABS) > 0) &&
                             knob(KNOB_FLAT_SLABS) != 0);
         const int64_t seq_slabs =
-            mr_ok || fg_ok ? (rows * K + kSlab - 1) / kSlab : rows * (int64_t)a.spr;
+            mr_ok || fg_ok || fgf_ok ? (rows * K + kSlab - 1) / kSlab : rows * (int64_t)a.spr;
         choose_task(geo, seq_slabs, a.spr, fuse != 0, bf16, !fuse && es == 2, fs_ok, table_ok,
                     cus);
         a.U = geo.U;
-        a.flat_slabs = fs_ok && a.U == 2 ? (mr_ok ? 2 : fg_ok ? 3 : 1) : 0;
+        a.flat_slabs = fgf_ok ? 3 : fs_ok && a.U == 2 ? (mr_ok ? 2 : fg_ok ? 3 : 1) : 0;
         if (a.flat_slabs >= 2) a.spr = 1;     // the sequence's rows are its slabs
         a.tpr = (a.spr + a.U - 1) / a.U;
         geo.flat_slabs = a.flat_slabs != 0;
@@ -338,6 +344,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         a.fs_total = rows * K;
         a.mr_shift = a.flat_slabs == 2 ? __builtin_ctzll((unsigned long long)a.ng) : -1;
         a.ng_div = make_fastdiv((uint32_t)a.ng);
+        a.k_div = make_fastdiv((uint32_t)K);
         const int64_t tasks = a.flat_slabs ? (a.n_slabs + a.U - 1) / a.U : rows * (int64_t)a.tpr;
         if (tasks >= INT32_MAX) return PTGQ_EUNSUPPORTED;
         a.n_tasks = (int32_t)tasks;

@@ -82,13 +82,15 @@ struct GroupArgs {
                               // whole-row slabs; 2: 16-bit input, K < kSlab and
                               // kSlab % K == 0, each slab kSlab / K whole rows;
                               // 3: any other K % kSlab != 0: slabs of kSlab
-                              // consecutive elements of the flattened tensor
+                              // consecutive elements of the flattened output
+                              // (fused: of the flattened gate and up halves)
     int64_t n_slabs;          // flat_slabs: slabs of the sequence
     FastDiv spr_div;          // flat_slabs: division by spr
     int32_t fs_row;           // flat_slabs: elements per row of the slab sequence
                               // (K; kSlab for multi-row slabs)
     int32_t mr_shift;         // flat_slabs == 2: log2(ng)
     FastDiv ng_div;           // flat_slabs == 3: division by ng
+    FastDiv k_div;            // flat_slabs == 3, fused: division by K
     int64_t fs_total;         // flat_slabs: elements of the tensor, M * K
     int32_t wpb;              // waves per block of the launch
 };

@@ -474,12 +474,13 @@ struct TaskLoc {
     int64_t m;
     int j;
     int next_row;   // flat-slab tasks: first slab (0..UMAX) that lies in row m + 1
+    uint32_t row0;  // fused slabs of the flattened tensor: the row `xb` points at
 };
 
 // `live` false: the loads are issued over an empty range (zeros, no memory
 // traffic), so that every path through the task loop issues the same loads
 // and the wait counts stay exact.
-template <int IN, bool FUSE, int UMAX>
+template <int IN, bool FUSE, int UMAX, int FS = 0>
 __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, int lane,
                                           bool live, TaskBuf<UMAX> &b)
 {
@@ -487,6 +488,21 @@ __device__ __forceinline__ void load_task(const GroupArgs &a, const TaskLoc &t, 
     constexpr int pol = kStreamPolicy;
     const uint32_t bytes = live ? t.xrange : 0u;
     const rsrc_t rg = make_rsrc(t.xb, bytes);
+    if constexpr (FUSE && FS == 3) {
+        // slabs of the flattened output: a lane's 8 elements lie in one row
+        // (8 divides G, which divides K); their gate and up halves sit at
+        // column c of row r's [gate | up] input, r counted from row0
+        const uint32_t K = (uint32_t)a.K;
+#pragma unroll
+        for (int s = 0; s < UMAX; ++s) {
+            const uint32_t e = ((uint32_t)t.m + s) * kSlab + (uint32_t)lane * 8;   // < 2^31
+            const uint32_t r = fastdiv(e, a.k_div);
+            const uint32_t off = ((r - t.row0) * 2 * K + (e - r * K)) * 2;
+            b.g[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, pol);
+            b.u[s] = __builtin_amdgcn_raw_buffer_load_b128(rg, off + K * 2, 0, pol);
+        }
+        return;
+    }
     // 16-bit: lane l holds elements 8l..8l+7 of a slab; fp32: 4l..4l+3 (g)
     // and 256+4l..256+4l+3 (gh), so every load instruction reads one
     // contiguous KiB
@@ -843,12 +859,37 @@ struct FlatMap {
 // except the tensor's last one.  The row of slab S is S / spr (a wave-uniform
 // multiply-high division).  The task is addressed from its first row, whose
 // range is extended by the slab that crosses into the next row.
-template <int IN, int UMAX>
+template <int IN, int UMAX, bool FUSE = false>
 struct FlatSlabMap {
     __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int /*lane*/)
     {
         constexpr int ES = IN == IN_FP32 ? 4 : 2;
         const uint32_t S = (uint32_t)t * UMAX;                      // first slab (< 2^31)
+        if constexpr (FUSE) {
+            // slabs of the flattened output, whose inputs are the gate and
+            // up halves of rows row0 .. r1 (the output has fewer than 2^31
+            // elements); the lanes address their own rows (load_task)
+            const uint32_t left = (uint32_t)a.n_slabs - S;           // >= 1 for live tasks
+            const uint32_t e0 = S * kSlab;
+            const uint32_t all = (left < UMAX ? left : UMAX) * kSlab;
+            const uint32_t rest = (uint32_t)(a.fs_total - e0);
+            const uint32_t cnt = rest < all ? rest : all;
+            const uint32_t r0 = fastdiv(e0, a.k_div);
+            const uint32_t r1 = fastdiv(e0 + cnt - 1, a.k_div);
+            TaskLoc l;
+            l.xb = static_cast<const char *>(a.x) + (uint64_t)r0 * a.in_stride;
+            l.qb = a.q + e0;
+            l.sbase = static_cast<uint8_t *>(a.s);
+            l.xrange = (r1 - r0 + 1) * (uint32_t)a.in_stride;
+            l.qrange = cnt;
+            l.c0 = 0;
+            l.codes = cnt;
+            l.m = S;
+            l.j = 0;
+            l.next_row = 1;
+            l.row0 = r0;
+            return l;
+        }
         const uint32_t m = fastdiv(S, a.spr_div);
         const uint32_t j = S - m * (uint32_t)a.spr;
         const uint32_t left = (uint32_t)a.n_slabs - S;               // >= 1 for live tasks
@@ -1043,14 +1084,14 @@ __device__ __forceinline__ void continue_tasks(const GroupArgs &a, Map &map, int
         const int tB = t + stride;
         const bool hasB = tB < n;
         const TaskLoc lB = map(a, hasB ? tB : t, lane);
-        load_task<IN, FUSE, UMAX>(a, lB, lane, hasB, spare);
+        load_task<IN, FUSE, UMAX, FS>(a, lB, lane, hasB, spare);
         process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL, FS>(a, lcur, lane, cur, tab);
         if (!hasB) break;
         t = tB;
         const int tA = t + stride;
         const bool hasA = tA < n;
         lcur = map(a, hasA ? tA : t, lane);
-        load_task<IN, FUSE, UMAX>(a, lcur, lane, hasA, cur);
+        load_task<IN, FUSE, UMAX, FS>(a, lcur, lane, hasA, cur);
         process_task<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL, FS>(a, lB, lane, spare, tab);
         if (!hasA) break;
         t = tA;
@@ -1071,7 +1112,7 @@ __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first
     TaskBuf<UMAX> A, B;
     if constexpr (STAGE && !FETCHED) table_fetch<TABLE>(tr);
     const TaskLoc lA = map(a, hasA0 ? first : 0, lane);
-    load_task<IN, FUSE, UMAX>(a, lA, lane, hasA0, A);
+    load_task<IN, FUSE, UMAX, FS>(a, lA, lane, hasA0, A);
     if constexpr (STAGE) table_store<TABLE>(tr, tab);
     if (!hasA0) return;
     continue_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, SPOL, FS>(a, map, first, lA, A, B, n, stride,
@@ -1122,10 +1163,11 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     const int lb = logical_block(blockIdx.x, gridDim.x, a.xcd_chunk);
     constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
     if constexpr (FS) {
-        static_assert(!FUSE && !TABLE, "flat-slab tasks: unfused inputs");
+        static_assert(FS == 3 || (!FUSE && !TABLE), "flat-slab tasks: unfused inputs");
         static_assert(FS != 2 || IN != IN_FP32, "multi-row slabs: 16-bit inputs");
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true, false, FS>(
-            a, FlatSlabMap<IN, UMAX>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
+            a, FlatSlabMap<IN, UMAX, FUSE>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane,
+            tab);
     } else {
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true>(
             a, FlatMap<IN, UMAX>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
@@ -2087,6 +2129,13 @@ static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid,
         } else if (a.flat_slabs == 3) {
             ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 3><<<grid, block, 0, st>>>(a);
         } else if (a.flat_slabs == 0)
+            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0><<<grid, block, 0, st>>>(a);
+        else
+            return hipErrorInvalidValue;
+    } else if constexpr (FUSE) {
+        if (a.flat_slabs == 3)
+            ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 3><<<grid, block, 0, st>>>(a);
+        else if (a.flat_slabs == 0)
             ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0><<<grid, block, 0, st>>>(a);
         else
             return hipErrorInvalidValue;

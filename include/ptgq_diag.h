@@ -108,7 +108,7 @@ PTGQ_API int ptgq_diag_fastdiv(uint32_t d, const uint32_t *n, uint32_t *q, int64
  *        (0/1), uncapped grid (0/1), flat-slab tasks (0 none; 1 the tensor's
  *        whole-row slabs taken as one sequence, tasks crossing row ends; 2
  *        slabs of several rows shorter than a slab; 3 slabs of the flattened
- *        tensor, for 16-bit rows that are not whole slabs); all zero when
+ *        tensor, for other rows that are not whole slabs, fused included); all zero when
  *        nothing would be launched.
  * Returns PTGQ_OK, PTGQ_EINVAL (invalid shape, cus < 1, out NULL) or
  * PTGQ_EUNSUPPORTED, as the calls would for the same shape.

@@ -134,10 +134,9 @@ def test_short_rows_take_multi_row_slabs(K):
     p = plan("bf16", rows, K, G=16)
     assert p["flat_slabs"] == 2 and p["slabs_per_task"] == 2 and p["uncapped"] == 1
     assert p["tasks"] == (8193 + 1) // 2 and p["block"] == 64
-    # fp32 input takes slabs of the flattened tensor; fused calls keep one
-    # row per slab
+    # fp32 input and fused calls take slabs of the flattened tensor
     assert plan("fp32", rows, K, G=16)["flat_slabs"] == 3
-    assert plan("bf16", rows, K, G=16, fuse=True)["flat_slabs"] == 0
+    assert plan("bf16", rows, K, G=16, fuse=True)["flat_slabs"] == 3
     # K not dividing the slab: slabs of the flattened tensor
     assert plan("bf16", 65536, 384)["flat_slabs"] == 3
     # the override's 0 restores one row per slab
@@ -177,9 +176,9 @@ def test_rules_hold_for_random_shapes(cus):
         else:
             assert p["tasks_per_row"] == -(-spr // U)
         if p["flat_slabs"] == 3:
-            assert U == 2 and not fuse and K % SLAB != 0
-            assert dt == "fp32" or not (K < SLAB and SLAB % K == 0)
-            assert p["tasks"] == -(-(-(-(rows * K) // SLAB)) // 2)
+            assert K % SLAB != 0 and (fuse or U == 2)
+            assert fuse or dt == "fp32" or not (K < SLAB and SLAB % K == 0)
+            assert p["tasks"] == -(-(-(-(rows * K) // SLAB)) // U)
         elif p["flat_slabs"] == 2:
             assert U == 2 and not fuse and dt != "fp32" and K < SLAB and SLAB % K == 0
             assert p["tasks"] == -(-(-(-(rows * K) // SLAB)) // 2)

@@ -188,6 +188,27 @@ def test_flattened_slabs(K, Gs):
                         f"{layout}", *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
 
 
+@pytest.mark.parametrize("K,G", [(48, 16), (96, 32), (256, 128), (640, 64), (1152, 128),
+                                 (1408, 128), (2880, 64)])
+def test_flattened_slabs_fused(K, G):
+    """Fused silu(gate)*up over rows that are not whole slabs: each lane reads
+    the gate and up halves of its own row; bf16 with the SiLU table (large)
+    and the direct evaluation (small), fp16 (direct); a last slab ending
+    inside the tensor."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for in_dtype, M in (("bf16", -(-(cus * 16 * 512) // K) + 3), ("bf16", 37),
+                        ("fp16", -(-(cus * 4 * 512) // K) + 1)):
+        p = aq.ptgq_plan_group(in_dtype, 0, M, K, G, True, 0, M, cus)
+        assert p["flat_slabs"] == 3
+        x = (W.normal_bf16(M * 3 + K, (M, 2 * K)) if in_dtype == "bf16"
+             else W.normal_fp16(M * 3 + K, (M, 2 * K)))
+        for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row")):
+            args = (x, in_dtype, M, K, G, True, out_dtype, fmt, layout)
+            compare(f"flattened slabs fused {in_dtype} M={M} K={K} G={G} table={p['silu_table']} "
+                    f"{out_dtype} {fmt} {layout}", *run_flat(*args),
+                    *oracle.ptgq(*args, eps=1e-10))
+
+
 @pytest.mark.parametrize("K", [16, 64, 256])
 def test_flattened_slabs_fp32_short_rows(K):
     """fp32 rows shorter than a slab take slabs of the flattened tensor."""
