@@ -83,7 +83,9 @@ struct GroupArgs {
                               // kSlab % K == 0, each slab kSlab / K whole rows;
                               // 3: any other K % kSlab != 0: slabs of kSlab
                               // consecutive elements of the flattened output
-                              // (fused: of the flattened gate and up halves)
+                              // (fused: of the flattened gate and up halves).
+                              // Masked: 0 or 3, each expert's live rows taken
+                              // as one such sequence (no task crosses experts)
     int64_t n_slabs;          // flat_slabs: slabs of the sequence
     FastDiv spr_div;          // flat_slabs: division by spr
     int32_t fs_row;           // flat_slabs: elements per row of the slab sequence

@@ -853,51 +853,70 @@ struct FlatMap {
     }
 };
 
-// Flat schedule, flat-slab tasks (unfused, K a multiple of the slab, so input
-// and codes are one contiguous sequence of whole-row slabs): task t is slabs
-// U*t .. U*t+U-1 of that sequence, crossing row ends; no task is short
-// except the tensor's last one.  The row of slab S is S / spr (a wave-uniform
-// multiply-high division).  The task is addressed from its first row, whose
-// range is extended by the slab that crosses into the next row.
-template <int IN, int UMAX, bool FUSE = false>
+// Task of UMAX slabs from slab S of a flattened output of `total` (< 2^31)
+// elements: codes S * kSlab .. up to the sequence's end (a sequence's last
+// task may be short), written from q; the output's rows of K codes come from
+// input rows of a.in_stride bytes from x, scales go to s.  Unfused input is
+// the same flat sequence; fused lanes address the gate and up halves of their
+// own rows (load_task), from row0, the row of the task's first code.  Slab s
+// of the task is "row" S + s (next_row 1).
+template <int IN, int UMAX, bool FUSE>
+__device__ __forceinline__ TaskLoc flat_seq_loc(const GroupArgs &a, const char *x, uint8_t *q,
+                                                uint8_t *s, uint32_t S, uint32_t total)
+{
+    constexpr int ES = IN == IN_FP32 ? 4 : 2;
+    const uint32_t e0 = S * kSlab;
+    const uint32_t rest = total - e0;                       // >= 1 for live tasks
+    const uint32_t cnt = rest < UMAX * kSlab ? rest : UMAX * kSlab;
+    TaskLoc l;
+    l.qb = q + e0;
+    l.sbase = s;
+    l.qrange = cnt;
+    l.c0 = 0;
+    l.codes = cnt;
+    l.m = S;
+    l.j = 0;
+    l.next_row = 1;
+    if constexpr (FUSE) {
+        const uint32_t r0 = fastdiv(e0, a.k_div);
+        const uint32_t r1 = fastdiv(e0 + cnt - 1, a.k_div);
+        l.xb = x + (uint64_t)r0 * a.in_stride;
+        l.xrange = (r1 - r0 + 1) * (uint32_t)a.in_stride;
+        l.row0 = r0;
+    } else {
+        l.xb = x + (uint64_t)e0 * ES;
+        l.xrange = cnt * ES;
+        l.row0 = 0;
+    }
+    return l;
+}
+
+// Flat schedule, flat-slab tasks: task t is slabs U*t .. U*t+U-1 of one
+// sequence of slabs over the whole tensor, crossing row ends.  FS 1 (unfused,
+// K a multiple of the slab, so input and codes are one contiguous sequence of
+// whole-row slabs): no task is short except the tensor's last one; the row of
+// slab S is S / spr (a wave-uniform multiply-high division), and the task is
+// addressed from its first row, whose range is extended by the slab that
+// crosses into the next row.  FS 2 (rows of kSlab elements, spr 1): the same
+// arithmetic, clipped to the tensor, which may end inside its last slab.
+// FS 3: slabs of the flattened output (flat_seq_loc).
+template <int IN, int UMAX, bool FUSE, int FS>
 struct FlatSlabMap {
     __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int /*lane*/)
     {
         constexpr int ES = IN == IN_FP32 ? 4 : 2;
         const uint32_t S = (uint32_t)t * UMAX;                      // first slab (< 2^31)
-        if constexpr (FUSE) {
-            // slabs of the flattened output, whose inputs are the gate and
-            // up halves of rows row0 .. r1 (the output has fewer than 2^31
-            // elements); the lanes address their own rows (load_task)
-            const uint32_t left = (uint32_t)a.n_slabs - S;           // >= 1 for live tasks
-            const uint32_t e0 = S * kSlab;
-            const uint32_t all = (left < UMAX ? left : UMAX) * kSlab;
-            const uint32_t rest = (uint32_t)(a.fs_total - e0);
-            const uint32_t cnt = rest < all ? rest : all;
-            const uint32_t r0 = fastdiv(e0, a.k_div);
-            const uint32_t r1 = fastdiv(e0 + cnt - 1, a.k_div);
-            TaskLoc l;
-            l.xb = static_cast<const char *>(a.x) + (uint64_t)r0 * a.in_stride;
-            l.qb = a.q + e0;
-            l.sbase = static_cast<uint8_t *>(a.s);
-            l.xrange = (r1 - r0 + 1) * (uint32_t)a.in_stride;
-            l.qrange = cnt;
-            l.c0 = 0;
-            l.codes = cnt;
-            l.m = S;
-            l.j = 0;
-            l.next_row = 1;
-            l.row0 = r0;
-            return l;
-        }
+        if constexpr (FS == 3)
+            return flat_seq_loc<IN, UMAX, FUSE>(a, static_cast<const char *>(a.x), a.q,
+                                                static_cast<uint8_t *>(a.s), S,
+                                                (uint32_t)a.fs_total);
         const uint32_t m = fastdiv(S, a.spr_div);
         const uint32_t j = S - m * (uint32_t)a.spr;
         const uint32_t left = (uint32_t)a.n_slabs - S;               // >= 1 for live tasks
         const uint32_t K = (uint32_t)a.fs_row;
         // the region is row m and the slabs after it up to the task's end
         // (the next row's first slab when the task crosses the row end),
-        // clipped to the tensor (a multi-row slab sequence may end inside
-        // its last slab)
+        // clipped to the tensor
         const uint32_t span = j * kSlab + (left < UMAX ? left : UMAX) * kSlab;
         const int64_t rest = a.fs_total - (int64_t)m * K;          // >= 1 for live tasks
         const uint32_t reach0 = span > K ? span : K;
@@ -963,11 +982,21 @@ struct MaskedRows {
     }
 };
 
+// Tasks of UMAX slabs over `live` flattened rows of K codes (live * K < 2^31).
+template <int UMAX>
+__device__ __forceinline__ int slab_tasks(int live, uint32_t K)
+{
+    constexpr uint32_t per = (uint32_t)UMAX * kSlab;
+    return (int)(((uint32_t)live * K + per - 1) / per);
+}
+
 // Inclusive prefix sum of clamp(masked_m[e], 0, rows) over e < E into LDS
-// `scan` (masked_m NULL: every row of every expert is live).  Wave 0 only;
-// the caller synchronizes.
+// `scan` (masked_m NULL: every row of every expert is live).  SLABS (UMAX
+// slabs per task): the sum is over the experts' task counts, and the clamped
+// live rows go to scan[E + e].  Wave 0 only; the caller synchronizes.
+template <int SLABS = 0>
 __device__ __forceinline__ void masked_prefix_sum(const int32_t *masked_m, int E, int64_t rows,
-                                                  int lane, int *scan)
+                                                  int lane, int *scan, uint32_t K = 0)
 {
     int carry = 0;
     for (int c = 0; c < E; c += 64) {
@@ -975,6 +1004,10 @@ __device__ __forceinline__ void masked_prefix_sum(const int32_t *masked_m, int E
         if (c + lane < E) {
             v = masked_m ? masked_m[c + lane] : (int)rows;
             v = v < 0 ? 0 : (v > rows ? (int)rows : v);
+            if constexpr (SLABS > 0) {
+                scan[E + c + lane] = v;
+                v = slab_tasks<SLABS>(v, K);
+            }
         }
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -1036,6 +1069,41 @@ struct MaskedMap {
         return masked_loc<IN, UMAX>(a, e, r, t - R * a.tpr);
     }
 };
+// Masked schedule in flattened slabs (rows whose length is not a multiple of
+// the slab): expert e's live rows are one sequence of live_e * K codes, cut
+// into tasks of UMAX slabs (its last task may be short; no task crosses
+// experts), and `tasks` walks the prefix sum of the experts' task counts.
+// REG (E <= 64): lane l holds expert l's live rows in `live`; else they are in
+// LDS at `lrows`.
+template <int IN, int UMAX, bool FUSE, bool REG>
+struct MaskedSlabMap {
+    MaskedRows tasks;
+    int live;
+    const int *lrows;
+
+    __device__ __forceinline__ MaskedSlabMap(int win, int live_, int E, int lane)
+        : tasks(win, E, lane), live(live_), lrows(nullptr)
+    {
+    }
+    __device__ __forceinline__ MaskedSlabMap(const int *scan, int E, int lane)
+        : tasks(scan, E, lane), live(0), lrows(scan + E)
+    {
+    }
+
+    __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int lane)
+    {
+        int e, tl;
+        tasks.locate(t, lane, e, tl);
+        e = __builtin_amdgcn_readfirstlane(e);
+        const int n = REG ? __builtin_amdgcn_readlane(live, e) : lrows[e];
+        return flat_seq_loc<IN, UMAX, FUSE>(
+            a, static_cast<const char *>(a.x) + (int64_t)e * a.x_expert_stride,
+            a.q + (int64_t)e * a.q_expert_stride,
+            static_cast<uint8_t *>(a.s) + (int64_t)e * a.s_expert_stride, (uint32_t)tl * UMAX,
+            (uint32_t)n * (uint32_t)a.K);
+    }
+};
+
 // The SiLU table staged into LDS in two steps, so that its global loads can
 // be issued before a wave's first task loads and its LDS stores wait for the
 // table alone (vector memory loads complete in issue order): table kernels
@@ -1166,7 +1234,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
         static_assert(FS == 3 || (!FUSE && !TABLE), "flat-slab tasks: unfused inputs");
         static_assert(FS != 2 || IN != IN_FP32, "multi-row slabs: 16-bit inputs");
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true, false, FS>(
-            a, FlatSlabMap<IN, UMAX, FUSE>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane,
+            a, FlatSlabMap<IN, UMAX, FUSE, FS>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane,
             tab);
     } else {
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true>(
@@ -1197,9 +1265,10 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
 // Masked layout, balanced over experts: masked_m (E values, clamped to [0,
 // tokens_pad]) is summed into a prefix sum (in each wave's registers for E <=
 // 64, else by wave 0 into LDS), and the grid walks the live rows of all
-// experts as one task space.  Rows at or past masked_m are never read or
-// written.  Dynamic LDS: E ints.
-template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
+// experts as one task space (FS 3: the flattened slabs of each expert's live
+// rows).  Rows at or past masked_m are never read or written.  Dynamic LDS: E
+// ints (FS 3: 2 E).
+template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int FS>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupArgs a)
 {
     __shared__ float tab[TABLE ? kSiluTab : 1];
@@ -1222,24 +1291,45 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
         table_fetch<TABLE>(tr);
         __builtin_amdgcn_sched_barrier(0);   // keep both loads ahead of the wait
         const int live = lane < E ? (raw < 0 ? 0 : (raw > a.rows ? (int)a.rows : raw)) : 0;
-        const int win = wave_inclusive_sum(live, lane);
-        const int n = __builtin_amdgcn_readlane(win, E - 1) * a.tpr;
-        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, true, true>(
-            a, MaskedMap<IN, UMAX>(win, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab,
-            tr);
+        if constexpr (FS == 3) {
+            const int win = wave_inclusive_sum(slab_tasks<UMAX>(live, (uint32_t)a.K), lane);
+            const int n = __builtin_amdgcn_readlane(win, E - 1);
+            run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, true, true, FS>(
+                a, MaskedSlabMap<IN, UMAX, FUSE, true>(win, live, E, lane), lb * wpb + wib, n,
+                gridDim.x * wpb, lane, tab, tr);
+        } else {
+            const int win = wave_inclusive_sum(live, lane);
+            const int n = __builtin_amdgcn_readlane(win, E - 1) * a.tpr;
+            run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, true, true>(
+                a, MaskedMap<IN, UMAX>(win, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane,
+                tab, tr);
+        }
         return;
     }
     // More experts: the table's loads, then the prefix sum of masked_m into
     // LDS (wave 0), then the table's stores, behind one barrier.
     TableRegs tr;
     table_fetch<TABLE>(tr);
-    if (wib == 0) masked_prefix_sum(a.masked_m, E, a.rows, lane, scan);
+    if (wib == 0) {
+        if constexpr (FS == 3)
+            masked_prefix_sum<UMAX>(a.masked_m, E, a.rows, lane, scan, (uint32_t)a.K);
+        else
+            masked_prefix_sum(a.masked_m, E, a.rows, lane, scan);
+    }
     if constexpr (TABLE) table_store<TABLE>(tr, tab);
     else __syncthreads();
-    const int n = scan[E - 1] * a.tpr;
-    if (lb * wpb >= n) return;                    // block-uniform: nothing to do
-    run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, false>(
-        a, MaskedMap<IN, UMAX>(scan, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab);
+    if constexpr (FS == 3) {
+        const int n = scan[E - 1];
+        if (lb * wpb >= n) return;                // block-uniform: nothing to do
+        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, false, false, FS>(
+            a, MaskedSlabMap<IN, UMAX, FUSE, false>(scan, E, lane), lb * wpb + wib, n,
+            gridDim.x * wpb, lane, tab);
+    } else {
+        const int n = scan[E - 1] * a.tpr;
+        if (lb * wpb >= n) return;                // block-uniform: nothing to do
+        run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, false>(
+            a, MaskedMap<IN, UMAX>(scan, E, lane), lb * wpb + wib, n, gridDim.x * wpb, lane, tab);
+    }
 }
 
 // --------------------------------------------------------------------------
@@ -2117,10 +2207,16 @@ template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE>
 static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid, unsigned block,
                                  hipStream_t st)
 {
-    if (masked)
-        ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE>
-            <<<grid, block, (size_t)a.num_experts * sizeof(int), st>>>(a);
-    else if constexpr (!FUSE && !TABLE && UMAX == 2) {
+    if (masked) {
+        if (a.flat_slabs == 3)
+            ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 3>
+                <<<grid, block, (size_t)a.num_experts * 2 * sizeof(int), st>>>(a);
+        else if (a.flat_slabs == 0)
+            ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0>
+                <<<grid, block, (size_t)a.num_experts * sizeof(int), st>>>(a);
+        else
+            return hipErrorInvalidValue;
+    } else if constexpr (!FUSE && !TABLE && UMAX == 2) {
         if (a.flat_slabs == 1)
             ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 1><<<grid, block, 0, st>>>(a);
         else if (a.flat_slabs == 2) {

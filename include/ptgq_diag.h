@@ -108,8 +108,9 @@ PTGQ_API int ptgq_diag_fastdiv(uint32_t d, const uint32_t *n, uint32_t *q, int64
  *        (0/1), uncapped grid (0/1), flat-slab tasks (0 none; 1 the tensor's
  *        whole-row slabs taken as one sequence, tasks crossing row ends; 2
  *        slabs of several rows shorter than a slab; 3 slabs of the flattened
- *        tensor, for other rows that are not whole slabs, fused included); all zero when
- *        nothing would be launched.
+ *        tensor, for other rows that are not whole slabs, fused included;
+ *        masked calls: 0, or 3 for slabs of each expert's flattened live
+ *        rows); all zero when nothing would be launched.
  * Returns PTGQ_OK, PTGQ_EINVAL (invalid shape, cus < 1, out NULL) or
  * PTGQ_EUNSUPPORTED, as the calls would for the same shape.
  */
@@ -136,9 +137,11 @@ PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, i
  * capped: resident blocks loop over the tasks; 1 uncapped: one wave per
  * task), 7 two-slab tasks of unfused flat calls whose K is a multiple of 512
  * (0 row tasks; 1 flat-slab tasks, which cross row ends; automatic: flat-slab
- * tasks for an odd number of slabs per row) and the slabs of 16-bit rows that
- * are not whole slabs (0 row tasks; otherwise automatic: multi-row or
- * flattened slabs).
+ * tasks for an odd number of slabs per row) and the slabs of rows that are
+ * not whole slabs (0 row tasks; otherwise automatic: multi-row or flattened
+ * slabs); masked calls: 0 row tasks, 1 flattened slabs of each expert's live
+ * rows, automatic: those for rows that are not whole slabs and for unfused
+ * rows of an odd number of slabs.
  * Results never depend on these; only speed does. Not synchronized with calls
  * running on other host threads. Returns PTGQ_OK or PTGQ_EINVAL.
  */

@@ -79,6 +79,34 @@ def test_masked_workload_sized_by_expected_rows():
     assert plan("bf16", 384, 7168, E=32)["uncapped"] == 0
 
 
+@pytest.mark.parametrize("K", [640, 1408, 1152, 384, 128, 2944])
+def test_masked_rows_not_whole_slabs_take_flattened_slabs(K):
+    # each expert's live rows are one sequence of slabs: the expected task
+    # count is per expert, rounded up to whole tasks
+    for fuse in (False, True):
+        for E, exp_m in ((32, 300), (3, 5), (80, 0)):
+            p = plan("bf16", 384, K, fuse=fuse, E=E, expected_m=exp_m)
+            hint = exp_m if exp_m > 0 else 384
+            per = p["slabs_per_task"] * SLAB
+            assert p["flat_slabs"] == 3 and p["tasks_per_row"] == 1 and p["uncapped"] == 0
+            assert p["tasks"] == E * (-(-hint * K // per))
+    # two-slab tasks once the expected slabs pass half a wave per slot (unfused)
+    assert plan("bf16", 384, 1408, E=32, expected_m=300)["slabs_per_task"] == 2
+    assert plan("bf16", 384, 1408, E=3, expected_m=5)["slabs_per_task"] == 1
+    # unfused rows of an odd number of whole slabs too; fused ones, and rows
+    # of an even number, keep row tasks unless the slab-sequence knob forces
+    # flattened slabs
+    assert plan("bf16", 384, 1536, E=32)["flat_slabs"] == 3
+    assert plan("fp16", 384, 512, E=32)["flat_slabs"] == 3
+    assert plan("bf16", 384, 1536, fuse=True, E=32)["flat_slabs"] == 0
+    assert plan("bf16", 384, 2048, E=32)["flat_slabs"] == 0
+    aq.ptgq_set_tuning(7, 1)
+    assert plan("bf16", 384, 1536, fuse=True, E=32)["flat_slabs"] == 3
+    assert plan("bf16", 384, 2048, E=32)["flat_slabs"] == 3
+    aq.ptgq_set_tuning(7, 0)
+    assert plan("bf16", 384, K, E=32)["flat_slabs"] == 0
+
+
 @pytest.mark.parametrize("K", [7168, 4096, 14336, 2048, 1024])
 def test_fp32_input_uncapped_and_xcd_chunked_for_every_row_length(K):
     p = plan("fp32", 8192 * 7168 // K, K)

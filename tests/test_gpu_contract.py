@@ -16,7 +16,7 @@ import torch
 import activation_quantization_amd as aq
 import oracle
 import workloads as W
-from gpu_util import DEV, Guarded, compare, run_flat, run_per_token, to_dev
+from gpu_util import DEV, Guarded, compare, run_flat, run_masked, run_per_token, to_dev
 
 pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -246,6 +246,94 @@ def test_flattened_slabs_padded_codes():
     rq, rs = oracle.ptgq(x, "bf16", M, K, G, False, "e4m3", "ue8m0", "col", eps=1e-10)
     compare("flattened slabs padded", qh[:M], s.host(), rq, rs)
     assert np.all(qh[M:] == 0)
+
+
+def masked_case(E, T, K, G, fuse, in_dtype, mm, exp_m, seed, out_dtype, fmt, layout):
+    gen = {"bf16": W.normal_bf16, "fp16": W.normal_fp16, "fp32": W.normal_f32}[in_dtype]
+    x = gen(seed, (E, T, 2 * K if fuse else K))
+    gq, gs = run_masked(x, in_dtype, E, T, K, G, fuse, mm, exp_m, out_dtype, fmt, layout)
+    sb = aq.ptgq_scale_bytes(T, K, G, fmt, layout)
+    rq, rs = oracle.ptgq_masked(x, in_dtype, E, T, K, G, fuse, mm, out_dtype, fmt, layout,
+                                q_init=np.full((E, T, K), 0x7F, np.uint8),
+                                s_init=np.full(E * sb, 0xFF, np.uint8))
+    compare(f"masked flattened slabs E={E} T={T} K={K} G={G} {in_dtype} fuse={fuse} "
+            f"expected_m={exp_m} {out_dtype} {fmt} {layout} masked_m={list(mm)}", gq, gs, rq, rs)
+
+
+@pytest.mark.parametrize("E,T,K,G,in_dtype", [
+    (5, 45, 640, 64, "bf16"),       # one-slab tasks, partial packed words
+    (65, 30, 1408, 128, "bf16"),    # prefix sums in LDS
+    (7, 33, 384, 128, "fp16"),      # rows shorter than a slab, not dividing it
+    (6, 50, 128, 32, "bf16"),       # rows dividing the slab
+    (4, 21, 1152, 128, "fp32"),
+])
+def test_masked_flattened_slabs(E, T, K, G, in_dtype):
+    """Masked layout, rows that are not whole slabs: each expert's live rows
+    are one flattened sequence of slabs whose tasks stop at the expert's end;
+    fused lanes read their own rows' gate and up halves.  One- and two-slab
+    tasks, the SiLU table and the direct evaluation, masked_m below 0, 0,
+    tokens_pad and past it; rows past masked_m keep their sentinels."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(E * 1000 + K)
+    mm = rng.integers(-3, T + 4, E).astype(np.int32)
+    mm[0], mm[-1] = T, 0
+    fuses = (False,) if in_dtype == "fp32" else (False, True)
+    try:
+        for fuse in fuses:
+            for U, table in ((1, -1), (2, 0), (1, 1)):
+                if table == 1 and not (fuse and in_dtype == "bf16"):
+                    continue
+                aq.ptgq_set_tuning(0, U)
+                aq.ptgq_set_tuning(4, table)
+                p = aq.ptgq_plan_group(in_dtype, E, T, K, G, fuse, 0, T, cus)
+                assert p["flat_slabs"] == 3 and p["slabs_per_task"] == U
+                masked_case(E, T, K, G, fuse, in_dtype, mm, 0, 50 + U + table + fuse,
+                            "e4m3", "ue8m0", "col")
+                masked_case(E, T, K, G, fuse, in_dtype, mm, 7, 60 + U + table + fuse,
+                            "int8", "f32", "row")
+    finally:
+        aq.ptgq_set_tuning(0, -1)
+        aq.ptgq_set_tuning(4, -1)
+
+
+@pytest.mark.parametrize("fuse", [False, True])
+def test_masked_flattened_slabs_large(fuse):
+    """Masked flattened slabs at a size where the chooser itself takes
+    two-slab tasks (unfused) or the SiLU table (fused): 32 experts of up to
+    384 rows of 1408."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    E, T, K = 32, 384, 1408
+    rng = np.random.default_rng(1408)
+    mm = rng.integers(0, T + 1, E).astype(np.int32)
+    mm[3], mm[9] = T, 0
+    p = aq.ptgq_plan_group("bf16", E, T, K, 128, fuse, int(mm.mean()), T, cus)
+    assert p["flat_slabs"] == 3
+    assert (p["silu_table"], p["slabs_per_task"]) == ((1, 1) if fuse else (0, 2))
+    masked_case(E, T, K, 128, fuse, "bf16", mm, int(mm.mean()), 1408 + fuse, "e4m3", "ue8m0",
+                "col")
+
+
+@pytest.mark.parametrize("K", [1536, 2048])
+def test_masked_flattened_slabs_whole_slab_rows(K):
+    """Masked rows of whole slabs: unfused rows of an odd number of slabs take
+    flattened slabs by themselves, the others when the slab-sequence knob
+    forces them."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    E, T = 9, 40
+    mm = np.array([40, 0, 13, 41, -1, 7, 40, 1, 39], np.int32)
+    try:
+        for knob in (-1, 1):
+            aq.ptgq_set_tuning(7, knob)
+            for fuse in (False, True):
+                natural = not fuse and (K // 512) % 2 == 1
+                want = 3 if natural or knob == 1 else 0
+                assert aq.ptgq_plan_group("bf16", E, T, K, 128, fuse, 0, T, cus)[
+                    "flat_slabs"] == want
+                if want == 3:
+                    masked_case(E, T, K, 128, fuse, "bf16", mm, 0, K + fuse, "e4m3", "ue8m0",
+                                "col")
+    finally:
+        aq.ptgq_set_tuning(7, -1)
 
 
 def test_multi_row_slabs_padded_codes():
