@@ -319,12 +319,61 @@ __device__ __forceinline__ uint2 narrow8(const float (&v)[8])
 }
 
 // --------------------------------------------------------------------------
-// SiLU lookup for bf16 gates.  s(g) = g / (1 + exp_cr(-g)) depends on the 16
-// bits of g only.  Outside |g| in [2^-25, 2^7) it has a closed form that the
-// IEEE steps reach exactly: |g| < 2^-25 gives e^-g rounded to 1, so s = g/2;
-// g >= 2^7 gives e^-g rounded to 0, so s = g; g <= -2^7 gives e^-g = +inf, so
-// s = -0.  The 2 x 32 binades in between (8192 values) are tabulated by the
-// direct evaluation above, on the device, once per device.
+// Direct SiLU for 16-bit gates: s(g) = g / (1 + e), e = e^-g correctly
+// rounded to fp32, the add and the quotient correctly rounded fp32 steps.
+//
+// e: Cody and Waite's reduction -g = k ln 2 + r (ln 2 split into a 32-bit
+// head and a tail, so k * head is exact; |r| <= ln 2 / 2), the Taylor
+// polynomial of e^r of degree 9 by Horner's rule, all fp64 FMAs, scaled by
+// 2^k and rounded once to fp32.  For each of the 128 768 finite bf16 and
+// fp16 gates its relative error (at most 2^-36.6) is smaller than the
+// distance of e^-g from the nearest fp32 rounding midpoint, so the rounding
+// is the correct one (established by simulating these fp64 steps on the host
+// against a 64-bit-mantissa e^-g for every gate; the device probe compares
+// every gate against the oracle).  Gates outside [-100, 120] are clamped to
+// it: e^-g then rounds to +inf (g < -88.73) or to 0 (g > 103.98) either way.
+//
+// The quotient: g times the reciprocal of d in fp64 (the hardware
+// reciprocal, about 2^-24.4 relative error, then one Newton step, which
+// squares it), rounded to fp32.  The fp64 product is within 2^-48.5 of
+// g / d, and over all gates no quotient that is not itself an fp32 value
+// lies within 2^-48 of an fp32 midpoint, so the rounding equals the IEEE
+// fp32 division (also checked for every gate by the probe).  d = +inf (g < -88.73): the
+// reciprocal is 0 and the Newton term NaN, which the max turns into -1, so
+// s = g * 0 = -0, the IEEE quotient.
+// --------------------------------------------------------------------------
+
+__device__ __forceinline__ float silu_s(float g)
+{
+    const float gc = __builtin_amdgcn_fmed3f(g, -100.0f, 120.0f);
+    const double x = -(double)gc;
+    const double k = __builtin_rint(x * 0x1.71547652b82fep+0);       // x / ln 2
+    double r = __builtin_fma(-k, 0x1.62e42fee00000p-1, x);           // ln 2, head
+    r = __builtin_fma(-k, 0x1.a39ef35793c76p-33, r);                  // ln 2, tail
+    double p = 0x1.71de3a556c734p-19;                                 // 1/9!
+    p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-16);                   // 1/8!
+    p = __builtin_fma(p, r, 0x1.a01a01a01a01ap-13);                   // 1/7!
+    p = __builtin_fma(p, r, 0x1.6c16c16c16c17p-10);                   // 1/6!
+    p = __builtin_fma(p, r, 0x1.1111111111111p-7);                    // 1/5!
+    p = __builtin_fma(p, r, 0x1.5555555555555p-5);                    // 1/4!
+    p = __builtin_fma(p, r, 0x1.5555555555555p-3);                    // 1/3!
+    p = __builtin_fma(p, r, 0.5);
+    p = __builtin_fma(p, r, 1.0);
+    p = __builtin_fma(p, r, 1.0);
+    const float e = (float)__builtin_ldexp(p, (int)k);
+    const double d = (double)(1.0f + e);
+    const double y0 = __builtin_amdgcn_rcp(d);
+    const double t = __builtin_fmax(__builtin_fma(-d, y0, 1.0), -1.0);
+    return (float)((double)g * __builtin_fma(y0, t, y0));
+}
+
+// --------------------------------------------------------------------------
+// SiLU lookup for bf16 gates.  s(g) depends on the 16 bits of g only.
+// Outside |g| in [2^-25, 2^7) it has a closed form that the IEEE steps reach
+// exactly: |g| < 2^-25 gives e^-g rounded to 1, so s = g/2; g >= 2^7 gives
+// e^-g rounded to 0, so s = g; g <= -2^7 gives e^-g = +inf, so s = -0.  The
+// 2 x 32 binades in between (8192 values) are tabulated by the direct
+// evaluation above, on the device, once per device.
 // --------------------------------------------------------------------------
 
 constexpr uint32_t kTabElo = 127 - 25;   // biased exponent of 2^-25
@@ -333,13 +382,6 @@ constexpr uint32_t kTabNE = kTabEhi - kTabElo + 1;
 constexpr int kSiluTab = 2 * kTabNE * 128;   // 8192 floats = 32 KiB
 
 __device__ float g_silu_table[kSiluTab];
-
-__device__ __forceinline__ float silu_s(float g)
-{
-    const float e = (float)exp(-(double)g);
-    const float d = 1.0f + e;
-    return g / d;
-}
 
 __global__ __launch_bounds__(256) void silu_table_init_kernel()
 {

@@ -30,8 +30,9 @@ extern "C" {
  *   uint8 [n]; both 4-byte aligned.
  * ptgq_probe_silu_mul: out[i] = silu(g[i]) * u[i] in fp32, where g, u are
  *   device arrays of in_dtype (PTGQ_BF16 or PTGQ_FP16) bit patterns [n]
- *   and out is device float [n].  path 0: the direct evaluation (e^-g in
- *   double precision rounded to fp32, then fp32 add, divide, multiply);
+ *   and out is device float [n].  path 0: the direct evaluation (e^-g
+ *   correctly rounded to fp32 from an fp64 polynomial, the fp32 add, the
+ *   quotient from an fp64 reciprocal rounded to fp32, the fp32 multiply);
  *   path 1 (bf16 only): the lookup of g / (1 + e^-g) that large fused calls
  *   use, followed by the multiply.
  * Errors: PTGQ_EINVAL (n < 0, NULL pointer, bad dtype or path), PTGQ_ELAUNCH,
