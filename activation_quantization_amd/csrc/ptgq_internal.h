@@ -17,8 +17,9 @@ enum : int { LAYOUT_ROW = 0, LAYOUT_COL = 1 };
 // consecutive slabs of one row; the last task of a row may run past its end
 // (those lanes read zeros and store nothing).
 constexpr int kSlab = 512;
+constexpr int kChunk = 128;   // output elements of a chunk task (fused calls of few slabs)
 constexpr int kMaxSlabsPerTask = 2;
-// Masked calls keep a prefix sum of E ints in LDS.
+// Masked calls keep a prefix sum of E ints in LDS (2 E with flattened slabs).
 constexpr int kMaxExperts = 4096;
 
 // Exact unsigned division by a divisor fixed on the host (Granlund and
@@ -84,8 +85,11 @@ struct GroupArgs {
                               // 3: any other K % kSlab != 0: slabs of kSlab
                               // consecutive elements of the flattened output
                               // (fused: of the flattened gate and up halves).
-                              // Masked: 0 or 3, each expert's live rows taken
-                              // as one such sequence (no task crosses experts)
+                              // 4 (fused, direct SiLU): chunk tasks of kChunk
+                              // output elements of a row, spr = tpr = chunks
+                              // per row.  Masked: 0 or 3, each expert's live
+                              // rows taken as one such sequence (no task
+                              // crosses experts)
     int64_t n_slabs;          // flat_slabs: slabs of the sequence
     FastDiv spr_div;          // flat_slabs: division by spr
     int32_t fs_row;           // flat_slabs: elements per row of the slab sequence

@@ -593,6 +593,60 @@ __device__ __forceinline__ void flat_group_scale(const GroupArgs &a, uint8_t *se
     }
 }
 
+// Fused calls of a few slabs, which are latency-bound: one wave per chunk of
+// kChunk output elements of a row, two per lane, so that the SiLU work of a
+// wave, its critical path, is a quarter of a slab's and spreads over four
+// times as many waves.  Task t is chunk t % tpr of row t / tpr (a row's last
+// chunk may be short: G divides K).  A group is G/2 adjacent lanes; its
+// leader stores the scale into the layout's slot.
+template <int IN, int G, int OUT, int SF>
+__device__ __forceinline__ void run_chunk_tasks(const GroupArgs &a, int first, int n, int stride,
+                                                int lane)
+{
+    constexpr int LPG = G / 2;                           // lanes per group (8..64)
+    constexpr bool ue8m0 = SF == SCALE_UE8M0;
+    constexpr int pol = kStreamPolicy;
+    static_assert(IN != IN_FP32, "fused calls take 16-bit inputs");
+    const uint32_t K = (uint32_t)a.K;
+    for (int t = first; t < n; t += stride) {
+        const uint32_t m = fastdiv((uint32_t)t, a.spr_div);
+        const uint32_t c0 = ((uint32_t)t - m * (uint32_t)a.spr) * (uint32_t)kChunk;
+        const uint32_t cnt = K - c0 < (uint32_t)kChunk ? K - c0 : (uint32_t)kChunk;
+        const char *xr = static_cast<const char *>(a.x) + (uint64_t)m * a.in_stride + c0 * 2;
+        const uint32_t wg =
+            __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(xr, cnt * 2), lane * 4, 0, pol);
+        const uint32_t wu = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(xr + K * 2, cnt * 2),
+                                                                 lane * 4, 0, pol);
+        float y[2];
+        if constexpr (IN == IN_BF16) {
+            y[0] = silu_s(__uint_as_float(wg << 16)) * __uint_as_float(wu << 16);
+            y[1] = silu_s(__uint_as_float(wg & 0xFFFF0000u)) *
+                   __uint_as_float(wu & 0xFFFF0000u);
+        } else {
+            y[0] = silu_s(fp16_to_f32(wg)) * fp16_to_f32(wu);
+            y[1] = silu_s(fp16_to_f32(wg >> 16)) * fp16_to_f32(wu >> 16);
+        }
+        uint32_t amax = __float_as_uint(
+            __builtin_elementwise_maximum(__builtin_fabsf(y[0]), __builtin_fabsf(y[1])));
+        if constexpr (LPG == 64)
+            amax = wave_max_bits(amax);
+        else
+            amax = cluster_max_bits<LPG>(amax);
+        const Scale sc = group_scale<OUT>(amax, __float_as_uint(a.eps), ue8m0);
+        float v[2];
+        scale_by<ue8m0 ? MUL_PLAIN : MUL_CHECK>(y, sc.inv, v);
+        const float v4[4] = {v[0], v[1], 0.0f, 0.0f};
+        const uint32_t codes = narrow4<OUT, !ue8m0>(v4);
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)codes,
+                                              make_rsrc(a.q + (uint64_t)m * K + c0, cnt),
+                                              lane * 2, 0, pol);
+        const uint32_t col = c0 + (uint32_t)lane * 2;
+        if (lane % LPG == 0 && col < K)
+            flat_group_scale<ue8m0>(a, static_cast<uint8_t *>(a.s), m * (uint32_t)a.ng + col / G,
+                                    sc);
+    }
+}
+
 // One slab of fp32 input: lane l holds elements 4l..4l+3 (half A, `ga`) and
 // 256+4l..256+4l+3 (half B, `gb`) of the slab, so a group of G elements is
 // held by G/4 adjacent lanes of one half and every lane derives two scales.
@@ -1261,7 +1315,8 @@ __device__ __forceinline__ int logical_block(int b, int nb, int chunk = 0)
     return (b - r) + (r & 7) * chunk + (r >> 3);
 }
 
-// FS: flat-slab tasks (FlatSlabMap) instead of row tasks (FlatMap).
+// FS: flat-slab tasks (FlatSlabMap) instead of row tasks (FlatMap); 4: chunk
+// tasks (fused calls of few slabs).
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int FS>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs a)
 {
@@ -1272,7 +1327,10 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     const int wpb = TABLE ? kTableLanes / 64 : a.wpb;
     const int lb = logical_block(blockIdx.x, gridDim.x, a.xcd_chunk);
     constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
-    if constexpr (FS) {
+    if constexpr (FS == 4) {
+        static_assert(FUSE && !TABLE && UMAX == 1, "chunk tasks: fused, direct SiLU");
+        run_chunk_tasks<IN, G, OUT, SF>(a, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane);
+    } else if constexpr (FS) {
         static_assert(FS == 3 || (!FUSE && !TABLE), "flat-slab tasks: unfused inputs");
         static_assert(FS != 2 || IN != IN_FP32, "multi-row slabs: 16-bit inputs");
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true, false, FS>(
@@ -2273,7 +2331,10 @@ static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid,
     } else if constexpr (FUSE) {
         if (a.flat_slabs == 3)
             ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 3><<<grid, block, 0, st>>>(a);
-        else if (a.flat_slabs == 0)
+        else if (a.flat_slabs == 4) {
+            if constexpr (TABLE || UMAX != 1) return hipErrorInvalidValue;
+            else ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 4><<<grid, block, 0, st>>>(a);
+        } else if (a.flat_slabs == 0)
             ptgq_flat_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0><<<grid, block, 0, st>>>(a);
         else
             return hipErrorInvalidValue;

@@ -110,6 +110,8 @@ PTGQ_API int ptgq_diag_fastdiv(uint32_t d, const uint32_t *n, uint32_t *q, int64
  *        whole-row slabs taken as one sequence, tasks crossing row ends; 2
  *        slabs of several rows shorter than a slab; 3 slabs of the flattened
  *        tensor, for other rows that are not whole slabs, fused included;
+ *        4 chunk tasks of 128 output elements of a row, for small fused
+ *        calls on the direct SiLU path, tasks per row then counting chunks;
  *        masked calls: 0, or 3 for slabs of each expert's flattened live
  *        rows); all zero when nothing would be launched.
  * Returns PTGQ_OK, PTGQ_EINVAL (invalid shape, cus < 1, out NULL) or
@@ -142,7 +144,9 @@ PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, i
  * not whole slabs (0 row tasks; otherwise automatic: multi-row or flattened
  * slabs); masked calls: 0 row tasks, 1 flattened slabs of each expert's live
  * rows, automatic: those for rows that are not whole slabs and for unfused
- * rows of an odd number of slabs.
+ * rows of an odd number of slabs; fused flat calls: 0 slab tasks, 2 chunk
+ * tasks whenever the SiLU table is not read, automatic: chunk tasks for
+ * small calls (knob 0 set also selects slab tasks).
  * Results never depend on these; only speed does. Not synchronized with calls
  * running on other host threads. Returns PTGQ_OK or PTGQ_EINVAL.
  */

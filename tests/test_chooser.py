@@ -79,6 +79,25 @@ def test_masked_workload_sized_by_expected_rows():
     assert plan("bf16", 384, 7168, E=32)["uncapped"] == 0
 
 
+def test_small_fused_calls_take_chunk_tasks():
+    # up to 8 chunk tasks of 128 output elements per CU, on the direct SiLU path
+    p = plan("bf16", 64, 4096, fuse=True)
+    assert p["flat_slabs"] == 4 and p["tasks"] == 64 * 32 and p["tasks_per_row"] == 32
+    assert p["uncapped"] == 1 and p["grid"] * p["block"] // 64 >= p["tasks"]
+    assert plan("bf16", 65, 4096, fuse=True)["flat_slabs"] == 0
+    assert plan("fp16", 1, 4160, G=64, fuse=True)["tasks_per_row"] == 33  # a short last chunk
+    assert plan("bf16", 64, 4096)["flat_slabs"] == 0                       # unfused: never
+    aq.ptgq_set_tuning(0, 1)                      # slab tasks forced
+    assert plan("bf16", 64, 4096, fuse=True)["flat_slabs"] == 0
+    aq.ptgq_set_tuning(0, -1)
+    aq.ptgq_set_tuning(7, 0)
+    assert plan("bf16", 64, 4096, fuse=True)["flat_slabs"] == 0
+    aq.ptgq_set_tuning(7, 2)                      # forced; the table still wins unless off
+    assert plan("bf16", 1000, 4096, fuse=True)["silu_table"] == 1
+    aq.ptgq_set_tuning(4, 0)
+    assert plan("bf16", 1000, 4096, fuse=True)["flat_slabs"] == 4
+
+
 @pytest.mark.parametrize("K", [640, 1408, 1152, 384, 128, 2944])
 def test_masked_rows_not_whole_slabs_take_flattened_slabs(K):
     # each expert's live rows are one sequence of slabs: the expected task
@@ -199,11 +218,17 @@ def test_rules_hold_for_random_shapes(cus):
         spr = -(-K // SLAB)
         U = p["slabs_per_task"]
         assert U in (1, 2)
-        if p["flat_slabs"] >= 2:
+        if p["flat_slabs"] == 4:
+            assert p["tasks_per_row"] == -(-K // 128)
+        elif p["flat_slabs"] >= 2:
             assert p["tasks_per_row"] == 1
         else:
             assert p["tasks_per_row"] == -(-spr // U)
-        if p["flat_slabs"] == 3:
+        if p["flat_slabs"] == 4:
+            # chunk tasks: fused calls of fewer slabs than SIMDs, direct SiLU
+            assert fuse and U == 1 and not p["silu_table"] and rows * -(-K // 128) <= cus * 8
+            assert p["tasks"] == rows * -(-K // 128) and p["uncapped"]
+        elif p["flat_slabs"] == 3:
             assert K % SLAB != 0 and (fuse or U == 2)
             assert fuse or dt == "fp32" or not (K < SLAB and SLAB % K == 0)
             assert p["tasks"] == -(-(-(-(rows * K) // SLAB)) // U)
@@ -222,7 +247,7 @@ def test_rules_hold_for_random_shapes(cus):
         waves = p["grid"] * p["block"] // 64
         if p["uncapped"]:
             assert waves >= p["tasks"]                  # one wave per task
-            assert not fuse and U == 2
+            assert (not fuse and U == 2) or p["flat_slabs"] == 4
         elif waves < p["tasks"]:
             assert p["grid"] % cus == 0                 # looping grids: equal blocks per CU
         if p["xcd_chunk"]:

@@ -196,17 +196,78 @@ def test_flattened_slabs_fused(K, G):
     and the direct evaluation (small), fp16 (direct); a last slab ending
     inside the tensor."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for in_dtype, M in (("bf16", -(-(cus * 16 * 512) // K) + 3), ("bf16", 37),
-                        ("fp16", -(-(cus * 4 * 512) // K) + 1)):
-        p = aq.ptgq_plan_group(in_dtype, 0, M, K, G, True, 0, M, cus)
-        assert p["flat_slabs"] == 3
-        x = (W.normal_bf16(M * 3 + K, (M, 2 * K)) if in_dtype == "bf16"
-             else W.normal_fp16(M * 3 + K, (M, 2 * K)))
-        for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row")):
-            args = (x, in_dtype, M, K, G, True, out_dtype, fmt, layout)
-            compare(f"flattened slabs fused {in_dtype} M={M} K={K} G={G} table={p['silu_table']} "
-                    f"{out_dtype} {fmt} {layout}", *run_flat(*args),
-                    *oracle.ptgq(*args, eps=1e-10))
+    try:
+        for in_dtype, M in (("bf16", -(-(cus * 16 * 512) // K) + 3), ("bf16", 37),
+                            ("fp16", -(-(cus * 4 * 512) // K) + 1)):
+            # a small call takes chunk tasks unless slab tasks are forced
+            aq.ptgq_set_tuning(0, 1 if M == 37 else -1)
+            p = aq.ptgq_plan_group(in_dtype, 0, M, K, G, True, 0, M, cus)
+            assert p["flat_slabs"] == 3
+            x = (W.normal_bf16(M * 3 + K, (M, 2 * K)) if in_dtype == "bf16"
+                 else W.normal_fp16(M * 3 + K, (M, 2 * K)))
+            for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row")):
+                args = (x, in_dtype, M, K, G, True, out_dtype, fmt, layout)
+                compare(f"flattened slabs fused {in_dtype} M={M} K={K} G={G} "
+                        f"table={p['silu_table']} {out_dtype} {fmt} {layout}", *run_flat(*args),
+                        *oracle.ptgq(*args, eps=1e-10))
+    finally:
+        aq.ptgq_set_tuning(0, -1)
+
+
+@pytest.mark.parametrize("K,Gs", [(4096, (128, 64)), (640, (128, 32)), (1408, (64, 16)),
+                                  (4160, (64, 32)), (48, (16,)), (192, (64, 32))])
+def test_chunk_tasks_of_small_fused_calls(K, Gs):
+    """Fused calls of fewer slabs than SIMDs run one wave per 128 output
+    elements of a row, two per lane: groups of 8 to 64 lanes (the whole wave
+    at G = 128), a short last chunk when 128 does not divide K, packed
+    column-major words from several waves, every format and layout."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for in_dtype in ("bf16", "fp16"):
+        for M in (1, 2, 7, 37):
+            x = (W.normal_bf16(M * 7 + K, (M, 2 * K), factor_cols=[1, K + 2], factor=30.0)
+                 if in_dtype == "bf16" else W.normal_fp16(M * 7 + K, (M, 2 * K)))
+            x[M // 2, : min(K, 64)] = 0
+            for G in Gs:
+                p = aq.ptgq_plan_group(in_dtype, 0, M, K, G, True, 0, M, cus)
+                assert p["flat_slabs"] == 4 and p["tasks"] == M * -(-K // 128)
+                for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row"),
+                                               ("e4m3", "f32", "col"), ("int8", "ue8m0", "row")):
+                    args = (x, in_dtype, M, K, G, True, out_dtype, fmt, layout)
+                    compare(f"chunk tasks {in_dtype} M={M} K={K} G={G} {out_dtype} {fmt} "
+                            f"{layout}", *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
+
+
+def test_chunk_tasks_forced_and_padded():
+    """Chunk tasks forced at a size that would take the SiLU table, and with
+    a padded code buffer: rows past M and the column-major pad slots are zero."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    try:
+        aq.ptgq_set_tuning(7, 2)
+        aq.ptgq_set_tuning(4, 0)
+        M, K, G = 1203, 4096, 128
+        assert aq.ptgq_plan_group("bf16", 0, M, K, G, True, 0, M, cus)["flat_slabs"] == 4
+        x = W.normal_bf16(1203, (M, 2 * K))
+        args = (x, "bf16", M, K, G, True, "e4m3", "ue8m0", "col")
+        compare("chunk tasks forced", *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
+    finally:
+        aq.ptgq_set_tuning(7, -1)
+        aq.ptgq_set_tuning(4, -1)
+    M, K, G = 5, 640, 128                          # 5 groups: a partial packed word
+    q_rows = M + 6
+    x = W.normal_bf16(55, (M, 2 * K))
+    assert aq.ptgq_plan_group("bf16", 0, M, K, G, True, 0, q_rows, cus)["flat_slabs"] == 4
+    q = Guarded((q_rows, K), torch.uint8, 0xCD)
+    sb = aq.ptgq_scale_bytes(M, K, G, "ue8m0", "col")
+    s = Guarded((sb,), torch.uint8, 0xCD)
+    aq.ptgq_quant_padded(to_dev(x), "bf16", M, K, G, True, "e4m3", "ue8m0", "col", 1e-10, q.t,
+                         q_rows, s.t)
+    torch.cuda.synchronize()
+    q.check("padded q")
+    s.check("padded s")
+    qh = q.host()
+    rq, rs = oracle.ptgq(x, "bf16", M, K, G, True, "e4m3", "ue8m0", "col", eps=1e-10)
+    compare("chunk tasks padded", qh[:M], s.host(), rq, rs)
+    assert np.all(qh[M:] == 0)
 
 
 @pytest.mark.parametrize("K", [16, 64, 256])
