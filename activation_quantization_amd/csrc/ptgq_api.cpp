@@ -440,6 +440,21 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
             if (E * rows * (int64_t)a.tpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
             tasks = hint * a.tpr * E;
         }
+        // Small fused calls on the direct SiLU path: chunk tasks, as for flat
+        // calls, over the expected live rows.
+        const int64_t cpr = (K + kChunk - 1) / kChunk;
+        const bool chunks = fuse && !geo.table && knob(KNOB_FLAT_SLABS) != 0 &&
+                            knob(KNOB_SLABS_PER_TASK) <= 0 && rows * a.ng < ((int64_t)1 << 31) &&
+                            (knob(KNOB_FLAT_SLABS) == 2 || hint * E * cpr <= (int64_t)cus * 8);
+        if (chunks) {
+            if (E * rows * cpr >= INT32_MAX) return PTGQ_EUNSUPPORTED;
+            geo.U = a.U = 1;
+            a.flat_slabs = 4;
+            a.spr = a.tpr = (int32_t)cpr;
+            a.spr_div = make_fastdiv((uint32_t)cpr);
+            a.ng_div = make_fastdiv((uint32_t)a.ng);
+            tasks = hint * cpr * E;
+        }
         geo.flat_slabs = a.flat_slabs != 0;
         choose_blocks(geo, tasks, cus, fuse != 0, es, false);
         a.n_tasks = (int32_t)tasks;          // expected; set on the device

@@ -596,12 +596,39 @@ __device__ __forceinline__ void flat_group_scale(const GroupArgs &a, uint8_t *se
 // Fused calls of a few slabs, which are latency-bound: one wave per chunk of
 // kChunk output elements of a row, two per lane, so that the SiLU work of a
 // wave, its critical path, is a quarter of a slab's and spreads over four
-// times as many waves.  Task t is chunk t % tpr of row t / tpr (a row's last
-// chunk may be short: G divides K).  A group is G/2 adjacent lanes; its
-// leader stores the scale into the layout's slot.
-template <int IN, int G, int OUT, int SF>
-__device__ __forceinline__ void run_chunk_tasks(const GroupArgs &a, int first, int n, int stride,
-                                                int lane)
+// times as many waves.  A row has tpr chunks, the last one possibly short (G
+// divides K).  A group is G/2 adjacent lanes; its leader stores the scale
+// into the layout's slot.
+// A chunk task's row: its input row (gate half first), its code row, the
+// scale tensor it writes, its row index m in that tensor, and the chunk's
+// first column.
+struct ChunkLoc {
+    const char *xr;
+    uint8_t *qr;
+    uint8_t *s;
+    uint32_t m;
+    uint32_t c0;
+};
+
+// Flat schedule: task t is chunk t % tpr of row t / tpr (spr = tpr).
+struct FlatChunkMap {
+    __device__ __forceinline__ ChunkLoc operator()(const GroupArgs &a, int t, int /*lane*/)
+    {
+        const uint32_t m = fastdiv((uint32_t)t, a.spr_div);
+        const uint32_t c0 = ((uint32_t)t - m * (uint32_t)a.spr) * (uint32_t)kChunk;
+        ChunkLoc l;
+        l.xr = static_cast<const char *>(a.x) + (uint64_t)m * a.in_stride;
+        l.qr = a.q + (uint64_t)m * a.K;
+        l.s = static_cast<uint8_t *>(a.s);
+        l.m = m;
+        l.c0 = c0;
+        return l;
+    }
+};
+
+template <int IN, int G, int OUT, int SF, class Map>
+__device__ __forceinline__ void run_chunk_tasks(const GroupArgs &a, Map map, int first, int n,
+                                                int stride, int lane)
 {
     constexpr int LPG = G / 2;                           // lanes per group (8..64)
     constexpr bool ue8m0 = SF == SCALE_UE8M0;
@@ -609,10 +636,10 @@ __device__ __forceinline__ void run_chunk_tasks(const GroupArgs &a, int first, i
     static_assert(IN != IN_FP32, "fused calls take 16-bit inputs");
     const uint32_t K = (uint32_t)a.K;
     for (int t = first; t < n; t += stride) {
-        const uint32_t m = fastdiv((uint32_t)t, a.spr_div);
-        const uint32_t c0 = ((uint32_t)t - m * (uint32_t)a.spr) * (uint32_t)kChunk;
+        const ChunkLoc l = map(a, t, lane);
+        const uint32_t c0 = l.c0;
         const uint32_t cnt = K - c0 < (uint32_t)kChunk ? K - c0 : (uint32_t)kChunk;
-        const char *xr = static_cast<const char *>(a.x) + (uint64_t)m * a.in_stride + c0 * 2;
+        const char *xr = l.xr + c0 * 2;
         const uint32_t wg =
             __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(xr, cnt * 2), lane * 4, 0, pol);
         const uint32_t wu = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(xr + K * 2, cnt * 2),
@@ -637,13 +664,11 @@ __device__ __forceinline__ void run_chunk_tasks(const GroupArgs &a, int first, i
         scale_by<ue8m0 ? MUL_PLAIN : MUL_CHECK>(y, sc.inv, v);
         const float v4[4] = {v[0], v[1], 0.0f, 0.0f};
         const uint32_t codes = narrow4<OUT, !ue8m0>(v4);
-        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)codes,
-                                              make_rsrc(a.q + (uint64_t)m * K + c0, cnt),
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)codes, make_rsrc(l.qr + c0, cnt),
                                               lane * 2, 0, pol);
         const uint32_t col = c0 + (uint32_t)lane * 2;
         if (lane % LPG == 0 && col < K)
-            flat_group_scale<ue8m0>(a, static_cast<uint8_t *>(a.s), m * (uint32_t)a.ng + col / G,
-                                    sc);
+            flat_group_scale<ue8m0>(a, l.s, l.m * (uint32_t)a.ng + col / G, sc);
     }
 }
 
@@ -1165,6 +1190,30 @@ struct MaskedMap {
         return masked_loc<IN, UMAX>(a, e, r, t - R * a.tpr);
     }
 };
+// Masked schedule in chunk tasks: task t is chunk t % tpr of live row t / tpr.
+struct MaskedChunkMap {
+    MaskedRows rows;
+
+    __device__ __forceinline__ MaskedChunkMap(const int *scan, int E, int lane)
+        : rows(scan, E, lane) {}
+    __device__ __forceinline__ MaskedChunkMap(int win, int E, int lane) : rows(win, E, lane) {}
+
+    __device__ __forceinline__ ChunkLoc operator()(const GroupArgs &a, int t, int lane)
+    {
+        const uint32_t R = fastdiv((uint32_t)t, a.spr_div);
+        int e, r;
+        rows.locate((int)R, lane, e, r);
+        ChunkLoc l;
+        l.xr = static_cast<const char *>(a.x) + (int64_t)e * a.x_expert_stride +
+               (int64_t)r * a.in_stride;
+        l.qr = a.q + (int64_t)e * a.q_expert_stride + (int64_t)r * a.K;
+        l.s = static_cast<uint8_t *>(a.s) + (int64_t)e * a.s_expert_stride;
+        l.m = (uint32_t)r;
+        l.c0 = ((uint32_t)t - R * (uint32_t)a.spr) * (uint32_t)kChunk;
+        return l;
+    }
+};
+
 // Masked schedule in flattened slabs (rows whose length is not a multiple of
 // the slab): expert e's live rows are one sequence of live_e * K codes, cut
 // into tasks of UMAX slabs (its last task may be short; no task crosses
@@ -1329,7 +1378,8 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
     constexpr int spol = TABLE ? kTableStorePolicy : kStreamPolicy;
     if constexpr (FS == 4) {
         static_assert(FUSE && !TABLE && UMAX == 1, "chunk tasks: fused, direct SiLU");
-        run_chunk_tasks<IN, G, OUT, SF>(a, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane);
+        run_chunk_tasks<IN, G, OUT, SF>(a, FlatChunkMap{}, lb * wpb + wib, a.n_tasks,
+                                        gridDim.x * wpb, lane);
     } else if constexpr (FS) {
         static_assert(FS == 3 || (!FUSE && !TABLE), "flat-slab tasks: unfused inputs");
         static_assert(FS != 2 || IN != IN_FP32, "multi-row slabs: 16-bit inputs");
@@ -1366,8 +1416,8 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
 // tokens_pad]) is summed into a prefix sum (in each wave's registers for E <=
 // 64, else by wave 0 into LDS), and the grid walks the live rows of all
 // experts as one task space (FS 3: the flattened slabs of each expert's live
-// rows).  Rows at or past masked_m are never read or written.  Dynamic LDS: E
-// ints (FS 3: 2 E).
+// rows; FS 4: chunk tasks of the live rows).  Rows at or past masked_m are
+// never read or written.  Dynamic LDS: E ints (FS 3: 2 E).
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int FS>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupArgs a)
 {
@@ -1391,7 +1441,12 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
         table_fetch<TABLE>(tr);
         __builtin_amdgcn_sched_barrier(0);   // keep both loads ahead of the wait
         const int live = lane < E ? (raw < 0 ? 0 : (raw > a.rows ? (int)a.rows : raw)) : 0;
-        if constexpr (FS == 3) {
+        if constexpr (FS == 4) {
+            const int win = wave_inclusive_sum(live, lane);
+            const int n = __builtin_amdgcn_readlane(win, E - 1) * a.tpr;
+            run_chunk_tasks<IN, G, OUT, SF>(a, MaskedChunkMap(win, E, lane), lb * wpb + wib, n,
+                                            gridDim.x * wpb, lane);
+        } else if constexpr (FS == 3) {
             const int win = wave_inclusive_sum(slab_tasks<UMAX>(live, (uint32_t)a.K), lane);
             const int n = __builtin_amdgcn_readlane(win, E - 1);
             run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, true, true, FS>(
@@ -1418,7 +1473,12 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
     }
     if constexpr (TABLE) table_store<TABLE>(tr, tab);
     else __syncthreads();
-    if constexpr (FS == 3) {
+    if constexpr (FS == 4) {
+        const int n = scan[E - 1] * a.tpr;
+        if (lb * wpb >= n) return;                // block-uniform: nothing to do
+        run_chunk_tasks<IN, G, OUT, SF>(a, MaskedChunkMap(scan, E, lane), lb * wpb + wib, n,
+                                        gridDim.x * wpb, lane);
+    } else if constexpr (FS == 3) {
         const int n = scan[E - 1];
         if (lb * wpb >= n) return;                // block-uniform: nothing to do
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, kStreamPolicy, false, false, FS>(
@@ -2311,7 +2371,12 @@ static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid,
         if (a.flat_slabs == 3)
             ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 3>
                 <<<grid, block, (size_t)a.num_experts * 2 * sizeof(int), st>>>(a);
-        else if (a.flat_slabs == 0)
+        else if (a.flat_slabs == 4) {
+            if constexpr (!FUSE || TABLE || UMAX != 1) return hipErrorInvalidValue;
+            else
+                ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 4>
+                    <<<grid, block, (size_t)a.num_experts * sizeof(int), st>>>(a);
+        } else if (a.flat_slabs == 0)
             ptgq_masked_kernel<IN, G, FUSE, OUT, SF, UMAX, TABLE, 0>
                 <<<grid, block, (size_t)a.num_experts * sizeof(int), st>>>(a);
         else

@@ -79,6 +79,15 @@ def test_masked_workload_sized_by_expected_rows():
     assert plan("bf16", 384, 7168, E=32)["uncapped"] == 0
 
 
+def test_small_masked_fused_calls_take_chunk_tasks():
+    # decode-sized masked calls: chunk tasks over the expected live rows
+    p = plan("bf16", 384, 2048, fuse=True, E=32, expected_m=4)
+    assert p["flat_slabs"] == 4 and p["tasks"] == 32 * 4 * 16 and p["tasks_per_row"] == 16
+    assert plan("bf16", 384, 2048, fuse=True, E=32, expected_m=5)["flat_slabs"] == 0
+    assert plan("bf16", 384, 2048, E=32, expected_m=1)["flat_slabs"] == 0     # unfused
+    assert plan("bf16", 384, 2048, fuse=True, E=32)["flat_slabs"] == 0        # all rows expected
+
+
 def test_small_fused_calls_take_chunk_tasks():
     # up to 8 chunk tasks of 128 output elements per CU, on the direct SiLU path
     p = plan("bf16", 64, 4096, fuse=True)
@@ -106,6 +115,10 @@ def test_masked_rows_not_whole_slabs_take_flattened_slabs(K):
         for E, exp_m in ((32, 300), (3, 5), (80, 0)):
             p = plan("bf16", 384, K, fuse=fuse, E=E, expected_m=exp_m)
             hint = exp_m if exp_m > 0 else 384
+            if fuse and hint * E * -(-K // 128) <= CUS * 8:
+                # small fused calls: chunk tasks of the live rows
+                assert p["flat_slabs"] == 4 and p["tasks"] == hint * E * -(-K // 128)
+                continue
             per = p["slabs_per_task"] * SLAB
             assert p["flat_slabs"] == 3 and p["tasks_per_row"] == 1 and p["uncapped"] == 0
             assert p["tasks"] == E * (-(-hint * K // per))

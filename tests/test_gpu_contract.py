@@ -237,6 +237,25 @@ def test_chunk_tasks_of_small_fused_calls(K, Gs):
                             f"{layout}", *run_flat(*args), *oracle.ptgq(*args, eps=1e-10))
 
 
+@pytest.mark.parametrize("E,T,K,G", [(32, 384, 2048, 128), (5, 40, 640, 32), (70, 12, 1408, 64),
+                                     (3, 9, 48, 16)])
+def test_masked_chunk_tasks(E, T, K, G):
+    """Decode-sized masked fused calls run chunk tasks over the live rows,
+    with the prefix sum in registers (E <= 64) or in LDS (E = 70); live rows
+    beyond the expected count make the waves loop; rows past masked_m keep
+    their sentinels."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.default_rng(E * 100 + K)
+    exp_m = 1
+    assert aq.ptgq_plan_group("bf16", E, T, K, G, True, exp_m, T, cus)["flat_slabs"] == 4
+    for mm in (np.ones(E, np.int32), rng.integers(-2, 5, E).astype(np.int32),
+               rng.integers(0, T + 3, E).astype(np.int32)):
+        for in_dtype in ("bf16", "fp16"):
+            for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row")):
+                masked_case(E, T, K, G, True, in_dtype, mm, exp_m, int(mm.sum()) + K,
+                            out_dtype, fmt, layout)
+
+
 def test_chunk_tasks_forced_and_padded():
     """Chunk tasks forced at a size that would take the SiLU table, and with
     a padded code buffer: rows past M and the column-major pad slots are zero."""
