@@ -266,12 +266,15 @@ def fused_calls(torch, aq, W):
     return d3, s3, c3, f3
 
 
-def masked_calls(torch, aq, W):
+def masked_calls(torch, aq, W, masked_m=None):
     """Masked MoE layout, bf16 [32, 384, 2*2048] fused, the seeded masked_m of
-    the workload, UE8M0 column-major scales per expert, over rotated buffer
-    sets.  Returns the workload, the calls, the algorithmic bytes (live rows
-    only, plus masked_m) and the live row count."""
-    d4 = W.cfg4()
+    the workload (or `masked_m`, e.g. one live row per expert as in decoding),
+    UE8M0 column-major scales per expert, over rotated buffer sets.  Returns
+    the workload (with the masked_m used), the calls, the algorithmic bytes
+    (live rows only, plus masked_m) and the live row count."""
+    d4 = dict(W.cfg4())
+    if masked_m is not None:
+        d4["masked_m"] = np.asarray(masked_m, dtype=np.int32)
     E, T, K4, mm = d4["E"], d4["T"], d4["K"], d4["masked_m"]
     live = int(np.clip(mm, 0, T).sum())
     f4 = live * (2 * K4 * 2 + K4 + K4 // 128) + 4 * E
@@ -728,6 +731,17 @@ def main():
                          s40[e * sb4:(e + 1) * sb4], np.arange(int(np.clip(mm[e], 0, T))))
             for e in (0, 1, 7, E - 1) if int(np.clip(mm[e], 0, T)) > 0])
         del c4
+        # the same layout at one live row per expert (decoding): the waves
+        # walk the 32 live rows only, never the 384-row padding
+        d4d, c4d, f4d, live_d = masked_calls(torch, aq, W, masked_m=np.ones(32, np.int32))
+        variants["masked_E32_T384_K2048_fused_1token"] = dict(variant_entry(timer, c4d, f4d),
+                                                              live_rows=live_d)
+        q4d, s4d = c4d[0].__defaults__[1], c4d[0].__defaults__[2]
+        checks["masked_E32_T384_K2048_fused_1token"] = merge_checks([
+            capture_flat(d4d["x"][e], "bf16", T, K4, 128, True, "e4m3", "ue8m0", "col", q4d[e],
+                         s4d[e * sb4:(e + 1) * sb4], np.arange(1))
+            for e in (0, 1, 7, E - 1)])
+        del c4d
         # fp16 [8192, 3584] -> int8, fp32 row-major scales, G = 128; per-token e4m3
         d5 = W.cfg5()
         f5 = alg_bytes_flat(8192, 3584, 128, 2, False, 4)
