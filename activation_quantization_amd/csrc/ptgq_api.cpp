@@ -24,9 +24,9 @@ namespace {
 // ----------------------------------------------------------------- devices
 //
 // Per-device state: the compute-unit count (queried once it succeeds; a
-// failed query is not remembered) and the SiLU lookup table of the fused bf16
-// kernels, a file-scope device array filled by one small kernel.  The table
-// is built stream-ordered on the stream of the first call that needs it and
+// failed query is not remembered) and the SiLU lookup tables of the fused
+// kernels (bf16 and fp16 gates), file-scope device arrays filled by one small
+// kernel.  The tables are built stream-ordered on the stream of the first call that needs it and
 // an event is recorded after the build; later calls on other streams wait for
 // that event on the device (hipStreamWaitEvent), and once the event has
 // completed the table is ready for every stream.  No call synchronizes the
@@ -150,7 +150,7 @@ int check_group_args(const void *x, int in_dtype, int fuse, int64_t outer, int64
 struct GroupGeom {
     int U;          // slabs per task
     int wpb;        // waves per block
-    bool table;     // fused bf16: LDS SiLU table (16-wave blocks)
+    bool table;     // fused 16-bit gates: LDS SiLU table (16-wave blocks)
     bool uncapped;  // one wave per task (no grid-stride loop)
     bool flat_slabs = false;  // flat-slab tasks (set before choose_blocks)
     bool fp32 = false;        // fp32 input
@@ -160,6 +160,7 @@ struct GroupGeom {
 
 constexpr int kTableWaves = 16;       // 1024-thread blocks stage the 32 KiB table once
 constexpr int kTableBlocksPerCu = 1;  // one table block of 16 waves per CU
+constexpr int kTable16SlabsPerCu = 32;
 
 // Loads in flight per CU that saturate HBM for this 2:1 read/write stream
 // (measured on MI355X: 48-64 KiB per CU, with every wave holding the next
@@ -171,8 +172,8 @@ constexpr int64_t kDequantXcdChunk = 16;
 constexpr int64_t kTokenXcdChunk = 32;      // per-token block mode, blocks per XCD chunk
 
 // Slabs per task (1 or 2) and the SiLU path, for `slabs` slabs of work in
-// total.  Fused bf16 work large enough to amortize staging the 32 KiB table in
-// LDS reads the table.  Few slabs (decode-sized M): one slab per task so the
+// total.  Fused work large enough to amortize staging the SiLU table in LDS
+// (32 KiB for bf16 gates, 144 KiB for fp16) reads the table.  Few slabs (decode-sized M): one slab per task so the
 // work spreads over as many waves and CUs as possible.  Many: two slabs per
 // task for the plain and direct-SiLU kernels when a row has an even number of
 // slabs (no task runs past a row), when the call takes flat-slab tasks, or
@@ -187,17 +188,21 @@ constexpr int64_t kTokenXcdChunk = 32;      // per-token block mode, blocks per 
 // slab (measured on MI355X, fp16 rows of 3, 5 and 7 slabs: 2-10 % faster than
 // capped one-slab tasks; one-slab rows stay one-slab).  `table_ok`: the SiLU
 // lookup table may be read (it is built and ordered before the call).
-void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, bool bf16, bool flat16,
+void choose_task(GroupGeom &g, int64_t slabs, int32_t spr, bool fuse, int in_dtype, bool flat16,
                  bool flat_slabs, bool table_ok, int cus)
 {
     const int64_t wave_slots = (int64_t)cus * 4 * 8;   // 8 waves per SIMD
-    // The table from one slab per wave of the table grid on (16 per CU):
-    // measured on MI355X, fused bf16 [M, 2 * 4096], the table against the
-    // direct evaluation: M = 512 4.71 against 4.89 us, M = 1024 6.29 against
-    // 7.66, M = 1536 7.98 against 11.02; M = 256 (8 slabs per CU) 4.30
-    // against 3.68.
-    g.table = fuse && bf16 && slabs >= (int64_t)cus * kTableWaves;
-    if (fuse && bf16 && knob(KNOB_SILU_TABLE) >= 0) g.table = knob(KNOB_SILU_TABLE) > 0;
+    // The bf16 table from one slab per wave of the table grid on (16 per
+    // CU): measured on MI355X, fused bf16 [M, 2 * 4096], the table against
+    // the direct evaluation: M = 512 4.71 against 4.89 us, M = 1024 6.29
+    // against 7.66, M = 1536 7.98 against 11.02; M = 256 (8 slabs per CU)
+    // 4.30 against 3.68.  The fp16 table, 4.5 times larger, from
+    // kTable16SlabsPerCu slabs per CU.
+    const bool tab16 = in_dtype == PTGQ_FP16;
+    const bool gate16 = in_dtype == PTGQ_BF16 || tab16;
+    g.table = fuse && gate16 &&
+              slabs >= (int64_t)cus * (tab16 ? kTable16SlabsPerCu : kTableWaves);
+    if (fuse && gate16 && knob(KNOB_SILU_TABLE) >= 0) g.table = knob(KNOB_SILU_TABLE) > 0;
     if (!table_ok) g.table = false;
     // Table kernels (16 waves per CU) run one-slab tasks: measured 6-8 % faster
     // than two-slab tasks for the fused flat and masked workloads.
@@ -297,7 +302,6 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
     a.spr = (int32_t)((K + kSlab - 1) / kSlab);
     a.scale_fmt = scale_fmt;
     a.scale_layout = scale_layout;
-    const bool bf16 = in_dtype == PTGQ_BF16;
 
     if (!masked) {
         // Flat-slab tasks for rows of an odd number of whole slabs (measured
@@ -330,7 +334,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
                             knob(KNOB_FLAT_SLABS) != 0);
         const int64_t seq_slabs =
             mr_ok || fg_ok || fgf_ok ? (rows * K + kSlab - 1) / kSlab : rows * (int64_t)a.spr;
-        choose_task(geo, seq_slabs, a.spr, fuse != 0, bf16, !fuse && es == 2, fs_ok, table_ok,
+        choose_task(geo, seq_slabs, a.spr, fuse != 0, in_dtype, !fuse && es == 2, fs_ok, table_ok,
                     cus);
         // Small fused calls on the direct SiLU path: chunk tasks of kChunk
         // elements, so that each wave's SiLU work, which bounds these
@@ -403,6 +407,9 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // tokens_pad rows of every expert when unknown); more live rows than
         // expected only make each wave loop longer.
         if (E > kMaxExperts) return PTGQ_EUNSUPPORTED;
+        // The fp16 table (144 KiB of LDS) beside the prefix sum's 2 E ints
+        // fits the 160 KiB of a workgroup up to 2048 experts.
+        if (in_dtype == PTGQ_FP16 && E > 2048) table_ok = false;
         const int64_t hint = std::max<int64_t>(
             (expected_m > 0 && expected_m < rows) ? expected_m : rows, 1);
         // Rows that are not whole slabs, and unfused rows of an odd number of
@@ -421,7 +428,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
                           knob(KNOB_FLAT_SLABS) > 0);
         int64_t tasks;
         if (mfg) {
-            choose_task(geo, (hint * K + kSlab - 1) / kSlab * E, 1, fuse != 0, bf16, false, true,
+            choose_task(geo, (hint * K + kSlab - 1) / kSlab * E, 1, fuse != 0, in_dtype, false, true,
                         table_ok, cus);
             a.U = geo.U;
             const int64_t per = (int64_t)a.U * kSlab;
@@ -433,7 +440,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
             a.k_div = make_fastdiv((uint32_t)K);
             tasks = (hint * K + per - 1) / per * E;
         } else {
-            choose_task(geo, hint * a.spr * E, a.spr, fuse != 0, bf16, false, false, table_ok,
+            choose_task(geo, hint * a.spr * E, a.spr, fuse != 0, in_dtype, false, false, table_ok,
                         cus);
             a.U = geo.U;
             a.tpr = (a.spr + a.U - 1) / a.U;
@@ -894,7 +901,7 @@ int ptgq_probe_silu_mul(const void *g, const void *u, int in_dtype, int path, fl
                         int64_t n, void *stream)
 {
     if (in_dtype != PTGQ_BF16 && in_dtype != PTGQ_FP16) return PTGQ_EINVAL;
-    if (path != 0 && !(path == 1 && in_dtype == PTGQ_BF16)) return PTGQ_EINVAL;
+    if (path != 0 && path != 1) return PTGQ_EINVAL;
     if (n < 0) return PTGQ_EINVAL;
     if (n == 0) return PTGQ_OK;
     if (!g || !u || !out) return PTGQ_EINVAL;

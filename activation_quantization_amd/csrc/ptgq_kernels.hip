@@ -383,6 +383,25 @@ constexpr int kSiluTab = 2 * kTabNE * 128;   // 8192 floats = 32 KiB
 
 __device__ float g_silu_table[kSiluTab];
 
+// SiLU lookup for fp16 gates: magnitudes below 8 (bit patterns below 0x4800:
+// the subnormals and the 17 binades 2^-14 .. 2^2), both signs, 36 864
+// values (144 KiB), tabulated by the direct evaluation; the entry of gate h
+// is (h & 0x7FFF) + (sign ? 0x4800 : 0).  Larger gates, rare in activations,
+// are evaluated directly.
+constexpr uint32_t kTab16Mag = 0x4800;
+constexpr int kSiluTab16 = 2 * (int)kTab16Mag;   // 36864 floats = 144 KiB
+
+__device__ float g_silu_table16[kSiluTab16];
+
+// Floats of the lookup table of a gate type.
+template <int IN>
+constexpr int table_floats()
+{
+    return IN == IN_BF16 ? kSiluTab : kSiluTab16;
+}
+
+// Both tables: threads [0, kSiluTab) the bf16 one, the next kSiluTab16 the
+// fp16 one.
 __global__ __launch_bounds__(256) void silu_table_init_kernel()
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -391,6 +410,10 @@ __global__ __launch_bounds__(256) void silu_table_init_kernel()
         const uint32_t E = kTabElo + ((uint32_t)i / 128) % kTabNE;
         const uint32_t h = (sign << 15) | (E << 7) | ((uint32_t)i & 127u);
         g_silu_table[i] = silu_s(__uint_as_float(h << 16));
+    } else if (i < kSiluTab + kSiluTab16) {
+        const uint32_t j = (uint32_t)(i - kSiluTab);
+        const uint32_t h = ((j / kTab16Mag) << 15) | (j % kTab16Mag);
+        g_silu_table16[j] = silu_s(fp16_to_f32(h));
     }
 }
 
@@ -434,6 +457,24 @@ __device__ __forceinline__ void silu_pair_offsets(uint32_t w, uint32_t &off_lo, 
 __device__ __forceinline__ float lds_f32_at(const float *tab, uint32_t byte_off)
 {
     return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(tab) + byte_off);
+}
+
+// Two fp16 gates packed in a dword -> byte offsets of their fp16-table
+// entries, each magnitude first clamped into the table (packed u16 min) so
+// that every offset lies inside it; `in_range` says whether both gates are
+// tabulated.  The two entry indices stay below 2^16, so they are formed on
+// the whole dword without a carry crossing the halves.
+__device__ __forceinline__ void silu16_pair_offsets(uint32_t w, uint32_t &off_lo,
+                                                    uint32_t &off_hi, bool &in_range)
+{
+    const uint32_t mag = w & 0x7FFF7FFFu;
+    const u16x2 top = {(unsigned short)(kTab16Mag - 1), (unsigned short)(kTab16Mag - 1)};
+    const uint32_t c = __builtin_bit_cast(
+        uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, mag), top));
+    in_range = c == mag;
+    const uint32_t idx = c + ((w >> 15) & 0x00010001u) * kTab16Mag;
+    off_lo = (idx & 0xFFFFu) << 2;
+    off_hi = (idx >> 16) << 2;
 }
 
 // --------------------------------------------------------------------------
@@ -813,16 +854,30 @@ __device__ __forceinline__ void process_task(const GroupArgs &a, const TaskLoc &
             uint32_t off[8];
             bool in[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) silu_pair_offsets(ww[k], off[2 * k], off[2 * k + 1], in[k]);
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (IN == IN_BF16)
+                    silu_pair_offsets(ww[k], off[2 * k], off[2 * k + 1], in[k]);
+                else
+                    silu16_pair_offsets(ww[k], off[2 * k], off[2 * k + 1], in[k]);
+            }
             if (__all(in[0] && in[1] && in[2] && in[3])) {
                 // every gate of the wave is tabulated: plain lookups
 #pragma unroll
                 for (int k = 0; k < 8; ++k) y[k] = lds_f32_at(tab, off[k]) * u[k];
-            } else {
+            } else if constexpr (IN == IN_BF16) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     y[2 * k] = silu_s_lookup(ww[k] & 0xFFFFu, tab) * u[2 * k];
                     y[2 * k + 1] = silu_s_lookup(ww[k] >> 16, tab) * u[2 * k + 1];
+                }
+            } else {
+                // fp16 gates of magnitude 8 or more: the direct evaluation
+                // (the clamped offsets keep every lookup inside the table)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t h = (k & 1) ? ww[k / 2] >> 16 : ww[k / 2] & 0xFFFFu;
+                    const float t = lds_f32_at(tab, off[k]);
+                    y[k] = ((h & 0x7FFFu) < kTab16Mag ? t : silu_s(fp16_to_f32(h))) * u[k];
                 }
             }
         } else if constexpr (IN == IN_FP32) {
@@ -1254,30 +1309,34 @@ struct MaskedSlabMap {
 // table alone (vector memory loads complete in issue order): table kernels
 // always run 1024-lane blocks, 2 float4 of the table per lane.
 constexpr int kTableLanes = 1024;
+static_assert(kSiluTab % (4 * kTableLanes) == 0 && kSiluTab16 % (4 * kTableLanes) == 0,
+              "whole float4 per lane");
+template <int IN>
 struct TableRegs {
-    float4 v[kSiluTab / 4 / kTableLanes];
+    float4 v[table_floats<IN>() / 4 / kTableLanes];   // bf16: 2, fp16: 9
 };
 
-template <bool TABLE>
-__device__ __forceinline__ void table_fetch(TableRegs &r)
+template <bool TABLE, int IN>
+__device__ __forceinline__ void table_fetch(TableRegs<IN> &r)
 {
     if constexpr (TABLE) {
-        const float4 *src = reinterpret_cast<const float4 *>(g_silu_table);
+        const float4 *src =
+            reinterpret_cast<const float4 *>(IN == IN_BF16 ? g_silu_table : g_silu_table16);
 #pragma unroll
-        for (int i = 0; i < kSiluTab / 4 / kTableLanes; ++i)
+        for (int i = 0; i < table_floats<IN>() / 4 / kTableLanes; ++i)
             r.v[i] = src[threadIdx.x + kTableLanes * i];
     }
 }
 
 // Stores the fetched table and synchronizes the block (call before any early
 // exit that is not block-uniform).
-template <bool TABLE>
-__device__ __forceinline__ void table_store(const TableRegs &r, float *tab)
+template <bool TABLE, int IN>
+__device__ __forceinline__ void table_store(const TableRegs<IN> &r, float *tab)
 {
     if constexpr (TABLE) {
         float4 *dst = reinterpret_cast<float4 *>(tab);
 #pragma unroll
-        for (int i = 0; i < kSiluTab / 4 / kTableLanes; ++i)
+        for (int i = 0; i < table_floats<IN>() / 4 / kTableLanes; ++i)
             dst[threadIdx.x + kTableLanes * i] = r.v[i];
         __syncthreads();
     }
@@ -1319,7 +1378,7 @@ template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int S
           bool STAGE, bool FETCHED = false, int FS = 0, class Map>
 __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first, int n,
                                           int stride, int lane, float *tab,
-                                          TableRegs tr = TableRegs{})
+                                          TableRegs<IN> tr = TableRegs<IN>{})
 {
     const bool hasA0 = first < n;
     TaskBuf<UMAX> A, B;
@@ -1369,7 +1428,7 @@ __device__ __forceinline__ int logical_block(int b, int nb, int chunk = 0)
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int FS>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs a)
 {
-    __shared__ float tab[TABLE ? kSiluTab : 1];
+    __shared__ float tab[TABLE ? table_floats<IN>() : 1];
     args_in_sgprs(a);
     const int lane = threadIdx.x & 63;
     const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1421,7 +1480,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
 template <int IN, int G, bool FUSE, int OUT, int SF, int UMAX, bool TABLE, int FS>
 __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupArgs a)
 {
-    __shared__ float tab[TABLE ? kSiluTab : 1];
+    __shared__ float tab[TABLE ? table_floats<IN>() : 1];
     extern __shared__ int scan[];
     args_in_sgprs(a);
     const int lane = threadIdx.x & 63;
@@ -1437,7 +1496,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
         // masked_m (never NULL here) read by every lane without a branch, so
         // that the table's loads are in flight while it arrives
         const int raw = a.masked_m[lane < E ? lane : E - 1];
-        TableRegs tr;
+        TableRegs<IN> tr;
         table_fetch<TABLE>(tr);
         __builtin_amdgcn_sched_barrier(0);   // keep both loads ahead of the wait
         const int live = lane < E ? (raw < 0 ? 0 : (raw > a.rows ? (int)a.rows : raw)) : 0;
@@ -1463,7 +1522,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_masked_kernel(GroupAr
     }
     // More experts: the table's loads, then the prefix sum of masked_m into
     // LDS (wave 0), then the table's stores, behind one barrier.
-    TableRegs tr;
+    TableRegs<IN> tr;
     table_fetch<TABLE>(tr);
     if (wib == 0) {
         if constexpr (FS == 3)
@@ -2347,7 +2406,27 @@ __global__ __launch_bounds__(256) void probe_silu_kernel(const uint16_t *__restr
             }
         } else {
             uf = fp16_to_f32(u[i]);
-            s = silu_s(fp16_to_f32(g[i]));
+            if (path == 1) {
+                // the fp16 lookup: the packed-pair offsets (gate i in either
+                // half), the table entry when the gate is tabulated, else the
+                // direct evaluation
+                const uint32_t other = g[(i + 12345) % n];
+                uint32_t lo0, hi0, lo1, hi1;
+                bool in0, in1;
+                silu16_pair_offsets((uint32_t)g[i] | (other << 16), lo0, hi0, in0);
+                silu16_pair_offsets(other | ((uint32_t)g[i] << 16), lo1, hi1, in1);
+                const bool tabulated = (g[i] & 0x7FFFu) < kTab16Mag;
+                const bool both = tabulated && (other & 0x7FFFu) < kTab16Mag;
+                if (in0 != both || in1 != both || lo0 != hi1)
+                    s = __uint_as_float(0x7FC00000u);            // NaN: never equal
+                else if (tabulated)
+                    s = lds_f32_at(g_silu_table16, lo0);
+                else
+                    s = silu_s(fp16_to_f32(g[i]));
+                (void)hi0; (void)lo1;
+            } else {
+                s = silu_s(fp16_to_f32(g[i]));
+            }
         }
         out[i] = s * uf;
     }
@@ -2359,7 +2438,8 @@ __global__ __launch_bounds__(256) void probe_silu_kernel(const uint16_t *__restr
 
 hipError_t launch_silu_table_init(hipStream_t stream)
 {
-    silu_table_init_kernel<<<kSiluTab / 256, 256, 0, stream>>>();
+    static_assert((kSiluTab + kSiluTab16) % 256 == 0, "whole blocks");
+    silu_table_init_kernel<<<(kSiluTab + kSiluTab16) / 256, 256, 0, stream>>>();
     return hipGetLastError();
 }
 
@@ -2410,12 +2490,12 @@ static hipError_t launch_group_t(const GroupArgs &a, bool masked, unsigned grid,
     return hipGetLastError();
 }
 
-// Task sizes: 1 or 2 slabs.  The LDS SiLU table exists for bf16 gates only.
+// Task sizes: 1 or 2 slabs.  The LDS SiLU tables exist for 16-bit gates.
 template <int IN, int G, bool FUSE, int OUT, int SF>
 static hipError_t launch_group_u(const GroupArgs &a, bool table, bool masked, unsigned grid,
                                  unsigned block, hipStream_t st)
 {
-    constexpr bool T = FUSE && IN == IN_BF16;
+    constexpr bool T = FUSE && IN != IN_FP32;
     if (a.U != 1 && a.U != 2) return hipErrorInvalidValue;
     if (T && table)
         return a.U == 1 ? launch_group_t<IN, G, FUSE, OUT, SF, 1, T>(a, masked, grid, block, st)
@@ -2475,7 +2555,7 @@ hipError_t launch_group(const GroupArgs &a, int in_dtype, int G, bool fuse, int 
     if (in_dtype == IN_BF16)
         return launch_group_g<IN_BF16>(a, G, fuse, out_dtype, table, masked, grid, block, stream);
     if (in_dtype == IN_FP16)
-        return launch_group_g<IN_FP16>(a, G, fuse, out_dtype, false, masked, grid, block, stream);
+        return launch_group_g<IN_FP16>(a, G, fuse, out_dtype, table, masked, grid, block, stream);
     if (in_dtype == IN_FP32)
         return launch_group_g<IN_FP32>(a, G, fuse, out_dtype, false, masked, grid, block, stream);
     return hipErrorInvalidValue;

@@ -33,8 +33,9 @@ extern "C" {
  *   and out is device float [n].  path 0: the direct evaluation (e^-g
  *   correctly rounded to fp32 from an fp64 polynomial, the fp32 add, the
  *   quotient from an fp64 reciprocal rounded to fp32, the fp32 multiply);
- *   path 1 (bf16 only): the lookup of g / (1 + e^-g) that large fused calls
- *   use, followed by the multiply.
+ *   path 1: the lookup of g / (1 + e^-g) that large fused calls use (bf16:
+ *   the closed forms outside the table; fp16: the direct evaluation for
+ *   gates of magnitude 8 or more), followed by the multiply.
  * Errors: PTGQ_EINVAL (n < 0, NULL pointer, bad dtype or path), PTGQ_ELAUNCH,
  * PTGQ_EDEVICE.
  */
@@ -131,7 +132,7 @@ PTGQ_API int ptgq_plan_group(int in_dtype, int64_t E, int64_t rows, int64_t K, i
  * per-token one-block-per-row mode: waves per row, 1..8; per-token one-wave-
  * per-row mode: rows per block, 1..4), 2 resident blocks per compute unit
  * (grid cap), 3 per-token mode (0 one wave per row, 1 one block per row, 2
- * two-pass block, 3 persistent waves walking the rows), 4 fused bf16 SiLU
+ * two-pass block, 3 persistent waves walking the rows), 4 fused SiLU
  * path (0 direct evaluation, 1 LDS lookup table), 5 blocks per XCD chunk of
  * the block-to-task mappings of the flat quantization, dequantization and
  * requantization kernels and of the per-token one-block-per-row mode (0 one

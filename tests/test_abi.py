@@ -217,7 +217,7 @@ def test_probe_validation(lib):
     assert aq.ptgq_probe_e4m3(A16, A16, -1, stream=0, check=False) == aq.PTGQ_EINVAL
     assert aq.ptgq_probe_e4m3(0, 0, 0, stream=0, check=False) == aq.PTGQ_OK
     assert aq.ptgq_probe_silu_mul(A16, A16, 2, 0, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
-    assert aq.ptgq_probe_silu_mul(A16, A16, "fp16", 1, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
+    assert aq.ptgq_probe_silu_mul(A16, A16, "fp16", 3, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
     assert aq.ptgq_probe_silu_mul(A16, A16, "bf16", 2, A16, 4, stream=0, check=False) == aq.PTGQ_EINVAL
     with pytest.raises(aq.PtgqError):
         aq.ptgq_set_tuning(9, 1)

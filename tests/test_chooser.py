@@ -65,8 +65,13 @@ def test_fused_large_call_takes_the_silu_table_one_block_per_cu():
     # from 16 slabs per CU (one per wave of the table grid) on
     assert plan("bf16", 256, 4096, fuse=True)["silu_table"] == 0
     assert plan("bf16", 512, 4096, fuse=True)["silu_table"] == 1
-    # fp16 gates never use the table
-    assert plan("fp16", 8192, 4096, fuse=True)["silu_table"] == 0
+    # fp16 gates: the 144 KiB table from 32 slabs per CU on
+    assert plan("fp16", 8192, 4096, fuse=True)["silu_table"] == 1
+    assert plan("fp16", 1023, 4096, fuse=True)["silu_table"] == 0
+    assert plan("fp16", 1024, 4096, fuse=True)["silu_table"] == 1
+    # masked: not beside the 2 E ints of a prefix sum of more than 2048 experts
+    assert plan("fp16", 384, 2048, fuse=True, E=2048)["silu_table"] == 1
+    assert plan("fp16", 384, 2048, fuse=True, E=2049)["silu_table"] == 0
 
 
 def test_masked_workload_sized_by_expected_rows():
@@ -266,7 +271,8 @@ def test_rules_hold_for_random_shapes(cus):
         if p["xcd_chunk"]:
             assert p["uncapped"] and p["grid"] >= 4 * 8 * p["xcd_chunk"]
         if p["silu_table"]:
-            assert fuse and dt == "bf16" and p["block"] == 1024
+            assert fuse and dt in ("bf16", "fp16") and p["block"] == 1024
+            assert rows * spr >= cus * (16 if dt == "bf16" else 32)
 
 
 def test_tuning_knobs_are_honoured():

@@ -256,6 +256,49 @@ def test_masked_chunk_tasks(E, T, K, G):
                             out_dtype, fmt, layout)
 
 
+def fp16_gates_with_large_values(seed, shape, K):
+    """N(0,1) fp16 [gate | up] rows whose gate columns 5 and K - 3 are scaled
+    x 40 (gates of magnitude 8 and more, outside the fp16 lookup table)."""
+    x = W.normal_fp16(seed, shape).view(np.float16).copy()
+    x[..., 5] *= np.float16(40)
+    x[..., K - 3] *= np.float16(40)
+    return x.view(np.uint16)
+
+
+@pytest.mark.parametrize("K", [4096, 1408])
+def test_fp16_silu_table_flat(K):
+    """Large fused fp16 calls read the 144 KiB fp16 SiLU table (row tasks at
+    K = 4096, flattened slabs at K = 1408); gates of magnitude 8 and more fall
+    back to the direct evaluation."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    M = -(-(cus * 32 * 512) // K) + 3
+    p = aq.ptgq_plan_group("fp16", 0, M, K, 128, True, 0, M, cus)
+    assert p["silu_table"] == 1 and p["block"] == 1024
+    x = fp16_gates_with_large_values(M + K, (M, 2 * K), K)
+    for out_dtype, fmt, layout in (("e4m3", "ue8m0", "col"), ("int8", "f32", "row")):
+        args = (x, "fp16", M, K, 128, True, out_dtype, fmt, layout)
+        compare(f"fp16 table M={M} K={K} {out_dtype} {fmt} {layout}", *run_flat(*args),
+                *oracle.ptgq(*args, eps=1e-10))
+
+
+@pytest.mark.parametrize("K", [2048, 1408])
+def test_fp16_silu_table_masked(K):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    E, T = 32, 384
+    exp_m = 128                                   # 128 x 32 rows of 3 or 4 slabs
+    assert aq.ptgq_plan_group("fp16", E, T, K, 128, True, exp_m, T, cus)["silu_table"] == 1
+    rng = np.random.default_rng(K)
+    mm = rng.integers(0, T + 1, E).astype(np.int32)
+    mm[0], mm[1] = 0, T
+    x = fp16_gates_with_large_values(K + 1, (E, T, 2 * K), K)
+    gq, gs = run_masked(x, "fp16", E, T, K, 128, True, mm, exp_m, "e4m3", "ue8m0", "col")
+    sb = aq.ptgq_scale_bytes(T, K, 128, "ue8m0", "col")
+    rq, rs = oracle.ptgq_masked(x, "fp16", E, T, K, 128, True, mm, "e4m3", "ue8m0", "col",
+                                q_init=np.full((E, T, K), 0x7F, np.uint8),
+                                s_init=np.full(E * sb, 0xFF, np.uint8))
+    compare(f"fp16 table masked K={K}", gq, gs, rq, rs)
+
+
 def test_chunk_tasks_forced_and_padded():
     """Chunk tasks forced at a size that would take the SiLU table, and with
     a padded code buffer: rows past M and the column-major pad slots are zero."""

@@ -54,7 +54,7 @@ def test_e4m3_narrowing_every_fp32_in_range():
     assert np.array_equal(got, oracle.e4m3(v))
 
 
-@pytest.mark.parametrize("in_dtype,path", [("bf16", 0), ("bf16", 1), ("fp16", 0)])
+@pytest.mark.parametrize("in_dtype,path", [("bf16", 0), ("bf16", 1), ("fp16", 0), ("fp16", 1)])
 def test_silu_mul_every_16bit_gate(in_dtype, path):
     g_bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
     gf = oracle.decode(g_bits, in_dtype)
