@@ -408,8 +408,8 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         // expected only make each wave loop longer.
         if (E > kMaxExperts) return PTGQ_EUNSUPPORTED;
         // The fp16 table (144 KiB of LDS) beside the prefix sum's 2 E ints
-        // fits the 160 KiB of a workgroup up to 2048 experts.
-        if (in_dtype == PTGQ_FP16 && E > 2048) table_ok = false;
+        // (8 KiB at 1024 experts) stays inside the 160 KiB of a workgroup.
+        if (in_dtype == PTGQ_FP16 && E > 1024) table_ok = false;
         const int64_t hint = std::max<int64_t>(
             (expected_m > 0 && expected_m < rows) ? expected_m : rows, 1);
         // Rows that are not whole slabs, and unfused rows of an odd number of

@@ -69,9 +69,9 @@ def test_fused_large_call_takes_the_silu_table_one_block_per_cu():
     assert plan("fp16", 8192, 4096, fuse=True)["silu_table"] == 1
     assert plan("fp16", 1023, 4096, fuse=True)["silu_table"] == 0
     assert plan("fp16", 1024, 4096, fuse=True)["silu_table"] == 1
-    # masked: not beside the 2 E ints of a prefix sum of more than 2048 experts
-    assert plan("fp16", 384, 2048, fuse=True, E=2048)["silu_table"] == 1
-    assert plan("fp16", 384, 2048, fuse=True, E=2049)["silu_table"] == 0
+    # masked: not beside the 2 E ints of a prefix sum of more than 1024 experts
+    assert plan("fp16", 384, 2048, fuse=True, E=1024)["silu_table"] == 1
+    assert plan("fp16", 384, 2048, fuse=True, E=1025)["silu_table"] == 0
 
 
 def test_masked_workload_sized_by_expected_rows():

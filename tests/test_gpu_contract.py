@@ -281,11 +281,14 @@ def test_fp16_silu_table_flat(K):
                 *oracle.ptgq(*args, eps=1e-10))
 
 
-@pytest.mark.parametrize("K", [2048, 1408])
-def test_fp16_silu_table_masked(K):
+@pytest.mark.parametrize("E,K", [(32, 2048), (32, 1408), (100, 2048), (100, 1408)])
+def test_fp16_silu_table_masked(E, K):
+    """Masked fused fp16 calls with the fp16 table: row tasks and flattened
+    slabs, the prefix sum in registers (32 experts) or beside the table in
+    LDS (100 experts)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    E, T = 32, 384
-    exp_m = 128                                   # 128 x 32 rows of 3 or 4 slabs
+    T = 384 if E == 32 else 64
+    exp_m = 128 if E == 32 else 48                # at least 32 slabs per CU
     assert aq.ptgq_plan_group("fp16", E, T, K, 128, True, exp_m, T, cus)["silu_table"] == 1
     rng = np.random.default_rng(K)
     mm = rng.integers(0, T + 1, E).astype(np.int32)
@@ -296,7 +299,7 @@ def test_fp16_silu_table_masked(K):
     rq, rs = oracle.ptgq_masked(x, "fp16", E, T, K, 128, True, mm, "e4m3", "ue8m0", "col",
                                 q_init=np.full((E, T, K), 0x7F, np.uint8),
                                 s_init=np.full(E * sb, 0xFF, np.uint8))
-    compare(f"fp16 table masked K={K}", gq, gs, rq, rs)
+    compare(f"fp16 table masked E={E} K={K}", gq, gs, rq, rs)
 
 
 def test_chunk_tasks_forced_and_padded():
