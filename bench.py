@@ -704,6 +704,17 @@ def main():
             checks[name] = capture_flat(d3m["x"], "bf16", M3, 4096, 128, True, "e4m3", "ue8m0",
                                         "col", s3m[0][1], s3m[0][2], spread(M3))
             del c3m, s3m
+        # the same fused call on fp16 gates and ups (N(0,1)), which reads the
+        # fp16 SiLU table
+        x3h = W.normal_fp16(3016, (8192, 2 * 4096))
+        s3h, c3h = make_flat_sets(torch, aq, x3h, 8192, 4096, 128, True, "e4m3", "ue8m0", "col",
+                                  "fp16", rotation_sets(f3))
+        variants["fused_silu_mul_fp16_M8192_K4096"] = dict(variant_entry(timer, c3h, f3),
+                                                           input_fnv1a=W.fnv1a(x3h))
+        checks["fused_silu_mul_fp16_M8192_K4096"] = capture_flat(
+            x3h, "fp16", 8192, 4096, 128, True, "e4m3", "ue8m0", "col", s3h[0][1], s3h[0][2],
+            spread(8192))
+        del c3h, s3h, x3h
         # the plain workload: bf16 [64, 2048] -> e4m3, fp32 row-major scales
         # (latency-bound), every row checked
         d1 = W.cfg1()
