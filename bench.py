@@ -21,7 +21,7 @@ dequantization error over its bound (null with --no-cpu-baseline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --profile-main   (only the headline loop, for rocprofv3)
-    python bench.py --profile-dequant / --profile-requant / --profile-fused /
+    python bench.py --profile-dequant / --profile-requant / --profile-fused [--fp16] /
                     --profile-masked / --profile-fp32 / --profile-per-token /
                     --profile-int8 [--int8-group G] / --profile-stream
                     (only that loop; --graph: the variant loops in HIP graphs)
@@ -256,13 +256,16 @@ def dequant_calls(torch, aq):
     return cd, fd, capture
 
 
-def fused_calls(torch, aq, W):
-    """Fused silu(gate)*up quantization, bf16 [8192, 2*4096] -> e4m3 [8192, 4096],
-    G = 128, UE8M0 column-major scales, over rotated buffer sets."""
-    d3 = W.cfg3(8192)
+def fused_calls(torch, aq, W, fp16=False):
+    """Fused silu(gate)*up quantization, bf16 [8192, 2*4096] -> e4m3 [8192, 4096]
+    (fp16: N(0,1) fp16 inputs of the same shape), G = 128, UE8M0 column-major
+    scales, over rotated buffer sets."""
+    d3 = dict(W.cfg3(8192))
+    if fp16:
+        d3["x"] = W.normal_fp16(3016, (8192, 2 * 4096))
     f3 = alg_bytes_flat(8192, 4096, 128, 2, True, 1)
     s3, c3 = make_flat_sets(torch, aq, d3["x"], 8192, 4096, 128, True, "e4m3", "ue8m0",
-                            "col", "bf16", rotation_sets(f3))
+                            "col", "fp16" if fp16 else "bf16", rotation_sets(f3))
     return d3, s3, c3, f3
 
 
@@ -515,6 +518,8 @@ def main():
                     help="only the no-arithmetic stream over the headline's element count")
     ap.add_argument("--int8-group", type=int, default=128, choices=[16, 32, 64, 128],
                     help="group size of the --profile-int8 loop")
+    ap.add_argument("--fp16", action="store_true",
+                    help="the --profile-fused loop on fp16 inputs")
     ap.add_argument("--graph", action="store_true",
                     help="variant profile loops: launch in HIP graphs of 200 launches")
     ap.add_argument("--tuning", action="append", default=[], metavar="KNOB=VALUE",
@@ -558,7 +563,8 @@ def main():
         elif args.profile_requant:
             name, (calls, nbytes, _) = "requant", requant_calls(torch, aq, 1024)
         elif args.profile_fused:
-            name, (_, _, calls, nbytes) = "fused", fused_calls(torch, aq, W)
+            name, (_, _, calls, nbytes) = ("fused_fp16" if args.fp16 else "fused",
+                                           fused_calls(torch, aq, W, fp16=args.fp16))
         elif args.profile_masked:
             name, (_, calls, nbytes, _) = "masked", masked_calls(torch, aq, W)
         elif args.profile_fp32:
@@ -706,15 +712,13 @@ def main():
             del c3m, s3m
         # the same fused call on fp16 gates and ups (N(0,1)), which reads the
         # fp16 SiLU table
-        x3h = W.normal_fp16(3016, (8192, 2 * 4096))
-        s3h, c3h = make_flat_sets(torch, aq, x3h, 8192, 4096, 128, True, "e4m3", "ue8m0", "col",
-                                  "fp16", rotation_sets(f3))
+        d3h, s3h, c3h, _ = fused_calls(torch, aq, W, fp16=True)
         variants["fused_silu_mul_fp16_M8192_K4096"] = dict(variant_entry(timer, c3h, f3),
-                                                           input_fnv1a=W.fnv1a(x3h))
+                                                           input_fnv1a=W.fnv1a(d3h["x"]))
         checks["fused_silu_mul_fp16_M8192_K4096"] = capture_flat(
-            x3h, "fp16", 8192, 4096, 128, True, "e4m3", "ue8m0", "col", s3h[0][1], s3h[0][2],
-            spread(8192))
-        del c3h, s3h, x3h
+            d3h["x"], "fp16", 8192, 4096, 128, True, "e4m3", "ue8m0", "col", s3h[0][1],
+            s3h[0][2], spread(8192))
+        del c3h, s3h, d3h
         # the plain workload: bf16 [64, 2048] -> e4m3, fp32 row-major scales
         # (latency-bound), every row checked
         d1 = W.cfg1()
