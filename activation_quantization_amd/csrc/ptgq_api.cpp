@@ -26,7 +26,8 @@ namespace {
 // Per-device state: the compute-unit count (queried once it succeeds; a
 // failed query is not remembered) and the SiLU lookup tables of the fused
 // kernels (bf16 and fp16 gates), file-scope device arrays filled by one small
-// kernel.  The tables are built stream-ordered on the stream of the first call that needs it and
+// kernel ("the table" below: both are built and ordered together).  The table
+// is built stream-ordered on the stream of the first call that needs it and
 // an event is recorded after the build; later calls on other streams wait for
 // that event on the device (hipStreamWaitEvent), and once the event has
 // completed the table is ready for every stream.  No call synchronizes the
@@ -158,7 +159,7 @@ struct GroupGeom {
     unsigned grid;  // blocks
 };
 
-constexpr int kTableWaves = 16;       // 1024-thread blocks stage the 32 KiB table once
+constexpr int kTableWaves = 16;       // 1024-thread blocks stage the table once
 constexpr int kTableBlocksPerCu = 1;  // one table block of 16 waves per CU
 constexpr int kTable16SlabsPerCu = 32;
 
@@ -173,8 +174,9 @@ constexpr int64_t kTokenXcdChunk = 32;      // per-token block mode, blocks per 
 
 // Slabs per task (1 or 2) and the SiLU path, for `slabs` slabs of work in
 // total.  Fused work large enough to amortize staging the SiLU table in LDS
-// (32 KiB for bf16 gates, 144 KiB for fp16) reads the table.  Few slabs (decode-sized M): one slab per task so the
-// work spreads over as many waves and CUs as possible.  Many: two slabs per
+// (32 KiB for bf16 gates, 144 KiB for fp16) reads the table.  Few slabs
+// (decode-sized M): one slab per task so the work spreads over as many waves
+// and CUs as possible.  Many: two slabs per
 // task for the plain and direct-SiLU kernels when a row has an even number of
 // slabs (no task runs past a row), when the call takes flat-slab tasks, or
 // for unfused 16-bit rows of at least 3 slabs; else one (measured best on
@@ -352,7 +354,10 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
                             (knob(KNOB_FLAT_SLABS) == 2 || chunk_tasks <= (int64_t)cus * 8);
         if (chunks) geo.U = 1;
         a.U = geo.U;
-        a.flat_slabs = chunks ? 4 : fgf_ok ? 3 : fs_ok && a.U == 2 ? (mr_ok ? 2 : fg_ok ? 3 : 1) : 0;
+        a.flat_slabs = chunks ? 4
+                       : fgf_ok ? 3
+                       : fs_ok && a.U == 2 ? (mr_ok ? 2 : fg_ok ? 3 : 1)
+                                           : 0;
         if (a.flat_slabs == 4)
             a.spr = (int32_t)((K + kChunk - 1) / kChunk);   // chunks per row
         else if (a.flat_slabs >= 2)
@@ -428,8 +433,8 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
                           knob(KNOB_FLAT_SLABS) > 0);
         int64_t tasks;
         if (mfg) {
-            choose_task(geo, (hint * K + kSlab - 1) / kSlab * E, 1, fuse != 0, in_dtype, false, true,
-                        table_ok, cus);
+            choose_task(geo, (hint * K + kSlab - 1) / kSlab * E, 1, fuse != 0, in_dtype, false,
+                        true, table_ok, cus);
             a.U = geo.U;
             const int64_t per = (int64_t)a.U * kSlab;
             if (E * ((rows * K + per - 1) / per) >= INT32_MAX) return PTGQ_EUNSUPPORTED;
