@@ -363,6 +363,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
         else if (a.flat_slabs >= 2)
             a.spr = 1;                        // the sequence's rows are its slabs
         a.tpr = (a.spr + a.U - 1) / a.U;
+        a.tpr_div = make_fastdiv((uint32_t)a.tpr);
         geo.flat_slabs = a.flat_slabs != 0;
         a.n_slabs = a.flat_slabs >= 2 ? seq_slabs : rows * (int64_t)a.spr;
         if (a.n_slabs >= INT32_MAX) return PTGQ_EUNSUPPORTED;
@@ -467,6 +468,7 @@ int plan_group(GroupArgs &a, GroupGeom &geo, int in_dtype, int64_t rows, int64_t
             a.ng_div = make_fastdiv((uint32_t)a.ng);
             tasks = hint * cpr * E;
         }
+        a.tpr_div = make_fastdiv((uint32_t)a.tpr);
         geo.flat_slabs = a.flat_slabs != 0;
         choose_blocks(geo, tasks, cus, fuse != 0, es, false);
         a.n_tasks = (int32_t)tasks;          // expected; set on the device

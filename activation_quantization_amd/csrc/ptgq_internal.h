@@ -92,6 +92,7 @@ struct GroupArgs {
                               // crosses experts)
     int64_t n_slabs;          // flat_slabs: slabs of the sequence
     FastDiv spr_div;          // flat_slabs: division by spr
+    FastDiv tpr_div;          // row and chunk tasks: division by tpr
     int32_t fs_row;           // flat_slabs: elements per row of the slab sequence
                               // (K; kSlab for multi-row slabs)
     int32_t mr_shift;         // flat_slabs == 2: log2(ng)

@@ -1017,12 +1017,22 @@ __device__ __forceinline__ TaskLoc row_task(const GroupArgs &a, const char *xrow
     return l;
 }
 
-// Flat schedule, row tasks: task t is task t % tpr of row t / tpr.
-template <int IN, int UMAX>
+// Flat schedule, row tasks: task t is task t % tpr of row t / tpr.  The
+// quotient by a multiply-high (the integer division's instruction sequence
+// lies on the path to a task's first load): measured faster for fused calls
+// (bf16 [2048, 2 * 4096] 9.46 -> 9.30 us) and one-slab tasks ([256, 7168]
+// 2.98 -> 2.82), but 2 % slower for the unfused two-slab tasks of [4096,
+// 7168] (15.40 -> 15.72, the same at M = 16384; cause not found), which keep
+// the division.
+template <int IN, int UMAX, bool FUSE>
 struct FlatMap {
     __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int /*lane*/)
     {
-        const int m = t / a.tpr;
+        int m;
+        if constexpr (FUSE || UMAX == 1)
+            m = (int)fastdiv((uint32_t)t, a.tpr_div);
+        else
+            m = t / a.tpr;
         return row_task<IN, UMAX>(a, static_cast<const char *>(a.x) + (int64_t)m * a.in_stride,
                                   a.q + (int64_t)m * a.K, static_cast<uint8_t *>(a.s), m,
                                   t - m * a.tpr);
@@ -1239,7 +1249,7 @@ struct MaskedMap {
 
     __device__ __forceinline__ TaskLoc operator()(const GroupArgs &a, int t, int lane)
     {
-        const int R = t / a.tpr;
+        const int R = (int)fastdiv((uint32_t)t, a.tpr_div);
         int e, r;
         rows.locate(R, lane, e, r);
         return masked_loc<IN, UMAX>(a, e, r, t - R * a.tpr);
@@ -1399,7 +1409,8 @@ __device__ __forceinline__ void run_tasks(const GroupArgs &a, Map map, int first
 __device__ __forceinline__ void args_in_sgprs(const GroupArgs &a)
 {
     asm volatile("" ::"s"(a.x), "s"(a.q), "s"(a.s), "s"(a.K), "s"(a.in_stride),
-                 "s"(a.n_tasks), "s"(a.tpr), "s"(a.xcd_chunk), "s"(a.n_slabs), "s"(a.spr_div.mul),
+                 "s"(a.n_tasks), "s"(a.tpr), "s"(a.tpr_div.mul), "s"(a.tpr_div.shift),
+                 "s"(a.xcd_chunk), "s"(a.n_slabs), "s"(a.spr_div.mul),
                  "s"(a.spr_div.shift), "s"(a.spr), "s"(a.wpb), "s"(a.q_pad_bytes),
                  "s"(gridDim.x));
 }
@@ -1447,7 +1458,7 @@ __global__ __launch_bounds__(TABLE ? 1024 : 256) void ptgq_flat_kernel(GroupArgs
             tab);
     } else {
         run_tasks<IN, G, FUSE, OUT, SF, UMAX, TABLE, spol, true>(
-            a, FlatMap<IN, UMAX>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
+            a, FlatMap<IN, UMAX, FUSE>{}, lb * wpb + wib, a.n_tasks, gridDim.x * wpb, lane, tab);
     }
     // code rows past M (a padded q buffer) are zero: 16 bytes per lane,
     // grid-strided over all waves
