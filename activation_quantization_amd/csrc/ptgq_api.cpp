@@ -751,6 +751,7 @@ int ptgq_requant_fp8(const uint8_t *x, int64_t E, int64_t T, int64_t K, int grou
     a.sg = scale_stride_g;
     a.s_bytes = (uint32_t)((smax + 1) * 4);
     a.inv_k = 1.0f / (float)K;
+    a.k_div = make_fastdiv((uint32_t)K);
     a.E = (int32_t)E;
     a.log2g = __builtin_ctz((unsigned)group_size);
     a.xcd_chunk = 0;
@@ -878,6 +879,10 @@ int ptgq_dequant(const uint8_t *q, int code_dtype, int64_t M, int64_t K, int gro
     a.dc = (uint32_t)(a.step % K);
     a.s_bytes = (uint32_t)s_bytes;
     a.inv_k = 1.0f / (float)K;
+    // every task's first code lies below total + 2 steps (the last round's
+    // offsets included): 32-bit offsets divide by a multiply-high
+    a.small = total + 2 * a.step < ((int64_t)1 << 31) ? 1 : 0;
+    a.k_div = make_fastdiv((uint32_t)K);
     a.ns = ns;
     a.log2g = __builtin_ctz((unsigned)group_size);
     // fp32 outputs (tasks of half as many codes) in chunks of 64 blocks:

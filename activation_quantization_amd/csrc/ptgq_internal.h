@@ -131,6 +131,7 @@ struct RequantArgs {
     int64_t tcodes;           // codes per task
     uint32_t s_bytes;         // bytes spanned by x_scale (buffer range)
     float inv_k;              // 1 / K, for the row estimate when K < a task
+    FastDiv k_div;            // division by K (code offsets within an expert, < 2^31)
     int32_t E;
     int32_t log2g;            // log2(group size)
     int32_t xcd_chunk;        // blocks per XCD chunk of the block -> task mapping (0: ranges)
@@ -158,6 +159,8 @@ struct DequantArgs {
     uint32_t dc;              // step % K
     uint32_t s_bytes;         // bytes of the scale tensor (buffer range)
     float inv_k;              // 1 / K, for the quotient estimate when K < a task
+    FastDiv k_div;            // division by K, for code offsets below 2^31
+    int32_t small;            // 1: every task's first code offset is below 2^31
     int32_t full;             // rounds of full tasks
     int32_t ns;               // sub-slabs per task: 1 or 4
     int32_t log2g;            // log2(G)
@@ -166,9 +169,9 @@ struct DequantArgs {
 
 // Launchers (defined in ptgq_kernels.hip).  They return the hipError_t of the
 // launch.  `grid`/`block` are chosen by the caller.
-// `table`: fused bf16 kernels read g / (1 + e^-g) from the LDS-staged lookup
-// table (launch with 1024-thread blocks); it must have been built on the
-// device by launch_silu_table_init and synchronized before.
+// `table`: fused kernels read g / (1 + e^-g) from their gate type's LDS-staged
+// lookup table (launch with 1024-thread blocks); the tables must have been
+// built on the device by launch_silu_table_init and ordered before.
 hipError_t launch_group(const GroupArgs &a, int in_dtype, int G, bool fuse, int out_dtype,
                         bool table, bool masked, unsigned grid, unsigned block,
                         hipStream_t stream);

@@ -1929,7 +1929,8 @@ __device__ __forceinline__ void requant_task_scan(const RequantArgs &a, int lane
             int r = a.masked_m ? a.masked_m[c + lane] : (int)a.T;
             r = r < 0 ? 0 : (r > a.T ? (int)a.T : r);
             live[c + lane] = r;
-            v = (int)(((int64_t)r * a.K + a.tcodes - 1) / a.tcodes);
+            v = (int)(((int64_t)r * a.K + a.tcodes - 1) >>
+                      __builtin_ctzll((unsigned long long)a.tcodes));   // a power of two
         }
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -1992,7 +1993,7 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(RequantArgs a)
         const int live_e = in_regs ? __builtin_amdgcn_readlane(live_lane, e) : live[e];
         const uint32_t region = (uint32_t)live_e * K;
         l.len = region - off0 < TS ? region - off0 : TS;
-        l.row0 = off0 / K;
+        l.row0 = fastdiv(off0, a.k_div);
         l.c0 = off0 - l.row0 * K;
         l.base = (int64_t)e * a.T * a.K + off0;
         l.sexp = (uint32_t)e * (uint32_t)a.se;
@@ -2170,7 +2171,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a)
         DqCursor u;
         u.i = i;
         u.e = e;
-        u.m = e / a.K;
+        u.m = a.small ? (int64_t)fastdiv((uint32_t)e, a.k_div) : e / a.K;
         u.c = (uint32_t)(e - u.m * a.K);
         return u;
     };
