@@ -1,7 +1,9 @@
-"""The entry points captured into one HIP graph and replayed: every replay,
-with new inputs and freshly filled sentinels written eagerly in between, gives
-the oracle's bytes (the calls are asynchronous, allocate nothing and never
-synchronize, so they can be captured after one ptgq_init)."""
+"""The entry points captured into one HIP graph and replayed (among them a
+small fused call in chunk tasks and a large fp16 one reading the fp16 SiLU
+table): every replay, with new inputs and freshly filled sentinels written
+eagerly in between, gives the oracle's bytes (the calls are asynchronous,
+allocate nothing and never synchronize, so they can be captured after one
+ptgq_init)."""
 import numpy as np
 import pytest
 import torch
@@ -44,6 +46,19 @@ def test_graph_replays_match_the_oracle():
     outr = torch.empty((Ed, Td, Kd), dtype=torch.uint8, device=DEV)
     yd = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
     r_strides = (Td * (Kd // 128), 1, Td)
+    Mc, Kc = 3, 640                              # fused, chunk tasks
+    xc = torch.empty((Mc, 2 * Kc), dtype=torch.int16, device=DEV)
+    qc = torch.empty((Mc, Kc), dtype=torch.uint8, device=DEV)
+    sc = torch.empty(aq.ptgq_scale_bytes(Mc, Kc, 128, "ue8m0", "col"), dtype=torch.uint8,
+                     device=DEV)
+    Mh, Kh = 1030, 4096                          # fused fp16, the fp16 SiLU table
+    xh = torch.empty((Mh, 2 * Kh), dtype=torch.int16, device=DEV)
+    qh = torch.empty((Mh, Kh), dtype=torch.uint8, device=DEV)
+    sh = torch.empty(aq.ptgq_scale_bytes(Mh, Kh, 128, "f32", "row"), dtype=torch.uint8,
+                     device=DEV)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert aq.ptgq_plan_group("bf16", 0, Mc, Kc, 128, True, 0, Mc, cus)["flat_slabs"] == 4
+    assert aq.ptgq_plan_group("fp16", 0, Mh, Kh, 128, True, 0, Mh, cus)["silu_table"] == 1
 
     def calls():
         aq.ptgq_quant_padded(xf, "bf16", M, K, G, False, "e4m3", "ue8m0", "col", 1e-10, qf, QR,
@@ -53,6 +68,8 @@ def test_graph_replays_match_the_oracle():
         aq.ptq_quant_fp8(xt, "bf16", Mt, Kt, qt, st)
         aq.ptgq_requant_fp8(xr, Ed, Td, Kd, 128, sr, r_strides, mr, 0, osr, outr)
         aq.ptgq_dequant(qf, "e4m3", M, K, G, sf, "ue8m0", "col", "bf16", yd)
+        aq.ptgq_quant(xc, "bf16", Mc, Kc, 128, True, "e4m3", "ue8m0", "col", 1e-10, qc, sc)
+        aq.ptgq_quant(xh, "fp16", Mh, Kh, 128, True, "int8", "f32", "row", 1e-10, qh, sh)
 
     def fill(seed):
         """New inputs and sentinels, written eagerly; returns host copies."""
@@ -68,6 +85,8 @@ def test_graph_replays_match_the_oracle():
         h["sr"] = rng.uniform(0.1, 4.0, Ed * Td * (Kd // 128)).astype(np.float32)
         h["mr"] = np.array([Td, 0, 7], np.int32)
         h["os"] = np.float32(rng.uniform(0.5, 3.0))
+        h["xc"] = W.normal_bf16(seed + 4, (Mc, 2 * Kc))
+        h["xh"] = W.normal_fp16(seed + 5, (Mh, 2 * Kh))
         xf.copy_(dev16(h["xf"]))
         xm.copy_(dev16(h["xm"]))
         mm.copy_(torch.from_numpy(h["mm"]))
@@ -76,7 +95,10 @@ def test_graph_replays_match_the_oracle():
         sr.copy_(torch.from_numpy(h["sr"]))
         mr.copy_(torch.from_numpy(h["mr"]))
         osr.fill_(float(h["os"]))
-        for t, v in ((qf, 0x5C), (sf, 0x5C), (qm, 0x7F), (sm, 0xFF), (qt, 0x33), (outr, 0x2C)):
+        xc.copy_(dev16(h["xc"]))
+        xh.copy_(dev16(h["xh"]))
+        for t, v in ((qf, 0x5C), (sf, 0x5C), (qm, 0x7F), (sm, 0xFF), (qt, 0x33), (outr, 0x2C),
+                     (qc, 0x5C), (sc, 0x5C), (qh, 0x5C), (sh, 0x5C)):
             t.fill_(v)
         st.fill_(float("nan"))
         yd.fill_(7.0)
@@ -103,6 +125,10 @@ def test_graph_replays_match_the_oracle():
         ry = oracle.dequant(rq, "e4m3", M, K, G, rs, "ue8m0", "col", "bf16")
         got = yd.view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(got, ry), f"{tag} dequant"
+        compare(f"{tag} fused chunk tasks", qc.cpu().numpy(), sc.cpu().numpy(),
+                *oracle.ptgq(h["xc"], "bf16", Mc, Kc, 128, True, "e4m3", "ue8m0", "col"))
+        compare(f"{tag} fused fp16 table", qh.cpu().numpy(), sh.cpu().numpy(),
+                *oracle.ptgq(h["xh"], "fp16", Mh, Kh, 128, True, "int8", "f32", "row"))
 
     # eager reference run (also makes the device ready for capture)
     h = fill(11)
