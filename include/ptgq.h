@@ -31,12 +31,13 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous on that stream and never synchronize the host, so they may
  *     be captured into a HIP graph, the first call on a device included.  The
- *     fused bf16 calls large enough to read the SiLU lookup table build it
- *     on their own stream the first time (one small kernel, stream-ordered;
- *     other streams then wait for it on the device); a call captured before
- *     the table exists evaluates SiLU directly instead (same results, slower).
+ *     fused calls large enough to read a SiLU lookup table (one for bf16
+ *     gates, 32 KiB, one for fp16 gates, 144 KiB) build both tables on their
+ *     own stream the first time (one small kernel, stream-ordered; other
+ *     streams then wait for it on the device); a call captured before the
+ *     tables exist evaluates SiLU directly instead (same results, slower).
  *     ptgq_init does that set-up ahead of time.
- *   - The library's only device memory of its own is that table; no entry
+ *   - The library's only device memory of its own is those tables; no entry
  *     point allocates or frees memory.
  *   - Arguments are validated on the host before anything is launched.  A
  *     negative return value means nothing was launched and nothing written.
@@ -270,10 +271,10 @@ PTGQ_API const char *ptgq_status_string(int status);
 
 /*
  * ptgq_init - optional: make `device` (a HIP ordinal) ready now: query its
- * compute-unit count and build its SiLU lookup table on the default stream,
+ * compute-unit count and build its SiLU lookup tables on the default stream,
  * then wait on the host until the build has finished (the one call of the
  * library that blocks the host; not to be called while a stream captures).
- * Calls captured into a HIP graph after it use the table.  A failed
+ * Calls captured into a HIP graph after it use the tables.  A failed
  * initialization is not remembered: a later call tries again.  Returns
  * PTGQ_OK or PTGQ_EDEVICE.
  */
