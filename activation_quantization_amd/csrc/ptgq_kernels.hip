@@ -328,10 +328,11 @@ __device__ __forceinline__ uint2 narrow8(const float (&v)[8])
 // 2^k and rounded once to fp32.  For each of the 128 768 finite bf16 and
 // fp16 gates its relative error (at most 2^-36.6) is smaller than the
 // distance of e^-g from the nearest fp32 rounding midpoint, so the rounding
-// is the correct one (established by simulating these fp64 steps on the host
-// against a 64-bit-mantissa e^-g for every gate; the device probe compares
-// every gate against the oracle).  Gates outside [-100, 120] are clamped to
-// it: e^-g then rounds to +inf (g < -88.73) or to 0 (g > 103.98) either way.
+// is the correct one: a host simulation of these fp64 steps gives the
+// correctly rounded e^-g for every gate (degree 8 does not), and the device
+// probe compares every gate against the oracle.  Gates outside [-100, 120]
+// are clamped to it: e^-g then rounds to +inf (g < -88.73) or to 0
+// (g > 103.98) either way.
 //
 // The quotient: g times the reciprocal of d in fp64 (the hardware
 // reciprocal, about 2^-24.4 relative error, then one Newton step, which
@@ -1317,7 +1318,8 @@ struct MaskedSlabMap {
 // The SiLU table staged into LDS in two steps, so that its global loads can
 // be issued before a wave's first task loads and its LDS stores wait for the
 // table alone (vector memory loads complete in issue order): table kernels
-// always run 1024-lane blocks, 2 float4 of the table per lane.
+// always run 1024-lane blocks, 2 (bf16 gates) or 9 (fp16) float4 of the
+// table per lane.
 constexpr int kTableLanes = 1024;
 static_assert(kSiluTab % (4 * kTableLanes) == 0 && kSiluTab16 % (4 * kTableLanes) == 0,
               "whole float4 per lane");
